@@ -1,0 +1,291 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU. The oracle is checked against hand-worked
+fixtures (tests/golden), exact rational arithmetic, closed forms of the
+quantizers on Gaussian inputs, brute force on tiny shapes and special cases
+(identity weights, keep = K, keep = 0), never against a retyped copy of itself.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.stats import norm
+
+import oracle as O
+from synth import activations_bf16, bf16_bits_to_f32, latent_weights, normal
+from tests.golden_io import arr, read_cases, scalar
+
+F32 = np.float32
+
+
+# ----------------------------------------------------------------------------- constants and sums
+def test_sqrt7_is_nearest_float32():
+    """The INT4 scale constant is the float32 nearest to sqrt(7) (exact rational bracket)."""
+    c = O.SQRT7_F32
+    lo = np.nextafter(c, F32(0))
+    hi = np.nextafter(c, F32(10))
+    mid_lo = (Fraction(float(lo)) + Fraction(float(c))) / 2
+    mid_hi = (Fraction(float(c)) + Fraction(float(hi))) / 2
+    assert mid_lo * mid_lo < 7 < mid_hi * mid_hi
+
+
+def test_exact_abs_sum_matches_rational_sum():
+    """exact_abs_sum is the correctly rounded double of the exact rational sum."""
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        n = int(rng.integers(1, 400))
+        # mantissas times wildly different powers of two: naive summation would lose bits
+        v = rng.standard_normal(n) * np.exp2(rng.integers(-60, 60, n).astype(np.float64))
+        v = v.astype(np.float32)
+        exact = sum((Fraction(float(abs(t))) for t in v), Fraction(0))
+        assert O.exact_abs_sum(v) == float(exact)      # float(Fraction) rounds correctly
+
+
+def test_roundclip_half_even_and_clip():
+    x = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 9.7, -9.7, 0.49999997])
+    assert O.roundclip(x, -8, 7).tolist() == [0, 2, 2, 0, -2, -2, 7, -8, 0]
+
+
+# ----------------------------------------------------------------------------- ternary weights
+@pytest.mark.parametrize("case", read_cases("ternary_hand.txt"))
+def test_ternary_hand_cases(case):
+    eps, w, alpha, codes = case
+    got_codes, got_alpha = O.ternarize(arr(w, np.float32), eps=scalar(eps))
+    assert got_alpha == F32(scalar(alpha))
+    np.testing.assert_array_equal(got_codes, arr(codes).astype(np.int8))
+
+
+def test_ternary_gaussian_closed_forms():
+    """For N(0, s^2) latents: alpha -> s*sqrt(2/pi) and P(code = 0) -> 2*Phi(0.5*sqrt(2/pi)) - 1 = 0.3101.
+
+    (The write-up's "roughly half become +-1" is loose; the threshold is alpha/2, which gives 69% nonzero.)
+    """
+    sigma = 0.02
+    w = latent_weights(77, 1024, 2048, sigma)
+    codes, alpha = O.ternarize(w)
+    assert abs(alpha - sigma * math.sqrt(2 / math.pi)) < 2e-5
+    p0 = 2 * norm.cdf(0.5 * math.sqrt(2 / math.pi)) - 1
+    n = codes.size
+    assert abs((codes == 0).mean() - p0) < 5 * math.sqrt(p0 * (1 - p0) / n)
+    assert set(np.unique(codes).tolist()) == {-1, 0, 1}
+    # sign symmetry
+    assert abs((codes == 1).mean() - (codes == -1).mean()) < 0.005
+
+
+def test_ternary_codes_bruteforce_against_fraction_threshold():
+    """Brute force: code = 0 iff |RN32(w/(alpha+eps))| <= 1/2, sign otherwise; alpha from exact rationals."""
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((6, 10)) * 0.05).astype(np.float32)
+    codes, alpha = O.ternarize(w, 1e-5)
+    exact_mean = sum((Fraction(float(abs(t))) for t in w.ravel()), Fraction(0)) / w.size
+    assert alpha == F32(float(exact_mean)) or abs(float(alpha) - float(exact_mean)) <= 2 ** -24 * float(exact_mean)
+    den = F32(alpha + F32(1e-5))
+    for i in range(6):
+        for j in range(10):
+            q = float(F32(w[i, j]) / den)
+            want = 0 if abs(q) <= 0.5 else (1 if q > 0 else -1)
+            assert codes[i, j] == want
+
+
+# ----------------------------------------------------------------------------- INT4
+@pytest.mark.parametrize("case", read_cases("int4_hand.txt"))
+def test_int4_hand_cases(case):
+    eps, x, beta, codes, dscale = case
+    c, d, b = O.quant_int4(arr(x, np.float32), eps=scalar(eps))
+    assert b[0] == F32(scalar(beta))
+    np.testing.assert_array_equal(c, arr(codes).astype(np.int8))
+    assert abs(float(d[0]) - scalar(dscale)) <= 1e-7 * max(1.0, scalar(dscale))
+
+
+def test_int4_gaussian_closed_forms():
+    """N(0,1) rows: beta -> sqrt(2/pi); P(c=0) = 2*Phi(t0)-1, P(c=7) = 1-Phi(6.5 b/sqrt7), P(c=-8) = Phi(-7.5 b/sqrt7).
+
+    Also the write-up's range statement: 8*beta/sqrt7 = 3.02 beta ~ 2.4 sigma covers ~98% of a Gaussian.
+    """
+    x = bf16_bits_to_f32(activations_bf16(123, 128, 4096))
+    c, d, beta = O.quant_int4(x)
+    b = math.sqrt(2 / math.pi)
+    assert abs(beta.mean() - b) < 0.005
+    step = b / math.sqrt(7)                      # one code step in units of sigma
+    n = c.size
+    p0 = 2 * norm.cdf(0.5 * step) - 1
+    p7 = 1 - norm.cdf(6.5 * step)
+    pm8 = norm.cdf(-7.5 * step)
+    for got, p in (((c == 0).mean(), p0), ((c == 7).mean(), p7), ((c == -8).mean(), pm8)):
+        assert abs(got - p) < 5 * math.sqrt(p * (1 - p) / n) + 0.002   # +bf16 discretisation slack
+    assert sorted(np.unique(c).tolist()) == list(range(-8, 8))          # exactly the 16 INT4 values
+    assert abs(8 / math.sqrt(7) - 3.02) < 0.01
+    assert abs((2 * norm.cdf(8 * step) - 1) - 0.98) < 0.01
+
+
+def test_int4_zero_row_and_scaling_invariance():
+    x = bf16_bits_to_f32(activations_bf16(9, 4, 256))
+    c1, d1, _ = O.quant_int4(x, eps=1e-30)
+    c2, d2, _ = O.quant_int4(x * F32(4.0), eps=1e-30)       # power-of-two scaling is exact
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(d2, d1 * F32(4.0))
+
+
+# ----------------------------------------------------------------------------- FP4
+@pytest.mark.parametrize("case", read_cases("fp4_hand.txt"))
+def test_fp4_hand_cases(case):
+    eps, x, nib, dbl = case
+    n, d2, ds, g = O.quant_fp4(arr(x, np.float32), eps=scalar(eps))
+    np.testing.assert_array_equal(n, arr(nib).astype(np.uint8))
+    np.testing.assert_array_equal(d2, arr(dbl).astype(np.int8))
+
+
+def test_e2m1_round_bruteforce():
+    """Nearest-value rounding against an exhaustive argmin over the 8 magnitudes (ties -> even code)."""
+    rng = np.random.default_rng(3)
+    mags = np.concatenate([rng.uniform(0, 7, 5000), np.arange(0, 6.5, 0.125)])
+    got = O.e2m1_round(mags)
+    g = O.E2M1_GRID
+    for m, i in zip(mags, got):
+        d = np.abs(g - m)
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        assert i == want, (m, i, want)
+
+
+def test_fp4_row_max_maps_to_six():
+    x = bf16_bits_to_f32(activations_bf16(31, 16, 512))
+    n, d2, ds, g = O.quant_fp4(x)
+    amax = np.abs(x).argmax(axis=1)
+    assert np.all(np.abs(d2[np.arange(16), amax]) == 12)
+    assert set(np.unique(np.abs(d2)).tolist()) <= {0, 1, 2, 3, 4, 6, 8, 12}
+
+
+# ----------------------------------------------------------------------------- Top-K + INT8
+@pytest.mark.parametrize("case", read_cases("int8_hand.txt"))
+def test_int8_hand_cases(case):
+    eps, keep, x, codes, dscale = case
+    k = int(scalar(keep))
+    c, m, d, g = O.quant_int8(arr(x, np.float32), eps=scalar(eps), keep=None if k < 0 else k)
+    np.testing.assert_array_equal(c, arr(codes).astype(np.int8))
+    assert abs(float(d[0]) - scalar(dscale)) <= 1e-7 * max(1e-3, scalar(dscale))
+
+
+def test_topk_bruteforce_pairs():
+    """Exactly keep survivors; every survivor beats every non-survivor by (|x| desc, index asc)."""
+    rng = np.random.default_rng(8)
+    # few distinct magnitudes -> many ties at the boundary
+    x = (rng.integers(-4, 5, (12, 40)) * 0.5).astype(np.float32)
+    for keep in (0, 1, 7, 20, 39, 40):
+        m = O.topk_mask(x, keep)
+        for r in range(x.shape[0]):
+            assert m[r].sum() == keep
+            a = np.abs(x[r])
+            s = np.flatnonzero(m[r])
+            ns = np.flatnonzero(~m[r])
+            for i in s:
+                for j in ns:
+                    assert a[i] > a[j] or (a[i] == a[j] and i < j)
+
+
+def test_int8_invariants_and_special_keeps():
+    x = bf16_bits_to_f32(activations_bf16(41, 32, 1024, outlier_scale=20.0, outlier_kind="t3"))
+    c, m, d, g = O.quant_int8(x)
+    assert c.min() >= -127 and c.max() <= 127                      # absmax never reaches -128
+    amax = np.abs(x).argmax(axis=1)
+    assert np.all(np.abs(c[np.arange(32), amax]) == 127)
+    cK, mK, _, _ = O.quant_int8(x, keep=1024)                      # keep = K is plain INT8 absmax
+    np.testing.assert_array_equal(cK, c)
+    c0, m0, _, _ = O.quant_int8(x, keep=0)
+    assert not c0.any() and not m0.any()
+    ch, mh, _, _ = O.quant_int8(x, keep=512)
+    assert np.all(mh.sum(axis=1) == 512)
+    np.testing.assert_array_equal(ch, np.where(mh, c, 0))          # mask-then-quantize == quantize-then-mask
+
+
+# ----------------------------------------------------------------------------- GEMM + epilogues
+def test_gemm_int_bruteforce():
+    rng = np.random.default_rng(2)
+    a = rng.integers(-128, 128, (5, 33)).astype(np.int8)
+    t = rng.integers(-1, 2, (7, 33)).astype(np.int8)
+    acc = O.gemm_int(a, t)
+    for i in range(5):
+        for j in range(7):
+            assert acc[i, j] == sum(int(a[i, k]) * int(t[j, k]) for k in range(33))
+
+
+def test_dequant_matches_float_matmul_of_dequantized_operands():
+    """y equals float64 matmul of Q_INT4(X) (dequantized) times Q_w(W)^T (dequantized)."""
+    x = bf16_bits_to_f32(activations_bf16(5, 6, 64))
+    w = latent_weights(6, 10, 64)
+    t, alpha = O.ternarize(w)
+    r = O.bitlinear_a4(x, t, alpha)
+    xq = r["codes"].astype(np.float64) * r["dscale"].astype(np.float64)[:, None]
+    wq = t.astype(np.float64) * float(alpha)
+    np.testing.assert_allclose(r["y"], xq @ wq.T, rtol=1e-12, atol=1e-300)
+
+
+def test_identity_weights_pin_layout():
+    """W = c*I ternarizes to I; then y[m, n] = dscale[m] * alpha * code[m, n] (pins transpose/layout)."""
+    K = 48
+    w = (np.eye(K) * 0.75).astype(np.float32)
+    t, alpha = O.ternarize(w)
+    np.testing.assert_array_equal(t, np.eye(K, dtype=np.int8))
+    x = bf16_bits_to_f32(activations_bf16(12, 5, K))
+    r = O.bitlinear_a4(x, t, alpha)
+    np.testing.assert_allclose(r["y"], r["codes"] * (r["dscale"][:, None].astype(np.float64) * float(alpha)),
+                               rtol=1e-15)
+    r8 = O.bitlinear_a8(x, t, alpha, keep=K // 2)
+    np.testing.assert_allclose(r8["y"], r8["codes"] * (r8["dscale"][:, None].astype(np.float64) * float(alpha)),
+                               rtol=1e-15)
+
+
+def test_fp4_gemm_counts_half_units():
+    x = bf16_bits_to_f32(activations_bf16(15, 4, 64))
+    w = latent_weights(16, 8, 64)
+    t, alpha = O.ternarize(w)
+    r = O.bitlinear_a4(x, t, alpha, fmt="fp4")
+    vals = O.E2M1_GRID[r["nibbles"] & 7] * np.where(r["nibbles"] & 8, -1.0, 1.0)
+    ref = (vals * r["dscale"].astype(np.float64)[:, None]) @ (t.astype(np.float64) * float(alpha)).T
+    np.testing.assert_allclose(r["y"], ref, rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("case", read_cases("relu2_hand.txt"))
+def test_relu2_hand_cases(case):
+    g, u, h = case
+    got = O.relu2_glu(arr(g, np.float32)[0], arr(u, np.float32)[0])
+    np.testing.assert_array_equal(got, arr(h, np.float32)[0])
+
+
+def test_ffn_composition_and_sparsity():
+    """FFN: h zero wherever the gate is <= 0 (about half for i.i.d. data); down input INT8 without Top-K."""
+    x = bf16_bits_to_f32(activations_bf16(21, 8, 256))
+    tg, ag = O.ternarize(latent_weights(22, 384, 256))
+    tu, au = O.ternarize(latent_weights(23, 384, 256))
+    td, ad = O.ternarize(latent_weights(24, 256, 384))
+    r = O.ffn_ref(x, tg, ag, tu, au, td, ad)
+    g = O.dequant_f32(r["acc_g"], r["dscale"], ag)
+    assert np.all(r["h"][g <= 0] == 0)
+    assert 0.4 < (r["h"] == 0).mean() < 0.6
+    np.testing.assert_array_equal(r["h_absmax"], np.abs(r["h"]).max(axis=1))
+    assert np.all(np.abs(r["h_codes"]).max(axis=1) == 127)
+    # down output against float64 matmul of the dequantized operands
+    hq = r["h_codes"].astype(np.float64) * r["h_dscale"].astype(np.float64)[:, None]
+    wq = td.astype(np.float64) * float(ad)
+    bound = 1e-12 * (np.abs(hq) @ np.abs(wq).T)          # cancellation-aware float64 bound
+    assert np.all(np.abs(r["y"] - hq @ wq.T) <= bound)
+
+
+def test_oproj_residual():
+    x = bf16_bits_to_f32(activations_bf16(51, 4, 128, outlier_scale=20.0, outlier_kind="t3"))
+    t, a = O.ternarize(latent_weights(52, 64, 128))
+    res = normal(53, 4 * 64).reshape(4, 64).astype(np.float32)
+    r = O.oproj_ref(x, t, a, res, keep=64)
+    r0 = O.bitlinear_a8(x, t, a, keep=64)
+    np.testing.assert_array_equal(r["y"], r0["y"] + res.astype(np.float64))
+    assert np.all(r["mask"].sum(axis=1) == 64)
+
+
+def test_generators_are_deterministic_and_gaussian():
+    a = normal(7, 200000)
+    assert np.array_equal(a, normal(7, 200000))
+    assert abs(a.mean()) < 0.01 and abs(a.std() - 1) < 0.01
+    bits = activations_bf16(3, 2, 16)
+    f = bf16_bits_to_f32(bits)
+    assert np.all((f.view(np.uint32) & 0xFFFF) == 0)
