@@ -1,0 +1,186 @@
+/*
+ * bitlinear.h -- C ABI of the BitNet a4.8 BitLinear hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "BitNet a4.8: 4-bit Activations for 1-bit LLMs" (architecture write-up,
+ * section 3.4 "Detailed, Sentence-Based Technical Breakdown"):
+ *   ternary weights      Q_w(W) = alpha * RoundClip(W/(alpha+eps), -1, 1), alpha = mean|W|     (paper Eq. 2)
+ *   4-bit activations    Y = Q_INT4(X) Q_w(W)^T, Q_INT4 absmean with sqrt(7)                    (paper Eq. 6-7)
+ *                        FP4 E2M1 MinMax quantizer as the floating-point alternative            (paper Eq. 8-9)
+ *   sparse 8-bit         Y = (Q_INT8(X) . M) Q_w(W)^T, M = Top_k(|X|), Q_INT8 absmax             (paper Eq. 1)
+ *   FFN gate             ReLU^2 GLU(X) = X W_up^T . ReLU^2(X W_gate^T)                           (paper Eq. 5)
+ * and section 3.2 "Big-Picture Architecture" (residual add after the output projection).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Pointers named d_* are DEVICE pointers (HIP device memory of the current device); pointers
+ *    named h_* are host pointers. The caller allocates and owns every buffer; the library never
+ *    allocates, frees or keeps state between calls (it is reentrant).
+ *  * `stream` is a hipStream_t passed as void* (NULL = the null stream). All device work is
+ *    enqueued on it; BL_OK means "validated and enqueued", results are ready when the stream is.
+ *  * Arguments are validated on the host before anything is enqueued. On any error status nothing
+ *    is enqueued and no output is touched. BL_ERR_HIP reports a failed launch (hipGetLastError).
+ *  * Activations X are row-major [M, K] (tokens x features) with row stride ldx elements.
+ *    Weights W are [N, K] as in a linear layer; outputs Y = X W^T are row-major [M, N], row stride ldy.
+ *  * Shapes: K % 256 == 0, N % 16 == 0, M >= 1 (any value, ragged tiles are masked); M*K, N*K < 2^31.
+ *  * Alignment: code buffers, packed weights and x must be 16-byte aligned; ldx*elem_size and
+ *    ldy*4 must be multiples of 16 bytes.
+ *  * Inputs are finite (no NaN or Inf). eps must be finite and > 0.
+ *  * Rounding: every float32 operation is a single IEEE operation, round to nearest even, never
+ *    fused; round() of the quantizers is round-half-to-even.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITLINEAR_ABI_VERSION 1
+
+typedef enum {
+  BL_OK = 0,
+  BL_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad enum, eps <= 0, ld too small, keep out of range */
+  BL_ERR_UNSUPPORTED_SHAPE = 2,  /* K % 256, N % 16, M > 8 for decode, size limits */
+  BL_ERR_MISALIGNED = 3,         /* a pointer or row stride breaks the 16-byte rule */
+  BL_ERR_WORKSPACE_TOO_SMALL = 4,
+  BL_ERR_HIP = 5
+} bl_status;
+
+typedef enum { BL_ACT_INT4 = 0, BL_ACT_FP4_E2M1 = 1, BL_ACT_INT8 = 2 } bl_act_format;
+typedef enum { BL_IN_BF16 = 0, BL_IN_F32 = 1 } bl_in_dtype;
+typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_epi_kind;
+
+/*
+ * Quantized activation codes (written by bitlinear_quantize_act, read by the matmul entry points):
+ *   INT4      M x K/2 bytes, row stride K/2: element 2j in the low nibble of byte j, 2j+1 in the high
+ *             nibble; two's-complement nibbles, codes in [-8, 7]. scale[m] = beta_m / sqrt(7).
+ *   FP4_E2M1  same nibble layout; nibble = sign<<3 | e, e indexes the E2M1 magnitudes
+ *             {0, 0.5, 1, 1.5, 2, 3, 4, 6} (OCP E2M1 encoding); zero is always +0. scale[m] = gamma_m / 6.
+ *   INT8      M x K bytes, row stride K, codes in [-127, 127] (0 where Top-K masked). scale[m] = gamma_m / 127.
+ * Dequantized activation = code value * scale[m].
+ *
+ * Packed ternary weights (bitlinear_pack_ternary output, N*K/4 bytes, 2 bits per weight):
+ *   2-bit field: 00 = 0, 01 = +1, 11 = -1 (10 is never written).
+ *   Tiles of 16 rows (n) x 256 columns (k), 1024 bytes each, tile (n/16, k/256) at byte offset
+ *   ((n/16) * (K/256) + k/256) * 1024. Inside a tile, with r = n % 16 and kk = k % 256:
+ *   lane L = 16 * (kk / 64) + r owns bytes [16 L, 16 L + 16) = four little-endian 32-bit words;
+ *   word i = (kk % 64) / 16 holds the 16 weights kk0..kk0+15 (kk0 = 16 * (kk / 16)); weight
+ *   kk0 + q (q < 8) sits in bits [4q, 4q+2) and weight kk0 + 8 + q in bits [4q+2, 4q+4).
+ *   (Each 1 KB tile is exactly four B operands of a 16x16x64 int8 MFMA, or two of a 16x16x128
+ *   FP4 MFMA, with no per-element shuffling.)
+ */
+
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_quantize_act: per-token activation quantizer (one row of X = one token).
+ *   INT4 absmean (section 3.4, 4-bit quantization, paper Eq. 6-7):
+ *     beta = RN32(RN64(sum_k |x|) / K) with the sum exact; s = RN32(RN32(sqrt7) / RN32(beta + eps));
+ *     code = clamp(rint(RN32(x * s)), -8, 7).
+ *   FP4 E2M1 MinMax (paper Eq. 8-9; reading: the row max maps to 6): gamma = max|x|;
+ *     s = RN32(6 / RN32(gamma + eps)); code = nearest E2M1 value of RN32(x * s), ties to even
+ *     mantissa, saturating at 6.
+ *   INT8 absmax with optional Top-K (section 3.4, sparsification, paper Eq. 1): gamma = max|x|
+ *     over the whole row; s = RN32(127 / RN32(gamma + eps)); code = clamp(rint(RN32(x * s)), -128, 127)
+ *     for the topk_keep entries of largest |x| (ties to the lower index), 0 elsewhere.
+ * Arguments:
+ *   d_x          [M, K] input, bf16 (in_dtype BL_IN_BF16) or float32 (BL_IN_F32), row stride ldx >= K.
+ *                INT4 and FP4 accept bf16 and float32; INT8 accepts both.
+ *   fmt          bl_act_format of the output.
+ *   topk_keep    INT8 only: number of survivors per row in [0, K]; < 0 disables the mask.
+ *                Must be < 0 for INT4 and FP4.
+ *   eps          > 0.
+ *   d_row_absmax_hint  optional [M] float32 equal to max_k |x[m, k]| bit for bit (for instance the
+ *                row_absmax output of the ReLU^2 GLU epilogue); INT8/FP4 then skip their max pass.
+ *                Ignored for INT4. NULL = compute it.
+ *   d_codes      output codes (layout above).   d_scale  output [M] float32 dequant scales.
+ *   d_mask       optional output [M][K/32] uint32 survivor bitmap (bit k%32 of word k/32); INT8 only.
+ * ------------------------------------------------------------------------------------------- */
+bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, int64_t K, int64_t ldx,
+                                 int32_t fmt, int32_t topk_keep, float eps,
+                                 const float* d_row_absmax_hint,
+                                 void* d_codes, float* d_scale, uint32_t* d_mask, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_pack_ternary: absmean ternary quantizer of a latent weight matrix (section 3.4,
+ * "Ternary Weight Quantization (BitLinear)", paper Eq. 2) and 2-bit packing.
+ *   alpha = RN32(RN64(sum |w|) / (N K)) with the sum exact over the whole tensor;
+ *   code = clamp(rint(RN32(w / RN32(alpha + eps))), -1, 1) (IEEE division per element).
+ *   The dequantized weight is alpha * code.
+ * Arguments:
+ *   d_w          [N, K] float32, row-major, contiguous.
+ *   d_packed     output, bitlinear_packed_bytes(N, K) bytes, layout above.
+ *   d_alpha      output, one float32 on the device.
+ *   d_workspace  scratch of at least bitlinear_pack_workspace_bytes() bytes, 16-byte aligned; its
+ *                contents on entry do not matter (the call clears what it uses).
+ * ------------------------------------------------------------------------------------------- */
+size_t bitlinear_packed_bytes(int64_t N, int64_t K);
+size_t bitlinear_pack_workspace_bytes(void);
+bl_status bitlinear_pack_ternary(const float* d_w, int64_t N, int64_t K, float eps,
+                                 void* d_packed, float* d_alpha,
+                                 void* d_workspace, size_t ws_bytes, void* stream);
+
+/* Epilogue of the matmul entry points (a HOST struct; the pointers in it are device pointers).
+ *   acc      exact integer sum_k code_x * code_w (FP4: sum of doubled E2M1 codes; counted in halves)
+ *   sc[m]    = RN32(scale[m] * alpha)
+ *   y0       = RN32(RN32(acc) * sc[m])          (FP4: RN32(RN32(acc * 0.5) * sc[m]))
+ *   NONE     y = y0
+ *   RESIDUAL y = RN32(y0 + residual[m, n]); d_residual (row stride ldr) may alias y.
+ *   RELU2_GLU (section 3.4, squared ReLU gating, paper Eq. 5): the main weights are W_gate,
+ *            d_up_packed / d_up_alpha are W_up; g = y0(gate), u = y0(up), g+ = g > 0 ? g : +0,
+ *            y = h = RN32(RN32(g+ * g+) * u). If d_row_absmax is non-NULL it receives
+ *            max_n |h[m, n]| per row (the call clears it first), which is exactly the gamma of
+ *            the following INT8 quantization. (h must stay finite: when g+ * g+ or the product
+ *            overflows float32 the row maximum is unspecified.)                                  */
+typedef struct {
+  int32_t kind;              /* bl_epi_kind */
+  const float* d_residual;   /* RESIDUAL */
+  int64_t ldr;
+  const void* d_up_packed;   /* RELU2_GLU */
+  const float* d_up_alpha;
+  float* d_row_absmax;       /* RELU2_GLU, optional [M] */
+} bl_epilogue;
+
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_gemm_w158a4: Y = Q_4bit(X) Q_w(W)^T (section 3.4, 4-bit activations).
+ *   fmt BL_ACT_INT4 runs on int8 matrix cores; BL_ACT_FP4_E2M1 runs on the block-scaled FP4
+ *   matrix cores with unit block scales (the per-token scale is applied in the fp32 epilogue,
+ *   which keeps the product exact).
+ *   d_codes/d_scale  activations from bitlinear_quantize_act, [M, K].
+ *   d_packed/d_alpha weights from bitlinear_pack_ternary, [N, K].
+ *   d_y              [M, N] float32 output, row stride ldy >= N.
+ *   h_epi            NULL or an epilogue description (host pointer).
+ * ------------------------------------------------------------------------------------------- */
+bl_status bitlinear_gemm_w158a4(int32_t fmt, const void* d_codes, const float* d_scale,
+                                int64_t M, int64_t K,
+                                const void* d_packed, const float* d_alpha, int64_t N,
+                                float* d_y, int64_t ldy, const bl_epilogue* h_epi, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_gemm_w158a8_sparse: Y = (Q_INT8(X) . M) Q_w(W)^T (section 3.4, sparsification,
+ * paper Eq. 1) for the attention output and FFN down projections. Codes are INT8 from
+ * bitlinear_quantize_act (masked entries already 0). Matrix-core work on 64-wide K slices whose
+ * activation codes are all zero for a 16-row group is skipped. Arguments as for the A4 GEMM.
+ * ------------------------------------------------------------------------------------------- */
+bl_status bitlinear_gemm_w158a8_sparse(const void* d_codes, const float* d_scale, int64_t M, int64_t K,
+                                       const void* d_packed, const float* d_alpha, int64_t N,
+                                       float* d_y, int64_t ldy, const bl_epilogue* h_epi, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_gemv_decode: the same products for decode batches, 1 <= M <= 8, fmt INT4 or INT8.
+ * Streams every packed weight tile once from HBM; a lane skips the load of a 64-wide K slice of
+ * weights when the activation codes of all M rows are zero there. Arguments as for the GEMMs.
+ * ------------------------------------------------------------------------------------------- */
+bl_status bitlinear_gemv_decode(int32_t fmt, const void* d_codes, const float* d_scale,
+                                int64_t M, int64_t K,
+                                const void* d_packed, const float* d_alpha, int64_t N,
+                                float* d_y, int64_t ldy, const bl_epilogue* h_epi, void* stream);
+
+const char* bitlinear_status_string(int32_t status);
+int32_t bitlinear_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITLINEAR_H */

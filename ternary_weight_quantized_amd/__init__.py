@@ -1,0 +1,206 @@
+"""Python binding of libbitlinear (ctypes): argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/bitlinear.h). PyTorch
+provides device memory and the current HIP stream; every step of the computation runs in the
+library's HIP kernels. There is no fallback: if the library is missing or fails to load, the
+functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+BL_OK = 0
+BL_ACT_INT4, BL_ACT_FP4_E2M1, BL_ACT_INT8 = 0, 1, 2
+BL_IN_BF16, BL_IN_F32 = 0, 1
+BL_EPI_NONE, BL_EPI_RESIDUAL, BL_EPI_RELU2_GLU = 0, 1, 2
+
+FORMATS = {"int4": BL_ACT_INT4, "fp4": BL_ACT_FP4_E2M1, "int8": BL_ACT_INT8}
+
+EXPORTED = (
+    "bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_packed_bytes",
+    "bitlinear_pack_workspace_bytes", "bitlinear_gemm_w158a4", "bitlinear_gemm_w158a8_sparse",
+    "bitlinear_gemv_decode", "bitlinear_status_string", "bitlinear_abi_version",
+)
+
+
+class BitlinearError(RuntimeError):
+    """A non-zero bl_status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib().bitlinear_status_string(status).decode() if _LIB is not None else str(status)
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+class bl_epilogue(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("d_residual", ctypes.c_void_p),
+        ("ldr", ctypes.c_int64),
+        ("d_up_packed", ctypes.c_void_p),
+        ("d_up_alpha", ctypes.c_void_p),
+        ("d_row_absmax", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+
+def _lib():
+    """Load libbitlinear.so once; raise if it is absent (no CPU fallback exists)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not built: run `python -m ternary_weight_quantized_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        ep = ctypes.POINTER(bl_epilogue)
+        lib.bitlinear_quantize_act.argtypes = [vp, i32, i64, i64, i64, i32, i32, f32, vp, vp, vp, vp, vp]
+        lib.bitlinear_quantize_act.restype = i32
+        lib.bitlinear_packed_bytes.argtypes = [i64, i64]
+        lib.bitlinear_packed_bytes.restype = sz
+        lib.bitlinear_pack_workspace_bytes.argtypes = []
+        lib.bitlinear_pack_workspace_bytes.restype = sz
+        lib.bitlinear_pack_ternary.argtypes = [vp, i64, i64, f32, vp, vp, vp, sz, vp]
+        lib.bitlinear_pack_ternary.restype = i32
+        for name in ("bitlinear_gemm_w158a4", "bitlinear_gemv_decode"):
+            getattr(lib, name).argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, i64, ep, vp]
+            getattr(lib, name).restype = i32
+        lib.bitlinear_gemm_w158a8_sparse.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i64, ep, vp]
+        lib.bitlinear_gemm_w158a8_sparse.restype = i32
+        lib.bitlinear_status_string.argtypes = [i32]
+        lib.bitlinear_status_string.restype = ctypes.c_char_p
+        lib.bitlinear_abi_version.argtypes = []
+        lib.bitlinear_abi_version.restype = i32
+        _LIB = lib
+    return _LIB
+
+
+def library():
+    """The loaded ctypes library (raises if it is missing)."""
+    return _lib()
+
+
+def _check(status: int, where: str):
+    if status != BL_OK:
+        raise BitlinearError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _fmt(fmt):
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def codes_shape(fmt, M, K):
+    """(rows, bytes per row) of the code buffer of a format."""
+    return (M, K if _fmt(fmt) == BL_ACT_INT8 else K // 2)
+
+
+# ------------------------------------------------------------------------------- entry points
+def bitlinear_quantize_act(x, fmt, topk_keep=-1, eps=1e-5, row_absmax_hint=None, want_mask=False,
+                           codes=None, scale=None, mask=None, stream=None):
+    """Per-token quantization of x [M, K] (bf16 or float32, CUDA). Returns (codes uint8, scale f32 [M], mask|None)."""
+    import torch
+    f = _fmt(fmt)
+    M, K = x.shape
+    in_dtype = {torch.bfloat16: BL_IN_BF16, torch.float32: BL_IN_F32}[x.dtype]
+    if codes is None:
+        codes = torch.empty(codes_shape(f, M, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    if want_mask and mask is None:
+        mask = torch.empty((M, K // 32), dtype=torch.int32, device=x.device)
+    st = _lib().bitlinear_quantize_act(_ptr(x), in_dtype, M, K, x.stride(0), f, int(topk_keep), float(eps),
+                                       _ptr(row_absmax_hint), _ptr(codes), _ptr(scale), _ptr(mask), _stream(stream))
+    _check(st, "bitlinear_quantize_act")
+    return codes, scale, mask
+
+
+def bitlinear_packed_bytes(N, K):
+    return int(_lib().bitlinear_packed_bytes(N, K))
+
+
+def bitlinear_pack_workspace_bytes():
+    return int(_lib().bitlinear_pack_workspace_bytes())
+
+
+def bitlinear_pack_ternary(w, eps=1e-5, packed=None, alpha=None, workspace=None, stream=None):
+    """Ternarize and pack w [N, K] float32 (CUDA). Returns (packed uint8 [N*K/4], alpha f32 [1])."""
+    import torch
+    N, K = w.shape
+    if packed is None:
+        packed = torch.empty(bitlinear_packed_bytes(N, K), dtype=torch.uint8, device=w.device)
+    if alpha is None:
+        alpha = torch.empty(1, dtype=torch.float32, device=w.device)
+    if workspace is None:
+        workspace = torch.empty(bitlinear_pack_workspace_bytes(), dtype=torch.uint8, device=w.device)
+    st = _lib().bitlinear_pack_ternary(_ptr(w), N, K, float(eps), _ptr(packed), _ptr(alpha), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "bitlinear_pack_ternary")
+    return packed, alpha
+
+
+def _epilogue(residual=None, up_packed=None, up_alpha=None, row_absmax=None):
+    if residual is not None:
+        return bl_epilogue(BL_EPI_RESIDUAL, residual.data_ptr(), residual.stride(0), None, None, None)
+    if up_packed is not None:
+        return bl_epilogue(BL_EPI_RELU2_GLU, None, 0, up_packed.data_ptr(), up_alpha.data_ptr(),
+                           None if row_absmax is None else row_absmax.data_ptr())
+    return None
+
+
+def _mm(fn_name, fmt, codes, scale, M, K, packed, alpha, N, y, residual, up_packed, up_alpha, row_absmax, stream):
+    import torch
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    epi = _epilogue(residual, up_packed, up_alpha, row_absmax)
+    epi_ref = ctypes.byref(epi) if epi is not None else None
+    fn = getattr(_lib(), fn_name)
+    args = [_ptr(codes), _ptr(scale), M, K, _ptr(packed), _ptr(alpha), N, _ptr(y), y.stride(0), epi_ref, _stream(stream)]
+    if fn_name != "bitlinear_gemm_w158a8_sparse":
+        args.insert(0, _fmt(fmt))
+    _check(fn(*args), fn_name)
+    return y
+
+
+def bitlinear_gemm_w158a4(fmt, codes, scale, K, packed, alpha, N, y=None, residual=None, up_packed=None,
+                          up_alpha=None, row_absmax=None, stream=None):
+    """Y [M, N] = Q_4bit(X) Q_w(W)^T with an optional epilogue (residual or ReLU^2 GLU with W_up)."""
+    return _mm("bitlinear_gemm_w158a4", fmt, codes, scale, scale.shape[0], K, packed, alpha, N, y, residual,
+               up_packed, up_alpha, row_absmax, stream)
+
+
+def bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, alpha, N, y=None, residual=None, up_packed=None,
+                                 up_alpha=None, row_absmax=None, stream=None):
+    """Y [M, N] = (Q_INT8(X) . M) Q_w(W)^T with an optional epilogue."""
+    return _mm("bitlinear_gemm_w158a8_sparse", BL_ACT_INT8, codes, scale, scale.shape[0], K, packed, alpha, N, y,
+               residual, up_packed, up_alpha, row_absmax, stream)
+
+
+def bitlinear_gemv_decode(fmt, codes, scale, K, packed, alpha, N, y=None, residual=None, up_packed=None,
+                          up_alpha=None, row_absmax=None, stream=None):
+    """Decode product for 1 <= M <= 8 tokens (INT4 or INT8 codes)."""
+    return _mm("bitlinear_gemv_decode", fmt, codes, scale, scale.shape[0], K, packed, alpha, N, y, residual,
+               up_packed, up_alpha, row_absmax, stream)
+
+
+def bitlinear_abi_version():
+    return int(_lib().bitlinear_abi_version())
+
+
+def bitlinear_status_string(status):
+    return _lib().bitlinear_status_string(int(status)).decode()

@@ -1,0 +1,149 @@
+// C-ABI layer: host-side argument validation, then kernel launches on the caller's stream.
+// Nothing is enqueued when validation fails; the library never allocates device memory.
+#include <cmath>
+#include <cstdint>
+
+#include "bl_kernels.h"
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0u; }
+inline bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.0f; }
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+bl_status hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+// Validation shared by the three matmul entry points.
+bl_status check_mm(int32_t fmt, const void* codes, const float* scale, int64_t M, int64_t K, const void* packed,
+                   const float* alpha, int64_t N, const float* y, int64_t ldy, const bl_epilogue* epi) {
+  if (!codes || !scale || !packed || !alpha || !y) return BL_ERR_INVALID_ARGUMENT;
+  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8) return BL_ERR_INVALID_ARGUMENT;
+  if (M < 1 || K < 1 || N < 1) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (K % 256 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (ldy < N) return BL_ERR_INVALID_ARGUMENT;
+  if (!aligned16(codes) || !aligned16(packed) || !aligned16(y) || (ldy * 4) % 16 != 0) return BL_ERR_MISALIGNED;
+  if (epi) {
+    if (epi->kind == BL_EPI_RESIDUAL) {
+      if (!epi->d_residual) return BL_ERR_INVALID_ARGUMENT;
+      if (epi->ldr < N) return BL_ERR_INVALID_ARGUMENT;
+    } else if (epi->kind == BL_EPI_RELU2_GLU) {
+      if (!epi->d_up_packed || !epi->d_up_alpha) return BL_ERR_INVALID_ARGUMENT;
+      if (!aligned16(epi->d_up_packed)) return BL_ERR_MISALIGNED;
+    } else if (epi->kind != BL_EPI_NONE) {
+      return BL_ERR_INVALID_ARGUMENT;
+    }
+  }
+  return BL_OK;
+}
+
+bl_mm_args make_args(int32_t fmt, const void* codes, const float* scale, int64_t M, int64_t K, const void* packed,
+                     const float* alpha, int64_t N, float* y, int64_t ldy, const bl_epilogue* epi) {
+  bl_mm_args a{};
+  a.fmt = fmt; a.A = codes; a.ascale = scale; a.M = (int)M; a.K = (int)K; a.N = (int)N;
+  a.W = packed; a.walpha = alpha; a.Y = y; a.ldy = (long)ldy;
+  a.epi = epi ? epi->kind : BL_EPI_NONE;
+  a.R = nullptr; a.ldr = 0; a.W2 = nullptr; a.w2alpha = nullptr; a.rowmax = nullptr;
+  if (epi && epi->kind == BL_EPI_RESIDUAL) { a.R = epi->d_residual; a.ldr = (long)epi->ldr; }
+  if (epi && epi->kind == BL_EPI_RELU2_GLU) { a.W2 = epi->d_up_packed; a.w2alpha = epi->d_up_alpha; a.rowmax = epi->d_row_absmax; }
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
+
+const char* bitlinear_status_string(int32_t s) {
+  switch (s) {
+    case BL_OK: return "ok";
+    case BL_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case BL_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case BL_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case BL_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case BL_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return (size_t)(N * K / 4);
+}
+
+size_t bitlinear_pack_workspace_bytes(void) { return 256 * sizeof(unsigned long long); }
+
+bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, int64_t K, int64_t ldx, int32_t fmt,
+                                 int32_t topk_keep, float eps, const float* d_row_absmax_hint, void* d_codes,
+                                 float* d_scale, uint32_t* d_mask, void* stream) {
+  if (!d_x || !d_codes || !d_scale) return BL_ERR_INVALID_ARGUMENT;
+  if (in_dtype != BL_IN_BF16 && in_dtype != BL_IN_F32) return BL_ERR_INVALID_ARGUMENT;
+  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8) return BL_ERR_INVALID_ARGUMENT;
+  if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
+  if (M < 1 || K < 1) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (K % 256 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (M * K >= kMaxElems || M * ldx >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < K) return BL_ERR_INVALID_ARGUMENT;
+  if (fmt != BL_ACT_INT8 && (topk_keep >= 0 || d_mask)) return BL_ERR_INVALID_ARGUMENT;
+  if (topk_keep > K) return BL_ERR_INVALID_ARGUMENT;
+  const int64_t esz = in_dtype == BL_IN_F32 ? 4 : 2;
+  if (!aligned16(d_x) || !aligned16(d_codes) || (ldx * esz) % 16 != 0) return BL_ERR_MISALIGNED;
+  if (d_mask && !aligned16(d_mask)) return BL_ERR_MISALIGNED;
+  const float* hint = fmt == BL_ACT_INT4 ? nullptr : d_row_absmax_hint;
+  return hip_status(bl_launch_quantize(d_x, in_dtype == BL_IN_F32, (int)M, (int)K, (long)ldx, fmt, (int)topk_keep,
+                                       eps, hint, d_codes, d_scale, d_mask, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_pack_ternary(const float* d_w, int64_t N, int64_t K, float eps, void* d_packed, float* d_alpha,
+                                 void* d_workspace, size_t ws_bytes, void* stream) {
+  if (!d_w || !d_packed || !d_alpha || !d_workspace) return BL_ERR_INVALID_ARGUMENT;
+  if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
+  if (N < 1 || K < 1 || K % 256 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (N * K >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (ws_bytes < bitlinear_pack_workspace_bytes()) return BL_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(d_w) || !aligned16(d_packed) || !aligned16(d_workspace)) return BL_ERR_MISALIGNED;
+  return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+static bl_status run_mm(bool decode, int32_t fmt, const void* d_codes, const float* d_scale, int64_t M, int64_t K,
+                        const void* d_packed, const float* d_alpha, int64_t N, float* d_y, int64_t ldy,
+                        const bl_epilogue* h_epi, void* stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  bl_mm_args a = make_args(fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, h_epi);
+  if (a.rowmax) {
+    const hipError_t e = bl_launch_fill_zero(a.rowmax, (long)M, st);
+    if (e != hipSuccess) return BL_ERR_HIP;
+  }
+  return hip_status(decode ? bl_launch_gemv(a, st) : bl_launch_gemm(a, st));
+}
+
+bl_status bitlinear_gemm_w158a4(int32_t fmt, const void* d_codes, const float* d_scale, int64_t M, int64_t K,
+                                const void* d_packed, const float* d_alpha, int64_t N, float* d_y, int64_t ldy,
+                                const bl_epilogue* h_epi, void* stream) {
+  const bl_status s = check_mm(fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, h_epi);
+  if (s != BL_OK) return s;
+  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1) return BL_ERR_INVALID_ARGUMENT;
+  return run_mm(false, fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, h_epi, stream);
+}
+
+bl_status bitlinear_gemm_w158a8_sparse(const void* d_codes, const float* d_scale, int64_t M, int64_t K,
+                                       const void* d_packed, const float* d_alpha, int64_t N, float* d_y,
+                                       int64_t ldy, const bl_epilogue* h_epi, void* stream) {
+  const bl_status s = check_mm(BL_ACT_INT8, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, h_epi);
+  if (s != BL_OK) return s;
+  return run_mm(false, BL_ACT_INT8, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, h_epi, stream);
+}
+
+bl_status bitlinear_gemv_decode(int32_t fmt, const void* d_codes, const float* d_scale, int64_t M, int64_t K,
+                                const void* d_packed, const float* d_alpha, int64_t N, float* d_y, int64_t ldy,
+                                const bl_epilogue* h_epi, void* stream) {
+  const bl_status s = check_mm(fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, h_epi);
+  if (s != BL_OK) return s;
+  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_INT8) return BL_ERR_INVALID_ARGUMENT;
+  if (M > 8) return BL_ERR_UNSUPPORTED_SHAPE;
+  return run_mm(true, fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, h_epi, stream);
+}
+
+}  // extern "C"

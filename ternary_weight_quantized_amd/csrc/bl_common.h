@@ -1,0 +1,129 @@
+// Shared device helpers of the BitLinear kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define BL_WAVE 64
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// RN32(sqrt(7)) = 2.6457512f, bit pattern 0x402953FD.
+#define BL_SQRT7_BITS 0x402953FDu
+
+__device__ __forceinline__ float bl_u2f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t bl_f2u(float f) { return __float_as_uint(f); }
+
+// bf16 bit pattern (low or high half of a dword) -> exactly equal float32.
+__device__ __forceinline__ float bl_bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bl_bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ------------------------------------------------------------------ wave reductions (wave64)
+__device__ __forceinline__ float bl_wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t bl_wave_max_u(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) { uint32_t t = __shfl_xor(v, o, 64); v = t > v ? t : v; }
+  return v;
+}
+__device__ __forceinline__ uint32_t bl_wave_min_u(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) { uint32_t t = __shfl_xor(v, o, 64); v = t < v ? t : v; }
+  return v;
+}
+// Sum of doubles; exact whenever every partial sum is representable (the callers check this).
+__device__ __forceinline__ double bl_wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ------------------------------------------------------------------ exact sums of |binary32| values
+// A non-negative binary32 value with biased exponent e and significand m (hidden bit included for
+// e >= 1) equals m * 2^(max(e,1) - 150). Sums of significands per exponent ("bins") are exact in
+// 64-bit integers; bl_bins_to_double turns the 256 bins into the correctly rounded double of the
+// exact total with a 384-bit integer in units of 2^-149.
+__host__ __device__ inline void bl_bin_split(uint32_t bits, uint32_t* e, uint32_t* m) {
+  uint32_t ex = (bits >> 23) & 0xFFu;
+  uint32_t mt = bits & 0x7FFFFFu;
+  *e = ex;
+  *m = ex ? (mt | 0x800000u) : mt;
+}
+
+__host__ __device__ inline double bl_bins_to_double(const unsigned long long* bins) {
+  uint32_t limb[12];
+  for (int i = 0; i < 12; ++i) limb[i] = 0u;
+  for (int e = 0; e < 255; ++e) {
+    unsigned long long b = bins[e];
+    if (!b) continue;
+    int sh = (e > 1 ? e : 1) - 1;                    // b * 2^sh in units of 2^-149
+    int w = sh >> 5, bit = sh & 31;
+    uint32_t p0 = (uint32_t)(b << bit);
+    uint32_t p1 = (uint32_t)(bit ? (b >> (32 - bit)) : (b >> 32));
+    uint32_t p2 = (uint32_t)(bit ? (b >> (64 - bit)) : 0ull);
+    unsigned long long c = 0;
+    uint32_t parts[3] = {p0, p1, p2};
+    for (int i = 0; i < 12 - w; ++i) {
+      unsigned long long add = (i < 3 ? parts[i] : 0u);
+      if (i >= 3 && c == 0) break;
+      unsigned long long t = (unsigned long long)limb[w + i] + add + c;
+      limb[w + i] = (uint32_t)t;
+      c = t >> 32;
+    }
+  }
+  int top = -1;
+  for (int i = 11; i >= 0; --i) {
+    if (limb[i]) {
+      int lz = 0;
+      uint32_t v = limb[i];
+      while (!(v & 0x80000000u)) { v <<= 1; ++lz; }
+      top = 32 * i + 31 - lz;
+      break;
+    }
+  }
+  if (top < 0) return 0.0;
+  // bit accessor
+  auto bitat = [&](int p) -> uint32_t { return (p < 0) ? 0u : ((limb[p >> 5] >> (p & 31)) & 1u); };
+  if (top <= 52) {
+    unsigned long long v = 0;
+    for (int p = top; p >= 0; --p) v = (v << 1) | bitat(p);
+    return ldexp((double)v, -149);
+  }
+  unsigned long long mant = 0;
+  for (int p = top; p >= top - 52; --p) mant = (mant << 1) | bitat(p);
+  uint32_t rbit = bitat(top - 53);
+  uint32_t sticky = 0;
+  for (int p = top - 54; p >= 0 && !sticky; --p) sticky |= bitat(p);
+  int ex = top;
+  if (rbit && (sticky || (mant & 1ull))) {
+    ++mant;
+    if (mant == (1ull << 53)) { mant >>= 1; ++ex; }
+  }
+  return ldexp((double)mant, ex - 52 - 149);
+}
+
+// ------------------------------------------------------------------ quantizer arithmetic
+// round-half-even then clamp, as an int
+__device__ __forceinline__ int bl_roundclip(float v, float lo, float hi) {
+  float r = __builtin_rintf(v);
+  r = fminf(fmaxf(r, lo), hi);
+  return (int)r;
+}
+
+// nearest E2M1 magnitude index of a non-negative float (ties to even mantissa, saturating at 6).
+// Midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 are exact binary32 values; a tie resolves to the even index.
+__device__ __forceinline__ uint32_t bl_e2m1_index(float a) {
+  uint32_t i = 0;
+  i += (a > 0.25f) ? 1u : 0u;   // 0 | 0.5 boundary: tie (== 0.25) -> 0 (even)
+  i += (a >= 0.75f) ? 1u : 0u;  // 0.5 | 1: tie -> 1.0 (index 2, even)
+  i += (a > 1.25f) ? 1u : 0u;   // 1 | 1.5: tie -> 1.0 (index 2)
+  i += (a >= 1.75f) ? 1u : 0u;  // 1.5 | 2: tie -> 2.0 (index 4)
+  i += (a > 2.5f) ? 1u : 0u;    // 2 | 3: tie -> 2.0 (index 4)
+  i += (a >= 3.5f) ? 1u : 0u;   // 3 | 4: tie -> 4.0 (index 6)
+  i += (a > 5.0f) ? 1u : 0u;    // 4 | 6: tie -> 4.0 (index 6)
+  return i;
+}

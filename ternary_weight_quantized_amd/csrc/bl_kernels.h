@@ -1,0 +1,34 @@
+// Launchers of the BitLinear kernels (called by the C-ABI layer after argument validation).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bitlinear.h"
+
+hipError_t bl_launch_quantize(const void* x, int in_f32, int M, int K, long ldx, int fmt, int keep, float eps,
+                              const float* hint, void* codes, float* scale, uint32_t* mask, hipStream_t st);
+
+hipError_t bl_launch_pack(const float* w, int N, int K, float eps, void* packed, float* alpha,
+                          void* ws, hipStream_t st);
+
+// Arguments shared by the GEMM and the decode GEMV.
+struct bl_mm_args {
+  int fmt;
+  const void* A;
+  const float* ascale;
+  int M, K, N;
+  const void* W;
+  const float* walpha;
+  float* Y;
+  long ldy;
+  int epi;
+  const float* R;
+  long ldr;
+  const void* W2;
+  const float* w2alpha;
+  float* rowmax;
+};
+
+hipError_t bl_launch_gemm(const bl_mm_args& a, hipStream_t st);
+hipError_t bl_launch_gemv(const bl_mm_args& a, hipStream_t st);
+hipError_t bl_launch_fill_zero(float* p, long n, hipStream_t st);

@@ -1,0 +1,427 @@
+// Per-token activation quantizers: INT4 absmean, FP4 E2M1 MinMax, INT8 absmax with Top-K mask.
+//
+// "BitNet a4.8: 4-bit Activations for 1-bit LLMs" (architecture write-up), section 3.4:
+//   "4-Bit Activation Quantization for Gaussian-Like Inputs" (INT4 absmean, paper Eq. 6-7;
+//    FP4 MinMax E2M1, paper Eq. 8-9) and "Sparsification Pipeline for Outlier-Heavy
+//    Intermediate States" (Top-K mask and INT8 absmax, paper Eq. 1).
+//
+// One wave64 owns one token row; a 256-thread block holds four rows. A lane owns four
+// consecutive elements of every 256-element group of the row (group g, elements
+// 256g + 4*lane .. +3), so each load and store of a wave is one contiguous segment.
+// Rows of up to 4096 elements stay in registers between the reduction and the quantization
+// ("resident" kernels); longer rows are read again from global memory ("streaming" kernels).
+#include "bl_common.h"
+#include "bl_kernels.h"
+
+namespace {
+
+template <int IN_F32>
+__device__ __forceinline__ void load4(const void* __restrict__ x, long off, float (&o)[4]) {
+  if (IN_F32) {
+    const float4 t = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+    o[0] = t.x; o[1] = t.y; o[2] = t.z; o[3] = t.w;
+  } else {
+    const uint2 t = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + off);
+    o[0] = bl_bf16lo(t.x); o[1] = bl_bf16hi(t.x); o[2] = bl_bf16lo(t.y); o[3] = bl_bf16hi(t.y);
+  }
+}
+
+__device__ __forceinline__ int ceil_log2(int K) { return K <= 1 ? 0 : 32 - __clz(K - 1); }
+
+// Accumulators of the absmean sum: double sum plus the exponent range of the nonzero terms.
+struct AbsSum {
+  double s = 0.0;
+  uint32_t emax = 0u, emin = 0xFFu;
+  __device__ __forceinline__ void add(float v) {
+    const uint32_t b = bl_f2u(v) & 0x7FFFFFFFu;
+    s += (double)bl_u2f(b);
+    const uint32_t e = b >> 23;
+    if (b) { emax = e > emax ? e : emax; emin = e < emin ? e : emin; }
+  }
+};
+
+// Exact-bins fallback for one wave: called only when the double sum might have rounded.
+__device__ __forceinline__ void bins_clear(unsigned long long* bins, int lane) {
+  for (int i = lane; i < 256; i += 64) bins[i] = 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+__device__ __forceinline__ void bins_add(unsigned long long* bins, float v) {
+  uint32_t e, m;
+  bl_bin_split(bl_f2u(v) & 0x7FFFFFFFu, &e, &m);
+  if (m) atomicAdd(&bins[e], (unsigned long long)m);
+}
+__device__ __forceinline__ double bins_finish(unsigned long long* bins, int lane) {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  double s = 0.0;
+  if (lane == 0) s = bl_bins_to_double(bins);
+  return __shfl(s, 0, 64);
+}
+
+// Is the double-precision sum of the row exact? All terms are multiples of 2^(max(emin,1)-150+24-sig)
+// and the total is below K * 2^(emax-126); exact when that integer count fits in 53 bits.
+template <int IN_F32>
+__device__ __forceinline__ bool sum_is_exact(uint32_t emax, uint32_t emin, int K) {
+  if (emin == 0xFFu) return true;                // all zero
+  const int e1 = emin < 1u ? 1 : (int)emin;
+  return ((int)emax - e1 + (IN_F32 ? 24 : 8) + ceil_log2(K)) <= 53;
+}
+
+// --- per element code functions (float32, one IEEE operation each) ---------------------------
+__device__ __forceinline__ uint32_t code_int4(float v, float s) {
+  return (uint32_t)bl_roundclip(v * s, -8.f, 7.f) & 0xFu;
+}
+__device__ __forceinline__ uint32_t code_fp4(float v, float s) {
+  const float p = v * s;
+  const uint32_t idx = bl_e2m1_index(fabsf(p));
+  const uint32_t neg = (bl_f2u(p) >> 31) & (idx != 0u ? 1u : 0u);
+  return idx | (neg << 3);
+}
+__device__ __forceinline__ uint32_t code_int8(float v, float s) {
+  return (uint32_t)bl_roundclip(v * s, -128.f, 127.f) & 0xFFu;
+}
+
+// Top-K threshold: the largest key T with count(|x| >= T) >= keep, found bit by bit.
+// bf16 inputs have 16 zero low bits in their float32 key, so their search stops at bit 16.
+// Ballot + popcount make each count a scalar: no cross-lane reduction is needed.
+template <typename CountFn>
+__device__ __forceinline__ uint32_t topk_threshold(int keep, int lo_bit, CountFn count_ge) {
+  uint32_t T = 0u;
+  for (int b = 30; b >= lo_bit; --b) {
+    const uint32_t cand = T | (1u << b);
+    if (count_ge(bl_u2f(cand)) >= keep) T = cand;
+  }
+  return T;
+}
+
+// Mask word assembly: lane holds a nibble for elements 4*lane..4*lane+3 of a 256-group; eight
+// lanes make one 32-bit word (bit k % 32 of word k / 32).
+__device__ __forceinline__ void store_mask_nibble(uint32_t* __restrict__ mrow, int g, int lane, uint32_t nib) {
+  uint32_t w = nib << (4 * (lane & 7));
+  w |= __shfl_xor(w, 1, 64);
+  w |= __shfl_xor(w, 2, 64);
+  w |= __shfl_xor(w, 4, 64);
+  if ((lane & 7) == 0) mrow[8 * g + (lane >> 3)] = w;
+}
+
+// ============================================================================ resident kernels
+template <int FMT, int IN_F32, int NGMAX>
+__global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, int M, int K, long ldx,
+                                                   int keep, float eps, const float* __restrict__ hint,
+                                                   uint8_t* __restrict__ codes, float* __restrict__ scale,
+                                                   uint32_t* __restrict__ mask) {
+  __shared__ unsigned long long bins[FMT == BL_ACT_INT4 ? 4 : 1][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= M) return;                         // wave-uniform; no block barriers below
+  const int NG = K >> 8;
+  const long base = (long)row * ldx + 4 * lane;
+  float v[NGMAX][4];
+#pragma unroll
+  for (int g = 0; g < NGMAX; ++g)
+    if (g < NG) load4<IN_F32>(x, base + 256 * g, v[g]);
+
+  if constexpr (FMT == BL_ACT_INT4) {
+    AbsSum acc;
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g)
+      if (g < NG) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc.add(v[g][j]);
+      }
+    double S = bl_wave_sum_d(acc.s);
+    const uint32_t emax = bl_wave_max_u(acc.emax), emin = bl_wave_min_u(acc.emin);
+    if (!sum_is_exact<IN_F32>(emax, emin, K)) {
+      unsigned long long* b = bins[wave];
+      bins_clear(b, lane);
+#pragma unroll
+      for (int g = 0; g < NGMAX; ++g)
+        if (g < NG) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bins_add(b, v[g][j]);
+        }
+      S = bins_finish(b, lane);
+    }
+    const float beta = (float)(S / (double)K);
+    const float s = bl_u2f(BL_SQRT7_BITS) / (beta + eps);
+    uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g)
+      if (g < NG) {
+        const uint32_t c = code_int4(v[g][0], s) | (code_int4(v[g][1], s) << 4) |
+                           (code_int4(v[g][2], s) << 8) | (code_int4(v[g][3], s) << 12);
+        crow[64 * g] = (uint16_t)c;
+      }
+    if (lane == 0) scale[row] = beta / bl_u2f(BL_SQRT7_BITS);
+  } else {
+    // gamma = max |x| over the whole row (exact); FP4 and INT8 share it.
+    float gamma;
+    if (hint) {
+      gamma = hint[row];
+    } else {
+      uint32_t mx = 0u;
+#pragma unroll
+      for (int g = 0; g < NGMAX; ++g)
+        if (g < NG) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t b = bl_f2u(v[g][j]) & 0x7FFFFFFFu;
+            mx = b > mx ? b : mx;
+          }
+        }
+      gamma = bl_u2f(bl_wave_max_u(mx));
+    }
+    if constexpr (FMT == BL_ACT_FP4_E2M1) {
+      const float s = 6.0f / (gamma + eps);
+      uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
+#pragma unroll
+      for (int g = 0; g < NGMAX; ++g)
+        if (g < NG) {
+          const uint32_t c = code_fp4(v[g][0], s) | (code_fp4(v[g][1], s) << 4) |
+                             (code_fp4(v[g][2], s) << 8) | (code_fp4(v[g][3], s) << 12);
+          crow[64 * g] = (uint16_t)c;
+        }
+      if (lane == 0) scale[row] = gamma / 6.0f;
+    } else {
+      const float s = 127.0f / (gamma + eps);
+      const bool all = keep < 0 || keep >= K;
+      const bool none = keep == 0;
+      float Tf = 0.0f;
+      int need = 0;
+      if (!all && !none) {
+        auto count_ge = [&](float c) {
+          int n = 0;
+#pragma unroll
+          for (int g = 0; g < NGMAX; ++g)
+            if (g < NG) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) n += __popcll(__ballot(fabsf(v[g][j]) >= c));
+            }
+          return n;
+        };
+        Tf = bl_u2f(topk_threshold(keep, IN_F32 ? 0 : 16, count_ge));
+        int greater = 0;
+#pragma unroll
+        for (int g = 0; g < NGMAX; ++g)
+          if (g < NG) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) greater += __popcll(__ballot(fabsf(v[g][j]) > Tf));
+          }
+        need = keep - greater;                    // >= 1 ties at T survive, lowest index first
+      }
+      uint32_t* crow = reinterpret_cast<uint32_t*>(codes + (long)row * K) + lane;
+      uint32_t* mrow = mask ? mask + (long)row * (K >> 5) : nullptr;
+      const unsigned long long lt = (1ull << lane) - 1ull;
+      int tie_base = 0;
+#pragma unroll
+      for (int g = 0; g < NGMAX; ++g)
+        if (g < NG) {
+          uint32_t keepbits;
+          if (all) {
+            keepbits = 0xFu;
+          } else if (none) {
+            keepbits = 0u;
+          } else {
+            uint32_t gt = 0u, eq = 0u;
+            int before = 0, tot = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float a = fabsf(v[g][j]);
+              gt |= (a > Tf ? 1u : 0u) << j;
+              const bool t = (a == Tf);
+              eq |= (t ? 1u : 0u) << j;
+              const unsigned long long bal = __ballot(t);
+              before += __popcll(bal & lt);
+              tot += __popcll(bal);
+            }
+            // rank of this lane's ties = ties of earlier groups + of lower lanes + of lower j
+            int rank = tie_base + before;
+            uint32_t kb = gt;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if ((eq >> j) & 1u) { kb |= (rank < need ? 1u : 0u) << j; ++rank; }
+            keepbits = kb;
+            tie_base += tot;
+          }
+          uint32_t c = 0u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if ((keepbits >> j) & 1u) c |= code_int8(v[g][j], s) << (8 * j);
+          crow[64 * g] = c;
+          if (mrow) store_mask_nibble(mrow, g, lane, keepbits);
+        }
+      if (lane == 0) scale[row] = gamma / 127.0f;
+    }
+  }
+}
+
+// ============================================================================ streaming kernels
+template <int FMT, int IN_F32>
+__global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x, int M, int K, long ldx,
+                                                      int keep, float eps, const float* __restrict__ hint,
+                                                      uint8_t* __restrict__ codes, float* __restrict__ scale,
+                                                      uint32_t* __restrict__ mask) {
+  __shared__ unsigned long long bins[FMT == BL_ACT_INT4 ? 4 : 1][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= M) return;
+  const int NG = K >> 8;
+  const long base = (long)row * ldx + 4 * lane;
+
+  if constexpr (FMT == BL_ACT_INT4) {
+    AbsSum acc;
+    for (int g = 0; g < NG; ++g) {
+      float v[4];
+      load4<IN_F32>(x, base + 256 * g, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc.add(v[j]);
+    }
+    double S = bl_wave_sum_d(acc.s);
+    const uint32_t emax = bl_wave_max_u(acc.emax), emin = bl_wave_min_u(acc.emin);
+    if (!sum_is_exact<IN_F32>(emax, emin, K)) {
+      unsigned long long* b = bins[wave];
+      bins_clear(b, lane);
+      for (int g = 0; g < NG; ++g) {
+        float v[4];
+        load4<IN_F32>(x, base + 256 * g, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bins_add(b, v[j]);
+      }
+      S = bins_finish(b, lane);
+    }
+    const float beta = (float)(S / (double)K);
+    const float s = bl_u2f(BL_SQRT7_BITS) / (beta + eps);
+    uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
+    for (int g = 0; g < NG; ++g) {
+      float v[4];
+      load4<IN_F32>(x, base + 256 * g, v);
+      crow[64 * g] = (uint16_t)(code_int4(v[0], s) | (code_int4(v[1], s) << 4) |
+                                 (code_int4(v[2], s) << 8) | (code_int4(v[3], s) << 12));
+    }
+    if (lane == 0) scale[row] = beta / bl_u2f(BL_SQRT7_BITS);
+  } else {
+    float gamma;
+    if (hint) {
+      gamma = hint[row];
+    } else {
+      uint32_t mx = 0u;
+      for (int g = 0; g < NG; ++g) {
+        float v[4];
+        load4<IN_F32>(x, base + 256 * g, v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t b = bl_f2u(v[j]) & 0x7FFFFFFFu;
+          mx = b > mx ? b : mx;
+        }
+      }
+      gamma = bl_u2f(bl_wave_max_u(mx));
+    }
+    if constexpr (FMT == BL_ACT_FP4_E2M1) {
+      const float s = 6.0f / (gamma + eps);
+      uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
+      for (int g = 0; g < NG; ++g) {
+        float v[4];
+        load4<IN_F32>(x, base + 256 * g, v);
+        crow[64 * g] = (uint16_t)(code_fp4(v[0], s) | (code_fp4(v[1], s) << 4) |
+                                   (code_fp4(v[2], s) << 8) | (code_fp4(v[3], s) << 12));
+      }
+      if (lane == 0) scale[row] = gamma / 6.0f;
+    } else {
+      const float s = 127.0f / (gamma + eps);
+      const bool all = keep < 0 || keep >= K;
+      const bool none = keep == 0;
+      float Tf = 0.0f;
+      int need = 0;
+      if (!all && !none) {
+        auto count_cmp = [&](float c, bool strict) {
+          int n = 0;
+          for (int g = 0; g < NG; ++g) {
+            float v[4];
+            load4<IN_F32>(x, base + 256 * g, v);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float a = fabsf(v[j]);
+              n += __popcll(__ballot(strict ? (a > c) : (a >= c)));
+            }
+          }
+          return n;
+        };
+        Tf = bl_u2f(topk_threshold(keep, IN_F32 ? 0 : 16, [&](float c) { return count_cmp(c, false); }));
+        need = keep - count_cmp(Tf, true);
+      }
+      uint32_t* crow = reinterpret_cast<uint32_t*>(codes + (long)row * K) + lane;
+      uint32_t* mrow = mask ? mask + (long)row * (K >> 5) : nullptr;
+      const unsigned long long lt = (1ull << lane) - 1ull;
+      int tie_base = 0;
+      for (int g = 0; g < NG; ++g) {
+        float v[4];
+        load4<IN_F32>(x, base + 256 * g, v);
+        uint32_t keepbits;
+        if (all) {
+          keepbits = 0xFu;
+        } else if (none) {
+          keepbits = 0u;
+        } else {
+          uint32_t gt = 0u, eq = 0u;
+          int before = 0, tot = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float a = fabsf(v[j]);
+            gt |= (a > Tf ? 1u : 0u) << j;
+            const bool t = (a == Tf);
+            eq |= (t ? 1u : 0u) << j;
+            const unsigned long long bal = __ballot(t);
+            before += __popcll(bal & lt);
+            tot += __popcll(bal);
+          }
+          int rank = tie_base + before;
+          uint32_t kb = gt;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if ((eq >> j) & 1u) { kb |= (rank < need ? 1u : 0u) << j; ++rank; }
+          keepbits = kb;
+          tie_base += tot;
+        }
+        uint32_t c = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if ((keepbits >> j) & 1u) c |= code_int8(v[j], s) << (8 * j);
+        crow[64 * g] = c;
+        if (mrow) store_mask_nibble(mrow, g, lane, keepbits);
+      }
+      if (lane == 0) scale[row] = gamma / 127.0f;
+    }
+  }
+}
+
+template <int FMT, int IN_F32>
+hipError_t launch_fmt(const void* x, int M, int K, long ldx, int keep, float eps, const float* hint,
+                      uint8_t* codes, float* scale, uint32_t* mask, hipStream_t st) {
+  const dim3 grid((M + 3) / 4), block(256);
+  const int NG = K >> 8;
+  if (NG <= 4)
+    hipLaunchKernelGGL((k_quant_res<FMT, IN_F32, 4>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale, mask);
+  else if (NG <= 8)
+    hipLaunchKernelGGL((k_quant_res<FMT, IN_F32, 8>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale, mask);
+  else if (NG <= 16)
+    hipLaunchKernelGGL((k_quant_res<FMT, IN_F32, 16>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale, mask);
+  else
+    hipLaunchKernelGGL((k_quant_stream<FMT, IN_F32>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale, mask);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t bl_launch_quantize(const void* x, int in_f32, int M, int K, long ldx, int fmt, int keep, float eps,
+                              const float* hint, void* codes, float* scale, uint32_t* mask, hipStream_t st) {
+  uint8_t* c = static_cast<uint8_t*>(codes);
+  if (fmt == BL_ACT_INT4)
+    return in_f32 ? launch_fmt<BL_ACT_INT4, 1>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st)
+                  : launch_fmt<BL_ACT_INT4, 0>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st);
+  if (fmt == BL_ACT_FP4_E2M1)
+    return in_f32 ? launch_fmt<BL_ACT_FP4_E2M1, 1>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st)
+                  : launch_fmt<BL_ACT_FP4_E2M1, 0>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st);
+  return in_f32 ? launch_fmt<BL_ACT_INT8, 1>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st)
+                : launch_fmt<BL_ACT_INT8, 0>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st);
+}

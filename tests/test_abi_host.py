@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is ever launched here).
+
+* the built library loads and exports every function declared in include/bitlinear.h;
+* every invalid-argument path returns its status before any HIP call (fake device pointers are
+  safe because validation rejects the call first);
+* the test-side decoder of the packed weight layout round-trips.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import ternary_weight_quantized_amd as tw
+from tests.packed_layout import pack_reference, unpack_ternary
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(tw.LIB_PATH), reason="libbitlinear.so not built (run build())")
+
+P = ctypes.c_void_p(4096)   # a fake, 16-byte aligned "device pointer" (never dereferenced)
+P_MIS = ctypes.c_void_p(4100)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(bitlinear_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_five_hot_path_calls():
+    fns = header_functions()
+    for f in ("bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_gemm_w158a4",
+              "bitlinear_gemm_w158a8_sparse", "bitlinear_gemv_decode"):
+        assert f in fns
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tw.LIB_PATH)
+    for f in header_functions():
+        assert hasattr(lib, f), f
+    assert set(tw.EXPORTED) == set(header_functions())
+
+
+@needs_lib
+def test_version_and_status_strings():
+    assert tw.bitlinear_abi_version() == 1
+    assert tw.bitlinear_status_string(0) == "ok"
+    assert "argument" in tw.bitlinear_status_string(1)
+    assert tw.bitlinear_packed_bytes(4096, 11008) == 4096 * 11008 // 4
+    assert tw.bitlinear_pack_workspace_bytes() >= 2048
+
+
+def _q(**kw):
+    a = dict(x=P, dt=0, M=4, K=256, ldx=256, fmt=0, keep=-1, eps=1e-5, hint=None, codes=P, scale=P, mask=None)
+    a.update(kw)
+    return tw.library().bitlinear_quantize_act(a["x"], a["dt"], a["M"], a["K"], a["ldx"], a["fmt"], a["keep"],
+                                               a["eps"], a["hint"], a["codes"], a["scale"], a["mask"], None)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(scale=None), 1),
+    (dict(dt=7), 1), (dict(fmt=9), 1), (dict(eps=0.0), 1), (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1),
+    (dict(M=0), 2), (dict(K=0), 2), (dict(K=100, ldx=100), 2), (dict(K=384, ldx=384), 2),
+    (dict(ldx=128), 1), (dict(fmt=0, keep=3), 1), (dict(fmt=1, mask=P), 1), (dict(fmt=2, keep=257), 1),
+    (dict(x=P_MIS), 3), (dict(codes=P_MIS), 3), (dict(ldx=260), 3), (dict(fmt=2, keep=5, mask=P_MIS), 3),
+    (dict(M=1 << 20, K=4096, ldx=4096), 2),
+])
+def test_quantize_validation(kw, status):
+    assert _q(**kw) == status
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), 1), (dict(packed=None), 1), (dict(alpha=None), 1), (dict(ws=None), 1),
+    (dict(eps=0.0), 1), (dict(N=10), 2), (dict(K=300), 2), (dict(N=0), 2),
+    (dict(wsb=100), 4), (dict(w=P_MIS), 3), (dict(packed=P_MIS), 3),
+])
+def test_pack_validation(kw, status):
+    a = dict(w=P, N=32, K=256, eps=1e-5, packed=P, alpha=P, ws=P, wsb=4096)
+    a.update(kw)
+    st = tw.library().bitlinear_pack_ternary(a["w"], a["N"], a["K"], a["eps"], a["packed"], a["alpha"], a["ws"],
+                                             a["wsb"], None)
+    assert st == status
+
+
+def _mm(name, **kw):
+    a = dict(fmt=0, codes=P, scale=P, M=4, K=256, packed=P, alpha=P, N=32, y=P, ldy=32, epi=None)
+    a.update(kw)
+    lib = tw.library()
+    epi = ctypes.byref(a["epi"]) if a["epi"] is not None else None
+    args = [a["codes"], a["scale"], a["M"], a["K"], a["packed"], a["alpha"], a["N"], a["y"], a["ldy"], epi, None]
+    if name != "bitlinear_gemm_w158a8_sparse":
+        args.insert(0, a["fmt"])
+    return getattr(lib, name)(*args)
+
+
+MM_CASES = [
+    (dict(codes=None), 1), (dict(scale=None), 1), (dict(packed=None), 1), (dict(alpha=None), 1), (dict(y=None), 1),
+    (dict(K=128), 2), (dict(N=24), 2), (dict(M=0), 2), (dict(ldy=16), 1), (dict(ldy=33), 3),
+    (dict(codes=P_MIS), 3), (dict(packed=P_MIS), 3), (dict(y=P_MIS), 3),
+    (dict(epi=tw.bl_epilogue(1, None, 32, None, None, None)), 1),
+    (dict(epi=tw.bl_epilogue(1, 4096, 8, None, None, None)), 1),
+    (dict(epi=tw.bl_epilogue(2, None, 0, None, 4096, None)), 1),
+    (dict(epi=tw.bl_epilogue(2, None, 0, 4100, 4096, None)), 3),
+    (dict(epi=tw.bl_epilogue(7, None, 0, None, None, None)), 1),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("name", ["bitlinear_gemm_w158a4", "bitlinear_gemm_w158a8_sparse", "bitlinear_gemv_decode"])
+@pytest.mark.parametrize("kw,status", MM_CASES)
+def test_matmul_validation(name, kw, status):
+    assert _mm(name, **kw) == status
+
+
+@needs_lib
+def test_format_restrictions():
+    assert _mm("bitlinear_gemm_w158a4", fmt=2) == 1          # INT8 goes through the sparse A8 entry point
+    assert _mm("bitlinear_gemv_decode", fmt=1) == 1          # decode takes INT4 or INT8
+    assert _mm("bitlinear_gemv_decode", M=9) == 2            # decode is for at most 8 tokens
+    assert _mm("bitlinear_gemm_w158a4", fmt=5) == 1
+
+
+def test_packed_layout_decoder_roundtrip():
+    rng = np.random.default_rng(0)
+    codes = rng.integers(-1, 2, (48, 768)).astype(np.int8)
+    packed = pack_reference(codes)
+    assert packed.size == 48 * 768 // 4
+    np.testing.assert_array_equal(unpack_ternary(packed, 48, 768), codes)
+
+
+def test_packed_layout_decoder_positions():
+    """A single +1 at (n, k) lands in the tile, lane, word and bit the header describes."""
+    N, K = 32, 512
+    for n, k in [(0, 0), (5, 7), (17, 8), (31, 511), (3, 300), (20, 64 + 16 + 9)]:
+        codes = np.zeros((N, K), np.int8)
+        codes[n, k] = 1
+        packed = pack_reference(codes)
+        kk = k % 256
+        tile = (n // 16) * (K // 256) + k // 256
+        lane = 16 * (kk // 64) + n % 16
+        word = (kk % 64) // 16
+        q = kk % 16
+        bit = 4 * q if q < 8 else 4 * (q - 8) + 2
+        words = packed.view("<u4")
+        idx = tile * 256 + lane * 4 + word
+        assert words[idx] == (1 << bit)
+        assert np.count_nonzero(words) == 1

@@ -1,0 +1,301 @@
+"""GPU parity: every entry point of libbitlinear (through the C ABI) against the CPU oracle.
+
+Codes, masks, scales and ternary weights must match bit for bit; float32 outputs must equal the
+oracle's fixed-order float32 dequantization of its exact integer accumulators bit for bit, and lie
+within 1e-5 relative of the float64 value. Shapes span several tiles with ragged M and N tails.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import ternary_weight_quantized_amd as tw
+from synth import activations_bf16, latent_weights, normal, to_bf16_bits
+from tests.gpu_util import (assert_y_close, dev_bf16, dev_f32, host, int4_values, int8_values, mask_bits,
+                            nibbles, torch_cuda, x_f32)
+from tests.packed_layout import unpack_ternary
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-5
+
+
+# ----------------------------------------------------------------------------- inputs
+def special_rows(K, rng, f32=False):
+    """Degenerate rows: all zero, huge exponent spread (forces the exact-sum fallback),
+    subnormals, few distinct magnitudes (Top-K ties), one nonzero."""
+    rows = []
+    rows.append(np.zeros(K))
+    wide = rng.standard_normal(K) * np.exp2(rng.integers(-70, 70, K).astype(np.float64))
+    rows.append(wide)
+    sub = rng.standard_normal(K) * 2.0 ** -130
+    rows.append(sub)
+    rows.append(rng.integers(-3, 4, K) * 0.5)
+    one = np.zeros(K)
+    one[K // 3] = -3.25
+    rows.append(one)
+    a = np.array(rows)
+    return a.astype(np.float32) if f32 else to_bf16_bits(a)
+
+
+def make_x(seed, M, K, f32=False, special=True):
+    rng = np.random.default_rng(seed)
+    if f32:
+        x = normal(seed, M * K).reshape(M, K).astype(np.float32)
+        if special and M >= 6:
+            x[1:6] = special_rows(K, rng, True)
+        return x
+    x = activations_bf16(seed, M, K)
+    if special and M >= 6:
+        x[1:6] = special_rows(K, rng)
+    return x
+
+
+def to_dev(x):
+    return dev_f32(x) if x.dtype == np.float32 else dev_bf16(x)
+
+
+def packed_weights(seed, N, K, sigma=0.02):
+    w = latent_weights(seed, N, K, sigma)
+    codes, alpha = O.ternarize(w, EPS)
+    packed, a = tw.bitlinear_pack_ternary(dev_f32(w), EPS)
+    return w, codes, alpha, packed, a
+
+
+# ----------------------------------------------------------------------------- pack
+@pytest.mark.parametrize("N,K", [(16, 256), (48, 768), (160, 4096), (2048, 2048)])
+def test_pack_ternary(N, K):
+    torch_cuda()
+    w, codes, alpha, packed, a = packed_weights(100 + N, N, K)
+    assert host(a)[0] == alpha, (host(a)[0], alpha)
+    np.testing.assert_array_equal(unpack_ternary(host(packed), N, K), codes)
+
+
+def test_pack_ternary_wide_exponents_and_zero():
+    torch_cuda()
+    rng = np.random.default_rng(4)
+    N, K = 32, 512
+    w = (rng.standard_normal((N, K)) * np.exp2(rng.integers(-60, 60, (N, K)))).astype(np.float32)
+    w[3] = 0.0
+    codes, alpha = O.ternarize(w, EPS)
+    packed, a = tw.bitlinear_pack_ternary(dev_f32(w), EPS)
+    assert host(a)[0] == alpha
+    np.testing.assert_array_equal(unpack_ternary(host(packed), N, K), codes)
+    z = np.zeros((16, 256), np.float32)
+    packed, a = tw.bitlinear_pack_ternary(dev_f32(z), EPS)
+    assert host(a)[0] == 0.0 and not host(packed).any()
+
+
+# ----------------------------------------------------------------------------- quantizers
+QSHAPES = [(1, 256), (7, 768), (64, 2048), (33, 4096), (9, 4352), (6, 11008)]
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("M,K", QSHAPES)
+def test_quantize_int4(M, K, f32):
+    torch_cuda()
+    x = make_x(1000 + M + K, M, K, f32)
+    codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), "int4", eps=EPS)
+    c, d, _ = O.quant_int4(x_f32(x), EPS)
+    np.testing.assert_array_equal(int4_values(host(codes)), c)
+    np.testing.assert_array_equal(host(scale), d)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("M,K", QSHAPES)
+def test_quantize_fp4(M, K, f32):
+    torch = torch_cuda()
+    x = make_x(2000 + M + K, M, K, f32)
+    codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), "fp4", eps=EPS)
+    nib, _, d, g = O.quant_fp4(x_f32(x), EPS)
+    np.testing.assert_array_equal(nibbles(host(codes)), nib)
+    np.testing.assert_array_equal(host(scale), d)
+    # the row-max hint path gives the same result
+    codes2, scale2, _ = tw.bitlinear_quantize_act(to_dev(x), "fp4", eps=EPS, row_absmax_hint=dev_f32(g))
+    np.testing.assert_array_equal(host(codes2), host(codes))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("M,K", QSHAPES)
+@pytest.mark.parametrize("keep_frac", [None, 0.0, 0.5, 1.0, "one", "k-1"])
+def test_quantize_int8_topk(M, K, f32, keep_frac):
+    torch_cuda()
+    if keep_frac is None:
+        keep = -1
+    elif keep_frac == "one":
+        keep = 1
+    elif keep_frac == "k-1":
+        keep = K - 1
+    else:
+        keep = int(keep_frac * K)
+    x = make_x(3000 + M + K, M, K, f32)
+    codes, scale, mask = tw.bitlinear_quantize_act(to_dev(x), "int8", topk_keep=keep, eps=EPS, want_mask=True)
+    c, m, d, g = O.quant_int8(x_f32(x), EPS, None if keep < 0 else keep)
+    np.testing.assert_array_equal(mask_bits(host(mask), K), m)
+    np.testing.assert_array_equal(int8_values(host(codes)), c)
+    np.testing.assert_array_equal(host(scale), d)
+
+
+def test_quantize_int8_hint_matches_max_pass():
+    torch_cuda()
+    x = make_x(77, 12, 11008, True)
+    _, _, _, g = O.quant_int8(x, EPS)
+    a = tw.bitlinear_quantize_act(dev_f32(x), "int8", eps=EPS)
+    b = tw.bitlinear_quantize_act(dev_f32(x), "int8", eps=EPS, row_absmax_hint=dev_f32(g))
+    np.testing.assert_array_equal(host(a[0]), host(b[0]))
+    np.testing.assert_array_equal(host(a[1]), host(b[1]))
+
+
+def test_quantize_strided_rows():
+    torch_cuda()
+    x = make_x(5, 10, 1024 + 256)
+    xs = to_dev(x)[:, :1024]                      # row stride 1280 elements
+    codes, scale, _ = tw.bitlinear_quantize_act(xs, "int4", eps=EPS)
+    c, d, _ = O.quant_int4(x_f32(x)[:, :1024], EPS)
+    np.testing.assert_array_equal(int4_values(host(codes)), c)
+    np.testing.assert_array_equal(host(scale), d)
+
+
+def test_quantize_is_deterministic():
+    torch_cuda()
+    x = to_dev(make_x(6, 64, 4096))
+    a = tw.bitlinear_quantize_act(x, "int8", topk_keep=2048, want_mask=True)
+    b = tw.bitlinear_quantize_act(x, "int8", topk_keep=2048, want_mask=True)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(host(u), host(v))
+
+
+# ----------------------------------------------------------------------------- GEMMs
+GSHAPES = [(1, 16, 256), (200, 272, 512), (129, 144, 768), (64, 2048, 2048)]
+
+
+def _quant(x, fmt, keep=-1):
+    codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), fmt, topk_keep=keep, eps=EPS)
+    if fmt == "int4":
+        c, d, _ = O.quant_int4(x_f32(x), EPS)
+        return codes, scale, c, d, 1.0
+    if fmt == "fp4":
+        _, c, d, _ = O.quant_fp4(x_f32(x), EPS)
+        return codes, scale, c, d, 0.5
+    c, _, d, _ = O.quant_int8(x_f32(x), EPS, None if keep < 0 else keep)
+    return codes, scale, c, d, 1.0
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4"])
+@pytest.mark.parametrize("M,N,K", GSHAPES)
+def test_gemm_a4(fmt, M, N, K):
+    torch_cuda()
+    x = make_x(4000 + M, M, K)
+    _, t, alpha, packed, a = packed_weights(4100 + N, N, K)
+    codes, scale, c, d, unit = _quant(x, fmt)
+    y = tw.bitlinear_gemm_w158a4(fmt, codes, scale, K, packed, a, N)
+    assert_y_close(host(y), O.gemm_int(c, t), d, alpha, unit)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4"])
+@pytest.mark.parametrize("M,N,K", [(200, 272, 512), (3, 48, 1024)])
+def test_gemm_a4_residual_inplace(fmt, M, N, K):
+    torch_cuda()
+    x = make_x(4200 + M, M, K)
+    _, t, alpha, packed, a = packed_weights(4300 + N, N, K)
+    codes, scale, c, d, unit = _quant(x, fmt)
+    r = normal(4400, M * N).reshape(M, N).astype(np.float32)
+    y = dev_f32(r)
+    tw.bitlinear_gemm_w158a4(fmt, codes, scale, K, packed, a, N, y=y, residual=y)   # y aliases residual
+    assert_y_close(host(y), O.gemm_int(c, t), d, alpha, unit, residual=r)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4"])
+@pytest.mark.parametrize("M,N,K", [(200, 272, 512), (64, 2048, 2048)])
+def test_gemm_a4_relu2_glu(fmt, M, N, K):
+    torch = torch_cuda()
+    x = make_x(4500 + M, M, K, special=False)     # (rows scaled by 2^70 would overflow g^2: out of contract)
+    x[1] = 0                                       # a zero row stays in
+    _, tg, ag, pg, dag = packed_weights(4600 + N, N, K)
+    _, tu, au, pu, dau = packed_weights(4700 + N, N, K)
+    codes, scale, c, d, unit = _quant(x, fmt)
+    rowmax = torch.full((M,), 123.0, dtype=torch.float32, device="cuda")          # must be cleared by the call
+    h = tw.bitlinear_gemm_w158a4(fmt, codes, scale, K, pg, dag, N, up_packed=pu, up_alpha=dau, row_absmax=rowmax)
+    g = O.dequant_f32(O.gemm_int(c, tg), d, ag, unit)
+    u = O.dequant_f32(O.gemm_int(c, tu), d, au, unit)
+    h_ref = O.relu2_glu(g, u)
+    np.testing.assert_array_equal(host(h).view(np.uint32), h_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(rowmax), np.abs(h_ref).max(axis=1))
+
+
+@pytest.mark.parametrize("M,N,K", GSHAPES + [(40, 64, 11008)])
+@pytest.mark.parametrize("keep_frac", [None, 0.5])
+def test_gemm_a8_sparse(M, N, K, keep_frac):
+    torch_cuda()
+    x = make_x(5000 + M, M, K, f32=True)
+    x[M // 2:, : K // 2] = 0.0                      # whole zero K slices exercise the skip path
+    _, t, alpha, packed, a = packed_weights(5100 + N, N, K)
+    keep = -1 if keep_frac is None else int(keep_frac * K)
+    codes, scale, c, d, _ = _quant(x, "int8", keep)
+    y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N)
+    assert_y_close(host(y), O.gemm_int(c, t), d, alpha)
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 272, 512), (33, 64, 11008)])
+def test_gemm_a8_residual_and_relu2(M, N, K):
+    torch = torch_cuda()
+    x = make_x(5200 + M, M, K, f32=True, special=False)
+    x[1] = 0.0
+    _, t, alpha, packed, a = packed_weights(5300 + N, N, K)
+    codes, scale, c, d, _ = _quant(x, "int8", K // 2)
+    acc = O.gemm_int(c, t)
+    r = normal(5400, M * N).reshape(M, N).astype(np.float32)
+    y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, residual=dev_f32(r))
+    assert_y_close(host(y), acc, d, alpha, residual=r)
+    _, tu, au, pu, dau = packed_weights(5500 + N, N, K)
+    rowmax = torch.zeros(M, dtype=torch.float32, device="cuda")
+    h = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, up_packed=pu, up_alpha=dau, row_absmax=rowmax)
+    h_ref = O.relu2_glu(O.dequant_f32(acc, d, alpha), O.dequant_f32(O.gemm_int(c, tu), d, au))
+    np.testing.assert_array_equal(host(h).view(np.uint32), h_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(rowmax), np.abs(h_ref).max(axis=1))
+
+
+# ----------------------------------------------------------------------------- decode
+@pytest.mark.parametrize("fmt", ["int4", "int8"])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8])
+@pytest.mark.parametrize("N,K", [(48, 512), (1024, 4096), (64, 11008)])
+def test_decode(fmt, M, N, K):
+    torch_cuda()
+    x = make_x(6000 + M + K, M, K, special=False)
+    if fmt == "int8":
+        x = x_f32(x)
+        x[:, 256:1024] = 0.0                      # zero slices: their weight loads are skipped
+    _, t, alpha, packed, a = packed_weights(6100 + N, N, K)
+    codes, scale, c, d, _ = _quant(x, fmt, -1)
+    y = tw.bitlinear_gemv_decode(fmt, codes, scale, K, packed, a, N)
+    assert_y_close(host(y), O.gemm_int(c, t), d, alpha)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8"])
+def test_decode_epilogues(fmt):
+    torch = torch_cuda()
+    M, N, K = 6, 96, 1024
+    x = x_f32(make_x(6200, M, K, special=False))
+    _, t, alpha, packed, a = packed_weights(6300, N, K)
+    codes, scale, c, d, _ = _quant(x, fmt, -1)
+    acc = O.gemm_int(c, t)
+    r = normal(6400, M * N).reshape(M, N).astype(np.float32)
+    y = tw.bitlinear_gemv_decode(fmt, codes, scale, K, packed, a, N, residual=dev_f32(r))
+    assert_y_close(host(y), acc, d, alpha, residual=r)
+    _, tu, au, pu, dau = packed_weights(6500, N, K)
+    rowmax = torch.zeros(M, dtype=torch.float32, device="cuda")
+    h = tw.bitlinear_gemv_decode(fmt, codes, scale, K, packed, a, N, up_packed=pu, up_alpha=dau, row_absmax=rowmax)
+    h_ref = O.relu2_glu(O.dequant_f32(acc, d, alpha), O.dequant_f32(O.gemm_int(c, tu), d, au))
+    np.testing.assert_array_equal(host(h).view(np.uint32), h_ref.view(np.uint32))
+    np.testing.assert_array_equal(host(rowmax), np.abs(h_ref).max(axis=1))
+
+
+def test_decode_matches_gemm():
+    torch_cuda()
+    M, N, K = 8, 512, 4096
+    x = make_x(6600, M, K, special=False)
+    _, t, alpha, packed, a = packed_weights(6700, N, K)
+    codes, scale, _, _, _ = _quant(x, "int4")
+    y1 = tw.bitlinear_gemv_decode("int4", codes, scale, K, packed, a, N)
+    y2 = tw.bitlinear_gemm_w158a4("int4", codes, scale, K, packed, a, N)
+    np.testing.assert_array_equal(host(y1), host(y2))
