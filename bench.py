@@ -1,0 +1,323 @@
+"""Benchmark of the BitNet a4.8 BitLinear hot path on one MI355X.
+
+One step = one pass of every hot-path operation over the synthetic workloads, inputs resident in HBM:
+  prefill_qkv  (M=4096, K=4096, N=12288, bf16 N(0,1) with 0.1% x20 outlier channels):
+               INT4 quantize + W1.58A4 int8-MFMA GEMM; FP4 quantize + W1.58A4 FP4-MFMA GEMM
+  ffn_7b       (M=2048, K=4096, N=11008): INT4 quantize, gate+up GEMM with the ReLU^2 GLU epilogue,
+               INT8 quantize of h (row max from the epilogue), W1.58A8 down GEMM
+  attn_out     (M=8192, K=N=4096, Student-t outlier channels): Top-K 50% + INT8 quantize,
+               W1.58A8 o_proj GEMM with the residual add
+  decode_a4    (M=1,4,8, K=4096, N=11008): INT4 quantize + decode GEMV, replayed from a HIP graph over
+               24 rotating weight copies (270 MB, larger than the 256 MB last-level cache)
+The headline value is the W1.58A4 INT4 prefill GEMM throughput in TOPS (2*M*N*K / average kernel time,
+HIP events on the launch stream); the decode GEMV bandwidth and every kernel's time and roofline
+fraction are reported beside it. The weights are ternarized and packed once, outside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0      # dense int8 MFMA
+FP4_PEAK_TOPS = 10100.0      # dense FP4/FP6 MFMA
+EPS = 1e-5
+ROTATE = 24
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=4096, help="rows of the prefill workload the oracle runs")
+    return p.parse_args()
+
+
+def bf16_dev(torch, bits):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+              "(the path shards by tokens or output columns without communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import ternary_weight_quantized_amd as tw
+    from synth import WORKLOADS, workload_inputs
+
+    tw.library()
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    t_setup = time.time()
+
+    # ------------------------------------------------------------------ inputs and packed weights
+    def pack(w):
+        return tw.bitlinear_pack_ternary(torch.from_numpy(w).to(dev), EPS)
+
+    P = WORKLOADS["prefill_qkv"]
+    pin = workload_inputs("prefill_qkv")
+    px = bf16_dev(torch, pin["x"])
+    pW, pA = pack(pin["w"])
+    del pin
+    pc4 = torch.empty((P["M"], P["K"] // 2), dtype=torch.uint8, device=dev)
+    ps4 = torch.empty(P["M"], dtype=torch.float32, device=dev)
+    pc6 = torch.empty((P["M"], 3 * P["K"] // 4), dtype=torch.uint8, device=dev)
+    ps6 = torch.empty(P["M"], dtype=torch.float32, device=dev)
+    pcf = torch.empty_like(pc4)
+    psf = torch.empty_like(ps4)
+    py4 = torch.empty((P["M"], P["N"]), dtype=torch.float32, device=dev)
+    pyf = torch.empty_like(py4)
+
+    F = WORKLOADS["ffn_7b"]
+    fin = workload_inputs("ffn_7b")
+    fx = bf16_dev(torch, fin["x"])
+    gW, gA = pack(fin["w_gate"])
+    uW, uA = pack(fin["w_up"])
+    dW, dA = pack(fin["w_down"])
+    del fin
+    fc = torch.empty((F["M"], 3 * F["K"] // 4), dtype=torch.uint8, device=dev)
+    fs = torch.empty(F["M"], dtype=torch.float32, device=dev)
+    fh = torch.empty((F["M"], F["N"]), dtype=torch.float32, device=dev)
+    frm = torch.empty(F["M"], dtype=torch.float32, device=dev)
+    fhc = torch.empty((F["M"], F["N"]), dtype=torch.uint8, device=dev)
+    fhs = torch.empty(F["M"], dtype=torch.float32, device=dev)
+    fy = torch.empty((F["M"], F["K"]), dtype=torch.float32, device=dev)
+
+    A = WORKLOADS["attn_out"]
+    ain = workload_inputs("attn_out")
+    ax = bf16_dev(torch, ain["x"])
+    ar = torch.from_numpy(ain["residual"]).to(dev)
+    oW, oA = pack(ain["w"])
+    del ain
+    ac = torch.empty((A["M"], A["K"]), dtype=torch.uint8, device=dev)
+    as_ = torch.empty(A["M"], dtype=torch.float32, device=dev)
+    am = torch.empty((A["M"], A["K"] // 32), dtype=torch.int32, device=dev)
+    ay = torch.empty((A["M"], A["N"]), dtype=torch.float32, device=dev)
+
+    D = WORKLOADS["decode_a4"]
+    din = workload_inputs("decode_a4")
+    dx = bf16_dev(torch, din["x"])
+    w0, a0 = pack(din["w"])
+    del din
+    dWs = [w0] + [w0.clone() for _ in range(ROTATE - 1)]       # distinct HBM copies of the same weights
+    dcs = {m: torch.empty((m, D["K"] // 2), dtype=torch.uint8, device=dev) for m in D["Ms"]}
+    dss = {m: torch.empty(m, dtype=torch.float32, device=dev) for m in D["Ms"]}
+    dys = {m: torch.empty((m, D["N"]), dtype=torch.float32, device=dev) for m in D["Ms"]}
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    # ------------------------------------------------------------------ decode graphs (launch-bound)
+    side = torch.cuda.Stream()
+    graphs = {}
+    for m in D["Ms"]:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            tw.bitlinear_quantize_act(dx[:m], "int4", eps=EPS, codes=dcs[m], scale=dss[m])
+            for r in range(ROTATE):
+                tw.bitlinear_gemv_decode("int4", dcs[m], dss[m], D["K"], dWs[r], a0, D["N"], y=dys[m])
+        graphs[m] = g
+    torch.cuda.synchronize()
+
+    names = ["quant_int4_e3m2_prefill", "gemm_a4_int4_fp6_prefill", "quant_int4_prefill", "gemm_a4_int4_i8_prefill",
+             "quant_fp4_prefill", "gemm_a4_fp4_prefill",
+             "quant_int4_e3m2_ffn", "gemm_a4_glu_ffn", "quant_int8_h", "gemm_a8_down", "quant_topk_int8_attn",
+             "gemm_a8_oproj_residual"] + [f"decode_m{m}_graph" for m in D["Ms"]]
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(record):
+        evs = [ev() for _ in range(len(names) + 1)] if record else None
+        i = 0
+
+        def mark():
+            nonlocal i
+            if record:
+                evs[i].record()
+            i += 1
+
+        mark()
+        tw.bitlinear_quantize_act(px, "int4_e3m2", eps=EPS, codes=pc6, scale=ps6); mark()
+        tw.bitlinear_gemm_w158a4("int4_e3m2", pc6, ps6, P["K"], pW, pA, P["N"], y=py4); mark()
+        tw.bitlinear_quantize_act(px, "int4", eps=EPS, codes=pc4, scale=ps4); mark()
+        tw.bitlinear_gemm_w158a4("int4", pc4, ps4, P["K"], pW, pA, P["N"], y=py4); mark()
+        tw.bitlinear_quantize_act(px, "fp4", eps=EPS, codes=pcf, scale=psf); mark()
+        tw.bitlinear_gemm_w158a4("fp4", pcf, psf, P["K"], pW, pA, P["N"], y=pyf); mark()
+        tw.bitlinear_quantize_act(fx, "int4_e3m2", eps=EPS, codes=fc, scale=fs); mark()
+        tw.bitlinear_gemm_w158a4("int4_e3m2", fc, fs, F["K"], gW, gA, F["N"], y=fh, up_packed=uW, up_alpha=uA,
+                                 row_absmax=frm); mark()
+        tw.bitlinear_quantize_act(fh, "int8", eps=EPS, row_absmax_hint=frm, codes=fhc, scale=fhs); mark()
+        tw.bitlinear_gemm_w158a8_sparse(fhc, fhs, F["N"], dW, dA, F["K"], y=fy); mark()
+        tw.bitlinear_quantize_act(ax, "int8", topk_keep=A["keep"], eps=EPS, codes=ac, scale=as_, mask=am); mark()
+        tw.bitlinear_gemm_w158a8_sparse(ac, as_, A["K"], oW, oA, A["N"], y=ay, residual=ar); mark()
+        for m in D["Ms"]:
+            graphs[m].replay(); mark()
+        return evs
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------ timed region
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    recs = [step(True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    times = {n: 0.0 for n in names}
+    for evs in recs:
+        for j, n in enumerate(names):
+            times[n] += evs[j].elapsed_time(evs[j + 1]) * 1e3 / args.steps     # microseconds
+    gemv_us = {m: times[f"decode_m{m}_graph"] / ROTATE for m in D["Ms"]}     # includes the tiny quantize
+
+    # ------------------------------------------------------------------ algorithmic work per kernel
+    Mp, Kp, Np = P["M"], P["K"], P["N"]
+    ops_prefill = 2.0 * Mp * Np * Kp
+    ops_glu = 2.0 * 2 * F["M"] * F["N"] * F["K"]
+    h_codes = fhc.view(torch.int8)
+    nnz_h = int((h_codes != 0).sum().item())
+    nnz_attn = int((ac.view(torch.int8) != 0).sum().item())
+    ops_down_alg = 2.0 * F["K"] * nnz_h
+    ops_down_dense = 2.0 * F["M"] * F["N"] * F["K"]
+    ops_oproj_alg = 2.0 * A["N"] * nnz_attn
+    ops_oproj_dense = 2.0 * A["M"] * A["N"] * A["K"]
+    wbytes = D["N"] * D["K"] / 4
+
+    def dec_bytes(m):
+        return wbytes + m * D["K"] / 2 + 4 * m + 4 + 4 * m * D["N"]      # weights + codes + scales + alpha + y
+
+    def tops(ops, us):
+        return ops / (us * 1e-6) / 1e12
+
+    def gbs(b, us):
+        return b / (us * 1e-6) / 1e9
+
+    kern = {
+        "quant_int4_e3m2_prefill": dict(us=times["quant_int4_e3m2_prefill"], bound="hbm",
+                                        gbs=gbs(Mp * Kp * 2 + Mp * Kp * 0.75 + 4 * Mp,
+                                                times["quant_int4_e3m2_prefill"])),
+        "gemm_a4_int4_fp6_prefill": dict(us=times["gemm_a4_int4_fp6_prefill"], bound="mfma",
+                                         tops=tops(ops_prefill, times["gemm_a4_int4_fp6_prefill"]),
+                                         peak=FP4_PEAK_TOPS),
+        "quant_int4_prefill": dict(us=times["quant_int4_prefill"], bound="hbm",
+                                   gbs=gbs(Mp * Kp * 2 + Mp * Kp / 2 + 4 * Mp, times["quant_int4_prefill"])),
+        "gemm_a4_int4_i8_prefill": dict(us=times["gemm_a4_int4_i8_prefill"], bound="mfma",
+                                        tops=tops(ops_prefill, times["gemm_a4_int4_i8_prefill"]), peak=INT8_PEAK_TOPS),
+        "quant_fp4_prefill": dict(us=times["quant_fp4_prefill"], bound="hbm",
+                                  gbs=gbs(Mp * Kp * 2 + Mp * Kp / 2 + 4 * Mp, times["quant_fp4_prefill"])),
+        "gemm_a4_fp4_prefill": dict(us=times["gemm_a4_fp4_prefill"], bound="mfma",
+                                    tops=tops(ops_prefill, times["gemm_a4_fp4_prefill"]), peak=FP4_PEAK_TOPS),
+        "quant_int4_e3m2_ffn": dict(us=times["quant_int4_e3m2_ffn"], bound="hbm",
+                                    gbs=gbs(F["M"] * F["K"] * 2.75 + 4 * F["M"], times["quant_int4_e3m2_ffn"])),
+        "gemm_a4_glu_ffn": dict(us=times["gemm_a4_glu_ffn"], bound="mfma",
+                                tops=tops(ops_glu, times["gemm_a4_glu_ffn"]), peak=FP4_PEAK_TOPS),
+        "quant_int8_h": dict(us=times["quant_int8_h"], bound="hbm",
+                             gbs=gbs(F["M"] * F["N"] * 5 + 8 * F["M"], times["quant_int8_h"])),
+        "gemm_a8_down": dict(us=times["gemm_a8_down"], bound="mfma",
+                             tops=tops(ops_down_alg, times["gemm_a8_down"]),
+                             dense_tops=tops(ops_down_dense, times["gemm_a8_down"]), peak=INT8_PEAK_TOPS),
+        "quant_topk_int8_attn": dict(us=times["quant_topk_int8_attn"], bound="hbm",
+                                     gbs=gbs(A["M"] * A["K"] * 3 + A["M"] * A["K"] / 8 + 4 * A["M"],
+                                             times["quant_topk_int8_attn"])),
+        "gemm_a8_oproj_residual": dict(us=times["gemm_a8_oproj_residual"], bound="mfma",
+                                       tops=tops(ops_oproj_alg, times["gemm_a8_oproj_residual"]),
+                                       dense_tops=tops(ops_oproj_dense, times["gemm_a8_oproj_residual"]),
+                                       peak=INT8_PEAK_TOPS),
+    }
+    for m in D["Ms"]:
+        kern[f"decode_m{m}"] = dict(us=gemv_us[m], bound="hbm", gbs=gbs(dec_bytes(m), gemv_us[m]))
+    for k in kern.values():
+        if "tops" in k:
+            k["frac"] = round(k["tops"] / k["peak"], 4)
+        else:
+            k["frac"] = round(k["gbs"] / HBM_PEAK_GBS, 4)
+        for f in ("us", "tops", "dense_tops", "gbs"):
+            if f in k:
+                k[f] = round(k[f], 3)
+
+    head_us = times["gemm_a4_int4_fp6_prefill"]
+    value = tops(ops_prefill, head_us)
+    roofline = {"bound": "mfma", "achieved": round(value, 2), "peak": FP4_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(value / FP4_PEAK_TOPS, 4), "traffic": None,
+                "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),
+                "kernel": "k_gemm_mx<INT4_E3M2,NONE>: INT4 codes on FP6 x FP4 matrix cores "
+                          "(prefill_qkv M=4096 K=4096 N=12288)",
+                "avg_kernel_us": round(head_us, 3),
+                "algorithmic": f"2*M*N*K = {ops_prefill:.4g} ops per launch"}
+    decode = {f"m{m}": {"us": round(gemv_us[m], 3), "gbs": round(gbs(dec_bytes(m), gemv_us[m]), 1),
+                        "frac_hbm": round(gbs(dec_bytes(m), gemv_us[m]) / HBM_PEAK_GBS, 4)} for m in D["Ms"]}
+
+    sparsity = {"ffn_h_zero_codes": round(1 - nnz_h / (F["M"] * F["N"]), 4),
+                "attn_zero_codes": round(1 - nnz_attn / (A["M"] * A["K"]), 4)}
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_rows)
+
+    out = {
+        "metric": "W1.58A4 GEMM TOPS (% int8 MFMA peak) + decode GEMV GB/s (% HBM peak)",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp6(e3m2) x fp4(e2m1) MFMA holding INT4 x ternary codes exactly, fp32 accumulate, fp32 epilogue",
+        "data": "synthetic (seeded N(0,1) bf16 activations, N(0,0.02) latent weights, outlier channels)",
+        "config": {"workload": "prefill_qkv: W1.58A4 BitLinear M=4096 K=4096 N=12288 (fused QKV, 7B-shaped)",
+                   "step": "all hot-path operations: prefill INT4+FP4, ffn_7b, attn_out, decode M=1/4/8",
+                   "global_batch": P["M"], "seq_len": None, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "decode_gemv": decode,
+        "kernels": kern,
+        "sparsity": sparsity,
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(rows):
+    """The oracle as it stands, on the first `rows` tokens of the prefill workload (quantize + exact
+    integer GEMM + dequantization); the weights are ternarized beforehand (offline in the method)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    from synth import WORKLOADS, bf16_bits_to_f32, workload_inputs
+    P = WORKLOADS["prefill_qkv"]
+    inp = workload_inputs("prefill_qkv")
+    t, alpha = O.ternarize(inp["w"], EPS)
+    x = bf16_bits_to_f32(inp["x"][:rows])
+    t0 = time.perf_counter()
+    O.bitlinear_a4(x, t, alpha, EPS)
+    dt = time.perf_counter() - t0
+    ops = 2.0 * rows * P["N"] * P["K"]
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle.bitlinear_a4 (INT4) on {rows} of the 4096 prefill tokens, N=12288, K=4096: "
+                      f"{dt:.2f} s", "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -49,7 +49,7 @@ typedef enum {
   BL_ERR_HIP = 5
 } bl_status;
 
-typedef enum { BL_ACT_INT4 = 0, BL_ACT_FP4_E2M1 = 1, BL_ACT_INT8 = 2 } bl_act_format;
+typedef enum { BL_ACT_INT4 = 0, BL_ACT_FP4_E2M1 = 1, BL_ACT_INT8 = 2, BL_ACT_INT4_E3M2 = 3 } bl_act_format;
 typedef enum { BL_IN_BF16 = 0, BL_IN_F32 = 1 } bl_in_dtype;
 typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_epi_kind;
 
@@ -60,6 +60,12 @@ typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_e
  *   FP4_E2M1  same nibble layout; nibble = sign<<3 | e, e indexes the E2M1 magnitudes
  *             {0, 0.5, 1, 1.5, 2, 3, 4, 6} (OCP E2M1 encoding); zero is always +0. scale[m] = gamma_m / 6.
  *   INT8      M x K bytes, row stride K, codes in [-127, 127] (0 where Top-K masked). scale[m] = gamma_m / 127.
+ *   INT4_E3M2 the INT4 absmean codes (same values and scale as INT4) stored 6 bits each as their exact
+ *             FP6 E3M2 bit pattern (sign bit 5, 3 exponent bits with bias 3, 2 mantissa bits:
+ *             1 = 0x0C, 2 = 0x10, 3 = 0x12, 4 = 0x14, 5 = 0x15, 6 = 0x16, 7 = 0x17, 8 = 0x18, 0 = 0x00);
+ *             M x 3K/4 bytes, code k of a row in bits [6k, 6k+6) of the row's little-endian bit stream.
+ *             This is the layout the FP6 x FP4 matrix cores read; bitlinear_gemm_w158a4 runs INT4
+ *             activations given in it on those cores, exactly.
  * Dequantized activation = code value * scale[m].
  *
  * Packed ternary weights (bitlinear_pack_ternary output, N*K/4 bytes, 2 bits per weight):
@@ -78,6 +84,7 @@ typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_e
  *   INT4 absmean (section 3.4, 4-bit quantization, paper Eq. 6-7):
  *     beta = RN32(RN64(sum_k |x|) / K) with the sum exact; s = RN32(RN32(sqrt7) / RN32(beta + eps));
  *     code = clamp(rint(RN32(x * s)), -8, 7).
+ *     fmt BL_ACT_INT4_E3M2 computes the same codes and stores them in the E3M2 layout above.
  *   FP4 E2M1 MinMax (paper Eq. 8-9; reading: the row max maps to 6): gamma = max|x|;
  *     s = RN32(6 / RN32(gamma + eps)); code = nearest E2M1 value of RN32(x * s), ties to even
  *     mantissa, saturating at 6.
@@ -89,7 +96,7 @@ typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_e
  *                INT4 and FP4 accept bf16 and float32; INT8 accepts both.
  *   fmt          bl_act_format of the output.
  *   topk_keep    INT8 only: number of survivors per row in [0, K]; < 0 disables the mask.
- *                Must be < 0 for INT4 and FP4.
+ *                Must be < 0 for the 4-bit formats.
  *   eps          > 0.
  *   d_row_absmax_hint  optional [M] float32 equal to max_k |x[m, k]| bit for bit (for instance the
  *                row_absmax output of the ReLU^2 GLU epilogue); INT8/FP4 then skip their max pass.
@@ -144,9 +151,10 @@ typedef struct {
 
 /* ---------------------------------------------------------------------------------------------
  * bitlinear_gemm_w158a4: Y = Q_4bit(X) Q_w(W)^T (section 3.4, 4-bit activations).
- *   fmt BL_ACT_INT4 runs on int8 matrix cores; BL_ACT_FP4_E2M1 runs on the block-scaled FP4
- *   matrix cores with unit block scales (the per-token scale is applied in the fp32 epilogue,
- *   which keeps the product exact).
+ *   fmt BL_ACT_INT4 runs on int8 matrix cores; BL_ACT_INT4_E3M2 (the same INT4 codes, 6-bit
+ *   layout) runs on the block-scaled FP6 x FP4 matrix cores and BL_ACT_FP4_E2M1 on FP4 x FP4 ones,
+ *   with unit block scales (the per-token scale is applied in the fp32 epilogue, which keeps the
+ *   product exact: every partial sum is an integer, or half-integer for FP4, below 2^24).
  *   d_codes/d_scale  activations from bitlinear_quantize_act, [M, K].
  *   d_packed/d_alpha weights from bitlinear_pack_ternary, [N, K].
  *   d_y              [M, N] float32 output, row stride ldy >= N.

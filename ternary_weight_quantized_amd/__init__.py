@@ -14,11 +14,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
 BL_OK = 0
-BL_ACT_INT4, BL_ACT_FP4_E2M1, BL_ACT_INT8 = 0, 1, 2
+BL_ACT_INT4, BL_ACT_FP4_E2M1, BL_ACT_INT8, BL_ACT_INT4_E3M2 = 0, 1, 2, 3
 BL_IN_BF16, BL_IN_F32 = 0, 1
 BL_EPI_NONE, BL_EPI_RESIDUAL, BL_EPI_RELU2_GLU = 0, 1, 2
 
-FORMATS = {"int4": BL_ACT_INT4, "fp4": BL_ACT_FP4_E2M1, "int8": BL_ACT_INT8}
+FORMATS = {"int4": BL_ACT_INT4, "fp4": BL_ACT_FP4_E2M1, "int8": BL_ACT_INT8, "int4_e3m2": BL_ACT_INT4_E3M2}
 
 EXPORTED = (
     "bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_packed_bytes",
@@ -107,7 +107,8 @@ def _fmt(fmt):
 
 def codes_shape(fmt, M, K):
     """(rows, bytes per row) of the code buffer of a format."""
-    return (M, K if _fmt(fmt) == BL_ACT_INT8 else K // 2)
+    f = _fmt(fmt)
+    return (M, K if f == BL_ACT_INT8 else 3 * K // 4 if f == BL_ACT_INT4_E3M2 else K // 2)
 
 
 # ------------------------------------------------------------------------------- entry points

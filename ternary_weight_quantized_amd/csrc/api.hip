@@ -17,7 +17,8 @@ bl_status hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP
 bl_status check_mm(int32_t fmt, const void* codes, const float* scale, int64_t M, int64_t K, const void* packed,
                    const float* alpha, int64_t N, const float* y, int64_t ldy, const bl_epilogue* epi) {
   if (!codes || !scale || !packed || !alpha || !y) return BL_ERR_INVALID_ARGUMENT;
-  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8) return BL_ERR_INVALID_ARGUMENT;
+  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8 && fmt != BL_ACT_INT4_E3M2)
+    return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1 || N < 1) return BL_ERR_UNSUPPORTED_SHAPE;
   if (K % 256 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
   if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
@@ -79,7 +80,8 @@ bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, i
                                  float* d_scale, uint32_t* d_mask, void* stream) {
   if (!d_x || !d_codes || !d_scale) return BL_ERR_INVALID_ARGUMENT;
   if (in_dtype != BL_IN_BF16 && in_dtype != BL_IN_F32) return BL_ERR_INVALID_ARGUMENT;
-  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8) return BL_ERR_INVALID_ARGUMENT;
+  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8 && fmt != BL_ACT_INT4_E3M2)
+    return BL_ERR_INVALID_ARGUMENT;
   if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1) return BL_ERR_UNSUPPORTED_SHAPE;
   if (K % 256 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
@@ -90,7 +92,7 @@ bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, i
   const int64_t esz = in_dtype == BL_IN_F32 ? 4 : 2;
   if (!aligned16(d_x) || !aligned16(d_codes) || (ldx * esz) % 16 != 0) return BL_ERR_MISALIGNED;
   if (d_mask && !aligned16(d_mask)) return BL_ERR_MISALIGNED;
-  const float* hint = fmt == BL_ACT_INT4 ? nullptr : d_row_absmax_hint;
+  const float* hint = (fmt == BL_ACT_INT4 || fmt == BL_ACT_INT4_E3M2) ? nullptr : d_row_absmax_hint;
   return hip_status(bl_launch_quantize(d_x, in_dtype == BL_IN_F32, (int)M, (int)K, (long)ldx, fmt, (int)topk_keep,
                                        eps, hint, d_codes, d_scale, d_mask, static_cast<hipStream_t>(stream)));
 }
@@ -124,7 +126,7 @@ bl_status bitlinear_gemm_w158a4(int32_t fmt, const void* d_codes, const float* d
                                 const bl_epilogue* h_epi, void* stream) {
   const bl_status s = check_mm(fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, h_epi);
   if (s != BL_OK) return s;
-  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1) return BL_ERR_INVALID_ARGUMENT;
+  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT4_E3M2) return BL_ERR_INVALID_ARGUMENT;
   return run_mm(false, fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, h_epi, stream);
 }
 

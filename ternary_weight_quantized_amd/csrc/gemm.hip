@@ -1,46 +1,131 @@
-// BitLinear GEMMs on CDNA4 matrix cores: W1.58A4 (INT4 and FP4 E2M1) and W1.58A8 (sparse INT8).
+// BitLinear GEMMs on CDNA4 matrix cores: W1.58A4 (INT4 on int8 or FP6 cores, FP4 E2M1) and
+// W1.58A8 (sparse INT8).
 //
 // "BitNet a4.8: 4-bit Activations for 1-bit LLMs" (architecture write-up), section 3.4:
 //   Y = Q_INT4(X) Q_w(W)^T ("4-Bit Activation Quantization for Gaussian-Like Inputs"),
 //   Y = (Q_INT8(X) . M) Q_w(W)^T ("Sparsification Pipeline ...", paper Eq. 1),
 //   ReLU^2 GLU epilogue ("Squared ReLU Gating ...", paper Eq. 5), residual add (section 3.2).
 //
-// Block tile 128 x 128 of Y, K step 256 (one packed weight tile), 4 waves in a 2 x 2 grid, each
-// wave 64 x 64 = 4 x 4 MFMA tiles of 16 x 16. Packed operands go global -> registers -> LDS
-// (double buffered); each wave expands its fragments in registers right before the MFMA:
-//   ternary 2-bit -> int8:  (w << s) & 0xC0C0C0C0 places a code in the top bits of a byte, i.e. 64*t;
-//   INT4 nibble   -> int8:  the nibble moved to the top of a byte is 16*c;
-//   INT8 codes are used as they are after a byte permutation.
-// The int32 accumulator therefore holds 1024*sum(c t) (INT4) or 64*sum(c t) (INT8), both far from
-// overflow for K < 2^18, and an exact arithmetic shift recovers sum(c t).
-// FP4 uses v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1 and unit block scales;
-// a ternary code placed in bits 2..3 of a nibble reads as E2M1 +-2.0, so the fp32 sum is
-// 2*sum(e t) = sum(doubled code * t), exact because every partial sum is an integer < 2^24.
+// Two kernels share the staging scheme: every K step of 256 (one packed weight tile) the block
+// copies its A rows and B tiles to LDS with 128-bit direct-to-LDS loads (no registers, double
+// buffered), A rows stored with a per-row chunk rotation that makes the fragment reads free of
+// bank conflicts; each wave then reads its fragments from LDS and feeds the matrix cores.
 //
-// The K order inside each 16- or 32-wide MFMA slice follows the packed weight word (see the public
-// header); activations are expanded into the same order, which leaves every dot product unchanged.
+//  k_gemm_mx  FP6 x FP4 / FP4 x FP4 (v_mfma_scale_f32_16x16x128_f8f6f4, unit block scales).
+//             4 waves, 256 x 256 block, 128 x 128 per wave. A is used as stored (E3M2 or E2M1);
+//             a ternary code placed in bits 2..3 of a nibble reads as E2M1 +-2.0, so the fp32 sum
+//             is 2*sum(c t) for E3M2 codes and sum(2e t) for E2M1 codes: integers below 2^24, exact.
+//  k_gemm_i8  int8 cores (v_mfma_i32_16x16x64_i8) for INT4 nibbles and INT8 codes. 8 waves.
+//             Fragments are expanded in registers: ternary -> 64*t via (w << s) & 0xC0C0C0C0,
+//             INT4 nibble -> 16*c by moving it to the top of a byte, INT8 bytes permuted; the int32
+//             accumulator holds 1024*sum(c t) (INT4) or 64*sum(c t) (INT8), exact after a shift.
+//
+// The K order inside each 16- or 32-wide MFMA slice follows the packed weight word (public header);
+// activations enter the MFMAs in the same order, which leaves every dot product unchanged.
 #include "bl_common.h"
 #include "bl_kernels.h"
 
 namespace {
 
-constexpr int BM = 128, BN = 128, NTHREADS = 256;
+typedef __attribute__((address_space(3))) void lds_void;
 
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Workgroup barrier without a memory fence. A __syncthreads() fence would wait for every
+// outstanding global load, including the next stage's prefetch, and so serialize load and compute.
+// The only LDS writes here are direct-to-LDS loads, made complete by an explicit vmcnt wait before
+// the barrier; LDS reads have returned (their data is consumed) before a wave reaches a barrier.
+// The "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// ----------------------------------------------------------------------------- A storage per format
 template <int FMT>
-struct ATraits {
-  static constexpr int ROW = (FMT == BL_ACT_INT8) ? 256 : 128;  // bytes of one A row per K step
-  static constexpr int STRIDE = ROW + 16;                       // padded LDS row stride
-  static constexpr int BYTES = BM * STRIDE;
-  static constexpr int CHUNKS = BM * ROW / 16;                  // 16-byte chunks per stage
-  static constexpr int PER_THREAD = CHUNKS / NTHREADS;
+struct AFmt {
+  static constexpr int ROW = FMT == BL_ACT_INT8 ? 256 : FMT == BL_ACT_INT4_E3M2 ? 192 : 128;  // bytes / K step
+  static constexpr int NCH = ROW / 16;                                                        // 16 B chunks
+  // chunk rotation of LDS row r (depends on r % 16 only); chosen so that the 16 lanes of a
+  // fragment read (rows r16 = 0..15) hit 16 disjoint bank groups
+  __device__ static __forceinline__ int rot(int r) {
+    const int r16 = r & 15;
+    return FMT == BL_ACT_INT8 ? r16 : FMT == BL_ACT_INT4_E3M2 ? (r16 >> 2) : ((r16 >> 1) & 7);
+  }
+  __device__ static __forceinline__ long row_bytes(int K) {
+    return FMT == BL_ACT_INT8 ? K : FMT == BL_ACT_INT4_E3M2 ? (3L * K / 4) : (K / 2);
+  }
 };
 
-template <int FMT, int EPI>
-struct Smem {
-  static constexpr int NB = (EPI == BL_EPI_RELU2_GLU) ? 2 : 1;
-  static constexpr int BBYTES = (BN / 16) * 1024;
-  static constexpr int STAGE = ATraits<FMT>::BYTES + NB * BBYTES;
+// One 16-byte-per-lane direct-to-LDS load: lane i's 16 bytes from gptr land at LDS byte address
+// lds_addr + 16 i (lds_addr is wave-uniform, passed in M0). Written as inline assembly so that the
+// compiler does not treat later LDS reads of the other stage buffer as dependent on it (it would
+// wait for every outstanding load); the kernels order these loads with explicit vmcnt waits and a
+// final vmcnt(0) before the waves end.
+__device__ __forceinline__ void dma16(const uint8_t* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Per-lane source offsets of this wave's share of the direct-to-LDS copies of one K step: A rows
+// [m0, m0+BM) (stored with the chunk rotation) and the B tiles of NB matrices x BN/16 tile rows.
+// Rows beyond M and tile rows beyond N are clamped to valid memory: they load real but unused
+// data (their outputs are never stored). The offsets are fixed for the whole K loop; step kb adds
+// kb * ROW to A and kb * 1024 to B.
+template <int FMT, int BM, int BN, int NB, int NW>
+struct StagePlan {
+  using F = AFmt<FMT>;
+  static constexpr int ASEG = BM * F::NCH / 64;           // 1 KB LDS segments of A
+  static constexpr int BSEG = NB * (BN / 16);             // 1 KB tiles of B
+  static_assert(ASEG % NW == 0 && BSEG % NW == 0, "every wave issues the same number of loads");
+  static constexpr int NA = ASEG / NW, NBL = BSEG / NW;
+  static constexpr int LOADS = NA + NBL;                  // loads per wave and stage
+  uint32_t aoff[NA];                                      // byte offset from A
+  uint32_t boff[NBL];                                     // byte offset from the tile row of its matrix
+  __device__ __forceinline__ void init(long arow, int m0, int M, int n0, int NG, int KB, int wave, int lane) {
+#pragma unroll
+    for (int qi = 0; qi < NA; ++qi) {
+      const int q = wave + NW * qi;
+      const int p = 64 * q + lane;                         // chunk position in the LDS tile
+      const int r = p / F::NCH, slot = p % F::NCH;
+      int c = slot - F::rot(r);
+      c += c < 0 ? F::NCH : 0;
+      const int m = min(m0 + r, M - 1);
+      aoff[qi] = (uint32_t)(m * arow + 16 * c);
+    }
+#pragma unroll
+    for (int qi = 0; qi < NBL; ++qi) {
+      const int q = wave + NW * qi;
+      const int t = q % (BN / 16);
+      const int G = min((n0 >> 4) + t, NG - 1);
+      boff[qi] = (uint32_t)(G * KB * 1024 + 16 * lane);
+    }
+  }
+  // issue the loads of K step kb into the stage buffer at LDS address lds
+  __device__ __forceinline__ void issue(uint32_t lds, const uint8_t* __restrict__ A, const uint8_t* const* Wm,
+                                        int kb, int wave) const {
+    const uint8_t* abase = A + (long)kb * F::ROW;
+#pragma unroll
+    for (int qi = 0; qi < NA; ++qi) dma16(abase + aoff[qi], lds + 1024u * (wave + NW * qi));
+#pragma unroll
+    for (int qi = 0; qi < NBL; ++qi) {
+      const int q = wave + NW * qi;
+      const int mtx = q / (BN / 16);
+      dma16(Wm[mtx] + (long)kb * 1024 + boff[qi], lds + BM * F::ROW + 1024u * q);
+    }
+  }
 };
+
+// Byte offset, inside an LDS A tile, of byte b (8-byte aligned, within one 16 B chunk) of row r.
+template <int FMT>
+__device__ __forceinline__ int a_off(int r, int b) {
+  using F = AFmt<FMT>;
+  int slot = (b >> 4) + F::rot(r);
+  slot -= slot >= F::NCH ? F::NCH : 0;
+  return r * F::ROW + 16 * slot + (b & 15);
+}
 
 __device__ __forceinline__ v4i expand_w_i8(uint32_t w) {
   v4i r;
@@ -76,232 +161,341 @@ __device__ __forceinline__ v8i expand_w_fp4(uint32_t w0, uint32_t w1) {
   r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
   return r;
 }
+__device__ __forceinline__ uint32_t word(const uint4& q, int i) {
+  return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
+}
 
-template <int FMT, int EPI>
-__global__ __launch_bounds__(NTHREADS, 1) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
-                                                       int M, int K, const uint8_t* __restrict__ W,
-                                                       const float* __restrict__ walpha,
-                                                       const uint8_t* __restrict__ W2,
-                                                       const float* __restrict__ w2alpha, int N,
-                                                       float* __restrict__ Y, long ldy,
-                                                       const float* R, long ldr,
-                                                       float* __restrict__ rowmax) {
-  using AT = ATraits<FMT>;
-  using SM = Smem<FMT, EPI>;
-  constexpr int NB = SM::NB;
-  constexpr bool FP4 = (FMT == BL_ACT_FP4_E2M1);
-  constexpr bool A8 = (FMT == BL_ACT_INT8);
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SM::STAGE];
+// Block -> tile mapping. Consecutive block ids go to the eight XCDs in turn, so ids are first
+// regrouped per XCD; inside an XCD the tiles are visited in groups of GROUP_M tile rows, so that
+// the blocks one XCD runs at the same time share A rows and B columns in its L2.
+__device__ __forceinline__ void tile_of(int b, int ntm, int ntn, int* tm, int* tn) {
+  const int nblocks = ntm * ntn;
+  if ((nblocks & 7) == 0) b = (b & 7) * (nblocks >> 3) + (b >> 3);
+  constexpr int GROUP_M = 4;
+  const int in_group = GROUP_M * ntn;
+  const int first_m = (b / in_group) * GROUP_M;
+  const int gm = min(ntm - first_m, GROUP_M);
+  const int r = b % in_group;
+  *tm = first_m + r % gm;
+  *tn = r / gm;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int KB = K >> 8;
-  const long arow = FP4 || !A8 ? (K >> 1) : K;     // bytes per A row in global memory
-  const int NG = N >> 4;
-
-  const uint8_t* Wm[2] = {W, W2};
-
-  uint4 ra[AT::PER_THREAD];
-  uint4 rb[NB][2];
-
-  auto gload = [&](int kb) {
+// fp32 epilogue for the 4 rows (mb .. mb+3) a lane holds in each 16x16 tile of one tile row.
+// acc(mtx, t, v) returns the exact sum of code products of matrix mtx, tile t, row v as a float.
+template <int EPI, int SN, typename AccFn>
+__device__ __forceinline__ void epilogue_rows(int mb, int nb, int r16, int M, int N, const float* __restrict__ ascale,
+                                              float alpha, float alpha2, float* __restrict__ Y, long ldy,
+                                              const float* R, long ldr, float* __restrict__ rowmax, AccFn acc) {
+  float rmax[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < AT::PER_THREAD; ++q) {
-      const int c = tid + NTHREADS * q;
-      const int r = c / (AT::ROW / 16), col = c % (AT::ROW / 16);
-      const int m = m0 + r;
-      if (m < M)
-        ra[q] = *reinterpret_cast<const uint4*>(A + (long)m * arow + (long)kb * AT::ROW + col * 16);
-      else
-        ra[q] = make_uint4(0u, 0u, 0u, 0u);
+  for (int v = 0; v < 4; ++v) {
+    const int m = mb + v;
+    const bool mok = m < M;
+    const float ds = mok ? ascale[m] : 0.f;
+    const float sc = ds * alpha;
+    const float sc2 = ds * alpha2;
+#pragma unroll
+    for (int t = 0; t < SN; ++t) {
+      const int n = nb + 16 * t + r16;
+      if (!mok || n >= N) continue;
+      const float y0 = acc(0, t, v) * sc;
+      float out;
+      if constexpr (EPI == BL_EPI_RESIDUAL) {
+        out = y0 + R[(long)m * ldr + n];
+      } else if constexpr (EPI == BL_EPI_RELU2_GLU) {
+        const float u0 = acc(1, t, v) * sc2;
+        const float gp = y0 > 0.f ? y0 : 0.f;
+        out = (gp * gp) * u0;
+        const float a = fabsf(out);
+        rmax[v] = a > rmax[v] ? a : rmax[v];
+      } else {
+        out = y0;
+      }
+      Y[(long)m * ldy + n] = out;
     }
-#pragma unroll
-    for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int c = tid + NTHREADS * q;
-        const int t = c >> 6, L = c & 63;
-        const int G = (n0 >> 4) + t;
-        if (G < NG)
-          rb[mtx][q] = *reinterpret_cast<const uint4*>(Wm[mtx] + ((long)G * KB + kb) * 1024 + L * 16);
-        else
-          rb[mtx][q] = make_uint4(0u, 0u, 0u, 0u);
-      }
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* base = smem + buf * SM::STAGE;
-#pragma unroll
-    for (int q = 0; q < AT::PER_THREAD; ++q) {
-      const int c = tid + NTHREADS * q;
-      const int r = c / (AT::ROW / 16), col = c % (AT::ROW / 16);
-      *reinterpret_cast<uint4*>(base + r * AT::STRIDE + col * 16) = ra[q];
-    }
-#pragma unroll
-    for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int c = tid + NTHREADS * q;
-        *reinterpret_cast<uint4*>(base + AT::BYTES + mtx * SM::BBYTES + c * 16) = rb[mtx][q];
-      }
-  };
-
-  // accumulators: [matrix][m subtile][n subtile]
-  v4i acci[NB][4][4];
-  v4f accf[NB][4][4];
-#pragma unroll
-  for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        acci[mtx][s][t] = v4i{0, 0, 0, 0};
-        accf[mtx][s][t] = v4f{0.f, 0.f, 0.f, 0.f};
-      }
-
-  const int r16 = lane & 15, g4 = lane >> 4;
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < KB) gload(kb + 1);
-    const uint8_t* As = smem + buf * SM::STAGE;
-    const uint8_t* Bs = As + AT::BYTES;
-    uint4 bw[NB][4];
-#pragma unroll
-    for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        bw[mtx][t] = *reinterpret_cast<const uint4*>(Bs + mtx * SM::BBYTES + (wn * 4 + t) * 1024 + lane * 16);
-
-    if constexpr (FP4) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        v8i bf[NB][4];
-#pragma unroll
-        for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t w0 = j ? bw[mtx][t].z : bw[mtx][t].x;
-            const uint32_t w1 = j ? bw[mtx][t].w : bw[mtx][t].y;
-            bf[mtx][t] = expand_w_fp4(w0, w1);
-          }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int row = wm * 64 + 16 * s + r16;
-          const uint4 q = *reinterpret_cast<const uint4*>(As + row * AT::STRIDE + 32 * g4 + 16 * j);
-          const v8i a = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-#pragma unroll
-          for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              accf[mtx][s][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  a, bf[mtx][t], accf[mtx][s][t], 4, 4, 0, 127, 0, 127);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v4i bf[NB][4];
-#pragma unroll
-        for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t w = i == 0 ? bw[mtx][t].x : i == 1 ? bw[mtx][t].y : i == 2 ? bw[mtx][t].z : bw[mtx][t].w;
-            bf[mtx][t] = expand_w_i8(w);
-          }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int row = wm * 64 + 16 * s + r16;
-          v4i a;
-          if constexpr (A8) {
-            const uint4 q = *reinterpret_cast<const uint4*>(As + row * AT::STRIDE + 64 * g4 + 16 * i);
-            // zero-slice skip: a 16-row x 64-k slice of all-zero codes contributes nothing
-            if (__ballot((q.x | q.y | q.z | q.w) != 0u) == 0ull) continue;
-            a = expand_a_int8(q);
-          } else {
-            const uint2 p = *reinterpret_cast<const uint2*>(As + row * AT::STRIDE + 32 * g4 + 8 * i);
-            a = expand_a_int4(p.x, p.y);
-          }
-#pragma unroll
-          for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              acci[mtx][s][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bf[mtx][t], acci[mtx][s][t], 0, 0, 0);
-        }
-      }
-    }
-    if (kb + 1 < KB) sstore(buf ^ 1);
-    __syncthreads();
   }
-
-  // ------------------------------------------------------------------ epilogue (fp32, fixed order)
-  const float alpha = *walpha;
-  const float alpha2 = (EPI == BL_EPI_RELU2_GLU) ? *w2alpha : 0.f;
-  constexpr int SHIFT = A8 ? 6 : 10;
+  if constexpr (EPI == BL_EPI_RELU2_GLU) {
+    if (rowmax) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int mb = m0 + wm * 64 + 16 * s + 4 * g4;
-    float rmax[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = mb + v;
-      const bool mok = m < M;
-      const float ds = mok ? ascale[m] : 0.f;
-      const float sc = ds * alpha;
-      const float sc2 = ds * alpha2;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = n0 + wn * 64 + 16 * t + r16;
-        if (!mok || n >= N) continue;
-        float y0, u0 = 0.f;
-        if constexpr (FP4) {
-          y0 = (accf[0][s][t][v] * 0.5f) * sc;
-          if constexpr (EPI == BL_EPI_RELU2_GLU) u0 = (accf[1][s][t][v] * 0.5f) * sc2;
-        } else {
-          y0 = (float)(acci[0][s][t][v] >> SHIFT) * sc;
-          if constexpr (EPI == BL_EPI_RELU2_GLU) u0 = (float)(acci[NB - 1][s][t][v] >> SHIFT) * sc2;
-        }
-        float out;
-        if constexpr (EPI == BL_EPI_RESIDUAL) {
-          out = y0 + R[(long)m * ldr + n];
-        } else if constexpr (EPI == BL_EPI_RELU2_GLU) {
-          const float gp = y0 > 0.f ? y0 : 0.f;
-          out = (gp * gp) * u0;
-          const float a = fabsf(out);
-          rmax[v] = a > rmax[v] ? a : rmax[v];
-        } else {
-          out = y0;
-        }
-        Y[(long)m * ldy + n] = out;
-      }
-    }
-    if constexpr (EPI == BL_EPI_RELU2_GLU) {
-      if (rowmax) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float r = rmax[v];
-          r = fmaxf(r, __shfl_xor(r, 1, 64));
-          r = fmaxf(r, __shfl_xor(r, 2, 64));
-          r = fmaxf(r, __shfl_xor(r, 4, 64));
-          r = fmaxf(r, __shfl_xor(r, 8, 64));
-          const int m = mb + v;
-          if (r16 == 0 && m < M) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, bl_f2u(r));
-        }
+      for (int v = 0; v < 4; ++v) {
+        float r = rmax[v];
+        r = fmaxf(r, __shfl_xor(r, 1, 64));
+        r = fmaxf(r, __shfl_xor(r, 2, 64));
+        r = fmaxf(r, __shfl_xor(r, 4, 64));
+        r = fmaxf(r, __shfl_xor(r, 8, 64));
+        const int m = mb + v;
+        if (r16 == 0 && m < M) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, bl_f2u(r));
       }
     }
   }
 }
 
+// ============================================================================ FP6 / FP4 matrix cores
+template <int FMT, int EPI>
+struct CfgMx {
+  static constexpr bool GLU = (EPI == BL_EPI_RELU2_GLU);
+  static constexpr int NB = GLU ? 2 : 1;
+  static constexpr int NW = 4, WGM = 2, WGN = 2;
+  static constexpr int BM = 256, BN = GLU ? 128 : 256;
+  static constexpr int SM = BM / WGM / 16, SN = BN / WGN / 16;
+  static constexpr int STAGE = BM * AFmt<FMT>::ROW + NB * (BN / 16) * 1024;
+  using Plan = StagePlan<FMT, BM, BN, NB, NW>;
+};
+
+template <int FMT, int EPI>
+__global__ __launch_bounds__(256, 1) void k_gemm_mx(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
+                                                     int M, int K, const uint8_t* __restrict__ W,
+                                                     const float* __restrict__ walpha,
+                                                     const uint8_t* __restrict__ W2,
+                                                     const float* __restrict__ w2alpha, int N,
+                                                     float* __restrict__ Y, long ldy, const float* R, long ldr,
+                                                     float* __restrict__ rowmax) {
+  using C = CfgMx<FMT, EPI>;
+  using F = AFmt<FMT>;
+  constexpr int NB = C::NB, SM = C::SM, SN = C::SN;
+  constexpr bool FP6 = (FMT == BL_ACT_INT4_E3M2);
+  constexpr int CBSZ = FP6 ? 3 : 4;                  // A operand: FP6 E3M2 or FP4 E2M1
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];   // two stage buffers
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int ntm = (M + C::BM - 1) / C::BM, ntn = (N + C::BN - 1) / C::BN;
+  int tm, tn;
+  tile_of(blockIdx.x, ntm, ntn, &tm, &tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int KB = K >> 8, NG = N >> 4;
+  const long arow = F::row_bytes(K);
+  const uint8_t* Wm[2] = {W, W2};
+  const int r16 = lane & 15, g4 = lane >> 4;
+
+  v4f acc[NB][SM][SN];
+#pragma unroll
+  for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+    for (int s = 0; s < SM; ++s)
+#pragma unroll
+      for (int t = 0; t < SN; ++t) acc[mtx][s][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // lane-constant LDS offsets of the A fragment parts (row r16 of the wave's first 16-row subtile):
+  // E3M2: 24 bytes at 48 g + 24 j as three 8-byte parts; E2M1: 16 bytes at 32 g + 16 j (one chunk)
+  const int arow0 = wm * SM * 16 + r16;
+  int aoff[2][3];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      aoff[j][p] = FP6 ? a_off<FMT>(arow0, 48 * g4 + 24 * j + 8 * p) : a_off<FMT>(arow0, 32 * g4 + 16 * j);
+
+  // one K step: wait for stage kb in `cur`, prefetch stage kb+1 into `nxt`, compute from `cur`
+  typename C::Plan plan;
+  plan.init(arow, m0, M, n0, NG, KB, wave, lane);
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto kstep = [&](int kb, const uint8_t* cur, uint32_t nxt) {
+    // every step issues the same number of loads (the last ones re-fetch a valid stage that is
+    // never read), so the wait below is the same on every path
+    plan.issue(nxt, A, Wm, min(kb + 1, KB - 1), wave);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::Plan::LOADS));
+    lds_barrier();
+    const uint8_t* Bs = cur + C::BM * F::ROW + (wn * SN) * 1024 + 16 * lane;
+    uint4 bw[NB][SN];
+#pragma unroll
+    for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+      for (int t = 0; t < SN; ++t)
+        bw[mtx][t] = *reinterpret_cast<const uint4*>(Bs + mtx * (C::BN / 16) * 1024 + t * 1024);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_sched_barrier(0);   // keep each K slice's loads and MFMAs together (register pressure)
+      v8i bf[NB][SN];
+#pragma unroll
+      for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+        for (int t = 0; t < SN; ++t) bf[mtx][t] = expand_w_fp4(word(bw[mtx][t], 2 * j), word(bw[mtx][t], 2 * j + 1));
+      // A fragments are read one 16-row subtile ahead of the MFMAs that use them
+      auto load_a = [&](int s) -> v8i {
+        const uint8_t* ar = cur + s * 16 * F::ROW;
+        if constexpr (FP6) {
+          // 24 bytes: j = 0 -> 16 + 8 bytes, j = 1 -> 8 + 16 bytes (each part inside one 16 B chunk)
+          if (j == 0) {
+            const uint4 p0 = *reinterpret_cast<const uint4*>(ar + aoff[0][0]);
+            const uint2 p1 = *reinterpret_cast<const uint2*>(ar + aoff[0][2]);
+            return v8i{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, 0, 0};
+          } else {
+            const uint2 p0 = *reinterpret_cast<const uint2*>(ar + aoff[1][0]);
+            const uint4 p1 = *reinterpret_cast<const uint4*>(ar + aoff[1][1]);
+            return v8i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w, 0, 0};
+          }
+        } else {
+          const uint4 q = *reinterpret_cast<const uint4*>(ar + aoff[j][0]);
+          return v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        }
+      };
+      v8i a_next = load_a(0);
+#pragma unroll
+      for (int s = 0; s < SM; ++s) {
+        const v8i a = a_next;
+        if (s + 1 < SM) a_next = load_a(s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+          for (int t = 0; t < SN; ++t)
+            acc[mtx][s][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf[mtx][t], acc[mtx][s][t], CBSZ, 4,
+                                                                              0, 127, 0, 127);
+      }
+    }
+    lds_barrier();
+  };
+  plan.issue(lds0, A, Wm, 0, wave);
+  for (int kb = 0; kb < KB; ++kb)
+    kstep(kb, smem + (kb & 1) * C::STAGE, lds0 + ((kb + 1) & 1) * C::STAGE);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the last (unused) prefetch lands before the waves end
+
+  // fp32 epilogue: the matrix-core sum is 2*sum(c t) (E3M2) or sum(2e t) = sum(doubled code * t)
+  // (E2M1); x 0.5 is exact and gives sum(c t), respectively the half-unit count of the oracle.
+  const float alpha = *walpha;
+  const float alpha2 = C::GLU ? *w2alpha : 0.f;
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    const int mb = m0 + wm * SM * 16 + 16 * s + 4 * g4;
+    const int nb = n0 + wn * SN * 16;
+    epilogue_rows<EPI, SN>(mb, nb, r16, M, N, ascale, alpha, alpha2, Y, ldy, R, ldr, rowmax,
+                           [&](int mtx, int t, int v) { return acc[mtx][s][t][v] * 0.5f; });
+  }
+}
+
+// ============================================================================ int8 matrix cores
+template <int FMT, int EPI>
+struct CfgI8 {
+  static constexpr bool A8 = (FMT == BL_ACT_INT8);
+  static constexpr bool GLU = (EPI == BL_EPI_RELU2_GLU);
+  static constexpr int NB = GLU ? 2 : 1;
+  static constexpr int NW = 8, WGM = 2, WGN = 4;
+  static constexpr int BM = A8 ? 128 : 256, BN = GLU ? 128 : 256;
+  static constexpr int SM = BM / WGM / 16, SN = BN / WGN / 16;
+  static constexpr int STAGE = BM * AFmt<FMT>::ROW + NB * (BN / 16) * 1024;
+  using Plan = StagePlan<FMT, BM, BN, NB, NW>;
+};
+
+template <int FMT, int EPI>
+__global__ __launch_bounds__(512, 1) void k_gemm_i8(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
+                                                     int M, int K, const uint8_t* __restrict__ W,
+                                                     const float* __restrict__ walpha,
+                                                     const uint8_t* __restrict__ W2,
+                                                     const float* __restrict__ w2alpha, int N,
+                                                     float* __restrict__ Y, long ldy, const float* R, long ldr,
+                                                     float* __restrict__ rowmax) {
+  using C = CfgI8<FMT, EPI>;
+  using F = AFmt<FMT>;
+  constexpr int NB = C::NB, SM = C::SM, SN = C::SN;
+  constexpr bool A8 = C::A8;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];   // two stage buffers
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int ntm = (M + C::BM - 1) / C::BM, ntn = (N + C::BN - 1) / C::BN;
+  int tm, tn;
+  tile_of(blockIdx.x, ntm, ntn, &tm, &tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int KB = K >> 8, NG = N >> 4;
+  const long arow = F::row_bytes(K);
+  const uint8_t* Wm[2] = {W, W2};
+  const int r16 = lane & 15, g4 = lane >> 4;
+
+  v4i acc[NB][SM][SN];
+#pragma unroll
+  for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+    for (int s = 0; s < SM; ++s)
+#pragma unroll
+      for (int t = 0; t < SN; ++t) acc[mtx][s][t] = v4i{0, 0, 0, 0};
+
+  // lane-constant fragment offsets: INT8 16 bytes at 64 g + 16 i, INT4 8 bytes at 32 g + 8 i
+  const int arow0 = wm * SM * 16 + r16;
+  int aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) aoff[i] = A8 ? a_off<FMT>(arow0, 64 * g4 + 16 * i) : a_off<FMT>(arow0, 32 * g4 + 8 * i);
+
+  typename C::Plan plan;
+  plan.init(arow, m0, M, n0, NG, KB, wave, lane);
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto kstep = [&](int kb, const uint8_t* cur, uint32_t nxt) {
+    // every step issues the same number of loads (the last ones re-fetch a valid stage that is
+    // never read), so the wait below is the same on every path
+    plan.issue(nxt, A, Wm, min(kb + 1, KB - 1), wave);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::Plan::LOADS));
+    lds_barrier();
+    const uint8_t* Bs = cur + C::BM * F::ROW + (wn * SN) * 1024 + 16 * lane;
+    uint4 bw[NB][SN];
+#pragma unroll
+    for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+      for (int t = 0; t < SN; ++t)
+        bw[mtx][t] = *reinterpret_cast<const uint4*>(Bs + mtx * (C::BN / 16) * 1024 + t * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_barrier(0);   // keep each K slice's loads and MFMAs together (register pressure)
+      v4i bf[NB][SN];
+#pragma unroll
+      for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+        for (int t = 0; t < SN; ++t) bf[mtx][t] = expand_w_i8(word(bw[mtx][t], i));
+#pragma unroll
+      for (int s = 0; s < SM; ++s) {
+        const uint8_t* ar = cur + s * 16 * F::ROW;
+        v4i a;
+        if constexpr (A8) {
+          const uint4 q = *reinterpret_cast<const uint4*>(ar + aoff[i]);
+          // zero-slice skip: a 16-row x 64-k slice of all-zero codes contributes nothing
+          if (__ballot((q.x | q.y | q.z | q.w) != 0u) == 0ull) continue;
+          a = expand_a_int8(q);
+        } else {
+          const uint2 p = *reinterpret_cast<const uint2*>(ar + aoff[i]);
+          a = expand_a_int4(p.x, p.y);
+        }
+#pragma unroll
+        for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+          for (int t = 0; t < SN; ++t)
+            acc[mtx][s][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bf[mtx][t], acc[mtx][s][t], 0, 0, 0);
+      }
+    }
+    lds_barrier();
+  };
+  plan.issue(lds0, A, Wm, 0, wave);
+  for (int kb = 0; kb < KB; ++kb)
+    kstep(kb, smem + (kb & 1) * C::STAGE, lds0 + ((kb + 1) & 1) * C::STAGE);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the last (unused) prefetch lands before the waves end
+
+  const float alpha = *walpha;
+  const float alpha2 = C::GLU ? *w2alpha : 0.f;
+  constexpr int SHIFT = A8 ? 6 : 10;
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    const int mb = m0 + wm * SM * 16 + 16 * s + 4 * g4;
+    const int nb = n0 + wn * SN * 16;
+    epilogue_rows<EPI, SN>(mb, nb, r16, M, N, ascale, alpha, alpha2, Y, ldy, R, ldr, rowmax,
+                           [&](int mtx, int t, int v) { return (float)(acc[mtx][s][t][v] >> SHIFT); });
+  }
+}
+
+// ----------------------------------------------------------------------------- launchers
 template <int FMT, int EPI>
 hipError_t launch(const bl_mm_args& a, hipStream_t st) {
-  const dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM), block(NTHREADS);
-  hipLaunchKernelGGL((k_gemm<FMT, EPI>), grid, block, 0, st, static_cast<const uint8_t*>(a.A), a.ascale, a.M, a.K,
-                     static_cast<const uint8_t*>(a.W), a.walpha, static_cast<const uint8_t*>(a.W2), a.w2alpha, a.N,
-                     a.Y, a.ldy, a.R, a.ldr, a.rowmax);
+  const uint8_t* A = static_cast<const uint8_t*>(a.A);
+  const uint8_t* W = static_cast<const uint8_t*>(a.W);
+  const uint8_t* W2 = static_cast<const uint8_t*>(a.W2);
+  if constexpr (FMT == BL_ACT_FP4_E2M1 || FMT == BL_ACT_INT4_E3M2) {
+    using C = CfgMx<FMT, EPI>;
+    const int ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
+    hipLaunchKernelGGL((k_gemm_mx<FMT, EPI>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A, a.ascale, a.M, a.K, W,
+                       a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
+  } else {
+    using C = CfgI8<FMT, EPI>;
+    const int ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
+    hipLaunchKernelGGL((k_gemm_i8<FMT, EPI>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A, a.ascale, a.M, a.K, W,
+                       a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
+  }
   return hipGetLastError();
 }
 
@@ -325,7 +519,10 @@ hipError_t bl_launch_fill_zero(float* p, long n, hipStream_t st) {
 }
 
 hipError_t bl_launch_gemm(const bl_mm_args& a, hipStream_t st) {
-  if (a.fmt == BL_ACT_INT4) return launch_epi<BL_ACT_INT4>(a, st);
-  if (a.fmt == BL_ACT_FP4_E2M1) return launch_epi<BL_ACT_FP4_E2M1>(a, st);
-  return launch_epi<BL_ACT_INT8>(a, st);
+  switch (a.fmt) {
+    case BL_ACT_INT4: return launch_epi<BL_ACT_INT4>(a, st);
+    case BL_ACT_FP4_E2M1: return launch_epi<BL_ACT_FP4_E2M1>(a, st);
+    case BL_ACT_INT4_E3M2: return launch_epi<BL_ACT_INT4_E3M2>(a, st);
+    default: return launch_epi<BL_ACT_INT8>(a, st);
+  }
 }

@@ -81,6 +81,24 @@ __device__ __forceinline__ uint32_t code_fp4(float v, float s) {
 __device__ __forceinline__ uint32_t code_int8(float v, float s) {
   return (uint32_t)bl_roundclip(v * s, -128.f, 127.f) & 0xFFu;
 }
+// INT4 code -> its exact FP6 E3M2 bit pattern (sign bit 5, exponent bias 3, 2 mantissa bits).
+// Magnitudes 0..8 encode as 00 0C 10 12 14 15 16 17 18 (five bits each, packed in one constant).
+__device__ __forceinline__ uint32_t code_e3m2(float v, float s) {
+  const int c = bl_roundclip(v * s, -8.f, 7.f);
+  const uint32_t a = (uint32_t)(c < 0 ? -c : c);
+  constexpr unsigned long long MAG = (0x00ull) | (0x0Cull << 5) | (0x10ull << 10) | (0x12ull << 15) |
+                                     (0x14ull << 20) | (0x15ull << 25) | (0x16ull << 30) | (0x17ull << 35) |
+                                     (0x18ull << 40);
+  return (uint32_t)((MAG >> (5 * a)) & 31ull) | (c < 0 ? 0x20u : 0u);
+}
+// Store the 4 codes (24 bits, code j at bits 6j) of elements 256g + 4 lane .. +3 into a row of
+// E3M2 codes (code k at bits [6k, 6k+6)): four lanes make 12 bytes, written as three dwords.
+__device__ __forceinline__ void store_e3m2(uint8_t* __restrict__ crow, int g, int lane, uint32_t v24) {
+  const uint32_t nxt = __shfl_down(v24, 1, 64);
+  const int i = lane & 3;
+  const uint32_t w = i == 0 ? (v24 | (nxt << 24)) : i == 1 ? ((v24 >> 8) | (nxt << 16)) : ((v24 >> 16) | (nxt << 8));
+  if (i < 3) *reinterpret_cast<uint32_t*>(crow + 192 * g + 12 * (lane >> 2) + 4 * i) = w;
+}
 
 // Top-K threshold: the largest key T with count(|x| >= T) >= keep, found bit by bit.
 // bf16 inputs have 16 zero low bits in their float32 key, so their search stops at bit 16.
@@ -111,7 +129,7 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
                                                    int keep, float eps, const float* __restrict__ hint,
                                                    uint8_t* __restrict__ codes, float* __restrict__ scale,
                                                    uint32_t* __restrict__ mask) {
-  __shared__ unsigned long long bins[FMT == BL_ACT_INT4 ? 4 : 1][256];
+  __shared__ unsigned long long bins[(FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2) ? 4 : 1][256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
   if (row >= M) return;                         // wave-uniform; no block barriers below
@@ -122,7 +140,7 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
   for (int g = 0; g < NGMAX; ++g)
     if (g < NG) load4<IN_F32>(x, base + 256 * g, v[g]);
 
-  if constexpr (FMT == BL_ACT_INT4) {
+  if constexpr (FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2) {
     AbsSum acc;
 #pragma unroll
     for (int g = 0; g < NGMAX; ++g)
@@ -145,14 +163,23 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
     }
     const float beta = (float)(S / (double)K);
     const float s = bl_u2f(BL_SQRT7_BITS) / (beta + eps);
-    uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
+    if constexpr (FMT == BL_ACT_INT4) {
+      uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
 #pragma unroll
-    for (int g = 0; g < NGMAX; ++g)
-      if (g < NG) {
-        const uint32_t c = code_int4(v[g][0], s) | (code_int4(v[g][1], s) << 4) |
-                           (code_int4(v[g][2], s) << 8) | (code_int4(v[g][3], s) << 12);
-        crow[64 * g] = (uint16_t)c;
-      }
+      for (int g = 0; g < NGMAX; ++g)
+        if (g < NG) {
+          const uint32_t c = code_int4(v[g][0], s) | (code_int4(v[g][1], s) << 4) |
+                             (code_int4(v[g][2], s) << 8) | (code_int4(v[g][3], s) << 12);
+          crow[64 * g] = (uint16_t)c;
+        }
+    } else {
+      uint8_t* crow = codes + (long)row * (3L * K / 4);
+#pragma unroll
+      for (int g = 0; g < NGMAX; ++g)
+        if (g < NG)
+          store_e3m2(crow, g, lane, code_e3m2(v[g][0], s) | (code_e3m2(v[g][1], s) << 6) |
+                                        (code_e3m2(v[g][2], s) << 12) | (code_e3m2(v[g][3], s) << 18));
+    }
     if (lane == 0) scale[row] = beta / bl_u2f(BL_SQRT7_BITS);
   } else {
     // gamma = max |x| over the whole row (exact); FP4 and INT8 share it.
@@ -262,14 +289,14 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
                                                       int keep, float eps, const float* __restrict__ hint,
                                                       uint8_t* __restrict__ codes, float* __restrict__ scale,
                                                       uint32_t* __restrict__ mask) {
-  __shared__ unsigned long long bins[FMT == BL_ACT_INT4 ? 4 : 1][256];
+  __shared__ unsigned long long bins[(FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2) ? 4 : 1][256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
   if (row >= M) return;
   const int NG = K >> 8;
   const long base = (long)row * ldx + 4 * lane;
 
-  if constexpr (FMT == BL_ACT_INT4) {
+  if constexpr (FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2) {
     AbsSum acc;
     for (int g = 0; g < NG; ++g) {
       float v[4];
@@ -292,12 +319,18 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
     }
     const float beta = (float)(S / (double)K);
     const float s = bl_u2f(BL_SQRT7_BITS) / (beta + eps);
-    uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
     for (int g = 0; g < NG; ++g) {
       float v[4];
       load4<IN_F32>(x, base + 256 * g, v);
-      crow[64 * g] = (uint16_t)(code_int4(v[0], s) | (code_int4(v[1], s) << 4) |
-                                 (code_int4(v[2], s) << 8) | (code_int4(v[3], s) << 12));
+      if constexpr (FMT == BL_ACT_INT4) {
+        uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;
+        crow[64 * g] = (uint16_t)(code_int4(v[0], s) | (code_int4(v[1], s) << 4) |
+                                   (code_int4(v[2], s) << 8) | (code_int4(v[3], s) << 12));
+      } else {
+        store_e3m2(codes + (long)row * (3L * K / 4), g, lane,
+                   code_e3m2(v[0], s) | (code_e3m2(v[1], s) << 6) | (code_e3m2(v[2], s) << 12) |
+                       (code_e3m2(v[3], s) << 18));
+      }
     }
     if (lane == 0) scale[row] = beta / bl_u2f(BL_SQRT7_BITS);
   } else {
@@ -419,6 +452,9 @@ hipError_t bl_launch_quantize(const void* x, int in_f32, int M, int K, long ldx,
   if (fmt == BL_ACT_INT4)
     return in_f32 ? launch_fmt<BL_ACT_INT4, 1>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st)
                   : launch_fmt<BL_ACT_INT4, 0>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st);
+  if (fmt == BL_ACT_INT4_E3M2)
+    return in_f32 ? launch_fmt<BL_ACT_INT4_E3M2, 1>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st)
+                  : launch_fmt<BL_ACT_INT4_E3M2, 0>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st);
   if (fmt == BL_ACT_FP4_E2M1)
     return in_f32 ? launch_fmt<BL_ACT_FP4_E2M1, 1>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st)
                   : launch_fmt<BL_ACT_FP4_E2M1, 0>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st);

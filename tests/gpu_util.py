@@ -41,6 +41,26 @@ def int4_values(codes_u8):
     return np.where(n >= 8, n - 16, n).astype(np.int8)
 
 
+def e3m2_values(codes_u8):
+    """uint8 [M, 3K/4] of 6-bit FP6 E3M2 fields (code k at bits [6k, 6k+6) of the row) -> int8 [M, K].
+
+    Decoded from the format definition (sign, 3 exponent bits with bias 3, 2 mantissa bits); every
+    field must hold an integer in [-8, 7].
+    """
+    b = np.asarray(codes_u8, dtype=np.uint32)
+    M, nb = b.shape
+    g = b.reshape(M, nb // 3, 3)
+    w = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)                       # 4 codes per 24 bits
+    f = np.stack([(w >> (6 * j)) & 63 for j in range(4)], axis=-1).reshape(M, -1)
+    sign = np.where(f & 32, -1.0, 1.0)
+    e = (f >> 2) & 7
+    m = (f & 3).astype(np.float64)
+    mag = np.where(e == 0, m / 16.0, np.exp2(e.astype(np.float64) - 3) * (1 + m / 4))
+    v = sign * mag
+    assert np.all(v == np.rint(v)) and v.min(initial=0) >= -8 and v.max(initial=0) <= 7, "non-INT4 E3M2 field"
+    return v.astype(np.int8)
+
+
 def int8_values(codes_u8):
     return np.asarray(codes_u8, dtype=np.uint8).view(np.int8)
 

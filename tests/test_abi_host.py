@@ -121,6 +121,7 @@ def test_matmul_validation(name, kw, status):
 def test_format_restrictions():
     assert _mm("bitlinear_gemm_w158a4", fmt=2) == 1          # INT8 goes through the sparse A8 entry point
     assert _mm("bitlinear_gemv_decode", fmt=1) == 1          # decode takes INT4 or INT8
+    assert _mm("bitlinear_gemv_decode", fmt=3) == 1
     assert _mm("bitlinear_gemv_decode", M=9) == 2            # decode is for at most 8 tokens
     assert _mm("bitlinear_gemm_w158a4", fmt=5) == 1
 

@@ -10,8 +10,8 @@ import pytest
 import oracle as O
 import ternary_weight_quantized_amd as tw
 from synth import activations_bf16, latent_weights, normal, to_bf16_bits
-from tests.gpu_util import (assert_y_close, dev_bf16, dev_f32, host, int4_values, int8_values, mask_bits,
-                            nibbles, torch_cuda, x_f32)
+from tests.gpu_util import (assert_y_close, dev_bf16, dev_f32, e3m2_values, host, int4_values, int8_values,
+                            mask_bits, nibbles, torch_cuda, x_f32)
 from tests.packed_layout import unpack_ternary
 
 pytestmark = pytest.mark.gpu
@@ -89,14 +89,16 @@ def test_pack_ternary_wide_exponents_and_zero():
 QSHAPES = [(1, 256), (7, 768), (64, 2048), (33, 4096), (9, 4352), (6, 11008)]
 
 
+@pytest.mark.parametrize("fmt", ["int4", "int4_e3m2"])
 @pytest.mark.parametrize("f32", [False, True])
 @pytest.mark.parametrize("M,K", QSHAPES)
-def test_quantize_int4(M, K, f32):
+def test_quantize_int4(M, K, f32, fmt):
     torch_cuda()
     x = make_x(1000 + M + K, M, K, f32)
-    codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), "int4", eps=EPS)
+    codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), fmt, eps=EPS)
     c, d, _ = O.quant_int4(x_f32(x), EPS)
-    np.testing.assert_array_equal(int4_values(host(codes)), c)
+    decode = int4_values if fmt == "int4" else e3m2_values
+    np.testing.assert_array_equal(decode(host(codes)), c)
     np.testing.assert_array_equal(host(scale), d)
 
 
@@ -171,7 +173,7 @@ GSHAPES = [(1, 16, 256), (200, 272, 512), (129, 144, 768), (64, 2048, 2048)]
 
 def _quant(x, fmt, keep=-1):
     codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), fmt, topk_keep=keep, eps=EPS)
-    if fmt == "int4":
+    if fmt in ("int4", "int4_e3m2"):
         c, d, _ = O.quant_int4(x_f32(x), EPS)
         return codes, scale, c, d, 1.0
     if fmt == "fp4":
@@ -181,8 +183,11 @@ def _quant(x, fmt, keep=-1):
     return codes, scale, c, d, 1.0
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp4"])
-@pytest.mark.parametrize("M,N,K", GSHAPES)
+A4_FMTS = ["int4", "int4_e3m2", "fp4"]
+
+
+@pytest.mark.parametrize("fmt", A4_FMTS)
+@pytest.mark.parametrize("M,N,K", GSHAPES + [(300, 528, 1280)])
 def test_gemm_a4(fmt, M, N, K):
     torch_cuda()
     x = make_x(4000 + M, M, K)
@@ -192,7 +197,7 @@ def test_gemm_a4(fmt, M, N, K):
     assert_y_close(host(y), O.gemm_int(c, t), d, alpha, unit)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp4"])
+@pytest.mark.parametrize("fmt", A4_FMTS)
 @pytest.mark.parametrize("M,N,K", [(200, 272, 512), (3, 48, 1024)])
 def test_gemm_a4_residual_inplace(fmt, M, N, K):
     torch_cuda()
@@ -205,8 +210,8 @@ def test_gemm_a4_residual_inplace(fmt, M, N, K):
     assert_y_close(host(y), O.gemm_int(c, t), d, alpha, unit, residual=r)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp4"])
-@pytest.mark.parametrize("M,N,K", [(200, 272, 512), (64, 2048, 2048)])
+@pytest.mark.parametrize("fmt", A4_FMTS)
+@pytest.mark.parametrize("M,N,K", [(200, 272, 512), (64, 2048, 2048), (257, 400, 768)])
 def test_gemm_a4_relu2_glu(fmt, M, N, K):
     torch = torch_cuda()
     x = make_x(4500 + M, M, K, special=False)     # (rows scaled by 2^70 would overflow g^2: out of contract)
@@ -223,7 +228,7 @@ def test_gemm_a4_relu2_glu(fmt, M, N, K):
     np.testing.assert_array_equal(host(rowmax), np.abs(h_ref).max(axis=1))
 
 
-@pytest.mark.parametrize("M,N,K", GSHAPES + [(40, 64, 11008)])
+@pytest.mark.parametrize("M,N,K", GSHAPES + [(40, 64, 11008), (300, 528, 1280)])
 @pytest.mark.parametrize("keep_frac", [None, 0.5])
 def test_gemm_a8_sparse(M, N, K, keep_frac):
     torch_cuda()
@@ -288,6 +293,20 @@ def test_decode_epilogues(fmt):
     h_ref = O.relu2_glu(O.dequant_f32(acc, d, alpha), O.dequant_f32(O.gemm_int(c, tu), d, au))
     np.testing.assert_array_equal(host(h).view(np.uint32), h_ref.view(np.uint32))
     np.testing.assert_array_equal(host(rowmax), np.abs(h_ref).max(axis=1))
+
+
+def test_gemm_formats_agree():
+    """INT4 on int8 cores and the same codes in E3M2 on FP6 cores give identical outputs."""
+    torch_cuda()
+    M, N, K = 520, 784, 2304
+    x = make_x(6800, M, K, special=False)
+    _, t, alpha, packed, a = packed_weights(6900, N, K)
+    c4, s4, _, _, _ = _quant(x, "int4")
+    c6, s6, _, _, _ = _quant(x, "int4_e3m2")
+    np.testing.assert_array_equal(host(s4), host(s6))
+    y4 = tw.bitlinear_gemm_w158a4("int4", c4, s4, K, packed, a, N)
+    y6 = tw.bitlinear_gemm_w158a4("int4_e3m2", c6, s6, K, packed, a, N)
+    np.testing.assert_array_equal(host(y4), host(y6))
 
 
 def test_decode_matches_gemm():

@@ -8,8 +8,8 @@ import pytest
 import oracle as O
 import ternary_weight_quantized_amd as tw
 from synth import WORKLOADS, bf16_bits_to_f32, workload_inputs
-from tests.gpu_util import (assert_y_close, dev_bf16, dev_f32, host, int4_values, int8_values, mask_bits,
-                            nibbles, torch_cuda)
+from tests.gpu_util import (assert_y_close, dev_bf16, dev_f32, e3m2_values, host, int4_values, int8_values,
+                            mask_bits, nibbles, torch_cuda)
 from tests.packed_layout import unpack_ternary
 
 pytestmark = pytest.mark.gpu
@@ -58,7 +58,7 @@ def test_decode_a4_full(M):
     assert_y_close(host(y), ref["acc"], ref["dscale"], alpha)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp4"])
+@pytest.mark.parametrize("fmt", ["int4", "int4_e3m2", "fp4"])
 def test_prefill_qkv_sampled(fmt):
     torch_cuda()
     wl = WORKLOADS["prefill_qkv"]
@@ -69,9 +69,11 @@ def test_prefill_qkv_sampled(fmt):
     y = tw.bitlinear_gemm_w158a4(fmt, codes, scale, K, packed, a, N)
     rows = sample_rows(M, seed=3)
     xs = bf16_bits_to_f32(inp["x"][rows])
-    ref = O.bitlinear_a4(xs, t, alpha, EPS, fmt=fmt)
+    ref = O.bitlinear_a4(xs, t, alpha, EPS, fmt="fp4" if fmt == "fp4" else "int4")
     if fmt == "int4":
         np.testing.assert_array_equal(int4_values(host(codes)[rows]), ref["codes"])
+    elif fmt == "int4_e3m2":
+        np.testing.assert_array_equal(e3m2_values(host(codes)[rows]), ref["codes"])
     else:
         np.testing.assert_array_equal(nibbles(host(codes)[rows]), ref["nibbles"])
     np.testing.assert_array_equal(host(scale)[rows], ref["dscale"])
@@ -86,9 +88,10 @@ def test_ffn_7b_sampled():
     tg, ag, pg, dag = weights(inp["w_gate"])
     tu, au, pu, dau = weights(inp["w_up"])
     td, ad, pd, dad = weights(inp["w_down"])
-    codes, scale, _ = tw.bitlinear_quantize_act(dev_bf16(inp["x"]), "int4", eps=EPS)
+    codes, scale, _ = tw.bitlinear_quantize_act(dev_bf16(inp["x"]), "int4_e3m2", eps=EPS)
     rowmax = torch.empty(M, dtype=torch.float32, device="cuda")
-    h = tw.bitlinear_gemm_w158a4("int4", codes, scale, K, pg, dag, N, up_packed=pu, up_alpha=dau, row_absmax=rowmax)
+    h = tw.bitlinear_gemm_w158a4("int4_e3m2", codes, scale, K, pg, dag, N, up_packed=pu, up_alpha=dau,
+                                 row_absmax=rowmax)
     hc, hs, _ = tw.bitlinear_quantize_act(h, "int8", eps=EPS, row_absmax_hint=rowmax)
     y = tw.bitlinear_gemm_w158a8_sparse(hc, hs, N, pd, dad, K)
     rows = sample_rows(M, seed=4)
