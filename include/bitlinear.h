@@ -62,21 +62,25 @@ typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_e
  *   INT8      M x K bytes, row stride K, codes in [-127, 127] (0 where Top-K masked). scale[m] = gamma_m / 127.
  *   INT4_E3M2 the INT4 absmean codes (same values and scale as INT4) stored 6 bits each as their exact
  *             FP6 E3M2 bit pattern (sign bit 5, 3 exponent bits with bias 3, 2 mantissa bits:
- *             1 = 0x0C, 2 = 0x10, 3 = 0x12, 4 = 0x14, 5 = 0x15, 6 = 0x16, 7 = 0x17, 8 = 0x18, 0 = 0x00);
- *             M x 3K/4 bytes, code k of a row in bits [6k, 6k+6) of the row's little-endian bit stream.
- *             This is the layout the FP6 x FP4 matrix cores read; bitlinear_gemm_w158a4 runs INT4
- *             activations given in it on those cores, exactly.
+ *             1 = 0x0C, 2 = 0x10, 3 = 0x12, 4 = 0x14, 5 = 0x15, 6 = 0x16, 7 = 0x17, 8 = 0x18, 0 = 0x00),
+ *             in tiles of 16 rows x 128 codes (1536 bytes): tile (m/16, k/128) at byte offset
+ *             ((m/16) * (K/128) + k/128) * 1536; inside it row m%16 takes 96 bytes and code k%128 sits
+ *             in bits [6 (k%128), 6 (k%128) + 6) of those bytes read as a little-endian bit stream.
+ *             The buffer holds ceil(M/16) * 16 rows (3K/4 bytes each); rows from M on are padding, never
+ *             written and never used. This is the layout the FP6 x FP4 matrix cores stream;
+ *             bitlinear_gemm_w158a4 runs INT4 activations given in it on those cores, exactly.
  * Dequantized activation = code value * scale[m].
  *
  * Packed ternary weights (bitlinear_pack_ternary output, N*K/4 bytes, 2 bits per weight):
  *   2-bit field: 00 = 0, 01 = +1, 11 = -1 (10 is never written).
- *   Tiles of 16 rows (n) x 256 columns (k), 1024 bytes each, tile (n/16, k/256) at byte offset
- *   ((n/16) * (K/256) + k/256) * 1024. Inside a tile, with r = n % 16 and kk = k % 256:
- *   lane L = 16 * (kk / 64) + r owns bytes [16 L, 16 L + 16) = four little-endian 32-bit words;
- *   word i = (kk % 64) / 16 holds the 16 weights kk0..kk0+15 (kk0 = 16 * (kk / 16)); weight
+ *   Tiles of 16 rows (n) x 128 columns (k), 512 bytes each, tile (k/128, n/16) at byte offset
+ *   ((k/128) * (N/16) + n/16) * 512 (all tiles of one 128-wide K slice are contiguous).
+ *   Inside a tile, with r = n % 16 and kk = k % 128:
+ *   lane L = 16 * (kk / 32) + r owns bytes [8 L, 8 L + 8) = two little-endian 32-bit words;
+ *   word i = (kk % 32) / 16 holds the 16 weights kk0..kk0+15 (kk0 = 16 * (kk / 16)); weight
  *   kk0 + q (q < 8) sits in bits [4q, 4q+2) and weight kk0 + 8 + q in bits [4q+2, 4q+4).
- *   (Each 1 KB tile is exactly four B operands of a 16x16x64 int8 MFMA, or two of a 16x16x128
- *   FP4 MFMA, with no per-element shuffling.)
+ *   (Each 512-byte tile is exactly two B operands of a 16x16x64 int8 MFMA, or one of a
+ *   16x16x128 FP4 MFMA, with no per-element shuffling.)
  */
 
 /* ---------------------------------------------------------------------------------------------

@@ -106,9 +106,11 @@ def _fmt(fmt):
 
 
 def codes_shape(fmt, M, K):
-    """(rows, bytes per row) of the code buffer of a format."""
+    """(rows, bytes per row) of the code buffer of a format (E3M2: tiled, rows padded to 16)."""
     f = _fmt(fmt)
-    return (M, K if f == BL_ACT_INT8 else 3 * K // 4 if f == BL_ACT_INT4_E3M2 else K // 2)
+    if f == BL_ACT_INT4_E3M2:
+        return ((M + 15) // 16 * 16, 3 * K // 4)
+    return (M, K if f == BL_ACT_INT8 else K // 2)
 
 
 # ------------------------------------------------------------------------------- entry points

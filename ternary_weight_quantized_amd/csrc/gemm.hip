@@ -6,10 +6,12 @@
 //   Y = (Q_INT8(X) . M) Q_w(W)^T ("Sparsification Pipeline ...", paper Eq. 1),
 //   ReLU^2 GLU epilogue ("Squared ReLU Gating ...", paper Eq. 5), residual add (section 3.2).
 //
-// Two kernels share the staging scheme: every K step of 256 (one packed weight tile) the block
-// copies its A rows and B tiles to LDS with 128-bit direct-to-LDS loads (no registers, double
-// buffered), A rows stored with a per-row chunk rotation that makes the fragment reads free of
-// bank conflicts; each wave then reads its fragments from LDS and feeds the matrix cores.
+// Two kernels share the staging scheme: for every K step of 128 (one packed weight tile) the block
+// copies its A rows and B tiles to LDS with 128-bit direct-to-LDS loads (no registers). Four stage
+// buffers keep three steps in flight ahead of the matrix cores, which hides the L2/MALL latency
+// that one buffered step cannot; A rows are stored with a per-row chunk rotation that makes the
+// fragment reads free of bank conflicts. Each wave reads its fragments from LDS and feeds the
+// matrix cores; one barrier per step both publishes a step and frees the buffer refilled next.
 //
 //  k_gemm_mx  FP6 x FP4 / FP4 x FP4 (v_mfma_scale_f32_16x16x128_f8f6f4, unit block scales).
 //             4 waves, 256 x 256 block, 128 x 128 per wave. A is used as stored (E3M2 or E2M1);
@@ -40,15 +42,17 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // ----------------------------------------------------------------------------- A storage per format
+constexpr int NST = 4;   // stage buffers (three steps in flight)
+
 template <int FMT>
 struct AFmt {
-  static constexpr int ROW = FMT == BL_ACT_INT8 ? 256 : FMT == BL_ACT_INT4_E3M2 ? 192 : 128;  // bytes / K step
-  static constexpr int NCH = ROW / 16;                                                        // 16 B chunks
-  // chunk rotation of LDS row r (depends on r % 16 only); chosen so that the 16 lanes of a
+  static constexpr int ROW = FMT == BL_ACT_INT8 ? 128 : FMT == BL_ACT_INT4_E3M2 ? 96 : 64;   // bytes per K step
+  static constexpr int NCH = ROW / 16;                                                      // 16 B chunks
+  // chunk rotation of LDS row r (depends on r % 16 only); chosen so that the 16 lanes of each
   // fragment read (rows r16 = 0..15) hit 16 disjoint bank groups
   __device__ static __forceinline__ int rot(int r) {
     const int r16 = r & 15;
-    return FMT == BL_ACT_INT8 ? r16 : FMT == BL_ACT_INT4_E3M2 ? (r16 >> 2) : ((r16 >> 1) & 7);
+    return FMT == BL_ACT_INT8 ? (r16 >> 1) : FMT == BL_ACT_INT4_E3M2 ? (r16 >> 3) : (r16 >> 2);
   }
   __device__ static __forceinline__ long row_bytes(int K) {
     return FMT == BL_ACT_INT8 ? K : FMT == BL_ACT_INT4_E3M2 ? (3L * K / 4) : (K / 2);
@@ -70,21 +74,28 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 }
 
 // Per-lane source offsets of this wave's share of the direct-to-LDS copies of one K step: A rows
-// [m0, m0+BM) (stored with the chunk rotation) and the B tiles of NB matrices x BN/16 tile rows.
-// Rows beyond M and tile rows beyond N are clamped to valid memory: they load real but unused
-// data (their outputs are never stored). The offsets are fixed for the whole K loop; step kb adds
-// kb * ROW to A and kb * 1024 to B.
+// [m0, m0+BM) (stored with the chunk rotation) and the 512-byte B tiles of NB matrices x BN/16 tile
+// rows (two tiles per 1 KB load). Rows beyond M and tile rows beyond N are clamped to valid memory:
+// they load real but unused data (their outputs are never stored). The offsets are fixed for the
+// whole K loop; step ks adds ks * ASTEP to A and ks * (N/16) * 512 to B (K-tile-major weights).
+// E3M2 activations come in 16-row x 128-code tiles, so a stage of them is 16 contiguous 1536-byte
+// runs; the other formats are row-major.
 template <int FMT, int BM, int BN, int NB, int NW>
 struct StagePlan {
   using F = AFmt<FMT>;
+  static constexpr bool TILED = (FMT == BL_ACT_INT4_E3M2);
   static constexpr int ASEG = BM * F::NCH / 64;           // 1 KB LDS segments of A
-  static constexpr int BSEG = NB * (BN / 16);             // 1 KB tiles of B
+  static constexpr int BT = NB * (BN / 16);               // 512-byte B tiles
+  static constexpr int BSEG = BT / 2;                     // 1 KB LDS segments of B
+  static constexpr int BYTES = BM * F::ROW + BT * 512;    // one stage
   static_assert(ASEG % NW == 0 && BSEG % NW == 0, "every wave issues the same number of loads");
   static constexpr int NA = ASEG / NW, NBL = BSEG / NW;
   static constexpr int LOADS = NA + NBL;                  // loads per wave and stage
   uint32_t aoff[NA];                                      // byte offset from A
-  uint32_t boff[NBL];                                     // byte offset from the tile row of its matrix
-  __device__ __forceinline__ void init(long arow, int m0, int M, int n0, int NG, int KB, int wave, int lane) {
+  uint32_t boff[NBL];                                     // byte offset from its matrix
+  uint32_t astep, bstep;                                  // bytes per K step
+  __device__ __forceinline__ void init(long arow, int m0, int M, int n0, int NG, int KS, int wave, int lane) {
+    const int mlast = TILED ? ((M + 15) & ~15) - 1 : M - 1;   // last row present in the buffer
 #pragma unroll
     for (int qi = 0; qi < NA; ++qi) {
       const int q = wave + NW * qi;
@@ -92,28 +103,31 @@ struct StagePlan {
       const int r = p / F::NCH, slot = p % F::NCH;
       int c = slot - F::rot(r);
       c += c < 0 ? F::NCH : 0;
-      const int m = min(m0 + r, M - 1);
-      aoff[qi] = (uint32_t)(m * arow + 16 * c);
+      const int m = min(m0 + r, mlast);
+      aoff[qi] = TILED ? (uint32_t)((m >> 4) * KS * 1536 + (m & 15) * F::ROW + 16 * c)
+                       : (uint32_t)(m * arow + 16 * c);
     }
 #pragma unroll
     for (int qi = 0; qi < NBL; ++qi) {
-      const int q = wave + NW * qi;
-      const int t = q % (BN / 16);
+      const int T = 2 * (wave + NW * qi) + (lane >> 5);   // B tile of this lane's 16 bytes
+      const int t = T % (BN / 16);
       const int G = min((n0 >> 4) + t, NG - 1);
-      boff[qi] = (uint32_t)(G * KB * 1024 + 16 * lane);
+      boff[qi] = (uint32_t)(G * 512 + 16 * (lane & 31));
     }
+    astep = TILED ? 1536u : (uint32_t)F::ROW;
+    bstep = (uint32_t)NG * 512u;
   }
-  // issue the loads of K step kb into the stage buffer at LDS address lds
+  // issue the loads of K step ks into the stage buffer at LDS address lds
   __device__ __forceinline__ void issue(uint32_t lds, const uint8_t* __restrict__ A, const uint8_t* const* Wm,
-                                        int kb, int wave) const {
-    const uint8_t* abase = A + (long)kb * F::ROW;
+                                        int ks, int wave, int lane) const {
+    const uint8_t* abase = A + (long)ks * astep;
 #pragma unroll
     for (int qi = 0; qi < NA; ++qi) dma16(abase + aoff[qi], lds + 1024u * (wave + NW * qi));
 #pragma unroll
     for (int qi = 0; qi < NBL; ++qi) {
       const int q = wave + NW * qi;
-      const int mtx = q / (BN / 16);
-      dma16(Wm[mtx] + (long)kb * 1024 + boff[qi], lds + BM * F::ROW + 1024u * q);
+      const int mtx = (2 * q + (lane >> 5)) / (BN / 16);
+      dma16(Wm[mtx] + (long)ks * bstep + boff[qi], lds + BM * F::ROW + 1024u * q);
     }
   }
 };
@@ -160,9 +174,6 @@ __device__ __forceinline__ v8i expand_w_fp4(uint32_t w0, uint32_t w1) {
   r[3] = (int)(w1 & 0xCCCCCCCCu);
   r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
   return r;
-}
-__device__ __forceinline__ uint32_t word(const uint4& q, int i) {
-  return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
 }
 
 // Block -> tile mapping. Consecutive block ids go to the eight XCDs in turn, so ids are first
@@ -238,7 +249,6 @@ struct CfgMx {
   static constexpr int NW = 4, WGM = 2, WGN = 2;
   static constexpr int BM = 256, BN = GLU ? 128 : 256;
   static constexpr int SM = BM / WGM / 16, SN = BN / WGN / 16;
-  static constexpr int STAGE = BM * AFmt<FMT>::ROW + NB * (BN / 16) * 1024;
   using Plan = StagePlan<FMT, BM, BN, NB, NW>;
 };
 
@@ -252,10 +262,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(const uint8_t* __restrict__ 
                                                      float* __restrict__ rowmax) {
   using C = CfgMx<FMT, EPI>;
   using F = AFmt<FMT>;
+  using P = typename C::Plan;
   constexpr int NB = C::NB, SM = C::SM, SN = C::SN;
   constexpr bool FP6 = (FMT == BL_ACT_INT4_E3M2);
   constexpr int CBSZ = FP6 ? 3 : 4;                  // A operand: FP6 E3M2 or FP4 E2M1
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];   // two stage buffers
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * P::BYTES];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(const uint8_t* __restrict__ 
   int tm, tn;
   tile_of(blockIdx.x, ntm, ntn, &tm, &tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
-  const int KB = K >> 8, NG = N >> 4;
+  const int KS = K >> 7, NG = N >> 4;
   const long arow = F::row_bytes(K);
   const uint8_t* Wm[2] = {W, W2};
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -276,80 +287,65 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(const uint8_t* __restrict__ 
 #pragma unroll
       for (int t = 0; t < SN; ++t) acc[mtx][s][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // lane-constant LDS offsets of the A fragment parts (row r16 of the wave's first 16-row subtile):
-  // E3M2: 24 bytes at 48 g + 24 j as three 8-byte parts; E2M1: 16 bytes at 32 g + 16 j (one chunk)
+  // lane-constant LDS offsets of the A fragment (row r16 of the wave's first 16-row subtile):
+  // E3M2 24 bytes at 24 g as three 8-byte parts; E2M1 16 bytes at 16 g (one chunk)
   const int arow0 = wm * SM * 16 + r16;
-  int aoff[2][3];
+  int aoff[3];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-      aoff[j][p] = FP6 ? a_off<FMT>(arow0, 48 * g4 + 24 * j + 8 * p) : a_off<FMT>(arow0, 32 * g4 + 16 * j);
+  for (int p = 0; p < 3; ++p) aoff[p] = FP6 ? a_off<FMT>(arow0, 24 * g4 + 8 * p) : a_off<FMT>(arow0, 16 * g4);
 
-  // one K step: wait for stage kb in `cur`, prefetch stage kb+1 into `nxt`, compute from `cur`
-  typename C::Plan plan;
-  plan.init(arow, m0, M, n0, NG, KB, wave, lane);
+  P plan;
+  plan.init(arow, m0, M, n0, NG, KS, wave, lane);
   const uint32_t lds0 = lds_addr_of(smem);
-  auto kstep = [&](int kb, const uint8_t* cur, uint32_t nxt) {
-    // every step issues the same number of loads (the last ones re-fetch a valid stage that is
-    // never read), so the wait below is the same on every path
-    plan.issue(nxt, A, Wm, min(kb + 1, KB - 1), wave);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::Plan::LOADS));
+  // prologue: steps 0..NST-2 in flight (indices past the end re-fetch the last step, never read)
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) plan.issue(lds0 + i * P::BYTES, A, Wm, min(i, KS - 1), wave, lane);
+
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint8_t* cur = smem + (ks % NST) * P::BYTES;
+    // step ks has landed when at most NST-2 later steps are still outstanding
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * P::LOADS));
     lds_barrier();
-    const uint8_t* Bs = cur + C::BM * F::ROW + (wn * SN) * 1024 + 16 * lane;
-    uint4 bw[NB][SN];
+    // refill the buffer every wave finished reading in step ks-1
+    plan.issue(lds0 + ((ks + NST - 1) % NST) * P::BYTES, A, Wm, min(ks + NST - 1, KS - 1), wave, lane);
+
+    const uint8_t* Bs = cur + C::BM * F::ROW + (wn * SN) * 512 + 8 * lane;
+    v8i bf[NB][SN];
 #pragma unroll
     for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
-      for (int t = 0; t < SN; ++t)
-        bw[mtx][t] = *reinterpret_cast<const uint4*>(Bs + mtx * (C::BN / 16) * 1024 + t * 1024);
+      for (int t = 0; t < SN; ++t) {
+        const uint2 w = *reinterpret_cast<const uint2*>(Bs + mtx * (C::BN / 16) * 512 + t * 512);
+        bf[mtx][t] = expand_w_fp4(w.x, w.y);
+      }
+    // A fragments are read one 16-row subtile ahead of the MFMAs that use them
+    auto load_a = [&](int s) -> v8i {
+      const uint8_t* ar = cur + s * 16 * F::ROW;
+      if constexpr (FP6) {
+        const uint2 p0 = *reinterpret_cast<const uint2*>(ar + aoff[0]);
+        const uint2 p1 = *reinterpret_cast<const uint2*>(ar + aoff[1]);
+        const uint2 p2 = *reinterpret_cast<const uint2*>(ar + aoff[2]);
+        return v8i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y, (int)p2.x, (int)p2.y, 0, 0};
+      } else {
+        const uint4 q = *reinterpret_cast<const uint4*>(ar + aoff[0]);
+        return v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      }
+    };
+    v8i a_next = load_a(0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      __builtin_amdgcn_sched_barrier(0);   // keep each K slice's loads and MFMAs together (register pressure)
-      v8i bf[NB][SN];
+    for (int s = 0; s < SM; ++s) {
+      const v8i a = a_next;
+      if (s + 1 < SM) a_next = load_a(s + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
-        for (int t = 0; t < SN; ++t) bf[mtx][t] = expand_w_fp4(word(bw[mtx][t], 2 * j), word(bw[mtx][t], 2 * j + 1));
-      // A fragments are read one 16-row subtile ahead of the MFMAs that use them
-      auto load_a = [&](int s) -> v8i {
-        const uint8_t* ar = cur + s * 16 * F::ROW;
-        if constexpr (FP6) {
-          // 24 bytes: j = 0 -> 16 + 8 bytes, j = 1 -> 8 + 16 bytes (each part inside one 16 B chunk)
-          if (j == 0) {
-            const uint4 p0 = *reinterpret_cast<const uint4*>(ar + aoff[0][0]);
-            const uint2 p1 = *reinterpret_cast<const uint2*>(ar + aoff[0][2]);
-            return v8i{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, 0, 0};
-          } else {
-            const uint2 p0 = *reinterpret_cast<const uint2*>(ar + aoff[1][0]);
-            const uint4 p1 = *reinterpret_cast<const uint4*>(ar + aoff[1][1]);
-            return v8i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y, (int)p1.z, (int)p1.w, 0, 0};
-          }
-        } else {
-          const uint4 q = *reinterpret_cast<const uint4*>(ar + aoff[j][0]);
-          return v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-        }
-      };
-      v8i a_next = load_a(0);
-#pragma unroll
-      for (int s = 0; s < SM; ++s) {
-        const v8i a = a_next;
-        if (s + 1 < SM) a_next = load_a(s + 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-          for (int t = 0; t < SN; ++t)
-            acc[mtx][s][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf[mtx][t], acc[mtx][s][t], CBSZ, 4,
-                                                                              0, 127, 0, 127);
-      }
+        for (int t = 0; t < SN; ++t)
+          acc[mtx][s][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf[mtx][t], acc[mtx][s][t], CBSZ, 4, 0,
+                                                                            127, 0, 127);
     }
-    lds_barrier();
-  };
-  plan.issue(lds0, A, Wm, 0, wave);
-  for (int kb = 0; kb < KB; ++kb)
-    kstep(kb, smem + (kb & 1) * C::STAGE, lds0 + ((kb + 1) & 1) * C::STAGE);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the last (unused) prefetch lands before the waves end
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the trailing (unused) loads land before the waves end
 
   // fp32 epilogue: the matrix-core sum is 2*sum(c t) (E3M2) or sum(2e t) = sum(doubled code * t)
   // (E2M1); x 0.5 is exact and gives sum(c t), respectively the half-unit count of the oracle.
@@ -373,7 +369,6 @@ struct CfgI8 {
   static constexpr int NW = 8, WGM = 2, WGN = 4;
   static constexpr int BM = A8 ? 128 : 256, BN = GLU ? 128 : 256;
   static constexpr int SM = BM / WGM / 16, SN = BN / WGN / 16;
-  static constexpr int STAGE = BM * AFmt<FMT>::ROW + NB * (BN / 16) * 1024;
   using Plan = StagePlan<FMT, BM, BN, NB, NW>;
 };
 
@@ -387,9 +382,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8(const uint8_t* __restrict__ 
                                                      float* __restrict__ rowmax) {
   using C = CfgI8<FMT, EPI>;
   using F = AFmt<FMT>;
+  using P = typename C::Plan;
   constexpr int NB = C::NB, SM = C::SM, SN = C::SN;
   constexpr bool A8 = C::A8;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];   // two stage buffers
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * P::BYTES];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
@@ -397,7 +393,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8(const uint8_t* __restrict__ 
   int tm, tn;
   tile_of(blockIdx.x, ntm, ntn, &tm, &tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
-  const int KB = K >> 8, NG = N >> 4;
+  const int KS = K >> 7, NG = N >> 4;
   const long arow = F::row_bytes(K);
   const uint8_t* Wm[2] = {W, W2};
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -410,36 +406,38 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8(const uint8_t* __restrict__ 
 #pragma unroll
       for (int t = 0; t < SN; ++t) acc[mtx][s][t] = v4i{0, 0, 0, 0};
 
-  // lane-constant fragment offsets: INT8 16 bytes at 64 g + 16 i, INT4 8 bytes at 32 g + 8 i
+  // lane-constant fragment offsets: INT8 16 bytes at 32 g + 16 i, INT4 16 bytes (both i) at 16 g
   const int arow0 = wm * SM * 16 + r16;
-  int aoff[4];
+  int aoff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) aoff[i] = A8 ? a_off<FMT>(arow0, 64 * g4 + 16 * i) : a_off<FMT>(arow0, 32 * g4 + 8 * i);
+  for (int i = 0; i < 2; ++i) aoff[i] = A8 ? a_off<FMT>(arow0, 32 * g4 + 16 * i) : a_off<FMT>(arow0, 16 * g4);
 
-  typename C::Plan plan;
-  plan.init(arow, m0, M, n0, NG, KB, wave, lane);
+  P plan;
+  plan.init(arow, m0, M, n0, NG, KS, wave, lane);
   const uint32_t lds0 = lds_addr_of(smem);
-  auto kstep = [&](int kb, const uint8_t* cur, uint32_t nxt) {
-    // every step issues the same number of loads (the last ones re-fetch a valid stage that is
-    // never read), so the wait below is the same on every path
-    plan.issue(nxt, A, Wm, min(kb + 1, KB - 1), wave);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::Plan::LOADS));
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) plan.issue(lds0 + i * P::BYTES, A, Wm, min(i, KS - 1), wave, lane);
+
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint8_t* cur = smem + (ks % NST) * P::BYTES;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * P::LOADS));
     lds_barrier();
-    const uint8_t* Bs = cur + C::BM * F::ROW + (wn * SN) * 1024 + 16 * lane;
-    uint4 bw[NB][SN];
+    plan.issue(lds0 + ((ks + NST - 1) % NST) * P::BYTES, A, Wm, min(ks + NST - 1, KS - 1), wave, lane);
+
+    const uint8_t* Bs = cur + C::BM * F::ROW + (wn * SN) * 512 + 8 * lane;
+    uint2 bw[NB][SN];
 #pragma unroll
     for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
-      for (int t = 0; t < SN; ++t)
-        bw[mtx][t] = *reinterpret_cast<const uint4*>(Bs + mtx * (C::BN / 16) * 1024 + t * 1024);
+      for (int t = 0; t < SN; ++t) bw[mtx][t] = *reinterpret_cast<const uint2*>(Bs + mtx * (C::BN / 16) * 512 + t * 512);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       __builtin_amdgcn_sched_barrier(0);   // keep each K slice's loads and MFMAs together (register pressure)
       v4i bf[NB][SN];
 #pragma unroll
       for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
-        for (int t = 0; t < SN; ++t) bf[mtx][t] = expand_w_i8(word(bw[mtx][t], i));
+        for (int t = 0; t < SN; ++t) bf[mtx][t] = expand_w_i8(i ? bw[mtx][t].y : bw[mtx][t].x);
 #pragma unroll
       for (int s = 0; s < SM; ++s) {
         const uint8_t* ar = cur + s * 16 * F::ROW;
@@ -450,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8(const uint8_t* __restrict__ 
           if (__ballot((q.x | q.y | q.z | q.w) != 0u) == 0ull) continue;
           a = expand_a_int8(q);
         } else {
-          const uint2 p = *reinterpret_cast<const uint2*>(ar + aoff[i]);
+          const uint2 p = *reinterpret_cast<const uint2*>(ar + aoff[0] + 8 * i);
           a = expand_a_int4(p.x, p.y);
         }
 #pragma unroll
@@ -460,12 +458,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8(const uint8_t* __restrict__ 
             acc[mtx][s][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bf[mtx][t], acc[mtx][s][t], 0, 0, 0);
       }
     }
-    lds_barrier();
-  };
-  plan.issue(lds0, A, Wm, 0, wave);
-  for (int kb = 0; kb < KB; ++kb)
-    kstep(kb, smem + (kb & 1) * C::STAGE, lds0 + ((kb + 1) & 1) * C::STAGE);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the last (unused) prefetch lands before the waves end
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   const float alpha = *walpha;
   const float alpha2 = C::GLU ? *w2alpha : 0.f;

@@ -4,11 +4,11 @@
 // products as the GEMMs (Y = Q(X) Q_w(W)^T with INT4 or INT8 activations) for a few tokens.
 //
 // One 256-thread block owns 16 output columns (one packed tile row, n-group G) and splits K over
-// its four waves. Every lane loads its 16-byte share of each 1 KB weight tile with one 128-bit
-// load (a wave reads whole tiles, fully coalesced) and issues all of them before any math, so a
-// wave keeps up to 8 KB in flight. The tile words feed 16x16x64 int8 MFMAs directly (the M rows
-// are padded to 16 with zeros); the four partial int32 tiles are summed exactly in LDS.
-// INT8 activations (the sparse intermediates) gate the weight loads: a lane skips the 64-wide K
+// its four waves. Every lane loads its 8-byte share of each 512-byte weight tile (a wave reads
+// whole tiles, fully coalesced) and issues all of them before any math, so a wave keeps up to
+// 4 KB in flight. The tile words feed 16x16x64 int8 MFMAs directly (the M rows are padded to 16
+// with zeros); the four partial int32 tiles are summed exactly in LDS.
+// INT8 activations (the sparse intermediates) gate the weight loads: a lane skips the 32-wide K
 // slice it would load when the codes of all M rows are zero there. INT4 activations do not gate,
 // so their weight loads never wait for the activation loads.
 #include "bl_common.h"
@@ -43,9 +43,6 @@ __device__ __forceinline__ v4i expand_a_int8(uint32_t x, uint32_t y, uint32_t z,
   r[3] = (int)__builtin_amdgcn_perm(w, z, 0x07050301u);
   return r;
 }
-__device__ __forceinline__ uint32_t pick(const uint4& q, int i) {
-  return i == 0 ? q.x : i == 1 ? q.y : i == 2 ? q.z : q.w;
-}
 
 template <int FMT, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
@@ -61,10 +58,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* __restrict__
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = blockIdx.x;
-  const int KB = K >> 8;
-  const int per = (KB + WAVES - 1) / WAVES;
-  const int kb_begin = wave * per;
-  const int kb_end = min(KB, kb_begin + per);
+  const int KT = K >> 7, NG = N >> 4;            // 128-wide weight tiles along K, 16-row groups
+  const int per = (KT + WAVES - 1) / WAVES;
+  const int kt_begin = wave * per;
+  const int kt_end = min(KT, kt_begin + per);
   const int r = lane & 15, g = lane >> 4;
   const bool row_ok = r < M;
   const long arow = A8 ? K : (K >> 1);
@@ -74,37 +71,36 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* __restrict__
 #pragma unroll
   for (int mtx = 0; mtx < NB; ++mtx) acc[mtx] = v4i{0, 0, 0, 0};
 
-  for (int kb0 = kb_begin; kb0 < kb_end; kb0 += CH) {
-    uint4 wt[NB][CH];
-    uint4 at[CH][A8 ? 4 : 2];
+  for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CH) {
+    uint2 wt[NB][CH];
+    uint4 at[CH][A8 ? 2 : 1];
     bool live[CH];
     if constexpr (A8) {
       // activations first: they decide which weight slices are needed
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const int kb = kb0 + c;
+        const int kt = kt0 + c;
         const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        if (kb < kb_end && row_ok) {
-          const uint4* p = reinterpret_cast<const uint4*>(A + (long)r * arow + (long)kb * 256 + 64 * g);
-          at[c][0] = p[0]; at[c][1] = p[1]; at[c][2] = p[2]; at[c][3] = p[3];
+        if (kt < kt_end && row_ok) {
+          const uint4* p = reinterpret_cast<const uint4*>(A + (long)r * arow + (long)kt * 128 + 32 * g);
+          at[c][0] = p[0]; at[c][1] = p[1];
         } else {
-          at[c][0] = z; at[c][1] = z; at[c][2] = z; at[c][3] = z;
+          at[c][0] = z; at[c][1] = z;
         }
-        const uint32_t nz = (at[c][0].x | at[c][0].y | at[c][0].z | at[c][0].w | at[c][1].x | at[c][1].y |
-                             at[c][1].z | at[c][1].w | at[c][2].x | at[c][2].y | at[c][2].z | at[c][2].w |
-                             at[c][3].x | at[c][3].y | at[c][3].z | at[c][3].w);
+        const uint32_t nz = at[c][0].x | at[c][0].y | at[c][0].z | at[c][0].w | at[c][1].x | at[c][1].y |
+                            at[c][1].z | at[c][1].w;
         const unsigned long long bal = __ballot(nz != 0u);
-        live[c] = kb < kb_end && ((bal >> (16 * g)) & 0xFFFFull) != 0ull;
+        live[c] = kt < kt_end && ((bal >> (16 * g)) & 0xFFFFull) != 0ull;
       }
 #pragma unroll
       for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-          const int kb = kb0 + c;
+          const int kt = kt0 + c;
           if (live[c])
-            wt[mtx][c] = *reinterpret_cast<const uint4*>(Wm[mtx] + ((long)G * KB + kb) * 1024 + lane * 16);
+            wt[mtx][c] = *reinterpret_cast<const uint2*>(Wm[mtx] + ((long)kt * NG + G) * 512 + lane * 8);
           else
-            wt[mtx][c] = make_uint4(0u, 0u, 0u, 0u);
+            wt[mtx][c] = make_uint2(0u, 0u);
         }
     } else {
       // weights first (the HBM stream), then the small activation slices
@@ -112,40 +108,38 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* __restrict__
       for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-          const int kb = kb0 + c;
-          if (kb < kb_end)
-            wt[mtx][c] = *reinterpret_cast<const uint4*>(Wm[mtx] + ((long)G * KB + kb) * 1024 + lane * 16);
+          const int kt = kt0 + c;
+          if (kt < kt_end)
+            wt[mtx][c] = *reinterpret_cast<const uint2*>(Wm[mtx] + ((long)kt * NG + G) * 512 + lane * 8);
           else
-            wt[mtx][c] = make_uint4(0u, 0u, 0u, 0u);
+            wt[mtx][c] = make_uint2(0u, 0u);
         }
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const int kb = kb0 + c;
-        live[c] = kb < kb_end;
-        if (live[c] && row_ok) {
-          const uint4* p = reinterpret_cast<const uint4*>(A + (long)r * arow + (long)kb * 128 + 32 * g);
-          at[c][0] = p[0]; at[c][1] = p[1];
-        } else {
-          at[c][0] = make_uint4(0u, 0u, 0u, 0u); at[c][1] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        const int kt = kt0 + c;
+        live[c] = kt < kt_end;
+        if (live[c] && row_ok)
+          at[c][0] = *reinterpret_cast<const uint4*>(A + (long)r * arow + (long)kt * 64 + 16 * g);
+        else
+          at[c][0] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      if (kb0 + c >= kb_end) break;
+      if (kt0 + c >= kt_end) break;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         v4i a;
         if constexpr (A8) {
-          const uint4 q = at[c][i];
-          a = expand_a_int8(q.x, q.y, q.z, q.w);
+          a = expand_a_int8(at[c][i].x, at[c][i].y, at[c][i].z, at[c][i].w);
         } else {
-          const uint4 q = at[c][i >> 1];
-          a = (i & 1) ? expand_a_int4(q.z, q.w) : expand_a_int4(q.x, q.y);
+          const uint4 q = at[c][0];
+          a = i ? expand_a_int4(q.z, q.w) : expand_a_int4(q.x, q.y);
         }
 #pragma unroll
         for (int mtx = 0; mtx < NB; ++mtx)
-          acc[mtx] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand_w_i8(pick(wt[mtx][c], i)), acc[mtx], 0, 0, 0);
+          acc[mtx] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand_w_i8(i ? wt[mtx][c].y : wt[mtx][c].x), acc[mtx],
+                                                           0, 0, 0);
       }
     }
   }

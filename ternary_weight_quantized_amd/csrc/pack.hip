@@ -8,7 +8,7 @@
 // significands are summed per exponent in 64-bit integers (LDS per block, then global atomics),
 // so the sum is independent of order; one thread turns the 256 bins into the correctly rounded
 // double of the exact total and divides by N*K. The pack kernel then writes one 32-bit word
-// (16 weights of one row) per thread in the tiled layout of the public header.
+// (16 weights of one row) per thread in the tiled layout of the public header (16 x 128 tiles).
 #include "bl_common.h"
 #include "bl_kernels.h"
 
@@ -47,19 +47,19 @@ __global__ void k_alpha(const unsigned long long* __restrict__ gbins, double cou
   }
 }
 
-// One thread per packed 32-bit word: tile (G, kb), lane L = 16 g + r, word i.
+// One thread per packed 32-bit word: tile (kt, G) of 16 rows x 128 columns, lane L = 16 g + r, word i.
 __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int N, int K, float eps,
                                               const float* __restrict__ alpha, uint32_t* __restrict__ out) {
   const long wid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const long nwords = (long)N * K / 16;
   if (wid >= nwords) return;
-  const int KB = K >> 8;
-  const long tile = wid >> 8;
-  const int t = (int)(wid & 255);
-  const int L = t >> 2, i = t & 3;
-  const int G = (int)(tile / KB), kb = (int)(tile % KB);
+  const int NG = N >> 4;
+  const long tile = wid >> 7;                                    // 128 words per 512-byte tile
+  const int t = (int)(wid & 127);
+  const int L = t >> 1, i = t & 1;
+  const int kt = (int)(tile / NG), G = (int)(tile % NG);         // K-tile-major tile order
   const int n = 16 * G + (L & 15);
-  const int k0 = 256 * kb + 64 * (L >> 4) + 16 * i;
+  const int k0 = 128 * kt + 32 * (L >> 4) + 16 * i;
   const float den = *alpha + eps;
   const float4* src = reinterpret_cast<const float4*>(w + (long)n * K + k0);
   uint32_t word = 0u;

@@ -91,13 +91,15 @@ __device__ __forceinline__ uint32_t code_e3m2(float v, float s) {
                                      (0x18ull << 40);
   return (uint32_t)((MAG >> (5 * a)) & 31ull) | (c < 0 ? 0x20u : 0u);
 }
-// Store the 4 codes (24 bits, code j at bits 6j) of elements 256g + 4 lane .. +3 into a row of
-// E3M2 codes (code k at bits [6k, 6k+6)): four lanes make 12 bytes, written as three dwords.
-__device__ __forceinline__ void store_e3m2(uint8_t* __restrict__ crow, int g, int lane, uint32_t v24) {
+// Store the 4 codes (24 bits, code j at bits 6j) of elements 256g + 4 lane .. +3 of row m into the
+// tiled E3M2 layout (16 rows x 128 codes per 1536-byte tile, 96 bytes per row, code k at bits 6k):
+// four lanes make 12 bytes, written as three dwords.
+__device__ __forceinline__ void store_e3m2(uint8_t* __restrict__ codes, int m, int K, int g, int lane, uint32_t v24) {
   const uint32_t nxt = __shfl_down(v24, 1, 64);
-  const int i = lane & 3;
+  const int i = lane & 3, q = lane >> 2;
   const uint32_t w = i == 0 ? (v24 | (nxt << 24)) : i == 1 ? ((v24 >> 8) | (nxt << 16)) : ((v24 >> 16) | (nxt << 8));
-  if (i < 3) *reinterpret_cast<uint32_t*>(crow + 192 * g + 12 * (lane >> 2) + 4 * i) = w;
+  const long tile = (long)(m >> 4) * (K >> 7) + 2 * g + (q >> 3);
+  if (i < 3) *reinterpret_cast<uint32_t*>(codes + tile * 1536 + (m & 15) * 96 + 12 * (q & 7) + 4 * i) = w;
 }
 
 // Top-K threshold: the largest key T with count(|x| >= T) >= keep, found bit by bit.
@@ -173,12 +175,11 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
           crow[64 * g] = (uint16_t)c;
         }
     } else {
-      uint8_t* crow = codes + (long)row * (3L * K / 4);
 #pragma unroll
       for (int g = 0; g < NGMAX; ++g)
         if (g < NG)
-          store_e3m2(crow, g, lane, code_e3m2(v[g][0], s) | (code_e3m2(v[g][1], s) << 6) |
-                                        (code_e3m2(v[g][2], s) << 12) | (code_e3m2(v[g][3], s) << 18));
+          store_e3m2(codes, row, K, g, lane, code_e3m2(v[g][0], s) | (code_e3m2(v[g][1], s) << 6) |
+                                                 (code_e3m2(v[g][2], s) << 12) | (code_e3m2(v[g][3], s) << 18));
     }
     if (lane == 0) scale[row] = beta / bl_u2f(BL_SQRT7_BITS);
   } else {
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
         crow[64 * g] = (uint16_t)(code_int4(v[0], s) | (code_int4(v[1], s) << 4) |
                                    (code_int4(v[2], s) << 8) | (code_int4(v[3], s) << 12));
       } else {
-        store_e3m2(codes + (long)row * (3L * K / 4), g, lane,
+        store_e3m2(codes, row, K, g, lane,
                    code_e3m2(v[0], s) | (code_e3m2(v[1], s) << 6) | (code_e3m2(v[2], s) << 12) |
                        (code_e3m2(v[3], s) << 18));
       }

@@ -41,17 +41,21 @@ def int4_values(codes_u8):
     return np.where(n >= 8, n - 16, n).astype(np.int8)
 
 
-def e3m2_values(codes_u8):
-    """uint8 [M, 3K/4] of 6-bit FP6 E3M2 fields (code k at bits [6k, 6k+6) of the row) -> int8 [M, K].
+def e3m2_values(codes_u8, M=None):
+    """Tiled FP6 E3M2 code buffer (16 rows x 128 codes per 1536-byte tile, 96 bytes per row, code k
+    at bits [6k, 6k+6) of the row's bytes) -> int8 [M, K].
 
     Decoded from the format definition (sign, 3 exponent bits with bias 3, 2 mantissa bits); every
     field must hold an integer in [-8, 7].
     """
-    b = np.asarray(codes_u8, dtype=np.uint32)
-    M, nb = b.shape
-    g = b.reshape(M, nb // 3, 3)
+    b = np.asarray(codes_u8, dtype=np.uint8)
+    Mp, rb = b.shape
+    K = rb * 4 // 3
+    t = b.reshape(Mp // 16, K // 128, 16, 96).transpose(0, 2, 1, 3).reshape(Mp, K // 128 * 96)   # row-major
+    g = t.astype(np.uint32).reshape(Mp, -1, 3)
     w = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)                       # 4 codes per 24 bits
-    f = np.stack([(w >> (6 * j)) & 63 for j in range(4)], axis=-1).reshape(M, -1)
+    f = np.stack([(w >> (6 * j)) & 63 for j in range(4)], axis=-1).reshape(Mp, -1)
+    f = f[: (Mp if M is None else M)]
     sign = np.where(f & 32, -1.0, 1.0)
     e = (f >> 2) & 7
     m = (f & 3).astype(np.float64)

@@ -137,17 +137,17 @@ def test_packed_layout_decoder_roundtrip():
 def test_packed_layout_decoder_positions():
     """A single +1 at (n, k) lands in the tile, lane, word and bit the header describes."""
     N, K = 32, 512
-    for n, k in [(0, 0), (5, 7), (17, 8), (31, 511), (3, 300), (20, 64 + 16 + 9)]:
+    for n, k in [(0, 0), (5, 7), (17, 8), (31, 511), (3, 300), (20, 64 + 16 + 9), (9, 127), (9, 128)]:
         codes = np.zeros((N, K), np.int8)
         codes[n, k] = 1
         packed = pack_reference(codes)
-        kk = k % 256
-        tile = (n // 16) * (K // 256) + k // 256
-        lane = 16 * (kk // 64) + n % 16
-        word = (kk % 64) // 16
+        kk = k % 128
+        tile = (k // 128) * (N // 16) + n // 16
+        lane = 16 * (kk // 32) + n % 16
+        word = (kk % 32) // 16
         q = kk % 16
         bit = 4 * q if q < 8 else 4 * (q - 8) + 2
         words = packed.view("<u4")
-        idx = tile * 256 + lane * 4 + word
+        idx = tile * 128 + lane * 2 + word
         assert words[idx] == (1 << bit)
         assert np.count_nonzero(words) == 1
