@@ -181,8 +181,9 @@ bl_status bitlinear_gemm_w158a8_sparse(const void* d_codes, const float* d_scale
 
 /* ---------------------------------------------------------------------------------------------
  * bitlinear_gemv_decode: the same products for decode batches, 1 <= M <= 8, fmt INT4 or INT8.
- * Streams every packed weight tile once from HBM; a lane skips the load of a 64-wide K slice of
- * weights when the activation codes of all M rows are zero there. Arguments as for the GEMMs.
+ * Streams every packed weight tile once from HBM. With INT8 codes a lane skips the load of its
+ * 32-wide K slice of a weight tile when the codes of all M rows are zero there. Arguments as for
+ * the GEMMs.
  * ------------------------------------------------------------------------------------------- */
 bl_status bitlinear_gemv_decode(int32_t fmt, const void* d_codes, const float* d_scale,
                                 int64_t M, int64_t K,

@@ -3,21 +3,23 @@
 // "BitNet a4.8: 4-bit Activations for 1-bit LLMs" (architecture write-up), section 3.4: the same
 // products as the GEMMs (Y = Q(X) Q_w(W)^T with INT4 or INT8 activations) for a few tokens.
 //
-// One 256-thread block owns 16 output columns (one packed tile row, n-group G) and splits K over
-// its four waves. Every lane loads its 8-byte share of each 512-byte weight tile (a wave reads
-// whole tiles, fully coalesced) and issues all of them before any math, so a wave keeps up to
-// 4 KB in flight. The tile words feed 16x16x64 int8 MFMAs directly (the M rows are padded to 16
-// with zeros); the four partial int32 tiles are summed exactly in LDS.
+// One 512-thread block owns 16 output columns (one packed tile row, n-group G) and splits the K
+// tiles over its eight waves; a wave issues all loads of a chunk of four K tiles at once (the
+// activation slices first, then its 8-byte share of each 512-byte weight tile, so a wave reads
+// whole tiles, fully coalesced) and feeds each tile to the matrix cores as soon as it has landed.
+// The tile words go to 16x16x64 int8 MFMAs directly; the M token rows occupy the first M of the 16
+// MFMA rows and the other rows repeat row M-1 (their outputs are never stored), which keeps every
+// load unconditional. The eight partial int32 tiles are summed exactly in LDS. The per-token scales,
+// alpha and the residual are fetched at the start so that nothing but the stores follows the sum.
 // INT8 activations (the sparse intermediates) gate the weight loads: a lane skips the 32-wide K
-// slice it would load when the codes of all M rows are zero there. INT4 activations do not gate,
-// so their weight loads never wait for the activation loads.
+// slice it would load when the codes of all M rows are zero there.
 #include "bl_common.h"
 #include "bl_kernels.h"
 
 namespace {
 
-constexpr int WAVES = 4;
-constexpr int CH = 8;     // weight tiles in flight per wave and matrix
+constexpr int WAVES = 8;
+constexpr int CH = 4;     // K tiles per chunk and wave
 
 __device__ __forceinline__ v4i expand_w_i8(uint32_t w) {
   v4i r;
@@ -35,13 +37,69 @@ __device__ __forceinline__ v4i expand_a_int4(uint32_t p0, uint32_t p1) {
   r[3] = (int)(p1 & 0xF0F0F0F0u);
   return r;
 }
-__device__ __forceinline__ v4i expand_a_int8(uint32_t x, uint32_t y, uint32_t z, uint32_t w) {
+__device__ __forceinline__ v4i expand_a_int8(uint4 q) {
   v4i r;
-  r[0] = (int)__builtin_amdgcn_perm(y, x, 0x06040200u);
-  r[1] = (int)__builtin_amdgcn_perm(w, z, 0x06040200u);
-  r[2] = (int)__builtin_amdgcn_perm(y, x, 0x07050301u);
-  r[3] = (int)__builtin_amdgcn_perm(w, z, 0x07050301u);
+  r[0] = (int)__builtin_amdgcn_perm(q.y, q.x, 0x06040200u);
+  r[1] = (int)__builtin_amdgcn_perm(q.w, q.z, 0x06040200u);
+  r[2] = (int)__builtin_amdgcn_perm(q.y, q.x, 0x07050301u);
+  r[3] = (int)__builtin_amdgcn_perm(q.w, q.z, 0x07050301u);
   return r;
+}
+
+// One chunk of up to CH K tiles starting at kt0 (kt0 < kt_end). FULL chunks load unconditionally, so
+// the compiler can wait for each tile separately; the ragged last chunk clamps its addresses and
+// drops the tiles past kt_end.
+template <bool A8, int NB, bool FULL>
+__device__ __forceinline__ void chunk(const uint8_t* arp, const uint8_t* const (&wp)[2], long wstep, int kt0,
+                                      int kt_end, int g, v4i (&acc)[NB][2]) {
+  constexpr int AV = A8 ? 2 : 1;              // 16-byte activation vectors per lane and tile
+  constexpr long ABYTES = A8 ? 128 : 64;      // activation bytes per row and tile
+  uint4 at[CH][AV];
+  uint2 wt[NB][CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int kt = FULL ? kt0 + c : min(kt0 + c, kt_end - 1);
+#pragma unroll
+    for (int v = 0; v < AV; ++v) at[c][v] = *reinterpret_cast<const uint4*>(arp + kt * ABYTES + 16 * v);
+  }
+  if constexpr (A8) {
+    // weights only where some row has a nonzero code in this lane's 32-wide K slice
+    bool live[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint32_t nz = at[c][0].x | at[c][0].y | at[c][0].z | at[c][0].w | at[c][1].x | at[c][1].y |
+                          at[c][1].z | at[c][1].w;
+      const unsigned long long bal = __ballot(nz != 0u);
+      live[c] = (FULL || kt0 + c < kt_end) && ((bal >> (16 * g)) & 0xFFFFull) != 0ull;
+    }
+#pragma unroll
+    for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        wt[mtx][c] = live[c] ? *reinterpret_cast<const uint2*>(wp[mtx] + (long)(kt0 + c) * wstep) : make_uint2(0u, 0u);
+  } else {
+#pragma unroll
+    for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int kt = FULL ? kt0 + c : min(kt0 + c, kt_end - 1);
+        wt[mtx][c] = *reinterpret_cast<const uint2*>(wp[mtx] + (long)kt * wstep);
+      }
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if (!FULL && kt0 + c >= kt_end) break;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      v4i a;
+      if constexpr (A8) a = expand_a_int8(at[c][i]);
+      else a = i ? expand_a_int4(at[c][0].z, at[c][0].w) : expand_a_int4(at[c][0].x, at[c][0].y);
+#pragma unroll
+      for (int mtx = 0; mtx < NB; ++mtx)
+        acc[mtx][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand_w_i8(i ? wt[mtx][c].y : wt[mtx][c].x),
+                                                            acc[mtx][i], 0, 0, 0);
+    }
+  }
 }
 
 template <int FMT, int EPI>
@@ -63,121 +121,61 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* __restrict__
   const int kt_begin = wave * per;
   const int kt_end = min(KT, kt_begin + per);
   const int r = lane & 15, g = lane >> 4;
-  const bool row_ok = r < M;
+  const int n = 16 * G + r;
   const long arow = A8 ? K : (K >> 1);
-  const uint8_t* Wm[2] = {W, W2};
+  const uint8_t* arp = A + (long)min(r, M - 1) * arow + (A8 ? 32 * g : 16 * g);
+  const uint8_t* const wp[2] = {W + (long)G * 512 + lane * 8, (NB > 1 ? W2 : W) + (long)G * 512 + lane * 8};
+  const long wstep = (long)NG * 512;
 
-  v4i acc[NB];
+  // everything the epilogue reads, fetched before the weight stream (rows past M repeat row M-1)
+  float ds[4], res[4];
 #pragma unroll
-  for (int mtx = 0; mtx < NB; ++mtx) acc[mtx] = v4i{0, 0, 0, 0};
+  for (int v = 0; v < 4; ++v) {
+    const int m = min(4 * g + v, M - 1);
+    ds[v] = ascale[m];
+    if constexpr (EPI == BL_EPI_RESIDUAL) res[v] = R[(long)m * ldr + n];
+  }
+  const float alpha = *walpha;
+  const float alpha2 = (EPI == BL_EPI_RELU2_GLU) ? *w2alpha : 0.f;
 
+  v4i acc[NB][2];
+#pragma unroll
+  for (int mtx = 0; mtx < NB; ++mtx) acc[mtx][0] = acc[mtx][1] = v4i{0, 0, 0, 0};
   for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CH) {
-    uint2 wt[NB][CH];
-    uint4 at[CH][A8 ? 2 : 1];
-    bool live[CH];
-    if constexpr (A8) {
-      // activations first: they decide which weight slices are needed
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int kt = kt0 + c;
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        if (kt < kt_end && row_ok) {
-          const uint4* p = reinterpret_cast<const uint4*>(A + (long)r * arow + (long)kt * 128 + 32 * g);
-          at[c][0] = p[0]; at[c][1] = p[1];
-        } else {
-          at[c][0] = z; at[c][1] = z;
-        }
-        const uint32_t nz = at[c][0].x | at[c][0].y | at[c][0].z | at[c][0].w | at[c][1].x | at[c][1].y |
-                            at[c][1].z | at[c][1].w;
-        const unsigned long long bal = __ballot(nz != 0u);
-        live[c] = kt < kt_end && ((bal >> (16 * g)) & 0xFFFFull) != 0ull;
-      }
-#pragma unroll
-      for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          const int kt = kt0 + c;
-          if (live[c])
-            wt[mtx][c] = *reinterpret_cast<const uint2*>(Wm[mtx] + ((long)kt * NG + G) * 512 + lane * 8);
-          else
-            wt[mtx][c] = make_uint2(0u, 0u);
-        }
-    } else {
-      // weights first (the HBM stream), then the small activation slices
-#pragma unroll
-      for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          const int kt = kt0 + c;
-          if (kt < kt_end)
-            wt[mtx][c] = *reinterpret_cast<const uint2*>(Wm[mtx] + ((long)kt * NG + G) * 512 + lane * 8);
-          else
-            wt[mtx][c] = make_uint2(0u, 0u);
-        }
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int kt = kt0 + c;
-        live[c] = kt < kt_end;
-        if (live[c] && row_ok)
-          at[c][0] = *reinterpret_cast<const uint4*>(A + (long)r * arow + (long)kt * 64 + 16 * g);
-        else
-          at[c][0] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (kt0 + c >= kt_end) break;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        v4i a;
-        if constexpr (A8) {
-          a = expand_a_int8(at[c][i].x, at[c][i].y, at[c][i].z, at[c][i].w);
-        } else {
-          const uint4 q = at[c][0];
-          a = i ? expand_a_int4(q.z, q.w) : expand_a_int4(q.x, q.y);
-        }
-#pragma unroll
-        for (int mtx = 0; mtx < NB; ++mtx)
-          acc[mtx] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, expand_w_i8(i ? wt[mtx][c].y : wt[mtx][c].x), acc[mtx],
-                                                           0, 0, 0);
-      }
-    }
+    if (kt0 + CH <= kt_end) chunk<A8, NB, true>(arp, wp, wstep, kt0, kt_end, g, acc);
+    else chunk<A8, NB, false>(arp, wp, wstep, kt0, kt_end, g, acc);
   }
 
-  // exact int32 reduction of the four K partitions
+  // exact int32 reduction of the eight K partitions
+#pragma unroll
+  for (int mtx = 0; mtx < NB; ++mtx) acc[mtx][0] += acc[mtx][1];
   if (wave > 0) {
 #pragma unroll
-    for (int mtx = 0; mtx < NB; ++mtx) red[mtx][wave - 1][lane] = acc[mtx];
+    for (int mtx = 0; mtx < NB; ++mtx) red[mtx][wave - 1][lane] = acc[mtx][0];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
-    for (int w = 0; w < WAVES - 1; ++w) acc[mtx] += red[mtx][w][lane];
+    for (int w = 0; w < WAVES - 1; ++w) acc[mtx][0] += red[mtx][w][lane];
 
   constexpr int SHIFT = A8 ? 6 : 10;
-  const float alpha = *walpha;
-  const float alpha2 = (EPI == BL_EPI_RELU2_GLU) ? *w2alpha : 0.f;
-  const int n = 16 * G + r;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int m = 4 * g + v;
-    float out = 0.f;
-    if (m < M) {
-      const float ds = ascale[m];
-      const float y0 = (float)(acc[0][v] >> SHIFT) * (ds * alpha);
-      if constexpr (EPI == BL_EPI_RESIDUAL) {
-        out = y0 + R[(long)m * ldr + n];
-      } else if constexpr (EPI == BL_EPI_RELU2_GLU) {
-        const float u0 = (float)(acc[NB - 1][v] >> SHIFT) * (ds * alpha2);
-        const float gp = y0 > 0.f ? y0 : 0.f;
-        out = (gp * gp) * u0;
-      } else {
-        out = y0;
-      }
-      Y[(long)m * ldy + n] = out;
+    const float y0 = (float)(acc[0][0][v] >> SHIFT) * (ds[v] * alpha);
+    float out;
+    if constexpr (EPI == BL_EPI_RESIDUAL) {
+      out = y0 + res[v];
+    } else if constexpr (EPI == BL_EPI_RELU2_GLU) {
+      const float u0 = (float)(acc[NB - 1][0][v] >> SHIFT) * (ds[v] * alpha2);
+      const float gp = y0 > 0.f ? y0 : 0.f;
+      out = (gp * gp) * u0;
+    } else {
+      out = y0;
     }
+    if (m < M) Y[(long)m * ldy + n] = out;
     if constexpr (EPI == BL_EPI_RELU2_GLU) {
       if (rowmax) {
         float a = fabsf(out);
