@@ -28,6 +28,7 @@ bl_status check_mm(int32_t fmt, const void* codes, const float* scale, int64_t M
     if (epi->kind == BL_EPI_RESIDUAL) {
       if (!epi->d_residual) return BL_ERR_INVALID_ARGUMENT;
       if (epi->ldr < N) return BL_ERR_INVALID_ARGUMENT;
+      if (!aligned16(epi->d_residual) || (epi->ldr * 4) % 16 != 0) return BL_ERR_MISALIGNED;
     } else if (epi->kind == BL_EPI_RELU2_GLU) {
       if (!epi->d_up_packed || !epi->d_up_alpha) return BL_ERR_INVALID_ARGUMENT;
       if (!aligned16(epi->d_up_packed)) return BL_ERR_MISALIGNED;

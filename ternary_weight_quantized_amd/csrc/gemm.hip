@@ -17,7 +17,10 @@
 //             4 waves, 256 x 256 block, 128 x 128 per wave. A is used as stored (E3M2 or E2M1);
 //             a ternary code placed in bits 2..3 of a nibble reads as E2M1 +-2.0, so the fp32 sum
 //             is 2*sum(c t) for E3M2 codes and sum(2e t) for E2M1 codes: integers below 2^24, exact.
-//  k_gemm_i8  int8 cores (v_mfma_i32_16x16x64_i8) for INT4 nibbles and INT8 codes. 8 waves.
+//  k_gemm_i8  int8 cores (v_mfma_i32_16x16x64_i8) for INT4 nibbles and INT8 codes. 4 waves, 128 x 256
+//             or 128 x 128 block, two blocks per CU. The weight fragment is the first
+//             MFMA operand, so a lane ends with four consecutive output columns of one token row and
+//             the epilogue moves 16-byte vectors.
 //             Fragments are expanded in registers: ternary -> 64*t via (w << s) & 0xC0C0C0C0,
 //             INT4 nibble -> 16*c by moving it to the top of a byte, INT8 bytes permuted; the int32
 //             accumulator holds 1024*sum(c t) (INT4) or 64*sum(c t) (INT8), exact after a shift.
@@ -361,43 +364,76 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx(const uint8_t* __restrict__ 
 }
 
 // ============================================================================ int8 matrix cores
-template <int FMT, int EPI>
+// Epilogue for accumulators of transposed 16x16 products (weights as the first MFMA operand): the
+// lane holds, for token row m, the four consecutive columns n .. n+3 (n % 4 == 0), so every output
+// and residual access is one 16-byte vector. Columns come in whole groups of 16 (N % 16 == 0), so
+// a lane's four columns are all in range or all out of range. val(mtx, v) is the exact sum of code
+// products of matrix mtx for column n + v.
+template <int EPI, typename ValFn>
+__device__ __forceinline__ void epilogue_cols(int m, int n, bool ok, float sc, float sc2, float* __restrict__ Y,
+                                              long ldy, const float4& res, float& rmax, ValFn val) {
+  float o[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float y0 = val(0, v) * sc;
+    if constexpr (EPI == BL_EPI_RESIDUAL) {
+      o[v] = y0 + (v == 0 ? res.x : v == 1 ? res.y : v == 2 ? res.z : res.w);
+    } else if constexpr (EPI == BL_EPI_RELU2_GLU) {
+      const float u0 = val(1, v) * sc2;
+      const float gp = y0 > 0.f ? y0 : 0.f;
+      o[v] = (gp * gp) * u0;
+      const float a = fabsf(o[v]);
+      rmax = (ok && a > rmax) ? a : rmax;
+    } else {
+      o[v] = y0;
+    }
+  }
+  if (ok) *reinterpret_cast<float4*>(Y + (long)m * ldy + n) = make_float4(o[0], o[1], o[2], o[3]);
+}
+
+template <int FMT, int EPI, int BN0>
 struct CfgI8 {
   static constexpr bool A8 = (FMT == BL_ACT_INT8);
   static constexpr bool GLU = (EPI == BL_EPI_RELU2_GLU);
   static constexpr int NB = GLU ? 2 : 1;
-  static constexpr int NW = 8, WGM = 2, WGN = 4;
-  static constexpr int BM = A8 ? 128 : 256, BN = GLU ? 128 : 256;
+  // 4 waves (2 x 2), 128 x BN0 block (per matrix: BN0 / NB), 64 x BN/2 per wave; two blocks share a
+  // CU (at most 80 KB of LDS and 256 registers per lane each), so one block's loads, LDS reads and
+  // epilogue overlap the other's matrix-core work
+  static constexpr int NW = 4, WGM = 2, WGN = 2;
+  static constexpr int BM = 128, BN = BN0 / NB;
   static constexpr int SM = BM / WGM / 16, SN = BN / WGN / 16;
   using Plan = StagePlan<FMT, BM, BN, NB, NW>;
+  static constexpr int NSTAGE = Plan::BYTES * NST <= 81920 ? NST : 3;
 };
 
-template <int FMT, int EPI>
-__global__ __launch_bounds__(512, 1) void k_gemm_i8(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
+template <int FMT, int EPI, int BN0>
+__global__ __launch_bounds__(256, 2) void k_gemm_i8(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
                                                      int M, int K, const uint8_t* __restrict__ W,
                                                      const float* __restrict__ walpha,
                                                      const uint8_t* __restrict__ W2,
                                                      const float* __restrict__ w2alpha, int N,
                                                      float* __restrict__ Y, long ldy, const float* R, long ldr,
                                                      float* __restrict__ rowmax) {
-  using C = CfgI8<FMT, EPI>;
+  using C = CfgI8<FMT, EPI, BN0>;
   using F = AFmt<FMT>;
   using P = typename C::Plan;
-  constexpr int NB = C::NB, SM = C::SM, SN = C::SN;
+  constexpr int NB = C::NB, SM = C::SM, SN = C::SN, NS = C::NSTAGE, BM = C::BM;
   constexpr bool A8 = C::A8;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * P::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * P::BYTES];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
-  const int ntm = (M + C::BM - 1) / C::BM, ntn = (N + C::BN - 1) / C::BN;
+  const int ntm = (M + BM - 1) / BM, ntn = (N + C::BN - 1) / C::BN;
   int tm, tn;
   tile_of(blockIdx.x, ntm, ntn, &tm, &tn);
-  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int m0 = tm * BM, n0 = tn * C::BN;
   const int KS = K >> 7, NG = N >> 4;
   const long arow = F::row_bytes(K);
   const uint8_t* Wm[2] = {W, W2};
   const int r16 = lane & 15, g4 = lane >> 4;
 
+  // acc[mtx][s][t] = (weight tile t) x (activation subtile s)^T: lane holds row r16 of subtile s,
+  // columns 4 g4 .. 4 g4 + 3 of tile t
   v4i acc[NB][SM][SN];
 #pragma unroll
   for (int mtx = 0; mtx < NB; ++mtx)
@@ -416,46 +452,60 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8(const uint8_t* __restrict__ 
   plan.init(arow, m0, M, n0, NG, KS, wave, lane);
   const uint32_t lds0 = lds_addr_of(smem);
 #pragma unroll
-  for (int i = 0; i < NST - 1; ++i) plan.issue(lds0 + i * P::BYTES, A, Wm, min(i, KS - 1), wave, lane);
+  for (int i = 0; i < NS - 1; ++i) plan.issue(lds0 + i * P::BYTES, A, Wm, min(i, KS - 1), wave, lane);
 
   for (int ks = 0; ks < KS; ++ks) {
-    const uint8_t* cur = smem + (ks % NST) * P::BYTES;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * P::LOADS));
+    const uint8_t* cur = smem + (ks % NS) * P::BYTES;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * P::LOADS));
     lds_barrier();
-    plan.issue(lds0 + ((ks + NST - 1) % NST) * P::BYTES, A, Wm, min(ks + NST - 1, KS - 1), wave, lane);
+    plan.issue(lds0 + ((ks + NS - 1) % NS) * P::BYTES, A, Wm, min(ks + NS - 1, KS - 1), wave, lane);
 
-    const uint8_t* Bs = cur + C::BM * F::ROW + (wn * SN) * 512 + 8 * lane;
+    // weight words of the step; each is expanded right before its first MFMA (subtile 0), so the
+    // expansion overlaps the matrix cores instead of delaying the first MFMA of the step
+    const uint8_t* Bs = cur + BM * F::ROW + (wn * SN) * 512 + 8 * lane;
     uint2 bw[NB][SN];
 #pragma unroll
     for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
       for (int t = 0; t < SN; ++t) bw[mtx][t] = *reinterpret_cast<const uint2*>(Bs + mtx * (C::BN / 16) * 512 + t * 512);
+    v4i bf[NB][SN][2];
+    // A fragments (both 64-wide K halves of the step) are read one 16-row subtile ahead
+    auto load_a = [&](int s, uint4 (&q)[2]) {
+      const uint8_t* ar = cur + s * 16 * F::ROW;
+      q[0] = *reinterpret_cast<const uint4*>(ar + aoff[0]);
+      if constexpr (A8) q[1] = *reinterpret_cast<const uint4*>(ar + aoff[1]);
+    };
+    uint4 qn[2];
+    load_a(0, qn);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      __builtin_amdgcn_sched_barrier(0);   // keep each K slice's loads and MFMAs together (register pressure)
-      v4i bf[NB][SN];
+    for (int s = 0; s < SM; ++s) {
+      const uint4 q[2] = {qn[0], qn[1]};
+      if (s + 1 < SM) load_a(s + 1, qn);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s > 0 && A8) {
+        // zero-slice skip: a 16-row x 128-k slice of all-zero codes contributes nothing (subtile 0
+        // always runs: it also expands the step's weights)
+        const uint32_t nz = q[0].x | q[0].y | q[0].z | q[0].w | q[1].x | q[1].y | q[1].z | q[1].w;
+        if (__ballot(nz != 0u) == 0ull) continue;
+      }
 #pragma unroll
-      for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-        for (int t = 0; t < SN; ++t) bf[mtx][t] = expand_w_i8(i ? bw[mtx][t].y : bw[mtx][t].x);
-#pragma unroll
-      for (int s = 0; s < SM; ++s) {
-        const uint8_t* ar = cur + s * 16 * F::ROW;
-        v4i a;
-        if constexpr (A8) {
-          const uint4 q = *reinterpret_cast<const uint4*>(ar + aoff[i]);
-          // zero-slice skip: a 16-row x 64-k slice of all-zero codes contributes nothing
-          if (__ballot((q.x | q.y | q.z | q.w) != 0u) == 0ull) continue;
-          a = expand_a_int8(q);
-        } else {
-          const uint2 p = *reinterpret_cast<const uint2*>(ar + aoff[0] + 8 * i);
-          a = expand_a_int4(p.x, p.y);
-        }
+      for (int i = 0; i < 2; ++i) {
+        const v4i a = A8 ? expand_a_int8(q[i]) : (i ? expand_a_int4(q[0].z, q[0].w) : expand_a_int4(q[0].x, q[0].y));
 #pragma unroll
         for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
-          for (int t = 0; t < SN; ++t)
-            acc[mtx][s][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bf[mtx][t], acc[mtx][s][t], 0, 0, 0);
+          for (int t = 0; t < SN; ++t) {
+            if (s == 0) bf[mtx][t][i] = expand_w_i8(i ? bw[mtx][t].y : bw[mtx][t].x);
+            acc[mtx][s][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[mtx][t][i], a, acc[mtx][s][t], 0, 0, 0);
+          }
+      }
+      if (s == 0) {
+        // interleave the weight expansion with the first subtile's MFMAs
+#pragma unroll
+        for (int k = 0; k < 2 * NB * SN; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        }
       }
     }
   }
@@ -464,12 +514,35 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8(const uint8_t* __restrict__ 
   const float alpha = *walpha;
   const float alpha2 = C::GLU ? *w2alpha : 0.f;
   constexpr int SHIFT = A8 ? 6 : 10;
+  const int nw0 = n0 + wn * SN * 16 + 4 * g4;
 #pragma unroll
   for (int s = 0; s < SM; ++s) {
-    const int mb = m0 + wm * SM * 16 + 16 * s + 4 * g4;
-    const int nb = n0 + wn * SN * 16;
-    epilogue_rows<EPI, SN>(mb, nb, r16, M, N, ascale, alpha, alpha2, Y, ldy, R, ldr, rowmax,
-                           [&](int mtx, int t, int v) { return (float)(acc[mtx][s][t][v] >> SHIFT); });
+    const int m = m0 + wm * SM * 16 + 16 * s + r16;
+    const bool mok = m < M;
+    const float ds = ascale[mok ? m : M - 1];
+    const float sc = ds * alpha, sc2 = ds * alpha2;
+    float4 res[SN];
+    if constexpr (EPI == BL_EPI_RESIDUAL) {
+#pragma unroll
+      for (int t = 0; t < SN; ++t) {
+        const int n = nw0 + 16 * t;
+        res[t] = (mok && n < N) ? *reinterpret_cast<const float4*>(R + (long)m * ldr + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float rmax = 0.f;
+#pragma unroll
+    for (int t = 0; t < SN; ++t) {
+      const int n = nw0 + 16 * t;
+      epilogue_cols<EPI>(m, n, mok && n < N, sc, sc2, Y, ldy, res[t], rmax,
+                         [&](int mtx, int v) { return (float)(acc[mtx][s][t][v] >> SHIFT); });
+    }
+    if constexpr (EPI == BL_EPI_RELU2_GLU) {
+      if (rowmax) {
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+        if (g4 == 0 && mok) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, bl_f2u(rmax));
+      }
+    }
   }
 }
 
@@ -485,10 +558,19 @@ hipError_t launch(const bl_mm_args& a, hipStream_t st) {
     hipLaunchKernelGGL((k_gemm_mx<FMT, EPI>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A, a.ascale, a.M, a.K, W,
                        a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
   } else {
-    using C = CfgI8<FMT, EPI>;
-    const int ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
-    hipLaunchKernelGGL((k_gemm_i8<FMT, EPI>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A, a.ascale, a.M, a.K, W,
-                       a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
+    // 128 x 256 tiles when they give every CU at least two blocks, 128 x 128 tiles otherwise
+    using C2 = CfgI8<FMT, EPI, 256>;
+    const int ntm = (a.M + 127) / 128;
+    const long wide = (long)ntm * ((a.N + C2::BN - 1) / C2::BN);
+    if (wide >= 512) {
+      hipLaunchKernelGGL((k_gemm_i8<FMT, EPI, 256>), dim3(wide), dim3(C2::NW * 64), 0, st, A, a.ascale, a.M, a.K, W,
+                         a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
+    } else {
+      using C1 = CfgI8<FMT, EPI, 128>;
+      hipLaunchKernelGGL((k_gemm_i8<FMT, EPI, 128>), dim3((long)ntm * ((a.N + C1::BN - 1) / C1::BN)), dim3(C1::NW * 64),
+                         0, st, A, a.ascale, a.M, a.K, W, a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr,
+                         a.rowmax);
+    }
   }
   return hipGetLastError();
 }

@@ -104,6 +104,8 @@ MM_CASES = [
     (dict(codes=P_MIS), 3), (dict(packed=P_MIS), 3), (dict(y=P_MIS), 3),
     (dict(epi=tw.bl_epilogue(1, None, 32, None, None, None)), 1),
     (dict(epi=tw.bl_epilogue(1, 4096, 8, None, None, None)), 1),
+    (dict(epi=tw.bl_epilogue(1, 4100, 32, None, None, None)), 3),
+    (dict(epi=tw.bl_epilogue(1, 4096, 33, None, None, None)), 3),
     (dict(epi=tw.bl_epilogue(2, None, 0, None, 4096, None)), 1),
     (dict(epi=tw.bl_epilogue(2, None, 0, 4100, 4096, None)), 3),
     (dict(epi=tw.bl_epilogue(7, None, 0, None, None, None)), 1),
