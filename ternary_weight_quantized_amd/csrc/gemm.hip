@@ -46,6 +46,9 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 
 // ----------------------------------------------------------------------------- A storage per format
 constexpr int NST = 4;   // stage buffers (three steps in flight)
+#ifndef MX_BM
+#define MX_BM 128        // FP6/FP4 GEMM block rows: 128 (two blocks per CU) or 256 (one)
+#endif
 
 template <int FMT>
 struct AFmt {
@@ -245,125 +248,6 @@ __device__ __forceinline__ void epilogue_rows(int mb, int nb, int r16, int M, in
 }
 
 // ============================================================================ FP6 / FP4 matrix cores
-template <int FMT, int EPI>
-struct CfgMx {
-  static constexpr bool GLU = (EPI == BL_EPI_RELU2_GLU);
-  static constexpr int NB = GLU ? 2 : 1;
-  static constexpr int NW = 4, WGM = 2, WGN = 2;
-  static constexpr int BM = 256, BN = GLU ? 128 : 256;
-  static constexpr int SM = BM / WGM / 16, SN = BN / WGN / 16;
-  using Plan = StagePlan<FMT, BM, BN, NB, NW>;
-};
-
-template <int FMT, int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm_mx(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
-                                                     int M, int K, const uint8_t* __restrict__ W,
-                                                     const float* __restrict__ walpha,
-                                                     const uint8_t* __restrict__ W2,
-                                                     const float* __restrict__ w2alpha, int N,
-                                                     float* __restrict__ Y, long ldy, const float* R, long ldr,
-                                                     float* __restrict__ rowmax) {
-  using C = CfgMx<FMT, EPI>;
-  using F = AFmt<FMT>;
-  using P = typename C::Plan;
-  constexpr int NB = C::NB, SM = C::SM, SN = C::SN;
-  constexpr bool FP6 = (FMT == BL_ACT_INT4_E3M2);
-  constexpr int CBSZ = FP6 ? 3 : 4;                  // A operand: FP6 E3M2 or FP4 E2M1
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * P::BYTES];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / C::WGN, wn = wave % C::WGN;
-  const int ntm = (M + C::BM - 1) / C::BM, ntn = (N + C::BN - 1) / C::BN;
-  int tm, tn;
-  tile_of(blockIdx.x, ntm, ntn, &tm, &tn);
-  const int m0 = tm * C::BM, n0 = tn * C::BN;
-  const int KS = K >> 7, NG = N >> 4;
-  const long arow = F::row_bytes(K);
-  const uint8_t* Wm[2] = {W, W2};
-  const int r16 = lane & 15, g4 = lane >> 4;
-
-  v4f acc[NB][SM][SN];
-#pragma unroll
-  for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-    for (int s = 0; s < SM; ++s)
-#pragma unroll
-      for (int t = 0; t < SN; ++t) acc[mtx][s][t] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // lane-constant LDS offsets of the A fragment (row r16 of the wave's first 16-row subtile):
-  // E3M2 24 bytes at 24 g as three 8-byte parts; E2M1 16 bytes at 16 g (one chunk)
-  const int arow0 = wm * SM * 16 + r16;
-  int aoff[3];
-#pragma unroll
-  for (int p = 0; p < 3; ++p) aoff[p] = FP6 ? a_off<FMT>(arow0, 24 * g4 + 8 * p) : a_off<FMT>(arow0, 16 * g4);
-
-  P plan;
-  plan.init(arow, m0, M, n0, NG, KS, wave, lane);
-  const uint32_t lds0 = lds_addr_of(smem);
-  // prologue: steps 0..NST-2 in flight (indices past the end re-fetch the last step, never read)
-#pragma unroll
-  for (int i = 0; i < NST - 1; ++i) plan.issue(lds0 + i * P::BYTES, A, Wm, min(i, KS - 1), wave, lane);
-
-  for (int ks = 0; ks < KS; ++ks) {
-    const uint8_t* cur = smem + (ks % NST) * P::BYTES;
-    // step ks has landed when at most NST-2 later steps are still outstanding
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * P::LOADS));
-    lds_barrier();
-    // refill the buffer every wave finished reading in step ks-1
-    plan.issue(lds0 + ((ks + NST - 1) % NST) * P::BYTES, A, Wm, min(ks + NST - 1, KS - 1), wave, lane);
-
-    const uint8_t* Bs = cur + C::BM * F::ROW + (wn * SN) * 512 + 8 * lane;
-    v8i bf[NB][SN];
-#pragma unroll
-    for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-      for (int t = 0; t < SN; ++t) {
-        const uint2 w = *reinterpret_cast<const uint2*>(Bs + mtx * (C::BN / 16) * 512 + t * 512);
-        bf[mtx][t] = expand_w_fp4(w.x, w.y);
-      }
-    // A fragments are read one 16-row subtile ahead of the MFMAs that use them
-    auto load_a = [&](int s) -> v8i {
-      const uint8_t* ar = cur + s * 16 * F::ROW;
-      if constexpr (FP6) {
-        const uint2 p0 = *reinterpret_cast<const uint2*>(ar + aoff[0]);
-        const uint2 p1 = *reinterpret_cast<const uint2*>(ar + aoff[1]);
-        const uint2 p2 = *reinterpret_cast<const uint2*>(ar + aoff[2]);
-        return v8i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y, (int)p2.x, (int)p2.y, 0, 0};
-      } else {
-        const uint4 q = *reinterpret_cast<const uint4*>(ar + aoff[0]);
-        return v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      }
-    };
-    v8i a_next = load_a(0);
-#pragma unroll
-    for (int s = 0; s < SM; ++s) {
-      const v8i a = a_next;
-      if (s + 1 < SM) a_next = load_a(s + 1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int mtx = 0; mtx < NB; ++mtx)
-#pragma unroll
-        for (int t = 0; t < SN; ++t)
-          acc[mtx][s][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bf[mtx][t], acc[mtx][s][t], CBSZ, 4, 0,
-                                                                            127, 0, 127);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the trailing (unused) loads land before the waves end
-
-  // fp32 epilogue: the matrix-core sum is 2*sum(c t) (E3M2) or sum(2e t) = sum(doubled code * t)
-  // (E2M1); x 0.5 is exact and gives sum(c t), respectively the half-unit count of the oracle.
-  const float alpha = *walpha;
-  const float alpha2 = C::GLU ? *w2alpha : 0.f;
-#pragma unroll
-  for (int s = 0; s < SM; ++s) {
-    const int mb = m0 + wm * SM * 16 + 16 * s + 4 * g4;
-    const int nb = n0 + wn * SN * 16;
-    epilogue_rows<EPI, SN>(mb, nb, r16, M, N, ascale, alpha, alpha2, Y, ldy, R, ldr, rowmax,
-                           [&](int mtx, int t, int v) { return acc[mtx][s][t][v] * 0.5f; });
-  }
-}
-
-// ============================================================================ int8 matrix cores
 // Epilogue for accumulators of transposed 16x16 products (weights as the first MFMA operand): the
 // lane holds, for token row m, the four consecutive columns n .. n+3 (n % 4 == 0), so every output
 // and residual access is one 16-byte vector. Columns come in whole groups of 16 (N % 16 == 0), so
@@ -391,6 +275,158 @@ __device__ __forceinline__ void epilogue_cols(int m, int n, bool ok, float sc, f
   if (ok) *reinterpret_cast<float4*>(Y + (long)m * ldy + n) = make_float4(o[0], o[1], o[2], o[3]);
 }
 
+template <int FMT, int EPI, int BM0>
+struct CfgMx {
+  static constexpr bool GLU = (EPI == BL_EPI_RELU2_GLU);
+  static constexpr int NB = GLU ? 2 : 1;
+  // 4 waves (2 x 2). BM0 = 256: 256 x 256 block, one block per CU (128 KB of LDS for E3M2);
+  // BM0 = 128: 128 x 256 block, two blocks per CU (at most 80 KB of LDS and 256 registers each).
+  static constexpr int NW = 4, WGM = 2, WGN = 2;
+  static constexpr int BM = BM0, BN = GLU ? 128 : 256;
+  static constexpr int SM = BM / WGM / 16, SN = BN / WGN / 16;
+  static constexpr int OCC = BM0 == 128 ? 2 : 1;
+  using Plan = StagePlan<FMT, BM, BN, NB, NW>;
+};
+
+template <int FMT, int EPI, int BM0>
+__global__ __launch_bounds__(256, (BM0 == 128 ? 2 : 1)) void k_gemm_mx(
+    const uint8_t* __restrict__ A, const float* __restrict__ ascale, int M, int K, const uint8_t* __restrict__ W,
+    const float* __restrict__ walpha, const uint8_t* __restrict__ W2, const float* __restrict__ w2alpha, int N,
+    float* __restrict__ Y, long ldy, const float* R, long ldr, float* __restrict__ rowmax) {
+  using C = CfgMx<FMT, EPI, BM0>;
+  using F = AFmt<FMT>;
+  using P = typename C::Plan;
+  constexpr int NB = C::NB, SM = C::SM, SN = C::SN, BM = C::BM;
+  constexpr bool FP6 = (FMT == BL_ACT_INT4_E3M2);
+  constexpr int AFMT = FP6 ? 3 : 4;                  // activation operand: FP6 E3M2 or FP4 E2M1
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * P::BYTES];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int ntm = (M + BM - 1) / BM, ntn = (N + C::BN - 1) / C::BN;
+  int tm, tn;
+  tile_of(blockIdx.x, ntm, ntn, &tm, &tn);
+  const int m0 = tm * BM, n0 = tn * C::BN;
+  const int KS = K >> 7, NG = N >> 4;
+  const long arow = F::row_bytes(K);
+  const uint8_t* Wm[2] = {W, W2};
+  const int r16 = lane & 15, g4 = lane >> 4;
+
+  // acc[mtx][s][t] = (weight tile t) x (activation subtile s)^T: lane holds row r16 of subtile s,
+  // columns 4 g4 .. 4 g4 + 3 of tile t
+  v4f acc[NB][SM][SN];
+#pragma unroll
+  for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+    for (int s = 0; s < SM; ++s)
+#pragma unroll
+      for (int t = 0; t < SN; ++t) acc[mtx][s][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // lane-constant LDS offsets of the activation fragment (row r16 of the wave's first 16-row
+  // subtile): E3M2 24 bytes at 24 g as three 8-byte parts; E2M1 16 bytes at 16 g (one chunk)
+  const int arow0 = wm * SM * 16 + r16;
+  int aoff[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) aoff[p] = FP6 ? a_off<FMT>(arow0, 24 * g4 + 8 * p) : a_off<FMT>(arow0, 16 * g4);
+
+  P plan;
+  plan.init(arow, m0, M, n0, NG, KS, wave, lane);
+  const uint32_t lds0 = lds_addr_of(smem);
+  // prologue: steps 0..NST-2 in flight (indices past the end re-fetch the last step, never read)
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) plan.issue(lds0 + i * P::BYTES, A, Wm, min(i, KS - 1), wave, lane);
+
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint8_t* cur = smem + (ks % NST) * P::BYTES;
+    // step ks has landed when at most NST-2 later steps are still outstanding
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * P::LOADS));
+    lds_barrier();
+    // refill the buffer every wave finished reading in step ks-1
+    plan.issue(lds0 + ((ks + NST - 1) % NST) * P::BYTES, A, Wm, min(ks + NST - 1, KS - 1), wave, lane);
+
+    // weight words of the step, expanded right before their first MFMA (subtile 0)
+    const uint8_t* Bs = cur + BM * F::ROW + (wn * SN) * 512 + 8 * lane;
+    uint2 bw[NB][SN];
+#pragma unroll
+    for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+      for (int t = 0; t < SN; ++t) bw[mtx][t] = *reinterpret_cast<const uint2*>(Bs + mtx * (C::BN / 16) * 512 + t * 512);
+    v8i bf[NB][SN];
+    // activation fragments are read one 16-row subtile ahead of the MFMAs that use them
+    auto load_a = [&](int s) -> v8i {
+      const uint8_t* ar = cur + s * 16 * F::ROW;
+      if constexpr (FP6) {
+        const uint2 p0 = *reinterpret_cast<const uint2*>(ar + aoff[0]);
+        const uint2 p1 = *reinterpret_cast<const uint2*>(ar + aoff[1]);
+        const uint2 p2 = *reinterpret_cast<const uint2*>(ar + aoff[2]);
+        return v8i{(int)p0.x, (int)p0.y, (int)p1.x, (int)p1.y, (int)p2.x, (int)p2.y, 0, 0};
+      } else {
+        const uint4 q = *reinterpret_cast<const uint4*>(ar + aoff[0]);
+        return v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      }
+    };
+    v8i a_next = load_a(0);
+#pragma unroll
+    for (int s = 0; s < SM; ++s) {
+      const v8i a = a_next;
+      if (s + 1 < SM) a_next = load_a(s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+        for (int t = 0; t < SN; ++t) {
+          if (s == 0) bf[mtx][t] = expand_w_fp4(bw[mtx][t].x, bw[mtx][t].y);
+          acc[mtx][s][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[mtx][t], a, acc[mtx][s][t], 4, AFMT, 0,
+                                                                            127, 0, 127);
+        }
+      if (s == 0) {
+#pragma unroll
+        for (int k = 0; k < NB * SN; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU: one tile's expansion
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the trailing (unused) loads land before the waves end
+
+  // fp32 epilogue: the matrix-core sum is 2*sum(c t) (E3M2) or sum(2e t) = sum(doubled code * t)
+  // (E2M1); x 0.5 is exact and gives sum(c t), respectively the half-unit count of the oracle.
+  const float alpha = *walpha;
+  const float alpha2 = C::GLU ? *w2alpha : 0.f;
+  const int nw0 = n0 + wn * SN * 16 + 4 * g4;
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    const int m = m0 + wm * SM * 16 + 16 * s + r16;
+    const bool mok = m < M;
+    const float ds = ascale[mok ? m : M - 1];
+    const float sc = ds * alpha, sc2 = ds * alpha2;
+    float4 res[SN];
+    if constexpr (EPI == BL_EPI_RESIDUAL) {
+#pragma unroll
+      for (int t = 0; t < SN; ++t) {
+        const int n = nw0 + 16 * t;
+        res[t] = (mok && n < N) ? *reinterpret_cast<const float4*>(R + (long)m * ldr + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float rmax = 0.f;
+#pragma unroll
+    for (int t = 0; t < SN; ++t) {
+      const int n = nw0 + 16 * t;
+      epilogue_cols<EPI>(m, n, mok && n < N, sc, sc2, Y, ldy, res[t], rmax,
+                         [&](int mtx, int v) { return acc[mtx][s][t][v] * 0.5f; });
+    }
+    if constexpr (EPI == BL_EPI_RELU2_GLU) {
+      if (rowmax) {
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+        if (g4 == 0 && mok) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, bl_f2u(rmax));
+      }
+    }
+  }
+}
+
+// ============================================================================ int8 matrix cores
 template <int FMT, int EPI, int BN0>
 struct CfgI8 {
   static constexpr bool A8 = (FMT == BL_ACT_INT8);
@@ -553,10 +589,10 @@ hipError_t launch(const bl_mm_args& a, hipStream_t st) {
   const uint8_t* W = static_cast<const uint8_t*>(a.W);
   const uint8_t* W2 = static_cast<const uint8_t*>(a.W2);
   if constexpr (FMT == BL_ACT_FP4_E2M1 || FMT == BL_ACT_INT4_E3M2) {
-    using C = CfgMx<FMT, EPI>;
+    using C = CfgMx<FMT, EPI, MX_BM>;
     const int ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
-    hipLaunchKernelGGL((k_gemm_mx<FMT, EPI>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A, a.ascale, a.M, a.K, W,
-                       a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
+    hipLaunchKernelGGL((k_gemm_mx<FMT, EPI, MX_BM>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A, a.ascale, a.M, a.K,
+                       W, a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
   } else {
     // 128 x 256 tiles when they give every CU at least two blocks, 128 x 128 tiles otherwise
     using C2 = CfgI8<FMT, EPI, 256>;
