@@ -197,57 +197,6 @@ __device__ __forceinline__ void tile_of(int b, int ntm, int ntn, int* tm, int* t
   *tn = r / gm;
 }
 
-// fp32 epilogue for the 4 rows (mb .. mb+3) a lane holds in each 16x16 tile of one tile row.
-// acc(mtx, t, v) returns the exact sum of code products of matrix mtx, tile t, row v as a float.
-template <int EPI, int SN, typename AccFn>
-__device__ __forceinline__ void epilogue_rows(int mb, int nb, int r16, int M, int N, const float* __restrict__ ascale,
-                                              float alpha, float alpha2, float* __restrict__ Y, long ldy,
-                                              const float* R, long ldr, float* __restrict__ rowmax, AccFn acc) {
-  float rmax[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int m = mb + v;
-    const bool mok = m < M;
-    const float ds = mok ? ascale[m] : 0.f;
-    const float sc = ds * alpha;
-    const float sc2 = ds * alpha2;
-#pragma unroll
-    for (int t = 0; t < SN; ++t) {
-      const int n = nb + 16 * t + r16;
-      if (!mok || n >= N) continue;
-      const float y0 = acc(0, t, v) * sc;
-      float out;
-      if constexpr (EPI == BL_EPI_RESIDUAL) {
-        out = y0 + R[(long)m * ldr + n];
-      } else if constexpr (EPI == BL_EPI_RELU2_GLU) {
-        const float u0 = acc(1, t, v) * sc2;
-        const float gp = y0 > 0.f ? y0 : 0.f;
-        out = (gp * gp) * u0;
-        const float a = fabsf(out);
-        rmax[v] = a > rmax[v] ? a : rmax[v];
-      } else {
-        out = y0;
-      }
-      Y[(long)m * ldy + n] = out;
-    }
-  }
-  if constexpr (EPI == BL_EPI_RELU2_GLU) {
-    if (rowmax) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float r = rmax[v];
-        r = fmaxf(r, __shfl_xor(r, 1, 64));
-        r = fmaxf(r, __shfl_xor(r, 2, 64));
-        r = fmaxf(r, __shfl_xor(r, 4, 64));
-        r = fmaxf(r, __shfl_xor(r, 8, 64));
-        const int m = mb + v;
-        if (r16 == 0 && m < M) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, bl_f2u(r));
-      }
-    }
-  }
-}
-
-// ============================================================================ FP6 / FP4 matrix cores
 // Epilogue for accumulators of transposed 16x16 products (weights as the first MFMA operand): the
 // lane holds, for token row m, the four consecutive columns n .. n+3 (n % 4 == 0), so every output
 // and residual access is one 16-byte vector. Columns come in whole groups of 16 (N % 16 == 0), so
