@@ -8,7 +8,9 @@ One step = one pass of every hot-path operation over the synthetic workloads, in
   attn_out     (M=8192, K=N=4096, Student-t outlier channels): Top-K 50% + INT8 quantize,
                W1.58A8 o_proj GEMM with the residual add
   decode_a4    (M=1,4,8, K=4096, N=11008): INT4 quantize + decode GEMV, replayed from a HIP graph over
-               24 rotating weight copies (270 MB, larger than the 256 MB last-level cache)
+               24 rotating weight copies (270 MB, larger than the 256 MB last-level cache); decode FFN
+               gate+up at the same shape, fused ReLU^2 GLU GEMV vs gate first + conditional up projection
+               (12 rotating copies of both matrices)
 The headline value is the W1.58A4 INT4 prefill GEMM throughput in TOPS (2*M*N*K / average kernel time,
 HIP events on the launch stream); the decode GEMV bandwidth and every kernel's time and roofline
 fraction are reported beside it. The weights are ternarized and packed once, outside the timed region.
@@ -30,6 +32,7 @@ INT8_PEAK_TOPS = 5000.0      # dense int8 MFMA
 FP4_PEAK_TOPS = 10100.0      # dense FP4/FP6 MFMA
 EPS = 1e-5
 ROTATE = 24
+ROTATE_GLU = 12                # 12 copies of gate + up (tiled and row-major) weights: 405 MB
 
 
 def parse():
@@ -113,6 +116,7 @@ def main():
     fx = bf16_dev(torch, fin["x"])
     gW, gA = pack(fin["w_gate"])
     uW, uA = pack(fin["w_up"])
+    uWr, _ = tw.bitlinear_pack_ternary_rows(torch.from_numpy(fin["w_up"]).to(dev), EPS)
     dW, dA = pack(fin["w_down"])
     del fin
     fc = torch.empty((F["M"], 3 * F["K"] // 4), dtype=torch.uint8, device=dev)
@@ -143,6 +147,12 @@ def main():
     dcs = {m: torch.empty((m, D["K"] // 2), dtype=torch.uint8, device=dev) for m in D["Ms"]}
     dss = {m: torch.empty(m, dtype=torch.float32, device=dev) for m in D["Ms"]}
     dys = {m: torch.empty((m, D["N"]), dtype=torch.float32, device=dev) for m in D["Ms"]}
+    # decode FFN gate+up (7B shape): fused ReLU^2 GLU GEMV vs gate-first conditional up projection
+    gWs = [gW] + [gW.clone() for _ in range(ROTATE_GLU - 1)]
+    uWs = [uW] + [uW.clone() for _ in range(ROTATE_GLU - 1)]
+    uWrs = [uWr] + [uWr.clone() for _ in range(ROTATE_GLU - 1)]
+    dgs = {m: torch.empty((m, F["N"]), dtype=torch.float32, device=dev) for m in D["Ms"]}
+    dhs = {m: torch.empty((m, F["N"]), dtype=torch.float32, device=dev) for m in D["Ms"]}
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
@@ -156,12 +166,27 @@ def main():
             for r in range(ROTATE):
                 tw.bitlinear_gemv_decode("int4", dcs[m], dss[m], D["K"], dWs[r], a0, D["N"], y=dys[m])
         graphs[m] = g
+    glu_graphs, cond_graphs = {}, {}
+    for m in D["Ms"]:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for r in range(ROTATE_GLU):
+                tw.bitlinear_gemv_decode("int4", dcs[m], dss[m], D["K"], gWs[r], gA, F["N"], y=dhs[m],
+                                         up_packed=uWs[r], up_alpha=uA)
+        glu_graphs[m] = g
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for r in range(ROTATE_GLU):
+                tw.bitlinear_gemv_decode_glu_conditional(dcs[m], dss[m], D["K"], gWs[r], gA, uWrs[r], uA, F["N"],
+                                                         gate=dgs[m], h=dhs[m])
+        cond_graphs[m] = g
     torch.cuda.synchronize()
 
     names = ["quant_int4_e3m2_prefill", "gemm_a4_int4_fp6_prefill", "quant_int4_prefill", "gemm_a4_int4_i8_prefill",
              "quant_fp4_prefill", "gemm_a4_fp4_prefill",
              "quant_int4_e3m2_ffn", "gemm_a4_glu_ffn", "quant_int8_h", "gemm_a8_down", "quant_topk_int8_attn",
-             "gemm_a8_oproj_residual"] + [f"decode_m{m}_graph" for m in D["Ms"]]
+             "gemm_a8_oproj_residual"] + [f"decode_m{m}_graph" for m in D["Ms"]] + \
+        [f"decode_glu_m{m}_graph" for m in D["Ms"]] + [f"decode_glu_cond_m{m}_graph" for m in D["Ms"]]
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -192,6 +217,10 @@ def main():
         tw.bitlinear_gemm_w158a8_sparse(ac, as_, A["K"], oW, oA, A["N"], y=ay, residual=ar); mark()
         for m in D["Ms"]:
             graphs[m].replay(); mark()
+        for m in D["Ms"]:
+            glu_graphs[m].replay(); mark()
+        for m in D["Ms"]:
+            cond_graphs[m].replay(); mark()
         return evs
 
     if args.copy_calibration:
@@ -217,6 +246,10 @@ def main():
         for j, n in enumerate(names):
             times[n] += evs[j].elapsed_time(evs[j + 1]) * 1e3 / args.steps     # microseconds
     gemv_us = {m: times[f"decode_m{m}_graph"] / ROTATE for m in D["Ms"]}     # includes the tiny quantize
+    glu_us = {m: times[f"decode_glu_m{m}_graph"] / ROTATE_GLU for m in D["Ms"]}
+    cond_us = {m: times[f"decode_glu_cond_m{m}_graph"] / ROTATE_GLU for m in D["Ms"]}
+    # live up rows of the conditional projection (channels whose gate is positive in some row)
+    live = {m: int((dgs[m] > 0).any(dim=0).sum().item()) for m in D["Ms"]}
 
     # ------------------------------------------------------------------ algorithmic work per kernel
     Mp, Kp, Np = P["M"], P["K"], P["N"]
@@ -294,6 +327,19 @@ def main():
                 "algorithmic": f"2*M*N*K = {ops_prefill:.4g} ops per launch"}
     decode = {f"m{m}": {"us": round(gemv_us[m], 3), "gbs": round(gbs(dec_bytes(m), gemv_us[m]), 1),
                         "frac_hbm": round(gbs(dec_bytes(m), gemv_us[m]) / HBM_PEAK_GBS, 4)} for m in D["Ms"]}
+    glu_w = F["N"] * F["K"] / 4
+
+    def glu_bytes(m, rows_up):
+        return glu_w + rows_up * F["K"] / 4 + m * F["K"] / 2 + 8 * m + 8 + 4 * m * F["N"] * (2 if rows_up < F["N"] else 1)
+
+    for m in D["Ms"]:
+        b_full, b_cond = glu_bytes(m, F["N"]), glu_bytes(m, live[m])
+        decode[f"glu_full_m{m}"] = {"us": round(glu_us[m], 3), "gbs": round(gbs(b_full, glu_us[m]), 1),
+                                    "frac_hbm": round(gbs(b_full, glu_us[m]) / HBM_PEAK_GBS, 4)}
+        decode[f"glu_conditional_m{m}"] = {
+            "us": round(cond_us[m], 3), "gbs": round(gbs(b_cond, cond_us[m]), 1),
+            "frac_hbm": round(gbs(b_cond, cond_us[m]) / HBM_PEAK_GBS, 4),
+            "live_up_rows": round(live[m] / F["N"], 4), "speedup_vs_fused": round(glu_us[m] / cond_us[m], 3)}
 
     sparsity = {"ffn_h_zero_codes": round(1 - nnz_h / (F["M"] * F["N"]), 4),
                 "attn_zero_codes": round(1 - nnz_attn / (A["M"] * A["K"]), 4)}

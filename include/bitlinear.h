@@ -190,6 +190,39 @@ bl_status bitlinear_gemv_decode(int32_t fmt, const void* d_codes, const float* d
                                 const void* d_packed, const float* d_alpha, int64_t N,
                                 float* d_y, int64_t ldy, const bl_epilogue* h_epi, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_pack_ternary_rows: the same ternary quantizer (alpha and codes exactly as
+ * bitlinear_pack_ternary) in the row-major 2-bit layout used by the gathered up projection:
+ * row n occupies bytes [n K/4, (n+1) K/4); 32-bit word i of the row (little-endian, at byte
+ * n K/4 + 4 i) holds weights k0 = 16 i .. 16 i + 15 with weight k0 + q (q < 8) in bits [4q, 4q+2)
+ * and weight k0 + 8 + q in bits [4q+2, 4q+4) (the same placement as inside a tile word).
+ * Arguments, shapes and errors as for bitlinear_pack_ternary.
+ * ------------------------------------------------------------------------------------------- */
+bl_status bitlinear_pack_ternary_rows(const float* d_w, int64_t N, int64_t K, float eps,
+                                      void* d_packed, float* d_alpha,
+                                      void* d_workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_gemv_decode_glu_conditional: the decode FFN gate and up projections with the
+ * conditional computation of section 3.4, "Squared ReLU Gating and Conditional Computation in the
+ * FFN": the gate projection is computed first, then the up projection only for channels whose
+ * gate is positive (relu(g)^2 vanishes elsewhere, so those rows of W_up are never read).
+ *   g = y0(gate) as in the epilogue above (INT4 activations, tiled W_gate), written to d_gate;
+ *   h[m, n] = RN32(RN32(g * g) * u) where g[m, n] > 0, with u = y0(up) (W_up in the row-major
+ *   layout of bitlinear_pack_ternary_rows), and h[m, n] = +0 where g[m, n] <= 0.
+ *   (Equal as numbers to the RELU2_GLU epilogue, which yields -0 where g <= 0 and u < 0.)
+ *   d_row_absmax, if non-NULL, receives max_n |h[m, n]| per row (cleared first).
+ * Arguments: d_codes/d_scale INT4 activations [M, K] (BL_ACT_INT4 layout), 1 <= M <= 8;
+ * d_gate [M, N] float32 output (row stride ldg >= N), d_h [M, N] float32 output
+ * (row stride ldh >= N, 16-byte aligned, ldh*4 a multiple of 16). Other rules as for the GEMMs.
+ * ------------------------------------------------------------------------------------------- */
+bl_status bitlinear_gemv_decode_glu_conditional(const void* d_codes, const float* d_scale,
+                                                int64_t M, int64_t K,
+                                                const void* d_gate_packed, const float* d_gate_alpha,
+                                                const void* d_up_rows, const float* d_up_alpha, int64_t N,
+                                                float* d_gate, int64_t ldg, float* d_h, int64_t ldh,
+                                                float* d_row_absmax, void* stream);
+
 const char* bitlinear_status_string(int32_t status);
 int32_t bitlinear_abi_version(void);
 

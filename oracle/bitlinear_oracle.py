@@ -41,6 +41,9 @@ reason in the design notes):
      over the whole row (which survives whenever keep >= 1).
   R9 FFN: ReLU^2 acts on the gate projection, h = RN32(RN32(g+ * g+) * u) with
      g, u the fp32 dequantized projections; the down input is INT8 without Top-K.
+  R14 Conditional up projection: a channel's up output is computed only when its gate is
+     positive in some row; entries with g <= 0 are +0 (the full form gives +0 * u, which is
+     -0 when u < 0: equal as numbers).
 """
 from __future__ import annotations
 
@@ -220,6 +223,41 @@ def relu2_glu(g, u):
     u = np.asarray(u, dtype=np.float32)
     gp = np.where(g > 0, g, F32(0.0)).astype(np.float32)
     return ((gp * gp).astype(np.float32) * u).astype(np.float32)
+
+
+def relu2_glu_conditional(g, u_fn):
+    """Conditional up projection of [GLU] (R14): the up projection is evaluated only for channels
+    whose gate is positive in some row; h = RN32(RN32(g * g) * u) where g > 0 and +0 elsewhere.
+
+    u_fn(cols) returns the dequantized up projection for the given column indices only (so the
+    reference, like the method, never forms u for a channel whose gate is non-positive in every
+    row). Returns (h, live_columns).
+    """
+    g = np.asarray(g, dtype=np.float32)
+    live = np.flatnonzero(np.any(g > 0, axis=0))
+    h = np.zeros(g.shape, dtype=np.float32)
+    if live.size:
+        gl = g[:, live]
+        ul = np.asarray(u_fn(live), dtype=np.float32)
+        hl = ((gl * gl).astype(np.float32) * ul).astype(np.float32)
+        h[:, live] = np.where(gl > 0, hl, F32(0.0))
+    return h, live
+
+
+def ffn_gate_up_conditional_ref(x, wg_codes, alpha_g, wu_codes, alpha_u, eps: float = 1e-5):
+    """Decode FFN front half with conditional computation: INT4 input -> gate projection g, then
+    the up projection only on the channels where some row of g is positive. [A4], [GLU]"""
+    codes, dscale, _ = quant_int4(x, eps)
+    acc_g = gemm_int(codes, wg_codes)
+    g = dequant_f32(acc_g, dscale, alpha_g)
+    wu = np.asarray(wu_codes)
+
+    def u_fn(cols):
+        return dequant_f32(gemm_int(codes, wu[cols]), dscale, alpha_u)
+
+    h, live = relu2_glu_conditional(g, u_fn)
+    return dict(codes=codes, dscale=dscale, g=g, h=h, live=live,
+                h_absmax=np.max(np.abs(h), axis=1).astype(np.float32))
 
 
 # --------------------------------------------------------------------------- end-to-end

@@ -21,9 +21,10 @@ BL_EPI_NONE, BL_EPI_RESIDUAL, BL_EPI_RELU2_GLU = 0, 1, 2
 FORMATS = {"int4": BL_ACT_INT4, "fp4": BL_ACT_FP4_E2M1, "int8": BL_ACT_INT8, "int4_e3m2": BL_ACT_INT4_E3M2}
 
 EXPORTED = (
-    "bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_packed_bytes",
+    "bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_pack_ternary_rows", "bitlinear_packed_bytes",
     "bitlinear_pack_workspace_bytes", "bitlinear_gemm_w158a4", "bitlinear_gemm_w158a8_sparse",
-    "bitlinear_gemv_decode", "bitlinear_status_string", "bitlinear_abi_version",
+    "bitlinear_gemv_decode", "bitlinear_gemv_decode_glu_conditional", "bitlinear_status_string",
+    "bitlinear_abi_version",
 )
 
 
@@ -67,6 +68,11 @@ def _lib():
         lib.bitlinear_pack_workspace_bytes.restype = sz
         lib.bitlinear_pack_ternary.argtypes = [vp, i64, i64, f32, vp, vp, vp, sz, vp]
         lib.bitlinear_pack_ternary.restype = i32
+        lib.bitlinear_pack_ternary_rows.argtypes = [vp, i64, i64, f32, vp, vp, vp, sz, vp]
+        lib.bitlinear_pack_ternary_rows.restype = i32
+        lib.bitlinear_gemv_decode_glu_conditional.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, i64, vp, i64, vp,
+                                                              i64, vp, vp]
+        lib.bitlinear_gemv_decode_glu_conditional.restype = i32
         for name in ("bitlinear_gemm_w158a4", "bitlinear_gemv_decode"):
             getattr(lib, name).argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, i64, ep, vp]
             getattr(lib, name).restype = i32
@@ -141,8 +147,7 @@ def bitlinear_pack_workspace_bytes():
     return int(_lib().bitlinear_pack_workspace_bytes())
 
 
-def bitlinear_pack_ternary(w, eps=1e-5, packed=None, alpha=None, workspace=None, stream=None):
-    """Ternarize and pack w [N, K] float32 (CUDA). Returns (packed uint8 [N*K/4], alpha f32 [1])."""
+def _pack(fn_name, w, eps, packed, alpha, workspace, stream):
     import torch
     N, K = w.shape
     if packed is None:
@@ -151,10 +156,20 @@ def bitlinear_pack_ternary(w, eps=1e-5, packed=None, alpha=None, workspace=None,
         alpha = torch.empty(1, dtype=torch.float32, device=w.device)
     if workspace is None:
         workspace = torch.empty(bitlinear_pack_workspace_bytes(), dtype=torch.uint8, device=w.device)
-    st = _lib().bitlinear_pack_ternary(_ptr(w), N, K, float(eps), _ptr(packed), _ptr(alpha), _ptr(workspace),
-                                       workspace.numel() * workspace.element_size(), _stream(stream))
-    _check(st, "bitlinear_pack_ternary")
+    st = getattr(_lib(), fn_name)(_ptr(w), N, K, float(eps), _ptr(packed), _ptr(alpha), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, fn_name)
     return packed, alpha
+
+
+def bitlinear_pack_ternary(w, eps=1e-5, packed=None, alpha=None, workspace=None, stream=None):
+    """Ternarize and pack w [N, K] float32 (CUDA), tiled layout. Returns (packed uint8 [N*K/4], alpha f32 [1])."""
+    return _pack("bitlinear_pack_ternary", w, eps, packed, alpha, workspace, stream)
+
+
+def bitlinear_pack_ternary_rows(w, eps=1e-5, packed=None, alpha=None, workspace=None, stream=None):
+    """Ternarize and pack w [N, K] float32 (CUDA), row-major layout (gathered up projection)."""
+    return _pack("bitlinear_pack_ternary_rows", w, eps, packed, alpha, workspace, stream)
 
 
 def _epilogue(residual=None, up_packed=None, up_alpha=None, row_absmax=None):
@@ -199,6 +214,24 @@ def bitlinear_gemv_decode(fmt, codes, scale, K, packed, alpha, N, y=None, residu
     """Decode product for 1 <= M <= 8 tokens (INT4 or INT8 codes)."""
     return _mm("bitlinear_gemv_decode", fmt, codes, scale, scale.shape[0], K, packed, alpha, N, y, residual,
                up_packed, up_alpha, row_absmax, stream)
+
+
+def bitlinear_gemv_decode_glu_conditional(codes, scale, K, gate_packed, gate_alpha, up_rows, up_alpha, N,
+                                           gate=None, h=None, row_absmax=None, stream=None):
+    """Decode gate projection, then the up projection only where the gate is positive.
+    Returns (gate [M, N] f32, h [M, N] f32)."""
+    import torch
+    M = scale.shape[0]
+    if gate is None:
+        gate = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    if h is None:
+        h = torch.empty((M, N), dtype=torch.float32, device=codes.device)
+    st = _lib().bitlinear_gemv_decode_glu_conditional(_ptr(codes), _ptr(scale), M, K, _ptr(gate_packed),
+                                                      _ptr(gate_alpha), _ptr(up_rows), _ptr(up_alpha), N,
+                                                      _ptr(gate), gate.stride(0), _ptr(h), h.stride(0),
+                                                      _ptr(row_absmax), _stream(stream))
+    _check(st, "bitlinear_gemv_decode_glu_conditional")
+    return gate, h
 
 
 def bitlinear_abi_version():

@@ -106,7 +106,19 @@ bl_status bitlinear_pack_ternary(const float* d_w, int64_t N, int64_t K, float e
   if (N * K >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ws_bytes < bitlinear_pack_workspace_bytes()) return BL_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(d_w) || !aligned16(d_packed) || !aligned16(d_workspace)) return BL_ERR_MISALIGNED;
-  return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace,
+  return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace, false,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_pack_ternary_rows(const float* d_w, int64_t N, int64_t K, float eps, void* d_packed,
+                                      float* d_alpha, void* d_workspace, size_t ws_bytes, void* stream) {
+  if (!d_w || !d_packed || !d_alpha || !d_workspace) return BL_ERR_INVALID_ARGUMENT;
+  if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
+  if (N < 1 || K < 1 || K % 256 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (N * K >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (ws_bytes < bitlinear_pack_workspace_bytes()) return BL_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(d_w) || !aligned16(d_packed) || !aligned16(d_workspace)) return BL_ERR_MISALIGNED;
+  return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace, true,
                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -147,6 +159,30 @@ bl_status bitlinear_gemv_decode(int32_t fmt, const void* d_codes, const float* d
   if (fmt != BL_ACT_INT4 && fmt != BL_ACT_INT8) return BL_ERR_INVALID_ARGUMENT;
   if (M > 8) return BL_ERR_UNSUPPORTED_SHAPE;
   return run_mm(true, fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, h_epi, stream);
+}
+
+bl_status bitlinear_gemv_decode_glu_conditional(const void* d_codes, const float* d_scale, int64_t M, int64_t K,
+                                                const void* d_gate_packed, const float* d_gate_alpha,
+                                                const void* d_up_rows, const float* d_up_alpha, int64_t N,
+                                                float* d_gate, int64_t ldg, float* d_h, int64_t ldh,
+                                                float* d_row_absmax, void* stream) {
+  const bl_status s = check_mm(BL_ACT_INT4, d_codes, d_scale, M, K, d_gate_packed, d_gate_alpha, N, d_gate, ldg,
+                               nullptr);
+  if (s != BL_OK) return s;
+  if (!d_up_rows || !d_up_alpha || !d_h) return BL_ERR_INVALID_ARGUMENT;
+  if (ldh < N) return BL_ERR_INVALID_ARGUMENT;
+  if (M > 8) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(d_up_rows) || !aligned16(d_h) || (ldh * 4) % 16 != 0) return BL_ERR_MISALIGNED;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d_row_absmax) {
+    const hipError_t e = bl_launch_fill_zero(d_row_absmax, (long)M, st);
+    if (e != hipSuccess) return BL_ERR_HIP;
+  }
+  bl_upcond_args u{};
+  u.A = d_codes; u.ascale = d_scale; u.M = (int)M; u.K = (int)K; u.N = (int)N;
+  u.G = d_gate; u.ldg = (long)ldg; u.Wup = d_up_rows; u.upalpha = d_up_alpha;
+  u.H = d_h; u.ldh = (long)ldh; u.rowmax = d_row_absmax;
+  return hip_status(bl_launch_glu_conditional_fused(u, d_gate_packed, d_gate_alpha, st));
 }
 
 }  // extern "C"

@@ -9,7 +9,7 @@ hipError_t bl_launch_quantize(const void* x, int in_f32, int M, int K, long ldx,
                               const float* hint, void* codes, float* scale, uint32_t* mask, hipStream_t st);
 
 hipError_t bl_launch_pack(const float* w, int N, int K, float eps, void* packed, float* alpha,
-                          void* ws, hipStream_t st);
+                          void* ws, bool rows, hipStream_t st);
 
 // Arguments shared by the GEMM and the decode GEMV.
 struct bl_mm_args {
@@ -32,3 +32,21 @@ struct bl_mm_args {
 hipError_t bl_launch_gemm(const bl_mm_args& a, hipStream_t st);
 hipError_t bl_launch_gemv(const bl_mm_args& a, hipStream_t st);
 hipError_t bl_launch_fill_zero(float* p, long n, hipStream_t st);
+
+// Decode FFN gate and conditional up projection: g = the dequantized gate projection (written to G),
+// h = relu(g)^2 * u only where g is positive (+0 elsewhere), u from row-major packed up weights.
+struct bl_upcond_args {
+  const void* A;          // INT4 codes [M, K/2]
+  const float* ascale;
+  int M, K, N;
+  float* G;               // dequantized gate [M, N] (output), row stride ldg
+  long ldg;
+  const void* Wup;        // row-major packed up weights
+  const float* upalpha;
+  float* H;               // [M, N], row stride ldh
+  long ldh;
+  float* rowmax;          // optional
+};
+// gate GEMV and conditional up projection in one launch (one block per 16 channels)
+hipError_t bl_launch_glu_conditional_fused(const bl_upcond_args& a, const void* Wg, const float* galpha,
+                                          hipStream_t st);

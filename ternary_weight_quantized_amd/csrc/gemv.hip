@@ -204,9 +204,171 @@ hipError_t launch_epi(const bl_mm_args& a, hipStream_t st) {
   return launch<FMT, BL_EPI_NONE>(a, st);
 }
 
+// ============================================================================ conditional up projection
+// "Squared ReLU Gating and Conditional Computation in the FFN" (section 3.4): once the gate
+// projection g is known, the up projection is only needed for channels whose gate is positive
+// (relu(g)^2 is zero elsewhere). Up weights come in the row-major 2-bit layout (row n = K/4
+// contiguous bytes), so a skipped channel costs no weight traffic.
+//
+// dot_ternary_int4: sum over one 64-wide K slice (16 weight bytes, 32 code bytes) of c * t. Ternary
+// fields f in {00, 01, 11} enter v_dot8 as signed 4-bit values f in {0, 1, 3}; with b the high bit
+// of the field, t = f - 4 b, so sum(c t) = dot(c, f) - 4 dot(c, b), exact in int32.
+__device__ __forceinline__ int dot_ternary_int4(uint4 w, uint4 a0, uint4 a1, int acc) {
+  // word i covers k 16 i .. 16 i + 15: bits 4q..4q+1 -> k = 16 i + q, bits 4q+2..4q+3 -> k = 16 i + 8 + q
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  const uint32_t as[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  int f = 0, b = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = ws[i] & 0x33333333u, hi = (ws[i] >> 2) & 0x33333333u;
+    f = __builtin_amdgcn_sdot8((int)as[2 * i], (int)lo, f, false);
+    f = __builtin_amdgcn_sdot8((int)as[2 * i + 1], (int)hi, f, false);
+    b = __builtin_amdgcn_sdot8((int)as[2 * i], (int)((lo >> 1) & 0x11111111u), b, false);
+    b = __builtin_amdgcn_sdot8((int)as[2 * i + 1], (int)((hi >> 1) & 0x11111111u), b, false);
+  }
+  return acc + f - 4 * b;
+}
+
+// Fused form for one block per 16-channel group (the tile row of W_gate): phase 1 is the INT4 decode
+// GEMV of the gate (eight waves split K, exact int32 sum in LDS); the block then knows g for its 16
+// channels and M rows, and in phase 2 each wave takes two channels and, if the gate of a channel is
+// positive in some row, streams its row-major up weights (K/4 bytes; 16 bytes per lane and 64-wide
+// K slice) against the INT4 codes with v_dot8 (dot_ternary_int4 above). Rows of W_up whose channel
+// is dead in every row are never read. One launch, so the up loads of a block overlap the gate loads
+// of others.
+__global__ __launch_bounds__(WAVES * 64) void k_glu_cond_fused(const uint8_t* __restrict__ A,
+                                                               const float* __restrict__ ascale, int M, int K,
+                                                               const uint8_t* __restrict__ Wg,
+                                                               const float* __restrict__ galpha,
+                                                               const uint8_t* __restrict__ Wup,
+                                                               const float* __restrict__ upalpha, int N,
+                                                               float* __restrict__ Gout, long ldg,
+                                                               float* __restrict__ H, long ldh,
+                                                               float* __restrict__ rowmax) {
+  __shared__ v4i red[WAVES - 1][64];
+  __shared__ float gl[8][16];                   // g[row][channel] of the block
+  __shared__ float hmax[8][16];                 // |h| for the row maxima
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = blockIdx.x;
+  const int KT = K >> 7, NG = N >> 4;
+  const int per = (KT + WAVES - 1) / WAVES;
+  const int kt_begin = wave * per;
+  const int kt_end = min(KT, kt_begin + per);
+  const int r = lane & 15, g4 = lane >> 4;
+  const long arow = K >> 1;
+  const uint8_t* arp = A + (long)min(r, M - 1) * arow + 16 * g4;
+  const uint8_t* const wp[2] = {Wg + (long)G * 512 + lane * 8, Wg + (long)G * 512 + lane * 8};
+  const long wstep = (long)NG * 512;
+  float ds[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) ds[v] = ascale[min(4 * g4 + v, M - 1)];
+  const float alpha = *galpha;
+
+  // ---- phase 1: gate projection of the block's 16 channels
+  v4i acc[1][2];
+  acc[0][0] = acc[0][1] = v4i{0, 0, 0, 0};
+  for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CH) {
+    if (kt0 + CH <= kt_end) chunk<false, 1, true>(arp, wp, wstep, kt0, kt_end, g4, acc);
+    else chunk<false, 1, false>(arp, wp, wstep, kt0, kt_end, g4, acc);
+  }
+  acc[0][0] += acc[0][1];
+  if (wave > 0) red[wave - 1][lane] = acc[0][0];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < WAVES - 1; ++w) acc[0][0] += red[w][lane];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * g4 + v;
+      const float g = (float)(acc[0][0][v] >> 10) * (ds[v] * alpha);
+      if (m < 8) gl[m][r] = g;
+      if (m < M) Gout[(long)m * ldg + 16 * G + r] = g;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: up projection of the live channels (two per wave)
+  const float ualpha = *upalpha;
+  const long wrow = K >> 2;
+  const int KC = K >> 6;
+  const int ch0 = 2 * wave;
+  bool live[2] = {false, false};
+  for (int m = 0; m < M; ++m) {
+    live[0] |= gl[m][ch0] > 0.f;
+    live[1] |= gl[m][ch0 + 1] > 0.f;
+  }
+  int uacc[2][8];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) uacc[q][m] = 0;
+  if (live[0] || live[1]) {
+    const uint8_t* wr0 = Wup + (long)(16 * G + ch0) * wrow;
+    for (int c = lane; c < KC; c += 64) {
+      // both weight rows first (only the live ones), then the codes of the M rows
+      uint4 w[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        w[q] = live[q] ? *reinterpret_cast<const uint4*>(wr0 + q * wrow + 16 * c) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (m >= M) break;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(A + (long)m * arow + 32 * c);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(A + (long)m * arow + 32 * c + 16);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          if (live[q]) uacc[q][m] = dot_ternary_int4(w[q], a0, a1, uacc[q][m]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (!live[q]) continue;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (m >= M) break;
+        int v = uacc[q][m];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
+        uacc[q][m] = v;
+      }
+    }
+  }
+  if (lane < 2 * M) {
+    const int q = lane & 1, m = lane >> 1, ch = ch0 + q;
+    int u0 = 0, u1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u0 = (i == m) ? uacc[0][i] : u0;
+      u1 = (i == m) ? uacc[1][i] : u1;
+    }
+    const float um = (float)(q ? u1 : u0);
+    const float g = gl[m][ch];
+    const float h = g > 0.f ? (g * g) * (um * (ascale[m] * ualpha)) : 0.f;
+    H[(long)m * ldh + 16 * G + ch] = h;
+    hmax[m][ch] = fabsf(h);
+  }
+  if (rowmax) {
+    __syncthreads();
+    if (wave == 0 && lane < M) {
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) a = fmaxf(a, hmax[lane][c]);
+      atomicMax(reinterpret_cast<unsigned int*>(rowmax) + lane, bl_f2u(a));
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t bl_launch_gemv(const bl_mm_args& a, hipStream_t st) {
   if (a.fmt == BL_ACT_INT8) return launch_epi<BL_ACT_INT8>(a, st);
   return launch_epi<BL_ACT_INT4>(a, st);
+}
+
+hipError_t bl_launch_glu_conditional_fused(const bl_upcond_args& a, const void* Wg, const float* galpha,
+                                          hipStream_t st) {
+  hipLaunchKernelGGL(k_glu_cond_fused, dim3(a.N / 16), dim3(WAVES * 64), 0, st, static_cast<const uint8_t*>(a.A),
+                     a.ascale, a.M, a.K, static_cast<const uint8_t*>(Wg), galpha, static_cast<const uint8_t*>(a.Wup),
+                     a.upalpha, a.N, a.G, a.ldg, a.H, a.ldh, a.rowmax);
+  return hipGetLastError();
 }

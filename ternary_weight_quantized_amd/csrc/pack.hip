@@ -8,7 +8,8 @@
 // significands are summed per exponent in 64-bit integers (LDS per block, then global atomics),
 // so the sum is independent of order; one thread turns the 256 bins into the correctly rounded
 // double of the exact total and divides by N*K. The pack kernel then writes one 32-bit word
-// (16 weights of one row) per thread in the tiled layout of the public header (16 x 128 tiles).
+// (16 weights of one row) per thread in the tiled layout of the public header (16 x 128 tiles), or
+// in the row-major layout used by the gathered (conditional) up projection.
 #include "bl_common.h"
 #include "bl_kernels.h"
 
@@ -79,10 +80,35 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int N
   out[wid] = word;
 }
 
+// Row-major variant: one thread per 32-bit word (n, i) holding weights 16 i .. 16 i + 15 of row n,
+// with the same placement inside the word; row n occupies K/4 contiguous bytes.
+__global__ __launch_bounds__(256) void k_pack_rows(const float* __restrict__ w, int N, int K, float eps,
+                                                   const float* __restrict__ alpha, uint32_t* __restrict__ out) {
+  const long wid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long nwords = (long)N * K / 16;
+  if (wid >= nwords) return;
+  const float den = *alpha + eps;
+  const float4* src = reinterpret_cast<const float4*>(w + wid * 16);   // row-major: word wid covers 16 * wid
+  uint32_t word = 0u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float4 v = src[c];
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = 4 * c + j;
+      const int code = bl_roundclip(vv[j] / den, -1.f, 1.f);
+      const int pos = q < 8 ? 4 * q : 4 * (q - 8) + 2;
+      word |= ((uint32_t)code & 3u) << pos;
+    }
+  }
+  out[wid] = word;
+}
+
 }  // namespace
 
 hipError_t bl_launch_pack(const float* w, int N, int K, float eps, void* packed, float* alpha,
-                          void* ws, hipStream_t st) {
+                          void* ws, bool rows, hipStream_t st) {
   unsigned long long* bins = static_cast<unsigned long long*>(ws);
   hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, st, bins, 256);
   const long n = (long)N * K;
@@ -91,7 +117,11 @@ hipError_t bl_launch_pack(const float* w, int N, int K, float eps, void* packed,
   hipLaunchKernelGGL(k_abs_bins, dim3((unsigned)blocks), dim3(256), 0, st, w, n, bins);
   hipLaunchKernelGGL(k_alpha, dim3(1), dim3(64), 0, st, bins, (double)n, alpha);
   const long nwords = n / 16;
-  hipLaunchKernelGGL(k_pack, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st, w, N, K, eps, alpha,
-                     static_cast<uint32_t*>(packed));
+  if (rows)
+    hipLaunchKernelGGL(k_pack_rows, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st, w, N, K, eps, alpha,
+                       static_cast<uint32_t*>(packed));
+  else
+    hipLaunchKernelGGL(k_pack, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st, w, N, K, eps, alpha,
+                       static_cast<uint32_t*>(packed));
   return hipGetLastError();
 }

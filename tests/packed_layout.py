@@ -26,3 +26,20 @@ def pack_reference(codes: np.ndarray) -> np.ndarray:
     f = np.where(c < 0, 3, c).astype(np.uint32)
     words = np.bitwise_or.reduce(f << _POS, axis=-1).astype("<u4")
     return words.reshape(-1).view(np.uint8)
+
+
+def unpack_ternary_rows(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Row-major layout (bitlinear_pack_ternary_rows): row n is K/4 bytes, word i holds k = 16 i .. 16 i + 15."""
+    w = np.ascontiguousarray(packed, dtype=np.uint8).view("<u4").reshape(N, K // 16)
+    f = (w[..., None] >> _POS) & np.uint32(3)
+    if np.any(f == 2):
+        raise ValueError("invalid 2-bit field 10b in packed weights")
+    return np.where(f == 3, -1, f.astype(np.int64)).astype(np.int8).reshape(N, K)
+
+
+def pack_rows_reference(codes: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_ternary_rows (used to test the decoder itself)."""
+    N, K = codes.shape
+    f = np.where(codes < 0, 3, codes).astype(np.uint32).reshape(N, K // 16, 16)
+    words = np.bitwise_or.reduce(f << _POS, axis=-1).astype("<u4")
+    return words.reshape(-1).view(np.uint8)

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import ternary_weight_quantized_amd as tw
-from tests.packed_layout import pack_reference, unpack_ternary
+from tests.packed_layout import pack_reference, pack_rows_reference, unpack_ternary, unpack_ternary_rows
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitlinear.h")
@@ -29,10 +29,11 @@ def header_functions():
     return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(bitlinear_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_five_hot_path_calls():
+def test_header_declares_the_hot_path_calls():
     fns = header_functions()
     for f in ("bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_gemm_w158a4",
-              "bitlinear_gemm_w158a8_sparse", "bitlinear_gemv_decode"):
+              "bitlinear_gemm_w158a8_sparse", "bitlinear_gemv_decode", "bitlinear_pack_ternary_rows",
+              "bitlinear_gemv_decode_glu_conditional"):
         assert f in fns
 
 
@@ -152,4 +153,46 @@ def test_packed_layout_decoder_positions():
         words = packed.view("<u4")
         idx = tile * 128 + lane * 2 + word
         assert words[idx] == (1 << bit)
+        assert np.count_nonzero(words) == 1
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), 1), (dict(packed=None), 1), (dict(eps=0.0), 1), (dict(N=10), 2), (dict(K=300), 2),
+    (dict(wsb=100), 4), (dict(packed=P_MIS), 3),
+])
+def test_pack_rows_validation(kw, status):
+    a = dict(w=P, N=32, K=256, eps=1e-5, packed=P, alpha=P, ws=P, wsb=4096)
+    a.update(kw)
+    st = tw.library().bitlinear_pack_ternary_rows(a["w"], a["N"], a["K"], a["eps"], a["packed"], a["alpha"], a["ws"],
+                                                  a["wsb"], None)
+    assert st == status
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(codes=None), 1), (dict(up=None), 1), (dict(upa=None), 1), (dict(h=None), 1), (dict(gate=None), 1),
+    (dict(M=9), 2), (dict(K=128), 2), (dict(N=24), 2),
+    (dict(ldh=16), 1), (dict(ldg=16), 1), (dict(up=P_MIS), 3), (dict(h=P_MIS), 3), (dict(ldh=33), 3),
+])
+def test_glu_conditional_validation(kw, status):
+    a = dict(codes=P, scale=P, M=4, K=256, gp=P, ga=P, up=P, upa=P, N=32, gate=P, ldg=32, h=P, ldh=32, rm=None)
+    a.update(kw)
+    st = tw.library().bitlinear_gemv_decode_glu_conditional(a["codes"], a["scale"], a["M"], a["K"], a["gp"], a["ga"],
+                                                            a["up"], a["upa"], a["N"], a["gate"], a["ldg"], a["h"],
+                                                            a["ldh"], a["rm"], None)
+    assert st == status
+
+
+def test_packed_rows_decoder_roundtrip_and_positions():
+    rng = np.random.default_rng(1)
+    codes = rng.integers(-1, 2, (24, 512)).astype(np.int8)
+    np.testing.assert_array_equal(unpack_ternary_rows(pack_rows_reference(codes), 24, 512), codes)
+    for n, k in [(0, 0), (3, 9), (7, 16), (23, 511)]:
+        c = np.zeros((24, 512), np.int8)
+        c[n, k] = -1
+        words = pack_rows_reference(c).view("<u4")
+        q = k % 16
+        bit = 4 * q if q < 8 else 4 * (q - 8) + 2
+        assert words[n * 512 // 16 + k // 16] == (3 << bit)
         assert np.count_nonzero(words) == 1

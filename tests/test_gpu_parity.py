@@ -12,7 +12,7 @@ import ternary_weight_quantized_amd as tw
 from synth import activations_bf16, latent_weights, normal, to_bf16_bits
 from tests.gpu_util import (assert_y_close, dev_bf16, dev_f32, e3m2_values, host, int4_values, int8_values,
                             mask_bits, nibbles, torch_cuda, x_f32)
-from tests.packed_layout import unpack_ternary
+from tests.packed_layout import unpack_ternary, unpack_ternary_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +68,16 @@ def test_pack_ternary(N, K):
     w, codes, alpha, packed, a = packed_weights(100 + N, N, K)
     assert host(a)[0] == alpha, (host(a)[0], alpha)
     np.testing.assert_array_equal(unpack_ternary(host(packed), N, K), codes)
+
+
+@pytest.mark.parametrize("N,K", [(16, 256), (48, 768), (160, 4096)])
+def test_pack_ternary_rows(N, K):
+    torch_cuda()
+    w = latent_weights(150 + N, N, K)
+    codes, alpha = O.ternarize(w, EPS)
+    packed, a = tw.bitlinear_pack_ternary_rows(dev_f32(w), EPS)
+    assert host(a)[0] == alpha
+    np.testing.assert_array_equal(unpack_ternary_rows(host(packed), N, K), codes)
 
 
 def test_pack_ternary_wide_exponents_and_zero():
@@ -318,3 +328,29 @@ def test_decode_matches_gemm():
     y1 = tw.bitlinear_gemv_decode("int4", codes, scale, K, packed, a, N)
     y2 = tw.bitlinear_gemm_w158a4("int4", codes, scale, K, packed, a, N)
     np.testing.assert_array_equal(host(y1), host(y2))
+
+
+# ----------------------------------------------------------------------------- conditional up projection
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("N,K", [(16, 256), (48, 768), (80, 4352), (1024, 4096)])
+def test_glu_conditional(M, N, K):
+    """Gate first, up only where the gate is positive: gate, h (bit patterns, +0 where g <= 0) and
+    the row maxima equal the oracle's; h equals the fused GLU decode as numbers."""
+    torch = torch_cuda()
+    x = make_x(7000 + M + K, M, K, special=False)
+    wg = latent_weights(7100 + N, N, K)
+    wu = latent_weights(7200 + N, N, K)
+    tg, ag = O.ternarize(wg, EPS)
+    tu, au = O.ternarize(wu, EPS)
+    pg, dag = tw.bitlinear_pack_ternary(dev_f32(wg), EPS)
+    pu_rows, dau = tw.bitlinear_pack_ternary_rows(dev_f32(wu), EPS)
+    pu, _ = tw.bitlinear_pack_ternary(dev_f32(wu), EPS)
+    codes, scale, _, _, _ = _quant(x, "int4")
+    rowmax = torch.empty(M, dtype=torch.float32, device="cuda")
+    gate, h = tw.bitlinear_gemv_decode_glu_conditional(codes, scale, K, pg, dag, pu_rows, dau, N, row_absmax=rowmax)
+    r = O.ffn_gate_up_conditional_ref(x_f32(x), tg, ag, tu, au, EPS)
+    np.testing.assert_array_equal(host(gate).view(np.uint32), r["g"].view(np.uint32))
+    np.testing.assert_array_equal(host(h).view(np.uint32), r["h"].view(np.uint32))
+    np.testing.assert_array_equal(host(rowmax), r["h_absmax"])
+    full = tw.bitlinear_gemv_decode("int4", codes, scale, K, pg, dag, N, up_packed=pu, up_alpha=dau)
+    np.testing.assert_array_equal(host(full), host(h))

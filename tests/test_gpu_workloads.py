@@ -124,3 +124,24 @@ def test_attn_out_sampled():
     np.testing.assert_array_equal(host(scale)[rows], ref["dscale"])
     assert_y_close(host(y)[rows], ref["acc"], ref["dscale"], alpha, residual=inp["residual"][rows])
     assert np.all(mask_bits(host(mask), K).sum(axis=1) == keep)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_decode_glu_conditional_full(M):
+    """Decode FFN front half at the 7B shape (K=4096, N=11008) with the conditional up projection."""
+    torch = torch_cuda()
+    F = WORKLOADS["ffn_7b"]
+    inp = workload_inputs("ffn_7b")
+    K, N = F["K"], F["N"]
+    xb = workload_inputs("decode_a4")["x"][:M]
+    tg, ag, pg, dag = weights(inp["w_gate"])
+    tu, au = O.ternarize(inp["w_up"], EPS)
+    pu_rows, dau = tw.bitlinear_pack_ternary_rows(dev_f32(inp["w_up"]), EPS)
+    codes, scale, _ = tw.bitlinear_quantize_act(dev_bf16(xb), "int4", eps=EPS)
+    rowmax = torch.empty(M, dtype=torch.float32, device="cuda")
+    gate, h = tw.bitlinear_gemv_decode_glu_conditional(codes, scale, K, pg, dag, pu_rows, dau, N, row_absmax=rowmax)
+    r = O.ffn_gate_up_conditional_ref(bf16_bits_to_f32(xb), tg, ag, tu, au, EPS)
+    np.testing.assert_array_equal(host(gate).view(np.uint32), r["g"].view(np.uint32))
+    np.testing.assert_array_equal(host(h).view(np.uint32), r["h"].view(np.uint32))
+    np.testing.assert_array_equal(host(rowmax), r["h_absmax"])
+    print(f"decode glu conditional M={M}: live up rows {r['live'].size / N:.3f}")

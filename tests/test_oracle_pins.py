@@ -272,6 +272,43 @@ def test_ffn_composition_and_sparsity():
     assert np.all(np.abs(r["y"] - hq @ wq.T) <= bound)
 
 
+def test_relu2_glu_conditional_skips_dead_channels_and_matches_full_glu():
+    """Conditional up projection: u is requested only for live channels; h equals the full ReLU^2
+    GLU as numbers and is +0 (bit pattern 0) wherever the gate is <= 0."""
+    rng = np.random.default_rng(5)
+    g = rng.standard_normal((3, 40)).astype(np.float32)
+    g[:, :6] = -np.abs(g[:, :6])                     # six channels dead in every row
+    g[0, 6] = 0.0
+    u = rng.standard_normal((3, 40)).astype(np.float32)
+    seen = []
+
+    def u_fn(cols):
+        seen.append(np.asarray(cols))
+        return u[:, cols]
+
+    h, live = O.relu2_glu_conditional(g, u_fn)
+    full = O.relu2_glu(g, u)
+    np.testing.assert_array_equal(h, full)          # -0 == +0 as numbers
+    assert np.all(h.view(np.uint32)[g <= 0] == 0)
+    np.testing.assert_array_equal(live, np.flatnonzero((g > 0).any(axis=0)))
+    assert len(seen) == 1 and not set(range(6)) & set(seen[0].tolist())
+    mask = g > 0
+    np.testing.assert_array_equal(h.view(np.uint32)[mask], full.view(np.uint32)[mask])
+
+
+def test_ffn_gate_up_conditional_matches_ffn_ref():
+    x = bf16_bits_to_f32(activations_bf16(25, 3, 256))
+    tg, ag = O.ternarize(latent_weights(26, 96, 256))
+    tu, au = O.ternarize(latent_weights(27, 96, 256))
+    td, ad = O.ternarize(latent_weights(28, 256, 96))
+    full = O.ffn_ref(x, tg, ag, tu, au, td, ad)
+    r = O.ffn_gate_up_conditional_ref(x, tg, ag, tu, au)
+    np.testing.assert_array_equal(r["h"], full["h"])
+    np.testing.assert_array_equal(r["g"], O.dequant_f32(full["acc_g"], full["dscale"], ag))
+    np.testing.assert_array_equal(r["h_absmax"], full["h_absmax"])
+    assert 0 < r["live"].size < 96
+
+
 def test_oproj_residual():
     x = bf16_bits_to_f32(activations_bf16(51, 4, 128, outlier_scale=20.0, outlier_kind="t3"))
     t, a = O.ternarize(latent_weights(52, 64, 128))
