@@ -49,7 +49,10 @@ typedef enum {
   BL_ERR_HIP = 5
 } bl_status;
 
-typedef enum { BL_ACT_INT4 = 0, BL_ACT_FP4_E2M1 = 1, BL_ACT_INT8 = 2, BL_ACT_INT4_E3M2 = 3 } bl_act_format;
+typedef enum {
+  BL_ACT_INT4 = 0, BL_ACT_FP4_E2M1 = 1, BL_ACT_INT8 = 2, BL_ACT_INT4_E3M2 = 3,
+  BL_ACT_FP4_E2M1_POW2 = 4   /* quantizer only: FP4 codes with a power-of-two scale (matmuls take them as FP4_E2M1) */
+} bl_act_format;
 typedef enum { BL_IN_BF16 = 0, BL_IN_F32 = 1 } bl_in_dtype;
 typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_epi_kind;
 
@@ -59,6 +62,8 @@ typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_e
  *             nibble; two's-complement nibbles, codes in [-8, 7]. scale[m] = beta_m / sqrt(7).
  *   FP4_E2M1  same nibble layout; nibble = sign<<3 | e, e indexes the E2M1 magnitudes
  *             {0, 0.5, 1, 1.5, 2, 3, 4, 6} (OCP E2M1 encoding); zero is always +0. scale[m] = gamma_m / 6.
+ *   FP4_E2M1_POW2 (quantizer output only) the FP4_E2M1 layout with scale[m] = 2^p_m, the power of two
+ *             of the scale variant below; the matmul entry points take these codes as BL_ACT_FP4_E2M1.
  *   INT8      M x K bytes, row stride K, codes in [-127, 127] (0 where Top-K masked). scale[m] = gamma_m / 127.
  *   INT4_E3M2 the INT4 absmean codes (same values and scale as INT4) stored 6 bits each as their exact
  *             FP6 E3M2 bit pattern (sign bit 5, 3 exponent bits with bias 3, 2 mantissa bits:
@@ -92,6 +97,9 @@ typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_e
  *   FP4 E2M1 MinMax (paper Eq. 8-9; reading: the row max maps to 6): gamma = max|x|;
  *     s = RN32(6 / RN32(gamma + eps)); code = nearest E2M1 value of RN32(x * s), ties to even
  *     mantissa, saturating at 6.
+ *     fmt BL_ACT_FP4_E2M1_POW2 (the reading of the same equations with a power-of-two scale): p is the
+ *     smallest integer with 6 * 2^p >= gamma (at least -126); s = 2^-p (x * s is exact), the same
+ *     rounding, scale[m] = 2^p; eps is not used and an all-zero row gets scale 0.
  *   INT8 absmax with optional Top-K (section 3.4, sparsification, paper Eq. 1): gamma = max|x|
  *     over the whole row; s = RN32(127 / RN32(gamma + eps)); code = clamp(rint(RN32(x * s)), -128, 127)
  *     for the topk_keep entries of largest |x| (ties to the lower index), 0 elsewhere.
@@ -112,6 +120,21 @@ bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, i
                                  int32_t fmt, int32_t topk_keep, float eps,
                                  const float* d_row_absmax_hint,
                                  void* d_codes, float* d_scale, uint32_t* d_mask, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_quantize_act_per_tensor: the activation quantizers with ONE scale for the whole [M, K]
+ * tensor (the pages' "all entries in X" read per tensor; the per-token form above is the default):
+ *   INT4 / INT4_E3M2: beta = RN32(RN64(exact sum over all M K entries of |x|) / (M K)), then every
+ *   row as above with that beta; FP4_E2M1 / FP4_E2M1_POW2 / INT8 (no Top-K): gamma = max |x| over the
+ *   tensor. scale[m] holds the same value for every row, so the matmuls take these codes unchanged.
+ * Arguments as for bitlinear_quantize_act, plus d_workspace of at least
+ * bitlinear_quantize_per_tensor_workspace_bytes(M) bytes (16-byte aligned; contents on entry do not
+ * matter, the call overwrites it).
+ * ------------------------------------------------------------------------------------------- */
+size_t bitlinear_quantize_per_tensor_workspace_bytes(int64_t M);
+bl_status bitlinear_quantize_act_per_tensor(const void* d_x, int32_t in_dtype, int64_t M, int64_t K, int64_t ldx,
+                                            int32_t fmt, float eps, void* d_workspace, size_t ws_bytes,
+                                            void* d_codes, float* d_scale, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * bitlinear_pack_ternary: absmean ternary quantizer of a latent weight matrix (section 3.4,

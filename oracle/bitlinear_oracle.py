@@ -41,9 +41,14 @@ reason in the design notes):
      over the whole row (which survives whenever keep >= 1).
   R9 FFN: ReLU^2 acts on the gate projection, h = RN32(RN32(g+ * g+) * u) with
      g, u the fp32 dequantized projections; the down input is INT8 without Top-K.
+  R15 FP4 power-of-two scale variant: the dequant scale is 2^p with p the smallest integer such that
+     6 * 2^p >= max|x| (p >= -126); codes are the E2M1 rounding of x * 2^-p (exact scaling).
   R14 Conditional up projection: a channel's up output is computed only when its gate is
      positive in some row; entries with g <= 0 are +0 (the full form gives +0 * u, which is
      -0 when u < 0: equal as numbers).
+  R16 Per-tensor variant (per_tensor=True): beta or gamma is taken over all M*K entries of X at
+     once, in the same form as R5 (K replaced by M*K), and every row is quantized with it; the
+     per-row dscale then holds that one value in every row.
 """
 from __future__ import annotations
 
@@ -101,14 +106,18 @@ def ternarize(w, eps: float = 1e-5):
 
 
 # --------------------------------------------------------------------------- activations
-def quant_int4(x, eps: float = 1e-5):
+def quant_int4(x, eps: float = 1e-5, per_tensor: bool = False):
     """Per-token Q_INT4: codes = RoundClip(sqrt7/(beta+eps) * x, -8, 7), beta = mean|x|. [A4], Eq. 6-7
 
+    per_tensor: beta is the mean over the whole tensor (R16).
     Returns (codes int8 [M, K] in [-8, 7], dscale float32 [M] = beta / sqrt7, beta float32 [M]).
     """
     x = _rows_f32(x)
     M, K = x.shape
-    beta = np.array([F32(exact_abs_sum(x[m]) / K) for m in range(M)], dtype=np.float32)
+    if per_tensor:
+        beta = np.full(M, F32(exact_abs_sum(x.ravel()) / (M * K)), dtype=np.float32)
+    else:
+        beta = np.array([F32(exact_abs_sum(x[m]) / K) for m in range(M)], dtype=np.float32)
     den = (beta + F32(eps)).astype(np.float32)
     s = (SQRT7_F32 / den).astype(np.float32)
     v = (x * s[:, None]).astype(np.float32)
@@ -128,24 +137,43 @@ def e2m1_round(mag):
     return idx.astype(np.int64)
 
 
-def quant_fp4(x, eps: float = 1e-5):
-    """Per-token FP4 (E2M1) MinMax quantizer. [A4], Eq. 8-9, reading R6.
+def fp4_pow2_exponent(gamma):
+    """Reading R15 of the FP4 scale: the smallest integer p with 6 * 2^p >= gamma, at least -126
+    (gamma > 0). [A4], Eq. 8-9 read with a power-of-two dynamic scale."""
+    g = np.asarray(gamma, dtype=np.float64)
+    frac, e2 = np.frexp(g)                       # g = frac * 2^e2, frac in [0.5, 1)
+    e = e2 - 1                                   # g = (2 frac) * 2^e, 2 frac in [1, 2)
+    p = np.where(2.0 * frac <= 1.5, e - 2, e - 1)
+    return np.maximum(p, -126).astype(np.int64)
+
+
+def quant_fp4(x, eps: float = 1e-5, pow2: bool = False, per_tensor: bool = False):
+    """Per-token FP4 (E2M1) MinMax quantizer. [A4], Eq. 8-9, reading R6 (pow2: reading R15;
+    per_tensor: gamma over the whole tensor, R16).
 
     Returns (nibbles uint8 [M, K] = sign<<3 | magnitude index,
              doubled codes int8 [M, K] = 2 * E2M1 value in {0, +-1, +-2, +-3, +-4, +-6, +-8, +-12},
-             dscale float32 [M] = gamma / 6, gamma float32 [M]).
+             dscale float32 [M] = gamma / 6 (pow2: 2^p, 0 for a zero row), gamma float32 [M]).
     """
     x = _rows_f32(x)
     gamma = np.max(np.abs(x), axis=1).astype(np.float32)
-    den = (gamma + F32(eps)).astype(np.float32)
-    s = (F32(6.0) / den).astype(np.float32)
+    if per_tensor:
+        gamma = np.full(x.shape[0], np.max(np.abs(x)) if x.size else 0.0, dtype=np.float32)
+    if pow2:
+        p = fp4_pow2_exponent(gamma)
+        zero = gamma == 0
+        s = np.where(zero, 0.0, np.ldexp(1.0, -p)).astype(np.float32)
+        dscale_p = np.where(zero, 0.0, np.ldexp(1.0, p)).astype(np.float32)
+    else:
+        den = (gamma + F32(eps)).astype(np.float32)
+        s = (F32(6.0) / den).astype(np.float32)
     v = (x * s[:, None]).astype(np.float32)
     idx = e2m1_round(np.abs(v))
     neg = (v < 0) & (idx > 0)
     nibbles = (idx | (neg.astype(np.int64) << 3)).astype(np.uint8)
     doubled = (2.0 * E2M1_GRID[idx]).astype(np.int64)
     doubled = np.where(neg, -doubled, doubled).astype(np.int8)
-    dscale = (gamma / F32(6.0)).astype(np.float32)
+    dscale = dscale_p if pow2 else (gamma / F32(6.0)).astype(np.float32)
     return nibbles, doubled, dscale, gamma
 
 
@@ -163,16 +191,21 @@ def topk_mask(x, keep: int):
     return mask
 
 
-def quant_int8(x, eps: float = 1e-5, keep: int | None = None):
+def quant_int8(x, eps: float = 1e-5, keep: int | None = None, per_tensor: bool = False):
     """Q_INT8(X) (.) M per token: codes = RoundClip(127/(gamma+eps) * x, -128, 127), gamma = max|x|. [SP]
 
-    ``keep`` None (or K) means no Top-K mask. Returns (codes int8 [M, K], mask bool [M, K],
-    dscale float32 [M] = gamma / 127, gamma float32 [M]).
+    ``keep`` None (or K) means no Top-K mask; per_tensor: gamma over the whole tensor (R16, no
+    Top-K). Returns (codes int8 [M, K], mask bool [M, K], dscale float32 [M] = gamma / 127,
+    gamma float32 [M]).
     """
     x = _rows_f32(x)
     M, K = x.shape
+    if per_tensor and keep is not None and keep != K:
+        raise ValueError("the per-tensor variant has no Top-K mask")
     mask = np.ones((M, K), dtype=bool) if keep is None or keep == K else topk_mask(x, keep)
     gamma = np.max(np.abs(x), axis=1).astype(np.float32) if K else np.zeros(M, np.float32)
+    if per_tensor:
+        gamma = np.full(M, np.max(np.abs(x)) if x.size else 0.0, dtype=np.float32)
     den = (gamma + F32(eps)).astype(np.float32)
     s = (F32(127.0) / den).astype(np.float32)
     v = (x * s[:, None]).astype(np.float32)
@@ -271,8 +304,8 @@ def bitlinear_a4(x, w_codes, alpha, eps: float = 1e-5, fmt: str = "int4"):
         acc = gemm_int(codes, w_codes)
         y = dequant(acc, dscale, alpha)
         return dict(codes=codes, dscale=dscale, acc=acc, y=y)
-    if fmt == "fp4":
-        nib, doubled, dscale, _ = quant_fp4(x, eps)
+    if fmt in ("fp4", "fp4_pow2"):
+        nib, doubled, dscale, _ = quant_fp4(x, eps, pow2=fmt == "fp4_pow2")
         acc = gemm_int(doubled, w_codes)          # doubled codes: acc counts half units
         y = dequant(acc, dscale, alpha, acc_unit=0.5)
         return dict(nibbles=nib, codes=doubled, dscale=dscale, acc=acc, y=y)

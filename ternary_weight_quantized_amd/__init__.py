@@ -14,17 +14,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
 BL_OK = 0
-BL_ACT_INT4, BL_ACT_FP4_E2M1, BL_ACT_INT8, BL_ACT_INT4_E3M2 = 0, 1, 2, 3
+BL_ACT_INT4, BL_ACT_FP4_E2M1, BL_ACT_INT8, BL_ACT_INT4_E3M2, BL_ACT_FP4_E2M1_POW2 = 0, 1, 2, 3, 4
 BL_IN_BF16, BL_IN_F32 = 0, 1
 BL_EPI_NONE, BL_EPI_RESIDUAL, BL_EPI_RELU2_GLU = 0, 1, 2
 
-FORMATS = {"int4": BL_ACT_INT4, "fp4": BL_ACT_FP4_E2M1, "int8": BL_ACT_INT8, "int4_e3m2": BL_ACT_INT4_E3M2}
+FORMATS = {"int4": BL_ACT_INT4, "fp4": BL_ACT_FP4_E2M1, "int8": BL_ACT_INT8, "int4_e3m2": BL_ACT_INT4_E3M2,
+           "fp4_pow2": BL_ACT_FP4_E2M1_POW2}
 
 EXPORTED = (
     "bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_pack_ternary_rows", "bitlinear_packed_bytes",
     "bitlinear_pack_workspace_bytes", "bitlinear_gemm_w158a4", "bitlinear_gemm_w158a8_sparse",
     "bitlinear_gemv_decode", "bitlinear_gemv_decode_glu_conditional", "bitlinear_status_string",
-    "bitlinear_abi_version",
+    "bitlinear_abi_version", "bitlinear_quantize_act_per_tensor", "bitlinear_quantize_per_tensor_workspace_bytes",
 )
 
 
@@ -68,6 +69,10 @@ def _lib():
         lib.bitlinear_pack_workspace_bytes.restype = sz
         lib.bitlinear_pack_ternary.argtypes = [vp, i64, i64, f32, vp, vp, vp, sz, vp]
         lib.bitlinear_pack_ternary.restype = i32
+        lib.bitlinear_quantize_act_per_tensor.argtypes = [vp, i32, i64, i64, i64, i32, f32, vp, sz, vp, vp, vp]
+        lib.bitlinear_quantize_act_per_tensor.restype = i32
+        lib.bitlinear_quantize_per_tensor_workspace_bytes.argtypes = [i64]
+        lib.bitlinear_quantize_per_tensor_workspace_bytes.restype = sz
         lib.bitlinear_pack_ternary_rows.argtypes = [vp, i64, i64, f32, vp, vp, vp, sz, vp]
         lib.bitlinear_pack_ternary_rows.restype = i32
         lib.bitlinear_gemv_decode_glu_conditional.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, i64, vp, i64, vp,
@@ -137,6 +142,28 @@ def bitlinear_quantize_act(x, fmt, topk_keep=-1, eps=1e-5, row_absmax_hint=None,
                                        _ptr(row_absmax_hint), _ptr(codes), _ptr(scale), _ptr(mask), _stream(stream))
     _check(st, "bitlinear_quantize_act")
     return codes, scale, mask
+
+
+def bitlinear_quantize_per_tensor_workspace_bytes(M):
+    return int(_lib().bitlinear_quantize_per_tensor_workspace_bytes(M))
+
+
+def bitlinear_quantize_act_per_tensor(x, fmt, eps=1e-5, codes=None, scale=None, workspace=None, stream=None):
+    """Quantization of x [M, K] with one scale for the whole tensor. Returns (codes, scale f32 [M])."""
+    import torch
+    f = _fmt(fmt)
+    M, K = x.shape
+    in_dtype = {torch.bfloat16: BL_IN_BF16, torch.float32: BL_IN_F32}[x.dtype]
+    if codes is None:
+        codes = torch.empty(codes_shape(f, M, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(bitlinear_quantize_per_tensor_workspace_bytes(M), dtype=torch.uint8, device=x.device)
+    st = _lib().bitlinear_quantize_act_per_tensor(_ptr(x), in_dtype, M, K, x.stride(0), f, float(eps), _ptr(workspace),
+                                                  workspace.numel(), _ptr(codes), _ptr(scale), _stream(stream))
+    _check(st, "bitlinear_quantize_act_per_tensor")
+    return codes, scale
 
 
 def bitlinear_packed_bytes(N, K):

@@ -81,7 +81,8 @@ bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, i
                                  float* d_scale, uint32_t* d_mask, void* stream) {
   if (!d_x || !d_codes || !d_scale) return BL_ERR_INVALID_ARGUMENT;
   if (in_dtype != BL_IN_BF16 && in_dtype != BL_IN_F32) return BL_ERR_INVALID_ARGUMENT;
-  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8 && fmt != BL_ACT_INT4_E3M2)
+  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8 && fmt != BL_ACT_INT4_E3M2 &&
+      fmt != BL_ACT_FP4_E2M1_POW2)
     return BL_ERR_INVALID_ARGUMENT;
   if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1) return BL_ERR_UNSUPPORTED_SHAPE;
@@ -96,6 +97,32 @@ bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, i
   const float* hint = (fmt == BL_ACT_INT4 || fmt == BL_ACT_INT4_E3M2) ? nullptr : d_row_absmax_hint;
   return hip_status(bl_launch_quantize(d_x, in_dtype == BL_IN_F32, (int)M, (int)K, (long)ldx, fmt, (int)topk_keep,
                                        eps, hint, d_codes, d_scale, d_mask, static_cast<hipStream_t>(stream)));
+}
+
+size_t bitlinear_quantize_per_tensor_workspace_bytes(int64_t M) {
+  if (M <= 0) return 0;
+  return (size_t)(2064 + ((4 * M + 15) / 16) * 16);
+}
+
+bl_status bitlinear_quantize_act_per_tensor(const void* d_x, int32_t in_dtype, int64_t M, int64_t K, int64_t ldx,
+                                            int32_t fmt, float eps, void* d_workspace, size_t ws_bytes,
+                                            void* d_codes, float* d_scale, void* stream) {
+  if (!d_x || !d_codes || !d_scale || !d_workspace) return BL_ERR_INVALID_ARGUMENT;
+  if (in_dtype != BL_IN_BF16 && in_dtype != BL_IN_F32) return BL_ERR_INVALID_ARGUMENT;
+  if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8 && fmt != BL_ACT_INT4_E3M2 &&
+      fmt != BL_ACT_FP4_E2M1_POW2)
+    return BL_ERR_INVALID_ARGUMENT;
+  if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
+  if (M < 1 || K < 1) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (K % 256 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (M * K >= kMaxElems || M * ldx >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < K) return BL_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < bitlinear_quantize_per_tensor_workspace_bytes(M)) return BL_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t esz = in_dtype == BL_IN_F32 ? 4 : 2;
+  if (!aligned16(d_x) || !aligned16(d_codes) || !aligned16(d_workspace) || (ldx * esz) % 16 != 0)
+    return BL_ERR_MISALIGNED;
+  return hip_status(bl_launch_quantize_per_tensor(d_x, in_dtype == BL_IN_F32, (int)M, (int)K, (long)ldx, fmt, eps,
+                                                  d_workspace, d_codes, d_scale, static_cast<hipStream_t>(stream)));
 }
 
 bl_status bitlinear_pack_ternary(const float* d_w, int64_t N, int64_t K, float eps, void* d_packed, float* d_alpha,

@@ -8,6 +8,10 @@
 hipError_t bl_launch_quantize(const void* x, int in_f32, int M, int K, long ldx, int fmt, int keep, float eps,
                               const float* hint, void* codes, float* scale, uint32_t* mask, hipStream_t st);
 
+// per-tensor scale variant; ws: 256 uint64 bins, the max at byte 2048, M floats at byte 2064
+hipError_t bl_launch_quantize_per_tensor(const void* x, int in_f32, int M, int K, long ldx, int fmt, float eps,
+                                         void* ws, void* codes, float* scale, hipStream_t st);
+
 hipError_t bl_launch_pack(const float* w, int N, int K, float eps, void* packed, float* alpha,
                           void* ws, bool rows, hipStream_t st);
 

@@ -1,4 +1,5 @@
-// Per-token activation quantizers: INT4 absmean, FP4 E2M1 MinMax, INT8 absmax with Top-K mask.
+// Per-token activation quantizers: INT4 absmean, FP4 E2M1 (MinMax or power-of-two scale), INT8 absmax
+// with Top-K mask.
 //
 // "BitNet a4.8: 4-bit Activations for 1-bit LLMs" (architecture write-up), section 3.4:
 //   "4-Bit Activation Quantization for Gaussian-Like Inputs" (INT4 absmean, paper Eq. 6-7;
@@ -10,6 +11,8 @@
 // 256g + 4*lane .. +3), so each load and store of a wave is one contiguous segment.
 // Rows of up to 4096 elements stay in registers between the reduction and the quantization
 // ("resident" kernels); longer rows are read again from global memory ("streaming" kernels).
+#include <algorithm>
+
 #include "bl_common.h"
 #include "bl_kernels.h"
 
@@ -102,6 +105,25 @@ __device__ __forceinline__ void store_e3m2(uint8_t* __restrict__ codes, int m, i
   if (i < 3) *reinterpret_cast<uint32_t*>(codes + tile * 1536 + (m & 15) * 96 + 12 * (q & 7) + 4 * i) = w;
 }
 
+// FP4 scales from the row maximum gamma. MinMax (BL_ACT_FP4_E2M1): the maximum maps to 6,
+// s = RN32(6 / RN32(gamma + eps)), dequant gamma / 6. Power of two (BL_ACT_FP4_E2M1_POW2): the dequant
+// scale is 2^p with p the smallest integer such that 6 * 2^p >= gamma (p >= -126), s = 2^-p, so
+// x * s is exact; an all-zero row gets s = 0 and scale 0.
+template <bool POW2>
+__device__ __forceinline__ void fp4_scales(float gamma, float eps, float* s, float* dscale) {
+  if constexpr (!POW2) {
+    *s = 6.0f / (gamma + eps);
+    *dscale = gamma / 6.0f;
+  } else {
+    const uint32_t b = bl_f2u(gamma);
+    const int E = (int)(b >> 23);
+    int p = E == 0 ? -126 : ((b & 0x7FFFFFu) <= 0x400000u ? E - 129 : E - 128);   // e - 2 or e - 1
+    p = p < -126 ? -126 : p;
+    *s = gamma == 0.0f ? 0.0f : bl_u2f((uint32_t)(127 - p) << 23);
+    *dscale = gamma == 0.0f ? 0.0f : bl_u2f((uint32_t)(127 + p) << 23);
+  }
+}
+
 // Top-K threshold: the largest key T with count(|x| >= T) >= keep, found bit by bit.
 // bf16 inputs have 16 zero low bits in their float32 key, so their search stops at bit 16.
 // Ballot + popcount make each count a scalar: no cross-lane reduction is needed.
@@ -143,27 +165,32 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
     if (g < NG) load4<IN_F32>(x, base + 256 * g, v[g]);
 
   if constexpr (FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2) {
-    AbsSum acc;
-#pragma unroll
-    for (int g = 0; g < NGMAX; ++g)
-      if (g < NG) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc.add(v[g][j]);
-      }
-    double S = bl_wave_sum_d(acc.s);
-    const uint32_t emax = bl_wave_max_u(acc.emax), emin = bl_wave_min_u(acc.emin);
-    if (!sum_is_exact<IN_F32>(emax, emin, K)) {
-      unsigned long long* b = bins[wave];
-      bins_clear(b, lane);
+    float beta;
+    if (hint) {
+      beta = hint[row];                           // a given beta (per-tensor variant)
+    } else {
+      AbsSum acc;
 #pragma unroll
       for (int g = 0; g < NGMAX; ++g)
         if (g < NG) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) bins_add(b, v[g][j]);
+          for (int j = 0; j < 4; ++j) acc.add(v[g][j]);
         }
-      S = bins_finish(b, lane);
+      double S = bl_wave_sum_d(acc.s);
+      const uint32_t emax = bl_wave_max_u(acc.emax), emin = bl_wave_min_u(acc.emin);
+      if (!sum_is_exact<IN_F32>(emax, emin, K)) {
+        unsigned long long* b = bins[wave];
+        bins_clear(b, lane);
+#pragma unroll
+        for (int g = 0; g < NGMAX; ++g)
+          if (g < NG) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bins_add(b, v[g][j]);
+          }
+        S = bins_finish(b, lane);
+      }
+      beta = (float)(S / (double)K);
     }
-    const float beta = (float)(S / (double)K);
     const float s = bl_u2f(BL_SQRT7_BITS) / (beta + eps);
     if constexpr (FMT == BL_ACT_INT4) {
       uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
@@ -200,8 +227,9 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
         }
       gamma = bl_u2f(bl_wave_max_u(mx));
     }
-    if constexpr (FMT == BL_ACT_FP4_E2M1) {
-      const float s = 6.0f / (gamma + eps);
+    if constexpr (FMT == BL_ACT_FP4_E2M1 || FMT == BL_ACT_FP4_E2M1_POW2) {
+      float s, dscale;
+      fp4_scales<FMT == BL_ACT_FP4_E2M1_POW2>(gamma, eps, &s, &dscale);
       uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
 #pragma unroll
       for (int g = 0; g < NGMAX; ++g)
@@ -210,7 +238,7 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
                              (code_fp4(v[g][2], s) << 8) | (code_fp4(v[g][3], s) << 12);
           crow[64 * g] = (uint16_t)c;
         }
-      if (lane == 0) scale[row] = gamma / 6.0f;
+      if (lane == 0) scale[row] = dscale;
     } else {
       const float s = 127.0f / (gamma + eps);
       const bool all = keep < 0 || keep >= K;
@@ -479,27 +507,32 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
   const long base = (long)row * ldx + 4 * lane;
 
   if constexpr (FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2) {
-    AbsSum acc;
-    for (int g = 0; g < NG; ++g) {
-      float v[4];
-      load4<IN_F32>(x, base + 256 * g, v);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc.add(v[j]);
-    }
-    double S = bl_wave_sum_d(acc.s);
-    const uint32_t emax = bl_wave_max_u(acc.emax), emin = bl_wave_min_u(acc.emin);
-    if (!sum_is_exact<IN_F32>(emax, emin, K)) {
-      unsigned long long* b = bins[wave];
-      bins_clear(b, lane);
+    float beta;
+    if (hint) {
+      beta = hint[row];                           // a given beta (per-tensor variant)
+    } else {
+      AbsSum acc;
       for (int g = 0; g < NG; ++g) {
         float v[4];
         load4<IN_F32>(x, base + 256 * g, v);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bins_add(b, v[j]);
+        for (int j = 0; j < 4; ++j) acc.add(v[j]);
       }
-      S = bins_finish(b, lane);
+      double S = bl_wave_sum_d(acc.s);
+      const uint32_t emax = bl_wave_max_u(acc.emax), emin = bl_wave_min_u(acc.emin);
+      if (!sum_is_exact<IN_F32>(emax, emin, K)) {
+        unsigned long long* b = bins[wave];
+        bins_clear(b, lane);
+        for (int g = 0; g < NG; ++g) {
+          float v[4];
+          load4<IN_F32>(x, base + 256 * g, v);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bins_add(b, v[j]);
+        }
+        S = bins_finish(b, lane);
+      }
+      beta = (float)(S / (double)K);
     }
-    const float beta = (float)(S / (double)K);
     const float s = bl_u2f(BL_SQRT7_BITS) / (beta + eps);
     for (int g = 0; g < NG; ++g) {
       float v[4];
@@ -532,8 +565,9 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
       }
       gamma = bl_u2f(bl_wave_max_u(mx));
     }
-    if constexpr (FMT == BL_ACT_FP4_E2M1) {
-      const float s = 6.0f / (gamma + eps);
+    if constexpr (FMT == BL_ACT_FP4_E2M1 || FMT == BL_ACT_FP4_E2M1_POW2) {
+      float s, dscale;
+      fp4_scales<FMT == BL_ACT_FP4_E2M1_POW2>(gamma, eps, &s, &dscale);
       uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
       for (int g = 0; g < NG; ++g) {
         float v[4];
@@ -541,7 +575,7 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
         crow[64 * g] = (uint16_t)(code_fp4(v[0], s) | (code_fp4(v[1], s) << 4) |
                                    (code_fp4(v[2], s) << 8) | (code_fp4(v[3], s) << 12));
       }
-      if (lane == 0) scale[row] = gamma / 6.0f;
+      if (lane == 0) scale[row] = dscale;
     } else {
       const float s = 127.0f / (gamma + eps);
       const bool all = keep < 0 || keep >= K;
@@ -610,6 +644,63 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
   }
 }
 
+// ============================================================================ per-tensor scale
+// Variant of the activation quantizers with one scale for the whole [M, K] tensor (reading of the
+// pages' "all entries in X"): beta = RN32(RN64(exact sum |x|) / (M K)) or gamma = max |x| over the
+// tensor, then every row is quantized with it (passed to the row kernels as a per-row value).
+// The sum uses the same exact per-exponent integer bins as the weight alpha.
+template <int IN_F32, bool SUM>
+__global__ __launch_bounds__(256) void k_tensor_reduce(const void* __restrict__ x, int M, int K, long ldx,
+                                                       unsigned long long* __restrict__ gbins,
+                                                       uint32_t* __restrict__ gmax) {
+  __shared__ unsigned long long bins[SUM ? 256 : 1];
+  if constexpr (SUM) {
+    bins[threadIdx.x] = 0ull;
+    __syncthreads();
+  }
+  uint32_t mx = 0u;
+  const long quads = (long)M * (K >> 2);
+  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += (long)gridDim.x * blockDim.x) {
+    const long row = q / (K >> 2), col = 4 * (q % (K >> 2));
+    float v[4];
+    load4<IN_F32>(x, row * ldx + col, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t b = bl_f2u(v[j]) & 0x7FFFFFFFu;
+      if constexpr (SUM) {
+        uint32_t e, m;
+        bl_bin_split(b, &e, &m);
+        if (m) atomicAdd(&bins[e], (unsigned long long)m);
+      } else {
+        mx = b > mx ? b : mx;
+      }
+    }
+  }
+  if constexpr (SUM) {
+    __syncthreads();
+    const unsigned long long b = bins[threadIdx.x];
+    if (b) atomicAdd(&gbins[threadIdx.x], b);
+  } else {
+    mx = bl_wave_max_u(mx);
+    if ((threadIdx.x & 63) == 0) atomicMax(gmax, mx);
+  }
+}
+
+__global__ void k_tensor_clear(unsigned long long* bins, uint32_t* gmax) {
+  bins[threadIdx.x] = 0ull;
+  if (threadIdx.x == 0) *gmax = 0u;
+}
+
+// one value for every row: beta (SUM) or gamma
+template <bool SUM>
+__global__ void k_tensor_scale(const unsigned long long* __restrict__ bins, const uint32_t* __restrict__ gmax,
+                               int M, double count, float* __restrict__ rowval) {
+  __shared__ float val;
+  if (threadIdx.x == 0) val = SUM ? (float)(bl_bins_to_double(bins) / count) : bl_u2f(*gmax);
+  __syncthreads();
+  for (int m = threadIdx.x; m < M; m += blockDim.x) rowval[m] = val;
+}
+
 template <int FMT, int IN_F32>
 hipError_t launch_fmt(const void* x, int M, int K, long ldx, int keep, float eps, const float* hint,
                       uint8_t* codes, float* scale, uint32_t* mask, hipStream_t st) {
@@ -655,6 +746,32 @@ hipError_t bl_launch_quantize(const void* x, int in_f32, int M, int K, long ldx,
   if (fmt == BL_ACT_FP4_E2M1)
     return in_f32 ? launch_fmt<BL_ACT_FP4_E2M1, 1>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st)
                   : launch_fmt<BL_ACT_FP4_E2M1, 0>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st);
+  if (fmt == BL_ACT_FP4_E2M1_POW2)
+    return in_f32 ? launch_fmt<BL_ACT_FP4_E2M1_POW2, 1>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st)
+                  : launch_fmt<BL_ACT_FP4_E2M1_POW2, 0>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st);
   return in_f32 ? launch_fmt<BL_ACT_INT8, 1>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st)
                 : launch_fmt<BL_ACT_INT8, 0>(x, M, K, ldx, keep, eps, hint, c, scale, mask, st);
+}
+
+hipError_t bl_launch_quantize_per_tensor(const void* x, int in_f32, int M, int K, long ldx, int fmt, float eps,
+                                         void* ws, void* codes, float* scale, hipStream_t st) {
+  unsigned long long* bins = static_cast<unsigned long long*>(ws);
+  uint32_t* gmax = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + 2048);
+  float* rowval = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + 2064);
+  const bool sum = (fmt == BL_ACT_INT4 || fmt == BL_ACT_INT4_E3M2);
+  hipLaunchKernelGGL(k_tensor_clear, dim3(1), dim3(256), 0, st, bins, gmax);
+  const long quads = (long)M * (K >> 2);
+  const unsigned blocks = (unsigned)std::min<long>((quads + 255) / 256, 2048);
+  if (sum) {
+    if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, true>), dim3(blocks), dim3(256), 0, st, x, M, K, ldx, bins, gmax);
+    else hipLaunchKernelGGL((k_tensor_reduce<0, true>), dim3(blocks), dim3(256), 0, st, x, M, K, ldx, bins, gmax);
+    hipLaunchKernelGGL((k_tensor_scale<true>), dim3(1), dim3(256), 0, st, bins, gmax, M, (double)M * K, rowval);
+  } else {
+    if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, false>), dim3(blocks), dim3(256), 0, st, x, M, K, ldx, bins, gmax);
+    else hipLaunchKernelGGL((k_tensor_reduce<0, false>), dim3(blocks), dim3(256), 0, st, x, M, K, ldx, bins, gmax);
+    hipLaunchKernelGGL((k_tensor_scale<false>), dim3(1), dim3(256), 0, st, bins, gmax, M, (double)M * K, rowval);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return bl_launch_quantize(x, in_f32, M, K, ldx, fmt, -1, eps, rowval, codes, scale, nullptr, st);
 }

@@ -33,7 +33,7 @@ def test_header_declares_the_hot_path_calls():
     fns = header_functions()
     for f in ("bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_gemm_w158a4",
               "bitlinear_gemm_w158a8_sparse", "bitlinear_gemv_decode", "bitlinear_pack_ternary_rows",
-              "bitlinear_gemv_decode_glu_conditional"):
+              "bitlinear_gemv_decode_glu_conditional", "bitlinear_quantize_act_per_tensor"):
         assert f in fns
 
 
@@ -67,6 +67,7 @@ def _q(**kw):
     (dict(dt=7), 1), (dict(fmt=9), 1), (dict(eps=0.0), 1), (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1),
     (dict(M=0), 2), (dict(K=0), 2), (dict(K=100, ldx=100), 2), (dict(K=384, ldx=384), 2),
     (dict(ldx=128), 1), (dict(fmt=0, keep=3), 1), (dict(fmt=1, mask=P), 1), (dict(fmt=2, keep=257), 1),
+    (dict(fmt=4, keep=3), 1), (dict(fmt=4, mask=P), 1), (dict(fmt=5), 1),
     (dict(x=P_MIS), 3), (dict(codes=P_MIS), 3), (dict(ldx=260), 3), (dict(fmt=2, keep=5, mask=P_MIS), 3),
     (dict(M=1 << 20, K=4096, ldx=4096), 2),
 ])
@@ -127,6 +128,7 @@ def test_format_restrictions():
     assert _mm("bitlinear_gemv_decode", fmt=3) == 1
     assert _mm("bitlinear_gemv_decode", M=9) == 2            # decode is for at most 8 tokens
     assert _mm("bitlinear_gemm_w158a4", fmt=5) == 1
+    assert _mm("bitlinear_gemm_w158a4", fmt=4) == 1          # FP4 power-of-two codes run as fmt 1
 
 
 def test_packed_layout_decoder_roundtrip():
@@ -182,6 +184,22 @@ def test_glu_conditional_validation(kw, status):
                                                             a["up"], a["upa"], a["N"], a["gate"], a["ldg"], a["h"],
                                                             a["ldh"], a["rm"], None)
     assert st == status
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(scale=None), 1), (dict(ws=None), 1),
+    (dict(dt=7), 1), (dict(fmt=9), 1), (dict(eps=0.0), 1), (dict(M=0), 2), (dict(K=100, ldx=100), 2),
+    (dict(ldx=128), 1), (dict(wsb=100), 4), (dict(x=P_MIS), 3), (dict(ws=P_MIS), 3), (dict(ldx=260), 3),
+    (dict(M=1 << 20, K=4096, ldx=4096, wsb=1 << 24), 2),
+])
+def test_quantize_per_tensor_validation(kw, status):
+    a = dict(x=P, dt=0, M=4, K=256, ldx=256, fmt=0, eps=1e-5, ws=P, wsb=4096, codes=P, scale=P)
+    a.update(kw)
+    st = tw.library().bitlinear_quantize_act_per_tensor(a["x"], a["dt"], a["M"], a["K"], a["ldx"], a["fmt"], a["eps"],
+                                                        a["ws"], a["wsb"], a["codes"], a["scale"], None)
+    assert st == status
+    assert tw.bitlinear_quantize_per_tensor_workspace_bytes(4) >= 2064 + 16
 
 
 def test_packed_rows_decoder_roundtrip_and_positions():

@@ -114,6 +114,47 @@ def test_quantize_int4(M, K, f32, fmt):
 
 @pytest.mark.parametrize("f32", [False, True])
 @pytest.mark.parametrize("M,K", QSHAPES)
+def test_quantize_fp4_pow2(M, K, f32):
+    torch_cuda()
+    x = make_x(3500 + M + K, M, K, f32)
+    codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), "fp4_pow2", eps=EPS)
+    nib, _, d, _ = O.quant_fp4(x_f32(x), EPS, pow2=True)
+    np.testing.assert_array_equal(nibbles(host(codes)), nib)
+    np.testing.assert_array_equal(host(scale), d)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int4_e3m2", "fp4", "fp4_pow2", "int8"])
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("M,K", [(1, 256), (7, 768), (33, 4096), (130, 1024), (5, 8192)])
+def test_quantize_per_tensor(M, K, f32, fmt):
+    """One scale for the whole tensor: codes bit-exact, the scale repeated in every row."""
+    torch = torch_cuda()
+    x = make_x(4100 + M + K, M, K, f32)
+    ws = torch.full((tw.bitlinear_quantize_per_tensor_workspace_bytes(M),), 0xAB, dtype=torch.uint8, device="cuda")
+    codes, scale = tw.bitlinear_quantize_act_per_tensor(to_dev(x), fmt, eps=EPS, workspace=ws)
+    xf = x_f32(x)
+    if fmt in ("int4", "int4_e3m2"):
+        c, d, _ = O.quant_int4(xf, EPS, per_tensor=True)
+        got = int4_values(host(codes)) if fmt == "int4" else e3m2_values(host(codes), M)
+        np.testing.assert_array_equal(got, c)
+    elif fmt == "int8":
+        c, _, d, _ = O.quant_int8(xf, EPS, per_tensor=True)
+        np.testing.assert_array_equal(int8_values(host(codes)), c)
+    else:
+        nib, _, d, _ = O.quant_fp4(xf, EPS, pow2=fmt == "fp4_pow2", per_tensor=True)
+        np.testing.assert_array_equal(nibbles(host(codes)), nib)
+    np.testing.assert_array_equal(host(scale), d)
+    # a second call over the same (dirty) workspace gives the same result
+    codes2, scale2 = tw.bitlinear_quantize_act_per_tensor(to_dev(x), fmt, eps=EPS, workspace=ws)
+    if fmt == "int4_e3m2":      # tile rows past M are padding the quantizer does not write
+        np.testing.assert_array_equal(e3m2_values(host(codes2), M), e3m2_values(host(codes), M))
+    else:
+        np.testing.assert_array_equal(host(codes2), host(codes))
+    np.testing.assert_array_equal(host(scale2), host(scale))
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("M,K", QSHAPES)
 def test_quantize_fp4(M, K, f32):
     torch = torch_cuda()
     x = make_x(2000 + M + K, M, K, f32)
@@ -303,6 +344,18 @@ def test_decode_epilogues(fmt):
     h_ref = O.relu2_glu(O.dequant_f32(acc, d, alpha), O.dequant_f32(O.gemm_int(c, tu), d, au))
     np.testing.assert_array_equal(host(h).view(np.uint32), h_ref.view(np.uint32))
     np.testing.assert_array_equal(host(rowmax), np.abs(h_ref).max(axis=1))
+
+
+def test_gemm_fp4_pow2_codes():
+    """FP4 codes of the power-of-two scale variant run through the FP4 GEMM unchanged."""
+    torch_cuda()
+    M, N, K = 70, 160, 768
+    x = make_x(6950, M, K, special=False)
+    _, t, alpha, packed, a = packed_weights(6960, N, K)
+    codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), "fp4_pow2", eps=EPS)
+    y = tw.bitlinear_gemm_w158a4("fp4", codes, scale, K, packed, a, N)
+    r = O.bitlinear_a4(x_f32(x), t, alpha, EPS, fmt="fp4_pow2")
+    assert_y_close(host(y), r["acc"], r["dscale"], alpha, 0.5)
 
 
 def test_gemm_formats_agree():

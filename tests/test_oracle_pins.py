@@ -158,6 +158,69 @@ def test_fp4_row_max_maps_to_six():
 
 
 # ----------------------------------------------------------------------------- Top-K + INT8
+def test_fp4_pow2_exponent_bruteforce():
+    """p is the smallest integer with 6 * 2^p >= gamma (exact rationals), clamped at -126."""
+    rng = np.random.default_rng(9)
+    gam = np.concatenate([np.float32([1.5, 1.5000001, 3.0, 6.0, 6.0000005, 12.0, 0.75, 1e-38, 2.0 ** -140]),
+                          (rng.standard_normal(300) * np.exp2(rng.integers(-60, 60, 300))).astype(np.float32)])
+    gam = np.abs(gam).astype(np.float32)
+    p = O.fp4_pow2_exponent(gam)
+    for g, q in zip(gam.tolist(), p.tolist()):
+        fg = Fraction(g)
+        if q > -126:
+            assert 6 * Fraction(2) ** q >= fg > 6 * Fraction(2) ** (q - 1)
+        else:
+            assert 6 * Fraction(2) ** -126 >= fg
+
+
+def test_fp4_pow2_codes_are_exact_scalings():
+    x = bf16_bits_to_f32(activations_bf16(31, 6, 256))
+    x[2] = 0.0
+    nib, doubled, d, g = O.quant_fp4(x, pow2=True)
+    assert d[2] == 0 and np.all(doubled[2] == 0)
+    for r in (0, 1, 3, 4, 5):
+        p = O.fp4_pow2_exponent(g[r:r + 1])[0]
+        assert d[r] == np.float32(2.0 ** p)
+        v = x[r].astype(np.float64) * 2.0 ** -p          # exact in float64
+        assert np.abs(v).max() <= 6.0 and np.abs(v).max() > 3.0
+        idx = O.e2m1_round(np.abs(v))
+        np.testing.assert_array_equal(np.abs(doubled[r]), 2 * O.E2M1_GRID[idx])
+
+
+def test_per_tensor_hand_example():
+    """One scale for the tensor [[1, -1], [3, -3]]: beta = 2, gamma = 3 (hand-computed codes)."""
+    x = np.float32([[1, -1], [3, -3]])
+    c, d, b = O.quant_int4(x, eps=1e-5, per_tensor=True)
+    assert np.all(b == np.float32(2.0))
+    np.testing.assert_array_equal(c, [[1, -1], [4, -4]])        # round(x * sqrt7 / 2)
+    c8, _, d8, g8 = O.quant_int8(x, eps=1e-5, per_tensor=True)
+    assert np.all(g8 == 3)
+    np.testing.assert_array_equal(c8, [[42, -42], [127, -127]])  # round(x * 127 / 3)
+    _, doubled, _, g4 = O.quant_fp4(x, eps=1e-5, per_tensor=True)
+    np.testing.assert_array_equal(doubled, [[4, -4], [12, -12]])  # x * 2 -> E2M1 2 and 6
+    _, doubled2, dp, _ = O.quant_fp4(x, per_tensor=True, pow2=True)
+    assert np.all(dp == 0.5)                                     # 6 * 2^-1 = 3 >= 3 > 1.5
+    np.testing.assert_array_equal(doubled2, [[4, -4], [12, -12]])
+    # per token the same rows give other codes
+    assert not np.array_equal(O.quant_int4(x, eps=1e-5)[0], c)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "fp4_pow2", "int8"])
+def test_per_tensor_is_per_token_of_one_long_row(fmt):
+    """per-tensor(X) == per-token(X.reshape(1, M*K)) with the scale repeated on every row."""
+    x = bf16_bits_to_f32(activations_bf16(77, 5, 512))
+    flat = x.reshape(1, -1)
+    if fmt == "int4":
+        (c, d, _), (cf, df, _) = O.quant_int4(x, per_tensor=True), O.quant_int4(flat)
+    elif fmt == "int8":
+        (c, _, d, _), (cf, _, df, _) = O.quant_int8(x, per_tensor=True), O.quant_int8(flat)
+    else:
+        pw = fmt == "fp4_pow2"
+        (_, c, d, _), (_, cf, df, _) = O.quant_fp4(x, per_tensor=True, pow2=pw), O.quant_fp4(flat, pow2=pw)
+    np.testing.assert_array_equal(c.reshape(1, -1), cf)
+    np.testing.assert_array_equal(d, np.full(5, df[0], np.float32))
+
+
 @pytest.mark.parametrize("case", read_cases("int8_hand.txt"))
 def test_int8_hand_cases(case):
     eps, keep, x, codes, dscale = case
