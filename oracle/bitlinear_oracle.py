@@ -13,6 +13,8 @@ Technical Breakdown", subsections
   [SP]  "Sparsification Pipeline for Outlier-Heavy Intermediate States"
         -- Y = (Q_INT8(X) . M) Q_w(W)^T, M = Top_k(|X|) (paper Eq. 1), Q_INT8 and gamma
   [GLU] "Squared ReLU Gating and Conditional Computation in the FFN" -- ReLU^2 GLU (paper Eq. 5)
+  [KV]  "Low-Bit KV Cache Quantization" -- post-RoPE absmax quantization of Q, K, V heads to
+        unsigned integers, 4-bit and 3-bit, BOS-token heads kept at 4 bits (paper Table 3)
 and section 3.2 "Big-Picture Architecture" for which projection gets which
 quantizer and where the residual add sits.
 
@@ -46,6 +48,11 @@ reason in the design notes):
   R14 Conditional up projection: a channel's up output is computed only when its gate is
      positive in some row; entries with g <= 0 are +0 (the full form gives +0 * u, which is
      -0 when u < 0: equal as numbers).
+  R17 KV cache: absmax per (token, head) over the head's D values, symmetric, Qp = 2^(b-1) - 1
+     (7 for 4 bits, 3 for 3 bits): c = RoundClip(RN32(x * RN32(Qp / RN32(gamma + eps))), -Qp-1, Qp),
+     stored unsigned as u = c + 2^(b-1); dequant scale RN32(gamma / Qp). RoPE is the rotate-half
+     form on (x_i, x_{i+D/2}) with caller cos/sin tables, each product and sum rounded to fp32.
+     BOS tokens (marked by the caller) get a 4-bit record beside the 3-bit one.
   R16 Per-tensor variant (per_tensor=True): beta or gamma is taken over all M*K entries of X at
      once, in the same form as R5 (K replaced by M*K), and every row is quantized with it; the
      per-row dscale then holds that one value in every row.
@@ -341,3 +348,61 @@ def ffn_ref(x, wg_codes, alpha_g, wu_codes, alpha_u, wd_codes, alpha_d, eps: flo
 def oproj_ref(x, w_codes, alpha, residual, keep: int, eps: float = 1e-5):
     """Attention output projection: Top-K + INT8, o_proj, residual add. [SP], section 3.2"""
     return bitlinear_a8(x, w_codes, alpha, eps, keep=keep, residual=residual)
+
+
+# --------------------------------------------------------------------------- KV cache
+def rope_rotate_half(x, pos, cos, sin):
+    """Rotary position embedding on [T, H, D] heads, rotate-half pairing (i, i + D/2), i < D/2:
+    out_i = RN32(RN32(x_i c) - RN32(x_j s)), out_j = RN32(RN32(x_j c) + RN32(x_i s)), j = i + D/2,
+    c = cos[pos[t], i], s = sin[pos[t], i] from caller tables [P, D/2]. [KV] (applied before the
+    quantizer, "post-RoPE"; R17)"""
+    x = np.asarray(x, dtype=np.float32)
+    T, H, D = x.shape
+    h = D // 2
+    c = np.asarray(cos, dtype=np.float32)[np.asarray(pos)][:, None, :]     # [T, 1, D/2]
+    s = np.asarray(sin, dtype=np.float32)[np.asarray(pos)][:, None, :]
+    a, b = x[..., :h], x[..., h:]
+    out = np.empty_like(x)
+    out[..., :h] = ((a * c).astype(np.float32) - (b * s).astype(np.float32)).astype(np.float32)
+    out[..., h:] = ((b * c).astype(np.float32) + (a * s).astype(np.float32)).astype(np.float32)
+    return out
+
+
+def kv_quant(x, bits: int, eps: float = 1e-5):
+    """Absmax quantization of each (token, head) of x [T, H, D] to ``bits``-bit unsigned codes. [KV], R17
+
+    Returns (u uint8 [T, H, D] in [0, 2^bits - 1], dscale float32 [T, H] = gamma / Qp,
+    gamma float32 [T, H]); the value of a code is (u - 2^(bits-1)) * dscale.
+    """
+    if bits not in (3, 4):
+        raise ValueError("bits must be 3 or 4")
+    x = np.asarray(x, dtype=np.float32)
+    qp = F32(2 ** (bits - 1) - 1)
+    gamma = np.max(np.abs(x), axis=2).astype(np.float32)
+    den = (gamma + F32(eps)).astype(np.float32)
+    s = (qp / den).astype(np.float32)
+    v = (x * s[..., None]).astype(np.float32)
+    c = roundclip(v, -int(qp) - 1, int(qp)).astype(np.int16)
+    u = (c + 2 ** (bits - 1)).astype(np.uint8)
+    dscale = (gamma / qp).astype(np.float32)
+    return u, dscale, gamma
+
+
+def kv_cache_quant(x, bits: int, eps: float = 1e-5, pos=None, cos=None, sin=None, bos=None):
+    """KV-cache write of T tokens: optional RoPE, then ``bits``-bit absmax codes per (token, head);
+    with bits == 3, tokens flagged in ``bos`` (bool [T]) also get 4-bit codes. [KV], R17
+
+    Returns dict(u, dscale, bos_u, bos_dscale) with bos_* = None unless bits == 3 and bos is given
+    (rows of non-BOS tokens there are undefined: filled with 0).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if cos is not None:
+        x = rope_rotate_half(x, pos, cos, sin)
+    u, d, _ = kv_quant(x, bits, eps)
+    out = dict(u=u, dscale=d, bos_u=None, bos_dscale=None)
+    if bits == 3 and bos is not None:
+        bos = np.asarray(bos, dtype=bool)
+        u4, d4, _ = kv_quant(x, 4, eps)
+        out["bos_u"] = np.where(bos[:, None, None], u4, 0).astype(np.uint8)
+        out["bos_dscale"] = np.where(bos[:, None], d4, 0).astype(np.float32)
+    return out

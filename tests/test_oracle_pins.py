@@ -389,3 +389,73 @@ def test_generators_are_deterministic_and_gaussian():
     bits = activations_bf16(3, 2, 16)
     f = bf16_bits_to_f32(bits)
     assert np.all((f.view(np.uint32) & 0xFFFF) == 0)
+
+
+# ----------------------------------------------------------------------------- KV cache (R17)
+def test_kv_quant_hand_example():
+    """gamma = 3: 3 bits scale by 3/(3+eps), 4 bits by 7/(3+eps); offsets 4 and 8 (hand-computed)."""
+    x = np.float32([[[1, -1, 0.5, -3]]])
+    u3, d3, g = O.kv_quant(x, 3)
+    np.testing.assert_array_equal(u3[0, 0], [5, 3, 4, 1])      # c = 1, -1, 0 (0.49999 rounds down), -3
+    assert d3[0, 0] == np.float32(1.0) and g[0, 0] == 3
+    u4, d4, _ = O.kv_quant(x, 4)
+    np.testing.assert_array_equal(u4[0, 0], [10, 6, 9, 1])     # c = 2, -2, 1, -7
+    assert d4[0, 0] == np.float32(3.0) / np.float32(7.0)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_kv_quant_range_and_error_bound(bits):
+    """Codes lie in [1, 2^b - 1], the head max maps to an end code, and the dequantized value is
+    within (gamma + eps) / (2 Qp) + eps of x (round-to-nearest on the absmax grid)."""
+    rng = np.random.default_rng(bits)
+    x = (rng.standard_normal((9, 4, 64)) * np.exp2(rng.integers(-8, 8, (9, 4, 1)))).astype(np.float32)
+    x[3, 2] = 0.0
+    eps = 1e-5
+    u, d, g = O.kv_quant(x, bits, eps)
+    off, qp = 2 ** (bits - 1), 2 ** (bits - 1) - 1
+    assert u.min() >= 1 and u.max() <= 2 ** bits - 1
+    assert np.all(u[3, 2] == off) and d[3, 2] == 0
+    am = np.abs(x).argmax(axis=2)
+    top = np.take_along_axis(u, am[..., None], axis=2)[..., 0].astype(int)
+    assert np.all((top == 2 * qp + 1) | (top == 1) | (g == 0))
+    deq = (u.astype(np.float64) - off) * g[..., None].astype(np.float64) / qp
+    bound = (g[..., None].astype(np.float64) + eps) / (2 * qp) * (1 + 1e-6) + eps
+    assert np.all(np.abs(deq - x) <= bound)
+    # a wrong level count (2^b - 1 in place of Qp) breaks the bound somewhere
+    wrong = (u.astype(np.float64) - off) * g[..., None] / (2 ** bits - 1)
+    assert np.any(np.abs(wrong - x) > bound)
+
+
+def test_rope_special_angles_and_complex_product():
+    rng = np.random.default_rng(5)
+    T, H, D = 6, 3, 16
+    x = rng.standard_normal((T, H, D)).astype(np.float32)
+    pos = np.array([0, 1, 2, 3, 0, 2])
+    ang = rng.uniform(-3, 3, (4, D // 2))
+    cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    cos[0], sin[0] = 1, 0                     # position 0: identity
+    cos[1], sin[1] = 0, 1                     # position 1: quarter turn, (a, b) -> (-b, a)
+    r = O.rope_rotate_half(x, pos, cos, sin)
+    np.testing.assert_array_equal(r[0], x[0])
+    np.testing.assert_array_equal(r[4], x[4])
+    np.testing.assert_array_equal(r[1], np.concatenate([-x[1, :, D // 2:], x[1, :, :D // 2]], axis=1))
+    # the pair turns as the complex product (a + ib)(c + is), to a few fp32 ulps
+    z = (x[..., :D // 2].astype(np.float64) + 1j * x[..., D // 2:]) * \
+        (cos[pos][:, None].astype(np.float64) + 1j * sin[pos][:, None])
+    ref = np.concatenate([z.real, z.imag], axis=2)
+    scale = np.abs(x[..., :D // 2]).astype(np.float64) + np.abs(x[..., D // 2:])
+    assert np.all(np.abs(r - ref) <= 4 * 2.0 ** -24 * np.concatenate([scale, scale], axis=2))
+    # swapping the halves' roles (a wrong pairing) is caught
+    assert not np.allclose(r[2:4], O.rope_rotate_half(x[2:4, :, ::-1].copy(), pos[2:4], cos, sin)[:, :, ::-1])
+
+
+def test_kv_cache_quant_bos_records():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((5, 2, 32)).astype(np.float32)
+    bos = np.array([True, False, False, True, False])
+    out = O.kv_cache_quant(x, 3, bos=bos)
+    u4, d4, _ = O.kv_quant(x, 4)
+    np.testing.assert_array_equal(out["bos_u"][bos], u4[bos])
+    np.testing.assert_array_equal(out["bos_dscale"][bos], d4[bos])
+    np.testing.assert_array_equal(out["u"], O.kv_quant(x, 3)[0])
+    assert O.kv_cache_quant(x, 4, bos=bos)["bos_u"] is None
