@@ -246,6 +246,45 @@ bl_status bitlinear_gemv_decode_glu_conditional(const void* d_codes, const float
                                                 float* d_gate, int64_t ldg, float* d_h, int64_t ldh,
                                                 float* d_row_absmax, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_kv_quantize: the low-bit KV cache of section 3.4, "Low-Bit KV Cache Quantization"
+ * (and the low-bit attention results of Table 3): after rotary position embedding, each
+ * (token, head) of Q, K or V is quantized with absmax to unsigned integers, 4 or 3 bits; in a
+ * 3-bit cache the heads of beginning-of-sequence (BOS) tokens are also kept at 4 bits.
+ *   optional RoPE (d_cos != NULL), rotate-half pairing of element i with i + D/2 (i < D/2):
+ *     a' = RN32(RN32(a c) - RN32(b s)),  b' = RN32(RN32(b c) + RN32(a s)),
+ *     c = cos[pos[t]][i], s = sin[pos[t]][i]  (caller tables, so any RoPE base or scaling works);
+ *   per (t, h): gamma = max_i |x'|, Qp = 2^(bits-1) - 1, s = RN32(Qp / RN32(gamma + eps)),
+ *     c_i = RoundClip(RN32(x'_i s), -Qp-1, Qp), stored u_i = c_i + 2^(bits-1) (1 .. 2^bits - 1),
+ *     scale[t][h] = RN32(gamma / Qp); the value of a code is (u - 2^(bits-1)) * scale.
+ * Arguments:
+ *   d_x        [T rows] of H heads x D values (head h at elements [h D, (h+1) D) of a row), bf16
+ *              or float32 (in_dtype), row stride ldx >= H D elements; 16-byte aligned, ldx * elem
+ *              size a multiple of 16. Typically the K or V columns of the QKV projection output.
+ *   D          head size: 64, 128 or 256.  T >= 0, H >= 1; with T == 0 only bits, dtype, H, D
+ *              and eps are checked (pointers may be NULL) and nothing is enqueued.
+ *   d_pos      [T] int32 positions (required with d_cos); d_cos, d_sin [P][D/2] float32, both or
+ *              neither, 16-byte aligned. A position outside [0, P) is out of contract; the kernel
+ *              clamps it into that range so it never reads outside the tables.
+ *   bits       3 or 4.  eps as for the activation quantizers.
+ *   d_codes    out, [T][H][D bits / 8] bytes, 16-byte aligned. 4 bits: code 2j of a head in the
+ *              low nibble of its byte j. 3 bits: codes 8g .. 8g+7 in the 24 bits of bytes
+ *              3g .. 3g+2 (little-endian), code 8g + q at bits [3q, 3q+3).
+ *   d_scale    out, [T][H] float32.
+ *   d_bos_slot optional [T] int32 (bits == 3 only): slot >= 0 marks token t as a BOS token whose
+ *              4-bit record (the 4-bit layout above) goes to d_bos_codes[slot] ([n_bos_slots][H]
+ *              [D/2] bytes, 16-byte aligned) with scales in d_bos_scale[slot][H]; slots outside
+ *              [0, n_bos_slots) are skipped. The 3-bit record of a BOS token is written as well.
+ * Errors: NULL required pointers, bad dtype or bits, cos without sin or pos, BOS arguments with
+ * bits == 4 -> INVALID_ARGUMENT; unsupported D or sizes -> UNSUPPORTED_SHAPE; alignment ->
+ * MISALIGNED.
+ * ------------------------------------------------------------------------------------------- */
+bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, int64_t H, int64_t D, int64_t ldx,
+                                const int32_t* d_pos, const float* d_cos, const float* d_sin, int64_t P,
+                                int32_t bits, float eps, void* d_codes, float* d_scale,
+                                const int32_t* d_bos_slot, int64_t n_bos_slots, void* d_bos_codes,
+                                float* d_bos_scale, void* stream);
+
 const char* bitlinear_status_string(int32_t status);
 int32_t bitlinear_abi_version(void);
 

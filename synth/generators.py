@@ -99,8 +99,18 @@ WORKLOADS = {
     "prefill_qkv":   dict(M=4096, K=4096, N=3 * 4096, outlier_scale=20.0),
     "ffn_7b":        dict(M=2048, K=4096, N=11008),
     "attn_out":      dict(M=8192, K=4096, N=4096, keep=2048, outlier_scale=20.0),
+    # Q, K and V heads of the prefill projection output (fp32 [T, 3 H D]), 4 sequences of 1024 tokens
+    "kv_cache":      dict(T=4096, H=32, D=128, seq_len=1024),
 }
 _WL_INDEX = {name: i + 1 for i, name in enumerate(WORKLOADS)}
+
+
+def rope_tables(P: int, D: int, base: float = 10000.0):
+    """cos and sin float32 [P, D/2] of the angles p * base^(-2i/D) (computed in float64)."""
+    p = np.arange(P, dtype=np.float64)[:, None]
+    inv = base ** (-2.0 * np.arange(D // 2, dtype=np.float64) / D)
+    ang = p * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
 def workload_inputs(name: str, M: int | None = None):
@@ -112,6 +122,12 @@ def workload_inputs(name: str, M: int | None = None):
     """
     wl = WORKLOADS[name]
     base = 1000 * _WL_INDEX[name]
+    if name == "kv_cache":
+        T = M if M is not None else wl["T"]
+        W = 3 * wl["H"] * wl["D"]
+        pos = (np.arange(T) % wl["seq_len"]).astype(np.int32)
+        cos, sin = rope_tables(wl["seq_len"], wl["D"])
+        return dict(qkv=normal(base + 1, T * W).astype(np.float32).reshape(T, W), pos=pos, cos=cos, sin=sin)
     K, N = wl["K"], wl["N"]
     if name == "decode_a4":
         Mx = M if M is not None else max(wl["Ms"])

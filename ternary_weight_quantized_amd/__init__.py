@@ -26,6 +26,7 @@ EXPORTED = (
     "bitlinear_pack_workspace_bytes", "bitlinear_gemm_w158a4", "bitlinear_gemm_w158a8_sparse",
     "bitlinear_gemv_decode", "bitlinear_gemv_decode_glu_conditional", "bitlinear_status_string",
     "bitlinear_abi_version", "bitlinear_quantize_act_per_tensor", "bitlinear_quantize_per_tensor_workspace_bytes",
+    "bitlinear_kv_quantize",
 )
 
 
@@ -69,6 +70,9 @@ def _lib():
         lib.bitlinear_pack_workspace_bytes.restype = sz
         lib.bitlinear_pack_ternary.argtypes = [vp, i64, i64, f32, vp, vp, vp, sz, vp]
         lib.bitlinear_pack_ternary.restype = i32
+        lib.bitlinear_kv_quantize.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, i64, i32, f32, vp, vp, vp, i64,
+                                              vp, vp, vp]
+        lib.bitlinear_kv_quantize.restype = i32
         lib.bitlinear_quantize_act_per_tensor.argtypes = [vp, i32, i64, i64, i64, i32, f32, vp, sz, vp, vp, vp]
         lib.bitlinear_quantize_act_per_tensor.restype = i32
         lib.bitlinear_quantize_per_tensor_workspace_bytes.argtypes = [i64]
@@ -164,6 +168,36 @@ def bitlinear_quantize_act_per_tensor(x, fmt, eps=1e-5, codes=None, scale=None, 
                                                   workspace.numel(), _ptr(codes), _ptr(scale), _stream(stream))
     _check(st, "bitlinear_quantize_act_per_tensor")
     return codes, scale
+
+
+def kv_record_bytes(D, bits):
+    return D * bits // 8
+
+
+def bitlinear_kv_quantize(x, H, D, bits, eps=1e-5, pos=None, cos=None, sin=None, bos_slot=None, n_bos_slots=0,
+                          codes=None, scale=None, bos_codes=None, bos_scale=None, stream=None):
+    """Post-RoPE absmax KV-cache quantization of x [T, >= H*D] (bf16 or float32 rows).
+
+    Returns (codes uint8 [T, H * D * bits / 8], scale f32 [T, H], bos_codes, bos_scale); the BOS
+    buffers ([n_bos_slots, H * D / 2] and [n_bos_slots, H]) only when bos_slot is given."""
+    import torch
+    T = x.shape[0]
+    in_dtype = {torch.bfloat16: BL_IN_BF16, torch.float32: BL_IN_F32}[x.dtype]
+    if codes is None:
+        codes = torch.empty((T, H * kv_record_bytes(D, bits)), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if bos_slot is not None:
+        if bos_codes is None:
+            bos_codes = torch.zeros((n_bos_slots, H * D // 2), dtype=torch.uint8, device=x.device)
+        if bos_scale is None:
+            bos_scale = torch.zeros((n_bos_slots, H), dtype=torch.float32, device=x.device)
+    P = cos.shape[0] if cos is not None else 0
+    st = _lib().bitlinear_kv_quantize(_ptr(x), in_dtype, T, H, D, x.stride(0), _ptr(pos), _ptr(cos), _ptr(sin), P,
+                                      bits, float(eps), _ptr(codes), _ptr(scale), _ptr(bos_slot), n_bos_slots,
+                                      _ptr(bos_codes), _ptr(bos_scale), _stream(stream))
+    _check(st, "bitlinear_kv_quantize")
+    return codes, scale, bos_codes, bos_scale
 
 
 def bitlinear_packed_bytes(N, K):

@@ -212,4 +212,34 @@ bl_status bitlinear_gemv_decode_glu_conditional(const void* d_codes, const float
   return hip_status(bl_launch_glu_conditional_fused(u, d_gate_packed, d_gate_alpha, st));
 }
 
+bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, int64_t H, int64_t D, int64_t ldx,
+                                const int32_t* d_pos, const float* d_cos, const float* d_sin, int64_t P,
+                                int32_t bits, float eps, void* d_codes, float* d_scale,
+                                const int32_t* d_bos_slot, int64_t n_bos_slots, void* d_bos_codes,
+                                float* d_bos_scale, void* stream) {
+  if (in_dtype != BL_IN_BF16 && in_dtype != BL_IN_F32) return BL_ERR_INVALID_ARGUMENT;
+  if (bits != 3 && bits != 4) return BL_ERR_INVALID_ARGUMENT;
+  if (T == 0 && H >= 1 && (D == 64 || D == 128 || D == 256) && eps_ok(eps)) return BL_OK;   // nothing to do
+  if (!d_x || !d_codes || !d_scale) return BL_ERR_INVALID_ARGUMENT;
+  if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
+  if ((d_cos == nullptr) != (d_sin == nullptr)) return BL_ERR_INVALID_ARGUMENT;
+  if (d_cos && (!d_pos || P < 1)) return BL_ERR_INVALID_ARGUMENT;
+  if (d_bos_slot && (bits != 3 || !d_bos_codes || !d_bos_scale || n_bos_slots < 1)) return BL_ERR_INVALID_ARGUMENT;
+  if (T < 0 || H < 1) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (D != 64 && D != 128 && D != 256) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < H * D) return BL_ERR_INVALID_ARGUMENT;
+  if (T * ldx >= kMaxElems || T * H * D >= kMaxElems || P * D >= kMaxElems || n_bos_slots * H * D >= kMaxElems)
+    return BL_ERR_UNSUPPORTED_SHAPE;
+  const int64_t esz = in_dtype == BL_IN_F32 ? 4 : 2;
+  if (!aligned16(d_x) || (ldx * esz) % 16 != 0 || !aligned16(d_codes)) return BL_ERR_MISALIGNED;
+  if (d_cos && (!aligned16(d_cos) || !aligned16(d_sin))) return BL_ERR_MISALIGNED;
+  if (d_bos_slot && !aligned16(d_bos_codes)) return BL_ERR_MISALIGNED;
+  bl_kv_args a{};
+  a.x = d_x; a.in_f32 = in_dtype == BL_IN_F32; a.T = (int)T; a.H = (int)H; a.D = (int)D; a.ldx = (long)ldx;
+  a.pos = d_pos; a.cos = d_cos; a.sin = d_sin; a.P = (int)P; a.bits = bits; a.eps = eps;
+  a.codes = d_codes; a.scale = d_scale;
+  a.bos_slot = d_bos_slot; a.nslots = (int)n_bos_slots; a.bos_codes = d_bos_codes; a.bos_scale = d_bos_scale;
+  return hip_status(bl_launch_kv_quant(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -54,3 +54,24 @@ struct bl_upcond_args {
 // gate GEMV and conditional up projection in one launch (one block per 16 channels)
 hipError_t bl_launch_glu_conditional_fused(const bl_upcond_args& a, const void* Wg, const float* galpha,
                                           hipStream_t st);
+
+// KV-cache quantizer (post-RoPE absmax, 4 or 3 bits, BOS records at 4 bits)
+struct bl_kv_args {
+  const void* x;          // [T rows of H heads x D], row stride ldx elements
+  int in_f32;
+  int T, H, D;
+  long ldx;
+  const int* pos;         // [T] (with cos/sin)
+  const float* cos;       // [P, D/2] or null (no rotation)
+  const float* sin;
+  int P;
+  int bits;               // 3 or 4
+  float eps;
+  void* codes;            // [T][H][D*bits/8]
+  float* scale;           // [T][H]
+  const int* bos_slot;    // [T] or null; slot >= 0 marks a BOS token (bits == 3 only)
+  int nslots;
+  void* bos_codes;        // [nslots][H][D/2]
+  float* bos_scale;       // [nslots][H]
+};
+hipError_t bl_launch_kv_quant(const bl_kv_args& a, hipStream_t st);

@@ -43,3 +43,17 @@ def pack_rows_reference(codes: np.ndarray) -> np.ndarray:
     f = np.where(codes < 0, 3, codes).astype(np.uint32).reshape(N, K // 16, 16)
     words = np.bitwise_or.reduce(f << _POS, axis=-1).astype("<u4")
     return words.reshape(-1).view(np.uint8)
+
+
+def unpack_kv(codes_u8, H, D, bits):
+    """KV-cache code buffer [T, H * D * bits / 8] -> unsigned codes uint8 [T, H, D], decoded from
+    the documented layout: 4 bits, code 2j in the low nibble of byte j of a head record; 3 bits,
+    codes 8g .. 8g+7 in the little-endian 24 bits of bytes 3g .. 3g+2, code 8g + q at bits 3q."""
+    b = np.asarray(codes_u8, dtype=np.uint8)
+    T = b.shape[0]
+    b = b.reshape(T, H, D * bits // 8)
+    if bits == 4:
+        return np.stack([b & 15, b >> 4], axis=-1).reshape(T, H, D)
+    g = b.reshape(T, H, D // 8, 3).astype(np.uint32)
+    w = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)
+    return np.stack([(w >> (3 * q)) & 7 for q in range(8)], axis=-1).reshape(T, H, D).astype(np.uint8)

@@ -33,7 +33,7 @@ def test_header_declares_the_hot_path_calls():
     fns = header_functions()
     for f in ("bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_gemm_w158a4",
               "bitlinear_gemm_w158a8_sparse", "bitlinear_gemv_decode", "bitlinear_pack_ternary_rows",
-              "bitlinear_gemv_decode_glu_conditional", "bitlinear_quantize_act_per_tensor"):
+              "bitlinear_gemv_decode_glu_conditional", "bitlinear_quantize_act_per_tensor", "bitlinear_kv_quantize"):
         assert f in fns
 
 
@@ -200,6 +200,43 @@ def test_quantize_per_tensor_validation(kw, status):
                                                         a["ws"], a["wsb"], a["codes"], a["scale"], None)
     assert st == status
     assert tw.bitlinear_quantize_per_tensor_workspace_bytes(4) >= 2064 + 16
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(scale=None), 1), (dict(dt=5), 1), (dict(bits=2), 1),
+    (dict(bits=8), 1), (dict(eps=0.0), 1), (dict(cos=P), 1), (dict(cos=P, sin=P), 1),
+    (dict(cos=P, sin=P, pos=P, Pn=0), 1), (dict(slot=P), 1), (dict(slot=P, bcodes=P, bscale=P, bits=4, ns=2), 1),
+    (dict(slot=P, bcodes=P, bscale=P, ns=0), 1), (dict(H=0), 2), (dict(D=96), 2), (dict(D=32, ldx=128), 2),
+    (dict(D=512, ldx=2048), 2), (dict(T=-1), 2), (dict(ldx=100), 1), (dict(x=P_MIS), 3), (dict(codes=P_MIS), 3),
+    (dict(ldx=258), 3), (dict(cos=P_MIS, sin=P, pos=P, Pn=4), 3), (dict(slot=P, bcodes=P_MIS, bscale=P, ns=2), 3),
+    (dict(T=1 << 20, H=32, D=128, ldx=4096), 2), (dict(T=0), 0),
+])
+def test_kv_quantize_validation(kw, status):
+    a = dict(x=P, dt=0, T=4, H=2, D=64, ldx=128, pos=None, cos=None, sin=None, Pn=0, bits=3, eps=1e-5, codes=P,
+             scale=P, slot=None, ns=0, bcodes=None, bscale=None)
+    a.update(kw)
+    st = tw.library().bitlinear_kv_quantize(a["x"], a["dt"], a["T"], a["H"], a["D"], a["ldx"], a["pos"], a["cos"],
+                                            a["sin"], a["Pn"], a["bits"], a["eps"], a["codes"], a["scale"],
+                                            a["slot"], a["ns"], a["bcodes"], a["bscale"], None)
+    assert st == status
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_kv_decoder_positions(bits):
+    """A single set bit lands where the documented KV layout says."""
+    from tests.packed_layout import unpack_kv
+    H, D = 2, 64
+    rb = D * bits // 8
+    for byte in (0, 1, 5, rb - 1, rb, 2 * rb - 1):
+        for bit in (0, 3, 7):
+            buf = np.zeros((1, H * rb), np.uint8)
+            buf[0, byte] = 1 << bit
+            dec = unpack_kv(buf, H, D, bits)
+            h, r = divmod(byte, rb)
+            pos = (8 * r + bit) // bits
+            assert dec[0, h, pos] == 1 << ((8 * r + bit) % bits)
+            assert np.count_nonzero(dec) == 1
 
 
 def test_packed_rows_decoder_roundtrip_and_positions():

@@ -1,0 +1,134 @@
+"""GPU parity of the post-RoPE absmax KV-cache quantizer against the oracle (bit-exact codes and
+scales), through the C ABI: small shapes spanning several waves with a ragged tail, strided rows,
+bf16 and float32 inputs, 3 and 4 bits, with and without RoPE, BOS records; and the full prefill
+KV workload (4096 tokens x 32 heads x 128) on sampled tokens.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import ternary_weight_quantized_amd as tw
+from synth import WORKLOADS, activations_bf16, bf16_bits_to_f32, normal, rope_tables, workload_inputs
+from tests.gpu_util import dev_bf16, dev_f32, host, torch_cuda
+from tests.packed_layout import unpack_kv
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-5
+
+
+def dev_i32(a):
+    torch = torch_cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def make_rows(seed, T, width, f32):
+    """[T, width] inputs; a few heads hold zeros, ties and a lone spike."""
+    if f32:
+        x = normal(seed, T * width).reshape(T, width).astype(np.float32)
+        x[0, 64:128] = 0.0
+        if T > 2:
+            x[2, 128:192] = 0.5
+            x[1, 64 + 7] = 1e4
+        return x, x
+    bits = activations_bf16(seed, T, width)
+    bits[0, 64:128] = 0
+    if T > 2:
+        bits[2, 128:192] = 0x3F00          # 0.5
+    return bits, bf16_bits_to_f32(bits)
+
+
+def dev(x):
+    return dev_f32(x) if x.dtype == np.float32 else dev_bf16(x)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("rope", [False, True])
+@pytest.mark.parametrize("T,H,D", [(1, 1, 64), (5, 3, 128), (37, 8, 256), (130, 5, 64), (33, 32, 128)])
+def test_kv_quantize(T, H, D, rope, bits, f32):
+    torch = torch_cuda()
+    extra = 64                                   # rows are wider than H * D: a strided view
+    x, xf = make_rows(7000 + T * H + D, T, H * D + extra, f32)
+    xd = dev(x)
+    view = xd[:, extra:]                         # the heads start after `extra` columns
+    pos = np.random.default_rng(T + D).integers(0, 40, T).astype(np.int32)
+    pos[0] = 0
+    cos, sin = rope_tables(40, D)
+    bos = pos == 0
+    slots = np.where(bos, np.cumsum(bos) - 1, -1).astype(np.int32)
+    nslots = int(bos.sum())
+    kw = dict(pos=dev_i32(pos), cos=dev_f32(cos), sin=dev_f32(sin)) if rope else {}
+    if bits == 3:
+        kw.update(bos_slot=dev_i32(slots), n_bos_slots=nslots)
+    codes, scale, bcodes, bscale = tw.bitlinear_kv_quantize(view, H, D, bits, eps=EPS, **kw)
+    torch.cuda.synchronize()
+    ref = O.kv_cache_quant(xf[:, extra:].reshape(T, H, D), bits, EPS, pos=pos if rope else None,
+                           cos=cos if rope else None, sin=sin if rope else None,
+                           bos=bos if bits == 3 else None)
+    np.testing.assert_array_equal(unpack_kv(host(codes), H, D, bits), ref["u"])
+    np.testing.assert_array_equal(host(scale), ref["dscale"])
+    if bits == 3:
+        got = unpack_kv(host(bcodes), H, D, 4)
+        np.testing.assert_array_equal(got, ref["bos_u"][bos])
+        np.testing.assert_array_equal(host(bscale), ref["bos_dscale"][bos])
+
+
+def test_kv_quantize_bos_slots_out_of_range_are_skipped():
+    torch = torch_cuda()
+    T, H, D = 6, 4, 64
+    x, xf = make_rows(7100, T, H * D, False)
+    slots = np.array([0, -1, 5, 1, -7, -1], np.int32)           # slot 5 is past n_bos_slots = 2
+    bc = torch.full((2, H * D // 2), 0xEE, dtype=torch.uint8, device="cuda")
+    bs = torch.full((2, H), -1.0, dtype=torch.float32, device="cuda")
+    codes, scale, bcodes, bscale = tw.bitlinear_kv_quantize(dev(x), H, D, 3, eps=EPS, bos_slot=dev_i32(slots),
+                                                            n_bos_slots=2, bos_codes=bc, bos_scale=bs)
+    ref = O.kv_cache_quant(xf.reshape(T, H, D), 3, EPS, bos=slots >= 0)
+    got = unpack_kv(host(bcodes), H, D, 4)
+    np.testing.assert_array_equal(got[0], ref["bos_u"][0])
+    np.testing.assert_array_equal(got[1], ref["bos_u"][3])
+    np.testing.assert_array_equal(host(bscale), ref["bos_dscale"][[0, 3]])
+    np.testing.assert_array_equal(unpack_kv(host(codes), H, D, 3), ref["u"])
+
+
+def test_kv_quantize_empty_is_a_no_op():
+    torch = torch_cuda()
+    x = torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda")[:0]
+    codes, scale, _, _ = tw.bitlinear_kv_quantize(x, 2, 64, 3, eps=EPS)
+    torch.cuda.synchronize()
+    assert codes.shape == (0, 48) and scale.shape == (0, 2)
+
+
+def kv_full_inputs():
+    wl = WORKLOADS["kv_cache"]
+    return wl, workload_inputs("kv_cache")
+
+
+@pytest.mark.parametrize("part,bits,rope", [("q", 4, True), ("k", 3, True), ("v", 3, False)])
+def test_kv_cache_full(part, bits, rope):
+    """The prefill KV workload: 4096 tokens (4 sequences of 1024), 32 heads of 128, read from the
+    fp32 QKV projection output [4096, 12288]; the GPU does every token, the oracle a sample."""
+    torch = torch_cuda()
+    wl, inp = kv_full_inputs()
+    T, H, D = wl["T"], wl["H"], wl["D"]
+    off = {"q": 0, "k": 1, "v": 2}[part] * H * D
+    qkv = dev_f32(inp["qkv"])
+    pos = inp["pos"]
+    bos = pos == 0
+    slots = np.where(bos, np.cumsum(bos) - 1, -1).astype(np.int32)
+    kw = dict(pos=dev_i32(pos), cos=dev_f32(inp["cos"]), sin=dev_f32(inp["sin"])) if rope else {}
+    if bits == 3:
+        kw.update(bos_slot=dev_i32(slots), n_bos_slots=int(bos.sum()))
+    codes, scale, bcodes, bscale = tw.bitlinear_kv_quantize(qkv[:, off:off + H * D], H, D, bits, eps=EPS, **kw)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(3).choice(T, 40, replace=False), [0, 1023, 1024, T - 1]]))
+    xs = inp["qkv"][rows, off:off + H * D].reshape(len(rows), H, D)
+    ref = O.kv_cache_quant(xs, bits, EPS, pos=pos[rows] if rope else None, cos=inp["cos"] if rope else None,
+                           sin=inp["sin"] if rope else None, bos=bos[rows] if bits == 3 else None)
+    np.testing.assert_array_equal(unpack_kv(host(codes)[rows], H, D, bits), ref["u"])
+    np.testing.assert_array_equal(host(scale)[rows], ref["dscale"])
+    if bits == 3:
+        b = bos[rows]
+        got = unpack_kv(host(bcodes), H, D, 4)[slots[rows][b]]
+        np.testing.assert_array_equal(got, ref["bos_u"][b])
+        np.testing.assert_array_equal(host(bscale)[slots[rows][b]], ref["bos_dscale"][b])
