@@ -138,6 +138,30 @@ def main():
     am = torch.empty((A["M"], A["K"] // 32), dtype=torch.int32, device=dev)
     ay = torch.empty((A["M"], A["N"]), dtype=torch.float32, device=dev)
 
+    # KV cache (post-RoPE, Q at 4 bits, K and V at 3 bits with BOS records at 4) read from the
+    # prefill QKV projection output [4096, 3 * 32 * 128]
+    KV = WORKLOADS["kv_cache"]
+    from synth import rope_tables
+    kT, kH, kD = KV["T"], KV["H"], KV["D"]
+    assert kT == P["M"] and 3 * kH * kD == P["N"]
+    kpos_np = (np.arange(kT) % KV["seq_len"]).astype(np.int32)
+    kpos = torch.from_numpy(kpos_np).to(dev)
+    kbos = kpos_np == 0
+    kslot = torch.from_numpy(np.where(kbos, np.cumsum(kbos) - 1, -1).astype(np.int32)).to(dev)
+    knslots = int(kbos.sum())
+    kcos_np, ksin_np = rope_tables(KV["seq_len"], kD)
+    kcos, ksin = torch.from_numpy(kcos_np).to(dev), torch.from_numpy(ksin_np).to(dev)
+    kq_c = torch.empty((kT, kH * kD // 2), dtype=torch.uint8, device=dev)
+    kq_s = torch.empty((kT, kH), dtype=torch.float32, device=dev)
+    kk_c = torch.empty((kT, kH * kD * 3 // 8), dtype=torch.uint8, device=dev)
+    kk_s = torch.empty_like(kq_s)
+    kv_c = torch.empty_like(kk_c)
+    kv_s = torch.empty_like(kq_s)
+    kkb_c = torch.empty((knslots, kH * kD // 2), dtype=torch.uint8, device=dev)
+    kkb_s = torch.empty((knslots, kH), dtype=torch.float32, device=dev)
+    kvb_c = torch.empty_like(kkb_c)
+    kvb_s = torch.empty_like(kkb_s)
+
     D = WORKLOADS["decode_a4"]
     din = workload_inputs("decode_a4")
     dx = bf16_dev(torch, din["x"])
@@ -185,7 +209,8 @@ def main():
     names = ["quant_int4_e3m2_prefill", "gemm_a4_int4_fp6_prefill", "quant_int4_prefill", "gemm_a4_int4_i8_prefill",
              "quant_fp4_prefill", "gemm_a4_fp4_prefill",
              "quant_int4_e3m2_ffn", "gemm_a4_glu_ffn", "quant_int8_h", "gemm_a8_down", "quant_topk_int8_attn",
-             "gemm_a8_oproj_residual"] + [f"decode_m{m}_graph" for m in D["Ms"]] + \
+             "gemm_a8_oproj_residual", "kv_quant_q4_rope", "kv_quant_k3_rope_bos", "kv_quant_v3_bos"] + \
+        [f"decode_m{m}_graph" for m in D["Ms"]] + \
         [f"decode_glu_m{m}_graph" for m in D["Ms"]] + [f"decode_glu_cond_m{m}_graph" for m in D["Ms"]]
 
     def ev():
@@ -215,6 +240,13 @@ def main():
         tw.bitlinear_gemm_w158a8_sparse(fhc, fhs, F["N"], dW, dA, F["K"], y=fy); mark()
         tw.bitlinear_quantize_act(ax, "int8", topk_keep=A["keep"], eps=EPS, codes=ac, scale=as_, mask=am); mark()
         tw.bitlinear_gemm_w158a8_sparse(ac, as_, A["K"], oW, oA, A["N"], y=ay, residual=ar); mark()
+        tw.bitlinear_kv_quantize(py4[:, :kH * kD], kH, kD, 4, eps=EPS, pos=kpos, cos=kcos, sin=ksin,
+                                 codes=kq_c, scale=kq_s); mark()
+        tw.bitlinear_kv_quantize(py4[:, kH * kD:2 * kH * kD], kH, kD, 3, eps=EPS, pos=kpos, cos=kcos, sin=ksin,
+                                 bos_slot=kslot, n_bos_slots=knslots, codes=kk_c, scale=kk_s, bos_codes=kkb_c,
+                                 bos_scale=kkb_s); mark()
+        tw.bitlinear_kv_quantize(py4[:, 2 * kH * kD:], kH, kD, 3, eps=EPS, bos_slot=kslot, n_bos_slots=knslots,
+                                 codes=kv_c, scale=kv_s, bos_codes=kvb_c, bos_scale=kvb_s); mark()
         for m in D["Ms"]:
             graphs[m].replay(); mark()
         for m in D["Ms"]:
@@ -305,6 +337,19 @@ def main():
                                        dense_tops=tops(ops_oproj_dense, times["gemm_a8_oproj_residual"]),
                                        peak=INT8_PEAK_TOPS),
     }
+    kv_rec = kT * kH
+
+    def kv_bytes(bits, rope, bos):
+        b = kv_rec * kD * 4 + kv_rec * (kD * bits / 8 + 4)                 # fp32 heads in, codes + scales out
+        if rope:
+            b += kT * (4 + kD * 4)                                         # position + cos/sin rows
+        if bos:
+            b += kT * 4 + knslots * kH * (kD / 2 + 4)                      # slots + 4-bit BOS records
+        return b
+
+    for n, bits, rope, bos in (("kv_quant_q4_rope", 4, True, False), ("kv_quant_k3_rope_bos", 3, True, True),
+                               ("kv_quant_v3_bos", 3, False, True)):
+        kern[n] = dict(us=times[n], bound="hbm", gbs=gbs(kv_bytes(bits, rope, bos), times[n]))
     for m in D["Ms"]:
         kern[f"decode_m{m}"] = dict(us=gemv_us[m], bound="hbm", gbs=gbs(dec_bytes(m), gemv_us[m]))
     for k in kern.values():
@@ -363,7 +408,8 @@ def main():
         "dtype": "fp6(e3m2) x fp4(e2m1) MFMA holding INT4 x ternary codes exactly, fp32 accumulate, fp32 epilogue",
         "data": "synthetic (seeded N(0,1) bf16 activations, N(0,0.02) latent weights, outlier channels)",
         "config": {"workload": "prefill_qkv: W1.58A4 BitLinear M=4096 K=4096 N=12288 (fused QKV, 7B-shaped)",
-                   "step": "all hot-path operations: prefill INT4+FP4, ffn_7b, attn_out, decode M=1/4/8",
+                   "step": "all hot-path operations: prefill INT4+FP4, ffn_7b, attn_out, KV-cache quantize "
+                           "(Q4/K3/V3 of the prefill QKV output), decode M=1/4/8",
                    "global_batch": P["M"], "seq_len": None, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "decode_gemv": decode,
