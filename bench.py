@@ -108,6 +108,11 @@ def main():
     ps6 = torch.empty(P["M"], dtype=torch.float32, device=dev)
     pcf = torch.empty_like(pc4)
     psf = torch.empty_like(ps4)
+    pcp = torch.empty_like(pc4)          # FP4 with power-of-two scales
+    psp = torch.empty_like(ps4)
+    pct = torch.empty_like(pc4)          # INT4 with one scale for the whole tensor
+    pst = torch.empty_like(ps4)
+    pws = torch.empty(tw.bitlinear_quantize_per_tensor_workspace_bytes(P["M"]), dtype=torch.uint8, device=dev)
     py4 = torch.empty((P["M"], P["N"]), dtype=torch.float32, device=dev)
     pyf = torch.empty_like(py4)
 
@@ -207,7 +212,8 @@ def main():
     torch.cuda.synchronize()
 
     names = ["quant_int4_e3m2_prefill", "gemm_a4_int4_fp6_prefill", "quant_int4_prefill", "gemm_a4_int4_i8_prefill",
-             "quant_fp4_prefill", "gemm_a4_fp4_prefill",
+             "quant_fp4_prefill", "gemm_a4_fp4_prefill", "quant_fp4_pow2_prefill",
+             "quant_int4_per_tensor_prefill",
              "quant_int4_e3m2_ffn", "gemm_a4_glu_ffn", "quant_int8_h", "gemm_a8_down", "quant_topk_int8_attn",
              "gemm_a8_oproj_residual", "kv_quant_q4_rope", "kv_quant_k3_rope_bos", "kv_quant_v3_bos"] + \
         [f"decode_m{m}_graph" for m in D["Ms"]] + \
@@ -233,6 +239,8 @@ def main():
         tw.bitlinear_gemm_w158a4("int4", pc4, ps4, P["K"], pW, pA, P["N"], y=py4); mark()
         tw.bitlinear_quantize_act(px, "fp4", eps=EPS, codes=pcf, scale=psf); mark()
         tw.bitlinear_gemm_w158a4("fp4", pcf, psf, P["K"], pW, pA, P["N"], y=pyf); mark()
+        tw.bitlinear_quantize_act(px, "fp4_pow2", eps=EPS, codes=pcp, scale=psp); mark()
+        tw.bitlinear_quantize_act_per_tensor(px, "int4", eps=EPS, codes=pct, scale=pst, workspace=pws); mark()
         tw.bitlinear_quantize_act(fx, "int4_e3m2", eps=EPS, codes=fc, scale=fs); mark()
         tw.bitlinear_gemm_w158a4("int4_e3m2", fc, fs, F["K"], gW, gA, F["N"], y=fh, up_packed=uW, up_alpha=uA,
                                  row_absmax=frm); mark()
@@ -320,6 +328,12 @@ def main():
                                   gbs=gbs(Mp * Kp * 2 + Mp * Kp / 2 + 4 * Mp, times["quant_fp4_prefill"])),
         "gemm_a4_fp4_prefill": dict(us=times["gemm_a4_fp4_prefill"], bound="mfma",
                                     tops=tops(ops_prefill, times["gemm_a4_fp4_prefill"]), peak=FP4_PEAK_TOPS),
+        "quant_fp4_pow2_prefill": dict(us=times["quant_fp4_pow2_prefill"], bound="hbm",
+                                       gbs=gbs(Mp * Kp * 2 + Mp * Kp / 2 + 4 * Mp, times["quant_fp4_pow2_prefill"])),
+        # two passes over x: the tensor-wide exact sum, then the row quantizer with the given beta
+        "quant_int4_per_tensor_prefill": dict(us=times["quant_int4_per_tensor_prefill"], bound="hbm",
+                                              gbs=gbs(2 * Mp * Kp * 2 + Mp * Kp / 2 + 8 * Mp,
+                                                      times["quant_int4_per_tensor_prefill"])),
         "quant_int4_e3m2_ffn": dict(us=times["quant_int4_e3m2_ffn"], bound="hbm",
                                     gbs=gbs(F["M"] * F["K"] * 2.75 + 4 * F["M"], times["quant_int4_e3m2_ffn"])),
         "gemm_a4_glu_ffn": dict(us=times["gemm_a4_glu_ffn"], bound="mfma",

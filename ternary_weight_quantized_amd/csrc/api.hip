@@ -101,7 +101,7 @@ bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, i
 
 size_t bitlinear_quantize_per_tensor_workspace_bytes(int64_t M) {
   if (M <= 0) return 0;
-  return (size_t)(2064 + ((4 * M + 15) / 16) * 16);
+  return bl_quantize_per_tensor_ws_bytes((long)M);
 }
 
 bl_status bitlinear_quantize_act_per_tensor(const void* d_x, int32_t in_dtype, int64_t M, int64_t K, int64_t ldx,

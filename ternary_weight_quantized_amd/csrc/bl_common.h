@@ -106,6 +106,74 @@ __host__ __device__ inline double bl_bins_to_double(const unsigned long long* bi
   return ldexp((double)mant, ex - 52 - 149);
 }
 
+// The same correctly rounded double for a whole block (blockDim.x threads, every thread calls it
+// with the same arguments and gets the result): bins are scattered into 32-bit limb sums in LDS in
+// parallel (each limb sum stays below 2^42), one thread propagates the carries and rounds.
+// lds: 12 unsigned long long of shared memory; out: one shared double.
+__device__ inline double bl_limbs_to_double(const uint32_t (&L)[12]) {
+  // the three most significant nonzero limbs (a, b, c) and whether anything below them is nonzero
+  uint32_t a = 0u, b = 0u, c = 0u;
+  int ti = -1, k = 0;
+  bool sticky = false;
+#pragma unroll
+  for (int i = 11; i >= 0; --i) {
+    const uint32_t v = L[i];
+    if (k == 0) {
+      if (v) { a = v; ti = i; k = 1; }
+    } else if (k == 1) {
+      b = v; k = 2;
+    } else if (k == 2) {
+      c = v; k = 3;
+    } else {
+      sticky |= v != 0u;
+    }
+  }
+  if (ti < 0) return 0.0;
+  const int lz = __clz(a);
+  unsigned long long u = ((unsigned long long)a << 32) | b;
+  u = lz ? ((u << lz) | (c >> (32 - lz))) : u;
+  const uint32_t c_rest = lz ? (c << lz) : c;                   // bits of c below the window
+  int P = 32 * ti + 31 - lz;                                    // position of the leading bit
+  unsigned long long mant = u >> 11;                            // 53 bits
+  const uint32_t rbit = (uint32_t)(u >> 10) & 1u;
+  sticky |= (u & 0x3FFull) != 0ull || c_rest != 0u;
+  if (rbit && (sticky || (mant & 1ull))) {
+    ++mant;
+    if (mant == (1ull << 53)) { mant >>= 1; ++P; }
+  }
+  return ldexp((double)mant, P - 52 - 149);
+}
+
+__device__ inline double bl_bins_to_double_block(const unsigned long long* bins, unsigned long long* lds,
+                                                 double* out) {
+  const int t = threadIdx.x;
+  if (t < 12) lds[t] = 0ull;
+  __syncthreads();
+  for (int e = t; e < 255; e += blockDim.x) {
+    const unsigned long long b = bins[e];
+    if (!b) continue;
+    const int sh = (e > 1 ? e : 1) - 1;                         // b * 2^sh in units of 2^-149
+    const int w = sh >> 5, bit = sh & 31;
+    atomicAdd(&lds[w], (unsigned long long)(uint32_t)(b << bit));
+    atomicAdd(&lds[w + 1], (unsigned long long)(uint32_t)(bit ? (b >> (32 - bit)) : (b >> 32)));
+    atomicAdd(&lds[w + 2], (unsigned long long)(uint32_t)(bit ? (b >> (64 - bit)) : 0ull));
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint32_t L[12];
+    unsigned long long carry = 0ull;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      const unsigned long long v = lds[i] + carry;
+      L[i] = (uint32_t)v;
+      carry = v >> 32;
+    }
+    *out = bl_limbs_to_double(L);
+  }
+  __syncthreads();
+  return *out;
+}
+
 // ------------------------------------------------------------------ quantizer arithmetic
 // round-half-even then clamp, as an int
 __device__ __forceinline__ int bl_roundclip(float v, float lo, float hi) {

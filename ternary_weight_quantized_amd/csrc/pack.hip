@@ -41,11 +41,12 @@ __global__ __launch_bounds__(256) void k_abs_bins(const float* __restrict__ w, l
   if (b) atomicAdd(&gbins[threadIdx.x], b);
 }
 
-__global__ void k_alpha(const unsigned long long* __restrict__ gbins, double count, float* __restrict__ alpha) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    const double S = bl_bins_to_double(gbins);
-    *alpha = (float)(S / count);
-  }
+__global__ __launch_bounds__(256) void k_alpha(const unsigned long long* __restrict__ gbins, double count,
+                                               float* __restrict__ alpha) {
+  __shared__ unsigned long long limbs[12];
+  __shared__ double total;
+  const double S = bl_bins_to_double_block(gbins, limbs, &total);
+  if (threadIdx.x == 0) *alpha = (float)(S / count);
 }
 
 // One thread per packed 32-bit word: tile (kt, G) of 16 rows x 128 columns, lane L = 16 g + r, word i.
@@ -115,7 +116,7 @@ hipError_t bl_launch_pack(const float* w, int N, int K, float eps, void* packed,
   long blocks = (n / 4 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_abs_bins, dim3((unsigned)blocks), dim3(256), 0, st, w, n, bins);
-  hipLaunchKernelGGL(k_alpha, dim3(1), dim3(64), 0, st, bins, (double)n, alpha);
+  hipLaunchKernelGGL(k_alpha, dim3(1), dim3(256), 0, st, bins, (double)n, alpha);
   const long nwords = n / 16;
   if (rows)
     hipLaunchKernelGGL(k_pack_rows, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st, w, N, K, eps, alpha,

@@ -648,57 +648,181 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
 // Variant of the activation quantizers with one scale for the whole [M, K] tensor (reading of the
 // pages' "all entries in X"): beta = RN32(RN64(exact sum |x|) / (M K)) or gamma = max |x| over the
 // tensor, then every row is quantized with it (passed to the row kernels as a per-row value).
-// The sum uses the same exact per-exponent integer bins as the weight alpha.
+// The exact sum: each thread adds its values in double, exact whenever the exponent span of its
+// terms allows it (else its values go to the bins one by one); the thread's exact double is split
+// into three non-negative floats (round down, remainder, remainder) that enter the per-exponent
+// integer bins shared with the weight alpha.
+__device__ __forceinline__ float round_down_f32(double d) {        // d >= 0, d < FLT_MAX
+  float f = (float)d;
+  if ((double)f > d) f = bl_u2f(bl_f2u(f) - 1u);
+  return f;
+}
+
+constexpr int kTensorBlocks = 512;     // blocks of the tensor-wide reduction
+constexpr int kTensorCopies = 64;      // global copies of the bins (block b adds into copy b % 64)
+
+template <int IN_F32>
+__device__ __forceinline__ void load8(const void* __restrict__ x, long off, float (&o)[8]) {
+  if (IN_F32) {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  } else {
+    const uint4 t = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+    o[0] = bl_bf16lo(t.x); o[1] = bl_bf16hi(t.x); o[2] = bl_bf16lo(t.y); o[3] = bl_bf16hi(t.y);
+    o[4] = bl_bf16lo(t.z); o[5] = bl_bf16hi(t.z); o[6] = bl_bf16lo(t.w); o[7] = bl_bf16hi(t.w);
+  }
+}
+
+// Adds one non-negative float per lane to the LDS bins, one atomic per distinct exponent of the
+// wave (lanes with equal exponents are summed first; 64 significands < 2^24 fit in 32 bits).
+// Called by all 64 lanes together.
+__device__ __forceinline__ void wave_bins_add(unsigned long long* bins, float v, int lane) {
+  uint32_t e, m;
+  bl_bin_split(bl_f2u(v) & 0x7FFFFFFFu, &e, &m);
+  bool pending = m != 0u;
+  for (;;) {
+    const unsigned long long act = __ballot(pending);
+    if (act == 0ull) break;
+    const int leader = __ffsll((long long)act) - 1;
+    const uint32_t e0 = __shfl(e, leader, 64);
+    const bool mine = pending && e == e0;
+    uint32_t part = mine ? m : 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (lane == leader) atomicAdd(&bins[e0], (unsigned long long)part);
+    pending = pending && !mine;
+  }
+}
+
+__global__ void k_tensor_clear(unsigned long long* __restrict__ gbins) {
+  for (int i = threadIdx.x; i < kTensorCopies * 256; i += blockDim.x) gbins[i] = 0ull;
+}
+
+// Each block adds its exact bins into global copy blockIdx % 64 (SUM) or writes its maximum to
+// slot blockIdx (the blocks sharing a copy are few, so the atomics seldom wait on each other).
+// Threads walk 8-element chunks of the row-major tensor with a grid stride.
 template <int IN_F32, bool SUM>
 __global__ __launch_bounds__(256) void k_tensor_reduce(const void* __restrict__ x, int M, int K, long ldx,
                                                        unsigned long long* __restrict__ gbins,
                                                        uint32_t* __restrict__ gmax) {
   __shared__ unsigned long long bins[SUM ? 256 : 1];
+  __shared__ uint32_t wmax[4];
+  const int t = threadIdx.x, lane = t & 63;
   if constexpr (SUM) {
-    bins[threadIdx.x] = 0ull;
+    bins[t] = 0ull;
     __syncthreads();
   }
   uint32_t mx = 0u;
-  const long quads = (long)M * (K >> 2);
-  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += (long)gridDim.x * blockDim.x) {
-    const long row = q / (K >> 2), col = 4 * (q % (K >> 2));
-    float v[4];
-    load4<IN_F32>(x, row * ldx + col, v);
+  AbsSum accs[4];                      // four independent sums shorten the chain of dependent adds
+  int cnt = 0;
+  const long KO = K >> 3, chunks = (long)M * KO;
+  const long q0 = (long)blockIdx.x * blockDim.x + t, qs = (long)gridDim.x * blockDim.x;
+  const long drow = qs / KO, dcol = qs % KO;
+  {
+    long row = q0 / KO, col = q0 % KO;
+#pragma unroll 4
+    for (long q = q0; q < chunks; q += qs) {
+      float v[8];
+      load8<IN_F32>(x, row * ldx + 8 * col, v);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t b = bl_f2u(v[j]) & 0x7FFFFFFFu;
-      if constexpr (SUM) {
-        uint32_t e, m;
-        bl_bin_split(b, &e, &m);
-        if (m) atomicAdd(&bins[e], (unsigned long long)m);
-      } else {
-        mx = b > mx ? b : mx;
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (SUM) {
+          accs[j & 3].add(v[j]);
+        } else {
+          const uint32_t b = bl_f2u(v[j]) & 0x7FFFFFFFu;
+          mx = b > mx ? b : mx;
+        }
       }
+      cnt += 8;
+      col += dcol;
+      row += drow;
+      if (col >= KO) { col -= KO; ++row; }
     }
   }
+  const int copy = blockIdx.x % kTensorCopies;
   if constexpr (SUM) {
+    AbsSum acc = accs[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      acc.s += accs[i].s;              // exact whenever the bound below holds for all the terms
+      acc.emax = accs[i].emax > acc.emax ? accs[i].emax : acc.emax;
+      acc.emin = accs[i].emin < acc.emin ? accs[i].emin : acc.emin;
+    }
+    const bool exact = sum_is_exact<IN_F32>(acc.emax, acc.emin, cnt) && acc.s < 1.0e38;
+    float hi = 0.f, mid = 0.f, lo = 0.f;
+    if (exact) {
+      hi = round_down_f32(acc.s);
+      const double r = acc.s - (double)hi;                          // exact, below ulp(hi)
+      mid = round_down_f32(r);
+      lo = (float)(r - (double)mid);                                 // exact: at most a few bits
+    } else {
+      long row = q0 / KO, col = q0 % KO;
+      for (long q = q0; q < chunks; q += qs) {
+        float v[8];
+        load8<IN_F32>(x, row * ldx + 8 * col, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bins_add(bins, v[j]);
+        col += dcol;
+        row += drow;
+        if (col >= KO) { col -= KO; ++row; }
+      }
+    }
+    wave_bins_add(bins, hi, lane);
+    wave_bins_add(bins, mid, lane);
+    wave_bins_add(bins, lo, lane);
     __syncthreads();
-    const unsigned long long b = bins[threadIdx.x];
-    if (b) atomicAdd(&gbins[threadIdx.x], b);
+    const unsigned long long b = bins[t];
+    if (b) atomicAdd(&gbins[copy * 256 + t], b);
   } else {
     mx = bl_wave_max_u(mx);
-    if ((threadIdx.x & 63) == 0) atomicMax(gmax, mx);
+    if (lane == 0) wmax[t >> 6] = mx;
+    __syncthreads();
+    if (t == 0) {
+      uint32_t m = wmax[0];
+      for (int w = 1; w < 4; ++w) m = wmax[w] > m ? wmax[w] : m;
+      gmax[blockIdx.x] = m;
+    }
   }
 }
 
-__global__ void k_tensor_clear(unsigned long long* bins, uint32_t* gmax) {
-  bins[threadIdx.x] = 0ull;
-  if (threadIdx.x == 0) *gmax = 0u;
-}
-
-// one value for every row: beta (SUM) or gamma
+// one value for every row: beta (SUM, from the bins) or gamma (the maximum); 1024 threads
 template <bool SUM>
-__global__ void k_tensor_scale(const unsigned long long* __restrict__ bins, const uint32_t* __restrict__ gmax,
-                               int M, double count, float* __restrict__ rowval) {
+__global__ __launch_bounds__(1024) void k_tensor_scale(const unsigned long long* __restrict__ gbins,
+                                                       const uint32_t* __restrict__ gmax, int M, double count,
+                                                       float* __restrict__ rowval) {
+  __shared__ unsigned long long part[4][256];
+  __shared__ unsigned long long bins[256];
+  __shared__ unsigned long long limbs[12];
+  __shared__ double total;
+  __shared__ uint32_t wmax[16];
   __shared__ float val;
-  if (threadIdx.x == 0) val = SUM ? (float)(bl_bins_to_double(bins) / count) : bl_u2f(*gmax);
+  const int t = threadIdx.x;
+  if constexpr (SUM) {
+    const int e = t & 255, grp = t >> 8;
+    unsigned long long b = 0ull;
+#pragma unroll
+    for (int k = grp; k < kTensorCopies; k += 4) b += gbins[k * 256 + e];
+    part[grp][e] = b;
+    __syncthreads();
+    if (t < 256) bins[t] = part[0][t] + part[1][t] + part[2][t] + part[3][t];
+    __syncthreads();
+    const double S = bl_bins_to_double_block(bins, limbs, &total);
+    if (t == 0) val = (float)(S / count);
+  } else {
+    uint32_t m = 0u;
+    for (int k = t; k < kTensorBlocks; k += 1024) m = gmax[k] > m ? gmax[k] : m;
+    m = bl_wave_max_u(m);
+    if ((t & 63) == 0) wmax[t >> 6] = m;
+    __syncthreads();
+    if (t == 0) {
+      uint32_t g = wmax[0];
+      for (int w = 1; w < 16; ++w) g = wmax[w] > g ? wmax[w] : g;
+      val = bl_u2f(g);
+    }
+  }
   __syncthreads();
-  for (int m = threadIdx.x; m < M; m += blockDim.x) rowval[m] = val;
+  for (int m = t; m < M; m += 1024) rowval[m] = val;
 }
 
 template <int FMT, int IN_F32>
@@ -755,21 +879,22 @@ hipError_t bl_launch_quantize(const void* x, int in_f32, int M, int K, long ldx,
 
 hipError_t bl_launch_quantize_per_tensor(const void* x, int in_f32, int M, int K, long ldx, int fmt, float eps,
                                          void* ws, void* codes, float* scale, hipStream_t st) {
-  unsigned long long* bins = static_cast<unsigned long long*>(ws);
-  uint32_t* gmax = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + 2048);
-  float* rowval = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + 2064);
+  // workspace: 64 copies of the 256 bins (uint64), 512 block maxima (uint32), then the M row values
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  unsigned long long* gbins = reinterpret_cast<unsigned long long*>(w);
+  uint32_t* gmax = reinterpret_cast<uint32_t*>(w + (size_t)kTensorCopies * 256 * 8);
+  float* rowval = reinterpret_cast<float*>(w + (size_t)kTensorCopies * 256 * 8 + (size_t)kTensorBlocks * 4);
   const bool sum = (fmt == BL_ACT_INT4 || fmt == BL_ACT_INT4_E3M2);
-  hipLaunchKernelGGL(k_tensor_clear, dim3(1), dim3(256), 0, st, bins, gmax);
-  const long quads = (long)M * (K >> 2);
-  const unsigned blocks = (unsigned)std::min<long>((quads + 255) / 256, 2048);
+  const dim3 grid(kTensorBlocks), block(256);
   if (sum) {
-    if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, true>), dim3(blocks), dim3(256), 0, st, x, M, K, ldx, bins, gmax);
-    else hipLaunchKernelGGL((k_tensor_reduce<0, true>), dim3(blocks), dim3(256), 0, st, x, M, K, ldx, bins, gmax);
-    hipLaunchKernelGGL((k_tensor_scale<true>), dim3(1), dim3(256), 0, st, bins, gmax, M, (double)M * K, rowval);
+    hipLaunchKernelGGL(k_tensor_clear, dim3(1), dim3(1024), 0, st, gbins);
+    if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, true>), grid, block, 0, st, x, M, K, ldx, gbins, gmax);
+    else hipLaunchKernelGGL((k_tensor_reduce<0, true>), grid, block, 0, st, x, M, K, ldx, gbins, gmax);
+    hipLaunchKernelGGL((k_tensor_scale<true>), dim3(1), dim3(1024), 0, st, gbins, gmax, M, (double)M * K, rowval);
   } else {
-    if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, false>), dim3(blocks), dim3(256), 0, st, x, M, K, ldx, bins, gmax);
-    else hipLaunchKernelGGL((k_tensor_reduce<0, false>), dim3(blocks), dim3(256), 0, st, x, M, K, ldx, bins, gmax);
-    hipLaunchKernelGGL((k_tensor_scale<false>), dim3(1), dim3(256), 0, st, bins, gmax, M, (double)M * K, rowval);
+    if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, false>), grid, block, 0, st, x, M, K, ldx, gbins, gmax);
+    else hipLaunchKernelGGL((k_tensor_reduce<0, false>), grid, block, 0, st, x, M, K, ldx, gbins, gmax);
+    hipLaunchKernelGGL((k_tensor_scale<false>), dim3(1), dim3(1024), 0, st, gbins, gmax, M, (double)M * K, rowval);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
