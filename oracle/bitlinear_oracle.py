@@ -43,19 +43,19 @@ reason in the design notes):
      over the whole row (which survives whenever keep >= 1).
   R9 FFN: ReLU^2 acts on the gate projection, h = RN32(RN32(g+ * g+) * u) with
      g, u the fp32 dequantized projections; the down input is INT8 without Top-K.
-  R15 FP4 power-of-two scale variant: the dequant scale is 2^p with p the smallest integer such that
-     6 * 2^p >= max|x| (p >= -126); codes are the E2M1 rounding of x * 2^-p (exact scaling).
   R14 Conditional up projection: a channel's up output is computed only when its gate is
      positive in some row; entries with g <= 0 are +0 (the full form gives +0 * u, which is
      -0 when u < 0: equal as numbers).
+  R15 FP4 power-of-two scale variant: the dequant scale is 2^p with p the smallest integer such that
+     6 * 2^p >= max|x| (p >= -126); codes are the E2M1 rounding of x * 2^-p (exact scaling).
+  R16 Per-tensor variant (per_tensor=True): beta or gamma is taken over all M*K entries of X at
+     once, in the same form as R5 (K replaced by M*K), and every row is quantized with it; the
+     per-row dscale then holds that one value in every row.
   R17 KV cache: absmax per (token, head) over the head's D values, symmetric, Qp = 2^(b-1) - 1
      (7 for 4 bits, 3 for 3 bits): c = RoundClip(RN32(x * RN32(Qp / RN32(gamma + eps))), -Qp-1, Qp),
      stored unsigned as u = c + 2^(b-1); dequant scale RN32(gamma / Qp). RoPE is the rotate-half
      form on (x_i, x_{i+D/2}) with caller cos/sin tables, each product and sum rounded to fp32.
      BOS tokens (marked by the caller) get a 4-bit record beside the 3-bit one.
-  R16 Per-tensor variant (per_tensor=True): beta or gamma is taken over all M*K entries of X at
-     once, in the same form as R5 (K replaced by M*K), and every row is quantized with it; the
-     per-row dscale then holds that one value in every row.
 """
 from __future__ import annotations
 
