@@ -312,6 +312,161 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
   }
 }
 
+// ============================================================================ block-per-row kernel
+// Quantizers without a Top-K mask (INT4 nibbles or E3M2 tiles, FP4 both scale modes, INT8 of the
+// whole row), one 256-thread block per row: thread t owns the 8-element chunks t, t + 256, ... of
+// the row (16- or 32-byte loads), the row statistic (exact absmean sum or max) is reduced across
+// the block, and every chunk's codes leave as one 4- or 8-byte store (E3M2: 12 bytes per thread
+// pair). Many more waves are in flight than with one wave per row.
+template <int IN_F32>
+__device__ __forceinline__ void load8v(const void* __restrict__ x, long off, float (&o)[8]) {
+  if (IN_F32) {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  } else {
+    const uint4 t = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+    o[0] = bl_bf16lo(t.x); o[1] = bl_bf16hi(t.x); o[2] = bl_bf16lo(t.y); o[3] = bl_bf16hi(t.y);
+    o[4] = bl_bf16lo(t.z); o[5] = bl_bf16hi(t.z); o[6] = bl_bf16lo(t.w); o[7] = bl_bf16hi(t.w);
+  }
+}
+
+template <int FMT, int IN_F32, int NCH>
+__global__ __launch_bounds__(256) void k_quant_blk(const void* __restrict__ x, int M, int K, long ldx, float eps,
+                                                   const float* __restrict__ hint, uint8_t* __restrict__ codes,
+                                                   float* __restrict__ scale) {
+  constexpr bool SUM = (FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2);
+  __shared__ double wsum[4];
+  __shared__ uint32_t wa[4], wb[4];
+  __shared__ unsigned long long bins[SUM ? 256 : 1];
+  __shared__ unsigned long long limbs[12];
+  __shared__ double total;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row = blockIdx.x;
+  const int nch = K >> 3;
+  float v[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    if (t + 256 * c < nch) load8v<IN_F32>(x, (long)row * ldx + 8 * (t + 256 * c), v[c]);
+
+  // the row statistic: beta (SUM) or gamma
+  float st_val;
+  if (hint) {
+    st_val = hint[row];
+  } else if constexpr (SUM) {
+    AbsSum acc;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (t + 256 * c < nch) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc.add(v[c][j]);
+      }
+    const double ws = bl_wave_sum_d(acc.s);
+    const uint32_t emax = bl_wave_max_u(acc.emax), emin = bl_wave_min_u(acc.emin);
+    if (lane == 0) { wsum[wave] = ws; wa[wave] = emax; wb[wave] = emin; }
+    __syncthreads();
+    double S = wsum[0] + wsum[1] + wsum[2] + wsum[3];           // exact when the check below holds
+    uint32_t e1 = wa[0], e0 = wb[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) { e1 = wa[w] > e1 ? wa[w] : e1; e0 = wb[w] < e0 ? wb[w] : e0; }
+    if (!sum_is_exact<IN_F32>(e1, e0, K)) {                      // block-uniform
+      bins[t] = 0ull;
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        if (t + 256 * c < nch) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) bins_add(bins, v[c][j]);
+        }
+      __syncthreads();
+      S = bl_bins_to_double_block(bins, limbs, &total);
+    }
+    st_val = (float)(S / (double)K);
+  } else {
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (t + 256 * c < nch) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t b = bl_f2u(v[c][j]) & 0x7FFFFFFFu;
+          mx = b > mx ? b : mx;
+        }
+      }
+    mx = bl_wave_max_u(mx);
+    if (lane == 0) wa[wave] = mx;
+    __syncthreads();
+    uint32_t g = wa[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) g = wa[w] > g ? wa[w] : g;
+    st_val = bl_u2f(g);
+  }
+
+  if constexpr (SUM) {
+    const float beta = st_val;
+    const float s = bl_u2f(BL_SQRT7_BITS) / (beta + eps);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = t + 256 * c;
+      if (ch >= nch) continue;                                   // whole wave pairs drop out together
+      if constexpr (FMT == BL_ACT_INT4) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w |= code_int4(v[c][j], s) << (4 * j);
+        reinterpret_cast<uint32_t*>(codes + (long)row * (K >> 1))[ch] = w;
+      } else {
+        // 8 codes x 6 bits; a thread pair (chunks 2i, 2i+1 of a 128-code group) writes 12 bytes
+        unsigned long long v48 = 0ull;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v48 |= (unsigned long long)code_e3m2(v[c][j], s) << (6 * j);
+        const uint32_t lo = (uint32_t)v48, hi = (uint32_t)(v48 >> 32);
+        const uint32_t plo = __shfl_xor(lo, 1, 64);
+        const int k = 8 * ch;
+        const long tile = (long)(row >> 4) * (K >> 7) + (k >> 7);
+        uint8_t* base = codes + tile * 1536 + (row & 15) * 96 + 6 * ((k & 127) >> 3);
+        if ((ch & 1) == 0) {
+          uint32_t* d = reinterpret_cast<uint32_t*>(base);
+          d[0] = lo;
+          d[1] = (hi & 0xFFFFu) | (plo << 16);
+        } else {
+          // own chunk starts 6 bytes into the pair: bytes 8..11 of the pair = own bits 16..47
+          *reinterpret_cast<uint32_t*>(base + 2) = (lo >> 16) | (hi << 16);
+        }
+      }
+    }
+    if (t == 0) scale[row] = beta / bl_u2f(BL_SQRT7_BITS);
+  } else if constexpr (FMT == BL_ACT_FP4_E2M1 || FMT == BL_ACT_FP4_E2M1_POW2) {
+    float s, dscale;
+    fp4_scales<FMT == BL_ACT_FP4_E2M1_POW2>(st_val, eps, &s, &dscale);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = t + 256 * c;
+      if (ch >= nch) continue;
+      uint32_t w = 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w |= code_fp4(v[c][j], s) << (4 * j);
+      reinterpret_cast<uint32_t*>(codes + (long)row * (K >> 1))[ch] = w;
+    }
+    if (t == 0) scale[row] = dscale;
+  } else {
+    const float gamma = st_val;
+    const float s = 127.0f / (gamma + eps);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = t + 256 * c;
+      if (ch >= nch) continue;
+      uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w0 |= code_int8(v[c][j], s) << (8 * j);
+        w1 |= code_int8(v[c][j + 4], s) << (8 * j);
+      }
+      reinterpret_cast<uint2*>(codes + (long)row * K)[ch] = make_uint2(w0, w1);
+    }
+    if (t == 0) scale[row] = gamma / 127.0f;
+  }
+}
+
 // ============================================================================ Top-K + INT8 of bf16 rows
 // INT8 absmax with the Top-K mask for bf16 rows of up to 4096 elements, on integer keys: the key of
 // |x| is its 15 magnitude bits (exponent << 7 | mantissa), so comparisons of magnitudes are integer
@@ -830,6 +985,18 @@ hipError_t launch_fmt(const void* x, int M, int K, long ldx, int keep, float eps
                       uint8_t* codes, float* scale, uint32_t* mask, hipStream_t st) {
   const dim3 grid((M + 3) / 4), block(256);
   const int NG = K >> 8;
+  // no Top-K mask: one block per row
+  const bool plain = FMT != BL_ACT_INT8 || (mask == nullptr && (keep < 0 || keep >= K));
+  if (plain && K <= 16384) {
+    const int per = (K / 8 + 255) / 256;                 // 8-element chunks per thread
+    if (per <= 2)
+      hipLaunchKernelGGL((k_quant_blk<FMT, IN_F32, 2>), dim3(M), block, 0, st, x, M, K, ldx, eps, hint, codes, scale);
+    else if (per <= 4)
+      hipLaunchKernelGGL((k_quant_blk<FMT, IN_F32, 4>), dim3(M), block, 0, st, x, M, K, ldx, eps, hint, codes, scale);
+    else
+      hipLaunchKernelGGL((k_quant_blk<FMT, IN_F32, 8>), dim3(M), block, 0, st, x, M, K, ldx, eps, hint, codes, scale);
+    return hipGetLastError();
+  }
   if constexpr (FMT == BL_ACT_INT8 && !IN_F32) {
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     if (NG <= 4)
