@@ -80,6 +80,31 @@ def test_prefill_qkv_sampled(fmt):
     assert_y_close(host(y)[rows], ref["acc"], ref["dscale"], alpha, 0.5 if fmt == "fp4" else 1.0)
 
 
+@pytest.mark.parametrize("fmt", ["int4", "fp4_pow2"])
+def test_prefill_scale_variants_sampled(fmt):
+    """The prefill activations with one scale for the whole 4096 x 4096 tensor (INT4) and with the
+    power-of-two FP4 scale, in the launch configuration the benchmark times; the per-tensor beta
+    comes from the exact sum over all 16.8M entries, the codes are compared on sampled rows."""
+    torch = torch_cuda()
+    wl = WORKLOADS["prefill_qkv"]
+    inp = workload_inputs("prefill_qkv")
+    M, K = wl["M"], wl["K"]
+    x = dev_bf16(inp["x"])
+    rows = sample_rows(M, seed=5)
+    xf = bf16_bits_to_f32(inp["x"])
+    if fmt == "int4":
+        ws = torch.empty(tw.bitlinear_quantize_per_tensor_workspace_bytes(M), dtype=torch.uint8, device="cuda")
+        codes, scale = tw.bitlinear_quantize_act_per_tensor(x, "int4", eps=EPS, workspace=ws)
+        c, d, _ = O.quant_int4(xf, EPS, per_tensor=True)
+        np.testing.assert_array_equal(int4_values(host(codes)[rows]), c[rows])
+        np.testing.assert_array_equal(host(scale), d)
+    else:
+        codes, scale, _ = tw.bitlinear_quantize_act(x, "fp4_pow2", eps=EPS)
+        nib, _, d, _ = O.quant_fp4(xf[rows], EPS, pow2=True)
+        np.testing.assert_array_equal(nibbles(host(codes)[rows]), nib)
+        np.testing.assert_array_equal(host(scale)[rows], d)
+
+
 def test_ffn_7b_sampled():
     torch = torch_cuda()
     wl = WORKLOADS["ffn_7b"]
