@@ -312,6 +312,205 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
   }
 }
 
+// ============================================================================ Top-K, block per row
+// INT8 absmax with the Top-K mask for bf16 rows (K <= 8192), one 256-thread block per row. Thread t
+// owns the 8-element chunks t, t + 256, ... (one 16-byte load each). The threshold key T (the
+// largest 15-bit magnitude key with count(key >= T) >= keep) comes from two radix passes over LDS
+// histograms, 16 copies (thread t adds to copy t % 16, so a wave's 64 increments spread over 16
+// copies): exponents (key >> 7), then the mantissas of the keys whose exponent is T's. Bin counts
+// are summed over the copies, scanned in descending key order across the block, and the bin where
+// the running count reaches keep gives the next digit. Ties at T are ranked by index with one block
+// scan of the per-thread tie counts of every chunk. Codes: RN32(x * s) is rounded to an integer by
+// adding 1.5 * 2^23 (round to nearest even; |x * s| < 127.5 always, so no clamping is needed) and
+// its low byte is the two's-complement code. A 32-element mask word comes from 4 neighbouring threads.
+constexpr int TK_COPIES = 16, TK_STRIDE = 264;     // 256 bins + 8 pad words per copy
+
+// Inclusive scan of one int per thread over the 256-thread block; returns (inclusive, total).
+__device__ __forceinline__ int2 tk_block_scan(int v, int* wtot, int t) {
+  const int lane = t & 63, wave = t >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    off += w < wave ? wtot[w] : 0;
+    tot += wtot[w];
+  }
+  __syncthreads();                                   // wtot may be reused by the next scan
+  return make_int2(incl + off, tot);
+}
+
+template <int NCH>
+__global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x, int M, int K, long ldx, int keep,
+                                                  float eps, const float* __restrict__ hint,
+                                                  uint8_t* __restrict__ codes, float* __restrict__ scale,
+                                                  uint32_t* __restrict__ mask) {
+  __shared__ uint32_t hist[TK_COPIES * TK_STRIDE];
+  __shared__ int wtot[4];
+  __shared__ int wtot_v[NCH][4];
+  __shared__ uint32_t wmax[4];
+  __shared__ int sel[2];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row = blockIdx.x;
+  const int nch = K >> 3;
+  uint4 w[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    if (t + 256 * c < nch) w[c] = *reinterpret_cast<const uint4*>(x + (long)row * ldx + 8 * (t + 256 * c));
+    else w[c] = make_uint4(0u, 0u, 0u, 0u);
+  auto key = [&](int c, int j) -> uint32_t {
+    const uint32_t d = j < 2 ? w[c].x : j < 4 ? w[c].y : j < 6 ? w[c].z : w[c].w;
+    return ((j & 1) ? (d >> 16) : d) & 0x7FFFu;
+  };
+  auto val = [&](int c, int j) -> float {
+    const uint32_t d = j < 2 ? w[c].x : j < 4 ? w[c].y : j < 6 ? w[c].z : w[c].w;
+    return bl_u2f((j & 1) ? (d & 0xFFFF0000u) : (d << 16));
+  };
+
+  float gamma;
+  if (hint) {
+    gamma = hint[row];
+  } else {
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = max(mx, key(c, j));       // padding chunks hold key 0
+    mx = bl_wave_max_u(mx);
+    if (lane == 0) wmax[wave] = mx;
+    __syncthreads();
+    gamma = bl_u2f(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])) << 16);
+  }
+  const float s = 127.0f / (gamma + eps);
+  const bool all = keep < 0 || keep >= K;
+
+  uint32_t T = all ? 0u : 0x8000u;                 // 0x8000: above every key (keep == 0)
+  int need = 0;
+  if (!all && keep > 0) {                          // block-uniform
+    uint32_t* hc = hist + (t & (TK_COPIES - 1)) * TK_STRIDE;
+    for (int i = t; i < TK_COPIES * TK_STRIDE; i += 256) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (t + 256 * c < nch) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) atomicAdd(&hc[key(c, j) >> 7], 1u);
+      }
+    __syncthreads();
+    // pass 1: thread t owns exponent bin 255 - t (descending keys)
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < TK_COPIES; ++k) cnt += (int)hist[k * TK_STRIDE + 255 - t];
+    int2 sc = tk_block_scan(cnt, wtot, t);
+    if (sc.x - cnt < keep && keep <= sc.x) { sel[0] = 255 - t; sel[1] = sc.x - cnt; }
+    // clear the mantissa bins (every thread has read its exponent bin above)
+    for (int i = t; i < TK_COPIES * 128; i += 256) hist[(i >> 7) * TK_STRIDE + (i & 127)] = 0u;
+    __syncthreads();
+    const uint32_t e = (uint32_t)sel[0];
+    const int above = sel[1];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (t + 256 * c < nch) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t k = key(c, j);
+          if ((k >> 7) == e) atomicAdd(&hc[k & 127u], 1u);
+        }
+      }
+    __syncthreads();
+    // pass 2: thread t < 128 owns mantissa bin 127 - t
+    cnt = 0;
+    if (t < 128) {
+#pragma unroll
+      for (int k = 0; k < TK_COPIES; ++k) cnt += (int)hist[k * TK_STRIDE + 127 - t];
+    }
+    sc = tk_block_scan(cnt, wtot, t);
+    const int ex = above + sc.x - cnt;
+    if (t < 128 && ex < keep && keep <= above + sc.x) { sel[0] = 127 - t; sel[1] = ex; }
+    __syncthreads();
+    T = (e << 7) | (uint32_t)sel[0];
+    need = keep - sel[1];                          // >= 1 ties at T survive, lowest index first
+  }
+
+  // tie ranks in index order: chunk c of all threads, then chunk c + 1
+  int rank[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) rank[c] = 0;
+  if (!all && keep > 0) {
+    int tc[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      tc[c] = 0;
+      if (t + 256 * c < nch) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tc[c] += key(c, j) == T ? 1 : 0;
+      }
+    }
+    int incl[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      incl[c] = tc[c];
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl[c], d, 64);
+        if (lane >= d) incl[c] += o;
+      }
+      if (lane == 63) wtot_v[c][wave] = incl[c];
+    }
+    __syncthreads();
+    int base = 0;                                  // ties of all earlier chunks
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      int off = 0, tot = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        off += q < wave ? wtot_v[c][q] : 0;
+        tot += wtot_v[c][q];
+      }
+      rank[c] = base + off + incl[c] - tc[c];
+      base += tot;
+    }
+  }
+
+  uint32_t* mrow = mask ? mask + (long)row * (K >> 5) : nullptr;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = t + 256 * c;
+    if (ch >= nch) continue;                       // whole groups of 4 threads drop out together
+    uint32_t kb = 0u;
+    int r = rank[c];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t k = key(c, j);
+      bool keepj = all || k > T;
+      if (!all && k == T) { keepj = r < need; ++r; }
+      kb |= (keepj ? 1u : 0u) << j;
+    }
+    uint32_t rr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float y = ((kb >> j) & 1u) ? val(c, j) * s : 0.0f;
+      rr[j] = bl_f2u(y + 12582912.0f);             // low byte = rint(y) in two's complement
+    }
+    const uint32_t lo = __builtin_amdgcn_perm(rr[1], rr[0], 0x0C0C0400u) | __builtin_amdgcn_perm(rr[3], rr[2], 0x04000C0Cu);
+    const uint32_t hi = __builtin_amdgcn_perm(rr[5], rr[4], 0x0C0C0400u) | __builtin_amdgcn_perm(rr[7], rr[6], 0x04000C0Cu);
+    reinterpret_cast<uint2*>(codes + (long)row * K)[ch] = make_uint2(lo, hi);
+    if (mrow) {
+      uint32_t mw = kb << (8 * (t & 3));
+      mw |= __shfl_xor(mw, 1, 64);
+      mw |= __shfl_xor(mw, 2, 64);
+      if ((t & 3) == 0) mrow[ch >> 2] = mw;
+    }
+  }
+  if (t == 0) scale[row] = gamma / 127.0f;
+}
+
 // ============================================================================ block-per-row kernel
 // Quantizers without a Top-K mask (INT4 nibbles or E3M2 tiles, FP4 both scale modes, INT8 of the
 // whole row), one 256-thread block per row: thread t owns the 8-element chunks t, t + 256, ... of
@@ -465,187 +664,6 @@ __global__ __launch_bounds__(256) void k_quant_blk(const void* __restrict__ x, i
     }
     if (t == 0) scale[row] = gamma / 127.0f;
   }
-}
-
-// ============================================================================ Top-K + INT8 of bf16 rows
-// INT8 absmax with the Top-K mask for bf16 rows of up to 4096 elements, on integer keys: the key of
-// |x| is its 15 magnitude bits (exponent << 7 | mantissa), so comparisons of magnitudes are integer
-// comparisons. The threshold key T (the largest key with count(key >= T) >= keep) comes from two
-// radix passes over per-wave LDS histograms: exponents, then the mantissas of the keys whose exponent
-// is T's. Four copies of each histogram (one per lane quarter, on distinct banks) keep the atomic
-// increments of equal exponents apart. Codes: RN32(x * s) is rounded to an integer by adding
-// 1.5 * 2^23 (round to nearest even; |x * s| < 127.5 always, so no clamping is needed) and its low
-// byte is the two's-complement code.
-constexpr int HSTRIDE = 272;                      // words per histogram copy (256 bins + 16 pad)
-
-template <int NGMAX>
-__global__ __launch_bounds__(256) void k_topk_bf16(const uint16_t* __restrict__ x, int M, int K, long ldx, int keep,
-                                                   float eps, const float* __restrict__ hint,
-                                                   uint8_t* __restrict__ codes, float* __restrict__ scale,
-                                                   uint32_t* __restrict__ mask) {
-  __shared__ uint32_t hist[4][4 * HSTRIDE];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= M) return;                         // wave-uniform; no block barriers below
-  const int NG = K >> 8;
-  uint2 w[NGMAX];
-  const uint16_t* xr = x + (long)row * ldx + 4 * lane;
-#pragma unroll
-  for (int g = 0; g < NGMAX; ++g)
-    if (g < NG) w[g] = *reinterpret_cast<const uint2*>(xr + 256 * g);
-  auto key = [&](int g, int j) -> uint32_t {
-    const uint32_t d = (j < 2) ? w[g].x : w[g].y;
-    return ((j & 1) ? (d >> 16) : d) & 0x7FFFu;
-  };
-  auto val = [&](int g, int j) -> float {
-    const uint32_t d = (j < 2) ? w[g].x : w[g].y;
-    return bl_u2f((j & 1) ? (d & 0xFFFF0000u) : (d << 16));
-  };
-
-  float gamma;
-  if (hint) {
-    gamma = hint[row];
-  } else {
-    uint32_t mx = 0u;
-#pragma unroll
-    for (int g = 0; g < NGMAX; ++g)
-      if (g < NG) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = max(mx, key(g, j));
-      }
-    gamma = bl_u2f(bl_wave_max_u(mx) << 16);
-  }
-  const float s = 127.0f / (gamma + eps);
-  const bool all = keep < 0 || keep >= K;
-
-  uint32_t T = all ? 0u : 0x8000u;              // 0x8000: above every key (keep == 0)
-  int need = 0;
-  if (!all && keep > 0) {
-    uint32_t* h = hist[wave];
-    uint32_t* hc = h + (lane & 3) * HSTRIDE;
-    for (int i = lane; i < 4 * HSTRIDE; i += 64) h[i] = 0u;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int g = 0; g < NGMAX; ++g)
-      if (g < NG) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) atomicAdd(&hc[key(g, j) >> 7], 1u);
-      }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // pass 1: lane L owns exponent bins 255-4L .. 252-4L (descending)
-    int c1[4], own = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = 255 - 4 * lane - i;
-      c1[i] = (int)(h[b] + h[HSTRIDE + b] + h[2 * HSTRIDE + b] + h[3 * HSTRIDE + b]);
-      own += c1[i];
-    }
-    int incl = own;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    int excl = incl - own;
-    const int L1 = __builtin_ctzll(__ballot(excl < keep && keep <= incl));
-    int e = 0, above = 0;
-    {
-      int run = excl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (run + c1[i] >= keep) { e = 255 - 4 * lane - i; above = run; break; }
-        run += c1[i];
-      }
-    }
-    e = __shfl(e, L1, 64);
-    above = __shfl(above, L1, 64);
-    // pass 2: mantissas of the keys with exponent e (bins 0..127 of the same copies, cleared)
-    __builtin_amdgcn_wave_barrier();
-    for (int i = lane; i < 4 * 128; i += 64) h[(i >> 7) * HSTRIDE + (i & 127)] = 0u;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int g = 0; g < NGMAX; ++g)
-      if (g < NG) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t k = key(g, j);
-          if ((int)(k >> 7) == e) atomicAdd(&hc[k & 127u], 1u);
-        }
-      }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    int c2[2];
-    own = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int b = 127 - 2 * lane - i;
-      c2[i] = (int)(h[b] + h[HSTRIDE + b] + h[2 * HSTRIDE + b] + h[3 * HSTRIDE + b]);
-      own += c2[i];
-    }
-    incl = own;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    excl = above + incl - own;
-    const int L2 = __builtin_ctzll(__ballot(excl < keep && keep <= above + incl));
-    int m = 0, gt = 0;
-    {
-      int run = excl;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (run + c2[i] >= keep) { m = 127 - 2 * lane - i; gt = run; break; }
-        run += c2[i];
-      }
-    }
-    m = __shfl(m, L2, 64);
-    gt = __shfl(gt, L2, 64);
-    T = ((uint32_t)e << 7) | (uint32_t)m;
-    need = keep - gt;                             // >= 1 ties at T survive, lowest index first
-  }
-
-  uint32_t* crow = reinterpret_cast<uint32_t*>(codes + (long)row * K) + lane;
-  uint32_t* mrow = mask ? mask + (long)row * (K >> 5) : nullptr;
-  int tie_base = 0;
-#pragma unroll
-  for (int g = 0; g < NGMAX; ++g)
-    if (g < NG) {
-      uint32_t kb = 0u, eq = 0u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t k = key(g, j);
-        kb |= (all || k > T ? 1u : 0u) << j;
-        eq |= (k == T ? 1u : 0u) << j;
-      }
-      if (!all && __ballot(eq != 0u) != 0ull) {
-        // ties at T in this group: rank = ties of earlier groups + of lower lanes + of lower j
-        const int cnt = __popc(eq);
-        int incl_t = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int o = __shfl_up(incl_t, d, 64);
-          if (lane >= d) incl_t += o;
-        }
-        int rank = tie_base + incl_t - cnt;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if ((eq >> j) & 1u) { kb |= (rank < need ? 1u : 0u) << j; ++rank; }
-        tie_base += __shfl(incl_t, 63, 64);
-      }
-      uint32_t r[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float y = ((kb >> j) & 1u) ? val(g, j) * s : 0.0f;
-        r[j] = bl_f2u(y + 12582912.0f);           // low byte = rint(y) in two's complement
-      }
-      crow[64 * g] = __builtin_amdgcn_perm(r[1], r[0], 0x0C0C0400u) | __builtin_amdgcn_perm(r[3], r[2], 0x04000C0Cu);
-      if (mrow) store_mask_nibble(mrow, g, lane, kb);
-    }
-  if (lane == 0) scale[row] = gamma / 127.0f;
 }
 
 // ============================================================================ streaming kernels
@@ -999,13 +1017,18 @@ hipError_t launch_fmt(const void* x, int M, int K, long ldx, int keep, float eps
   }
   if constexpr (FMT == BL_ACT_INT8 && !IN_F32) {
     const uint16_t* xb = static_cast<const uint16_t*>(x);
-    if (NG <= 4)
-      hipLaunchKernelGGL((k_topk_bf16<4>), grid, block, 0, st, xb, M, K, ldx, keep, eps, hint, codes, scale, mask);
-    else if (NG <= 16)
-      hipLaunchKernelGGL((k_topk_bf16<16>), grid, block, 0, st, xb, M, K, ldx, keep, eps, hint, codes, scale, mask);
-    else
-      hipLaunchKernelGGL((k_quant_stream<FMT, IN_F32>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
-                         mask);
+    if (K <= 8192) {
+      const int per = (K / 8 + 255) / 256;
+      if (per <= 1)
+        hipLaunchKernelGGL((k_topk_blk<1>), dim3(M), block, 0, st, xb, M, K, ldx, keep, eps, hint, codes, scale, mask);
+      else if (per <= 2)
+        hipLaunchKernelGGL((k_topk_blk<2>), dim3(M), block, 0, st, xb, M, K, ldx, keep, eps, hint, codes, scale, mask);
+      else
+        hipLaunchKernelGGL((k_topk_blk<4>), dim3(M), block, 0, st, xb, M, K, ldx, keep, eps, hint, codes, scale, mask);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((k_quant_stream<FMT, IN_F32>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
+                       mask);
   } else {
     if (NG <= 4)
       hipLaunchKernelGGL((k_quant_res<FMT, IN_F32, 4>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
