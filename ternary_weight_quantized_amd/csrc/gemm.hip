@@ -46,6 +46,9 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 
 // ----------------------------------------------------------------------------- A storage per format
 constexpr int NST = 4;   // stage buffers (three steps in flight)
+#ifndef I8_ROWSTORE
+#define I8_ROWSTORE 1    // int8-core GEMM: whole-row output stores through LDS (1) or direct (0)
+#endif
 #ifndef MX_BM
 #define MX_BM 128        // FP6/FP4 GEMM block rows: 128 (two blocks per CU) or 256 (one)
 #endif
@@ -203,9 +206,8 @@ __device__ __forceinline__ void tile_of(int b, int ntm, int ntn, int* tm, int* t
 // a lane's four columns are all in range or all out of range. val(mtx, v) is the exact sum of code
 // products of matrix mtx for column n + v.
 template <int EPI, typename ValFn>
-__device__ __forceinline__ void epilogue_cols(int m, int n, bool ok, float sc, float sc2, float* __restrict__ Y,
-                                              long ldy, const float4& res, float& rmax, ValFn val) {
-  float o[4];
+__device__ __forceinline__ void epilogue_vals(bool ok, float sc, float sc2, const float4& res, float& rmax, ValFn val,
+                                              float (&o)[4]) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const float y0 = val(0, v) * sc;
@@ -221,7 +223,42 @@ __device__ __forceinline__ void epilogue_cols(int m, int n, bool ok, float sc, f
       o[v] = y0;
     }
   }
+}
+
+template <int EPI, typename ValFn>
+__device__ __forceinline__ void epilogue_cols(int m, int n, bool ok, float sc, float sc2, float* __restrict__ Y,
+                                              long ldy, const float4& res, float& rmax, ValFn val) {
+  float o[4];
+  epilogue_vals<EPI>(ok, sc, sc2, res, rmax, val, o);
   if (ok) *reinterpret_cast<float4*>(Y + (long)m * ldy + n) = make_float4(o[0], o[1], o[2], o[3]);
+}
+
+// Stores one 16-row subtile of a wave's outputs (SN tiles of 16 columns) through LDS so that every
+// store instruction writes whole rows: lane (r, g) holds row r, columns 4g .. 4g + 3 of each tile;
+// the subtile goes to the wave's LDS region in that layout and comes back as two rows of 16 SN
+// contiguous floats per instruction (16-byte pieces, lanes 0..31 row 2i, lanes 32..63 row 2i + 1).
+template <int SN>
+__device__ __forceinline__ void store_subtile_rows(float* __restrict__ Y, long ldy, int M, int N, int m0, int n0,
+                                                   const float (&o)[SN][4], float* __restrict__ region, int lane) {
+  constexpr int RS = 16 * SN + 4;                  // row stride in floats (4 pad floats)
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < SN; ++t)
+    *reinterpret_cast<float4*>(region + r * RS + 16 * t + 4 * g) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  constexpr int LPR = 4 * SN;                      // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;                    // rows per instruction
+  const int rr = lane / LPR, cc = lane % LPR;
+#pragma unroll
+  for (int i = 0; i < 16 / RPI; ++i) {
+    const int row = RPI * i + rr;
+    const float4 q = *reinterpret_cast<const float4*>(region + row * RS + 4 * cc);
+    const int m = m0 + row, n = n0 + 4 * cc;
+    if (m < M && n < N) *reinterpret_cast<float4*>(Y + (long)m * ldy + n) = q;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();                 // the region is rewritten by the next subtile
 }
 
 template <int FMT, int EPI, int BM0>
@@ -338,6 +375,7 @@ __global__ __launch_bounds__(256, (BM0 == 128 ? 2 : 1)) void k_gemm_mx(
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the trailing (unused) loads land before the waves end
+  lds_barrier();                               // every wave is done with the stage buffers (reused below)
 
   // fp32 epilogue: the matrix-core sum is 2*sum(c t) (E3M2) or sum(2e t) = sum(doubled code * t)
   // (E2M1); x 0.5 is exact and gives sum(c t), respectively the half-unit count of the oracle.
@@ -359,11 +397,24 @@ __global__ __launch_bounds__(256, (BM0 == 128 ? 2 : 1)) void k_gemm_mx(
       }
     }
     float rmax = 0.f;
+    float o[SN][4];
 #pragma unroll
     for (int t = 0; t < SN; ++t) {
       const int n = nw0 + 16 * t;
-      epilogue_cols<EPI>(m, n, mok && n < N, sc, sc2, Y, ldy, res[t], rmax,
-                         [&](int mtx, int v) { return acc[mtx][s][t][v] * 0.5f; });
+      epilogue_vals<EPI>(mok && n < N, sc, sc2, res[t], rmax, [&](int mtx, int v) { return acc[mtx][s][t][v] * 0.5f; },
+                         o[t]);
+    }
+    if constexpr (EPI == BL_EPI_RELU2_GLU) {
+      // 4 tiles per subtile: the direct 64-byte row pieces measured faster than the staged rows
+#pragma unroll
+      for (int t = 0; t < SN; ++t) {
+        const int n = nw0 + 16 * t;
+        if (mok && n < N) *reinterpret_cast<float4*>(Y + (long)m * ldy + n) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+      }
+    } else {
+      // whole-row stores through the wave's LDS region
+      store_subtile_rows<SN>(Y, ldy, M, N, m0 + wm * SM * 16 + 16 * s, n0 + wn * SN * 16, o,
+                             reinterpret_cast<float*>(smem) + wave * (16 * (16 * SN + 4)), lane);
     }
     if constexpr (EPI == BL_EPI_RELU2_GLU) {
       if (rowmax) {
@@ -495,6 +546,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_i8(const uint8_t* __restrict__ 
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();                               // every wave is done with the stage buffers (reused below)
 
   const float alpha = *walpha;
   const float alpha2 = C::GLU ? *w2alpha : 0.f;
@@ -515,11 +567,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_i8(const uint8_t* __restrict__ 
       }
     }
     float rmax = 0.f;
+    if constexpr (EPI == BL_EPI_RELU2_GLU || I8_ROWSTORE == 0) {
 #pragma unroll
-    for (int t = 0; t < SN; ++t) {
-      const int n = nw0 + 16 * t;
-      epilogue_cols<EPI>(m, n, mok && n < N, sc, sc2, Y, ldy, res[t], rmax,
-                         [&](int mtx, int v) { return (float)(acc[mtx][s][t][v] >> SHIFT); });
+      for (int t = 0; t < SN; ++t) {
+        const int n = nw0 + 16 * t;
+        epilogue_cols<EPI>(m, n, mok && n < N, sc, sc2, Y, ldy, res[t], rmax,
+                           [&](int mtx, int v) { return (float)(acc[mtx][s][t][v] >> SHIFT); });
+      }
+    } else {
+      float o[SN][4];
+#pragma unroll
+      for (int t = 0; t < SN; ++t) {
+        const int n = nw0 + 16 * t;
+        epilogue_vals<EPI>(mok && n < N, sc, sc2, res[t], rmax,
+                           [&](int mtx, int v) { return (float)(acc[mtx][s][t][v] >> SHIFT); }, o[t]);
+      }
+      store_subtile_rows<SN>(Y, ldy, M, N, m0 + wm * SM * 16 + 16 * s, n0 + wn * SN * 16, o,
+                             reinterpret_cast<float*>(smem) + wave * (16 * (16 * SN + 4)), lane);
     }
     if constexpr (EPI == BL_EPI_RELU2_GLU) {
       if (rowmax) {
