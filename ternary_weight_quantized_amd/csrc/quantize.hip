@@ -6,11 +6,16 @@
 //    FP4 MinMax E2M1, paper Eq. 8-9) and "Sparsification Pipeline for Outlier-Heavy
 //    Intermediate States" (Top-K mask and INT8 absmax, paper Eq. 1).
 //
-// One wave64 owns one token row; a 256-thread block holds four rows. A lane owns four
-// consecutive elements of every 256-element group of the row (group g, elements
-// 256g + 4*lane .. +3), so each load and store of a wave is one contiguous segment.
-// Rows of up to 4096 elements stay in registers between the reduction and the quantization
-// ("resident" kernels); longer rows are read again from global memory ("streaming" kernels).
+// Kernels, by case:
+//  - k_quant_blk: every format without a Top-K mask, rows of up to 16384 elements. One 256-thread
+//    block per row; thread t owns the 8-element chunks t, t + 256, ... of the row.
+//  - k_topk_blk: INT8 with the Top-K mask for bf16 rows of up to 8192 elements, one block per row.
+//  - k_quant_res / k_quant_stream: the remaining cases (float32 rows with a Top-K mask, longer
+//    rows). One wave64 owns one token row, four rows per block; a lane owns four consecutive
+//    elements of every 256-element group (group g, elements 256g + 4*lane .. +3). Rows of up to
+//    4096 elements stay in registers between the reduction and the quantization ("resident");
+//    longer rows are read again from global memory ("streaming").
+//  - k_tensor_*: the statistics of the per-tensor variant.
 #include <algorithm>
 
 #include "bl_common.h"
