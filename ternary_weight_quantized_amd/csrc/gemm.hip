@@ -352,6 +352,9 @@ __global__ __launch_bounds__(256, (BM0 == 128 ? 2 : 1)) void k_gemm_mx(
       }
     };
     v8i a_next = load_a(0);
+    // the matrix-core phase runs at raised wave priority: while one wave of the CU issues its
+    // MFMA chain, the sibling block's waves (stage waits, fragment reads, DMA issue) yield to it
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < SM; ++s) {
       const v8i a = a_next;
@@ -373,6 +376,7 @@ __global__ __launch_bounds__(256, (BM0 == 128 ? 2 : 1)) void k_gemm_mx(
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the trailing (unused) loads land before the waves end
   lds_barrier();                               // every wave is done with the stage buffers (reused below)
