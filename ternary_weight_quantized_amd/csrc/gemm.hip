@@ -315,6 +315,13 @@ __global__ __launch_bounds__(256, (BM0 == 128 ? 2 : 1)) void k_gemm_mx(
 #pragma unroll
   for (int p = 0; p < 3; ++p) aoff[p] = FP6 ? a_off<FMT>(arow0, 24 * g4 + 8 * p) : a_off<FMT>(arow0, 16 * g4);
 
+  // epilogue scalars are fetched before the K loop, which hides their latency
+  float dsv[SM];
+#pragma unroll
+  for (int s = 0; s < SM; ++s) dsv[s] = ascale[min(m0 + wm * SM * 16 + 16 * s + r16, M - 1)];
+  const float alpha = *walpha;
+  const float alpha2 = C::GLU ? *w2alpha : 0.f;
+
   P plan;
   plan.init(arow, m0, M, n0, NG, KS, wave, lane);
   const uint32_t lds0 = lds_addr_of(smem);
@@ -380,18 +387,18 @@ __global__ __launch_bounds__(256, (BM0 == 128 ? 2 : 1)) void k_gemm_mx(
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the trailing (unused) loads land before the waves end
   lds_barrier();                               // every wave is done with the stage buffers (reused below)
+  // the epilogue keeps the raised priority: its LDS staging and stores go ahead of the other
+  // block's loads and fragment reads
+  __builtin_amdgcn_s_setprio(1);
 
   // fp32 epilogue: the matrix-core sum is 2*sum(c t) (E3M2) or sum(2e t) = sum(doubled code * t)
   // (E2M1); x 0.5 is exact and gives sum(c t), respectively the half-unit count of the oracle.
-  const float alpha = *walpha;
-  const float alpha2 = C::GLU ? *w2alpha : 0.f;
   const int nw0 = n0 + wn * SN * 16 + 4 * g4;
 #pragma unroll
   for (int s = 0; s < SM; ++s) {
     const int m = m0 + wm * SM * 16 + 16 * s + r16;
     const bool mok = m < M;
-    const float ds = ascale[mok ? m : M - 1];
-    const float sc = ds * alpha, sc2 = ds * alpha2;
+    const float sc = dsv[s] * alpha, sc2 = dsv[s] * alpha2;
     float4 res[SN];
     if constexpr (EPI == BL_EPI_RESIDUAL) {
 #pragma unroll
