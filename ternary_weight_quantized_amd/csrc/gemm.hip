@@ -14,7 +14,8 @@
 // matrix cores; one barrier per step both publishes a step and frees the buffer refilled next.
 //
 //  k_gemm_mx  FP6 x FP4 / FP4 x FP4 (v_mfma_scale_f32_16x16x128_f8f6f4, unit block scales).
-//             4 waves, 256 x 256 block, 128 x 128 per wave. A is used as stored (E3M2 or E2M1);
+//             4 waves, 128 x 256 block (128 x 128 per matrix for the GLU), 64 x 128 per wave, two
+//             blocks per CU. A is used as stored (E3M2 or E2M1);
 //             a ternary code placed in bits 2..3 of a nibble reads as E2M1 +-2.0, so the fp32 sum
 //             is 2*sum(c t) for E3M2 codes and sum(2e t) for E2M1 codes: integers below 2^24, exact.
 //  k_gemm_i8  int8 cores (v_mfma_i32_16x16x64_i8) for INT4 nibbles and INT8 codes. 4 waves, 128 x 256
@@ -334,8 +335,6 @@ __global__ __launch_bounds__(256, (BM0 == 128 ? 2 : 1)) void k_gemm_mx(
     // step ks has landed when at most NST-2 later steps are still outstanding
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * P::LOADS));
     lds_barrier();
-    // refill the buffer every wave finished reading in step ks-1
-    plan.issue(lds0 + ((ks + NST - 1) % NST) * P::BYTES, A, Wm, min(ks + NST - 1, KS - 1), wave, lane);
 
     // weight words of the step, expanded right before their first MFMA (subtile 0)
     const uint8_t* Bs = cur + BM * F::ROW + (wn * SN) * 512 + 8 * lane;
@@ -359,6 +358,9 @@ __global__ __launch_bounds__(256, (BM0 == 128 ? 2 : 1)) void k_gemm_mx(
       }
     };
     v8i a_next = load_a(0);
+    // refill the buffer every wave finished reading in step ks-1; issued after this step's
+    // fragment reads, so that their LDS latency runs under the DMA issue
+    plan.issue(lds0 + ((ks + NST - 1) % NST) * P::BYTES, A, Wm, min(ks + NST - 1, KS - 1), wave, lane);
     // the matrix-core phase runs at raised wave priority: while one wave of the CU issues its
     // MFMA chain, the sibling block's waves (stage waits, fragment reads, DMA issue) yield to it
     __builtin_amdgcn_s_setprio(1);
@@ -505,7 +507,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_i8(const uint8_t* __restrict__ 
     const uint8_t* cur = smem + (ks % NS) * P::BYTES;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * P::LOADS));
     lds_barrier();
-    plan.issue(lds0 + ((ks + NS - 1) % NS) * P::BYTES, A, Wm, min(ks + NS - 1, KS - 1), wave, lane);
 
     // weight words of the step; each is expanded right before its first MFMA (subtile 0), so the
     // expansion overlaps the matrix cores instead of delaying the first MFMA of the step
@@ -524,6 +525,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_i8(const uint8_t* __restrict__ 
     };
     uint4 qn[2];
     load_a(0, qn);
+    // refill of the buffer freed in step ks-1, issued after this step's fragment reads
+    plan.issue(lds0 + ((ks + NS - 1) % NS) * P::BYTES, A, Wm, min(ks + NS - 1, KS - 1), wave, lane);
 #pragma unroll
     for (int s = 0; s < SM; ++s) {
       const uint4 q[2] = {qn[0], qn[1]};
