@@ -39,14 +39,39 @@ __device__ __forceinline__ int ceil_log2(int K) { return K <= 1 ? 0 : 32 - __clz
 // Accumulators of the absmean sum: double sum plus the exponent range of the nonzero terms.
 struct AbsSum {
   double s = 0.0;
-  uint32_t emax = 0u, emin = 0xFFu;
+  // largest magnitude bits, and smallest nonzero magnitude bits minus one (a zero gives 0xFFFFFFFF
+  // and never wins the minimum): two integer ops per element, no branch
+  uint32_t bmax = 0u, bmin1 = 0xFFFFFFFFu;
   __device__ __forceinline__ void add(float v) {
     const uint32_t b = bl_f2u(v) & 0x7FFFFFFFu;
     s += (double)bl_u2f(b);
-    const uint32_t e = b >> 23;
-    if (b) { emax = e > emax ? e : emax; emin = e < emin ? e : emin; }
+    bmax = b > bmax ? b : bmax;
+    bmin1 = b - 1u < bmin1 ? b - 1u : bmin1;
+  }
+  __device__ __forceinline__ void merge(const AbsSum& o) {
+    s += o.s;                          // exact whenever the span check holds for all the terms
+    bmax = o.bmax > bmax ? o.bmax : bmax;
+    bmin1 = o.bmin1 < bmin1 ? o.bmin1 : bmin1;
+  }
+  // biased exponents of the largest magnitude and of the smallest nonzero one, packed as
+  // (emax << 16) | (255 - emin), so that one packed 16-bit maximum reduces both; all zero -> emin 0xFF
+  __device__ __forceinline__ uint32_t exps() const {
+    const uint32_t emin = bmin1 == 0xFFFFFFFFu ? 0xFFu : (bmin1 + 1u) >> 23;
+    return ((bmax >> 23) << 16) | (255u - emin);
   }
 };
+__device__ __forceinline__ uint32_t exps_emax(uint32_t p) { return p >> 16; }
+__device__ __forceinline__ uint32_t exps_emin(uint32_t p) { return 255u - (p & 0xFFFFu); }
+// packed (emax, 255 - emin) maximum over the wave: both halves at once
+__device__ __forceinline__ uint32_t wave_max_exps(uint32_t p) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t q = __shfl_xor(p, o, 64);
+    p = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, p), __builtin_bit_cast(us2, q)));
+  }
+  return p;
+}
 
 // Exact-bins fallback for one wave: called only when the double sum might have rounded.
 __device__ __forceinline__ void bins_clear(unsigned long long* bins, int lane) {
@@ -182,7 +207,8 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
           for (int j = 0; j < 4; ++j) acc.add(v[g][j]);
         }
       double S = bl_wave_sum_d(acc.s);
-      const uint32_t emax = bl_wave_max_u(acc.emax), emin = bl_wave_min_u(acc.emin);
+      const uint32_t ex = wave_max_exps(acc.exps());
+      const uint32_t emax = exps_emax(ex), emin = exps_emin(ex);
       if (!sum_is_exact<IN_F32>(emax, emin, K)) {
         unsigned long long* b = bins[wave];
         bins_clear(b, lane);
@@ -566,7 +592,8 @@ __global__ __launch_bounds__(256) void k_quant_blk(const void* __restrict__ x, i
         for (int j = 0; j < 8; ++j) acc.add(v[c][j]);
       }
     const double ws = bl_wave_sum_d(acc.s);
-    const uint32_t emax = bl_wave_max_u(acc.emax), emin = bl_wave_min_u(acc.emin);
+    const uint32_t ex = wave_max_exps(acc.exps());
+    const uint32_t emax = exps_emax(ex), emin = exps_emin(ex);
     if (lane == 0) { wsum[wave] = ws; wa[wave] = emax; wb[wave] = emin; }
     __syncthreads();
     double S = wsum[0] + wsum[1] + wsum[2] + wsum[3];           // exact when the check below holds
@@ -697,7 +724,8 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
         for (int j = 0; j < 4; ++j) acc.add(v[j]);
       }
       double S = bl_wave_sum_d(acc.s);
-      const uint32_t emax = bl_wave_max_u(acc.emax), emin = bl_wave_min_u(acc.emin);
+      const uint32_t ex = wave_max_exps(acc.exps());
+      const uint32_t emax = exps_emax(ex), emin = exps_emin(ex);
       if (!sum_is_exact<IN_F32>(emax, emin, K)) {
         unsigned long long* b = bins[wave];
         bins_clear(b, lane);
@@ -923,11 +951,10 @@ __global__ __launch_bounds__(256) void k_tensor_reduce(const void* __restrict__ 
     AbsSum acc = accs[0];
 #pragma unroll
     for (int i = 1; i < 4; ++i) {
-      acc.s += accs[i].s;              // exact whenever the bound below holds for all the terms
-      acc.emax = accs[i].emax > acc.emax ? accs[i].emax : acc.emax;
-      acc.emin = accs[i].emin < acc.emin ? accs[i].emin : acc.emin;
+      acc.merge(accs[i]);
     }
-    const bool exact = sum_is_exact<IN_F32>(acc.emax, acc.emin, cnt) && acc.s < 1.0e38;
+    const uint32_t ex = acc.exps();
+    const bool exact = sum_is_exact<IN_F32>(exps_emax(ex), exps_emin(ex), cnt) && acc.s < 1.0e38;
     float hi = 0.f, mid = 0.f, lo = 0.f;
     if (exact) {
       hi = round_down_f32(acc.s);
