@@ -182,16 +182,3 @@ __device__ __forceinline__ int bl_roundclip(float v, float lo, float hi) {
   return (int)r;
 }
 
-// nearest E2M1 magnitude index of a non-negative float (ties to even mantissa, saturating at 6).
-// Midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 are exact binary32 values; a tie resolves to the even index.
-__device__ __forceinline__ uint32_t bl_e2m1_index(float a) {
-  uint32_t i = 0;
-  i += (a > 0.25f) ? 1u : 0u;   // 0 | 0.5 boundary: tie (== 0.25) -> 0 (even)
-  i += (a >= 0.75f) ? 1u : 0u;  // 0.5 | 1: tie -> 1.0 (index 2, even)
-  i += (a > 1.25f) ? 1u : 0u;   // 1 | 1.5: tie -> 1.0 (index 2)
-  i += (a >= 1.75f) ? 1u : 0u;  // 1.5 | 2: tie -> 2.0 (index 4)
-  i += (a > 2.5f) ? 1u : 0u;    // 2 | 3: tie -> 2.0 (index 4)
-  i += (a >= 3.5f) ? 1u : 0u;   // 3 | 4: tie -> 4.0 (index 6)
-  i += (a > 5.0f) ? 1u : 0u;    // 4 | 6: tie -> 4.0 (index 6)
-  return i;
-}

@@ -105,25 +105,41 @@ __device__ __forceinline__ bool sum_is_exact(uint32_t emax, uint32_t emin, int K
 __device__ __forceinline__ uint32_t code_int4(float v, float s) {
   return (uint32_t)bl_roundclip(v * s, -8.f, 7.f) & 0xFu;
 }
-__device__ __forceinline__ uint32_t code_fp4(float v, float s) {
-  const float p = v * s;
-  const uint32_t idx = bl_e2m1_index(fabsf(p));
-  const uint32_t neg = (bl_f2u(p) >> 31) & (idx != 0u ? 1u : 0u);
-  return idx | (neg << 3);
+// FP4 E2M1 codes of p = RN32(v * s), two per byte (the first in the low nibble), through the CDNA4
+// conversion v_cvt_scalef32_pk_fp4_f32 at scale 1: it rounds to nearest with ties to the even
+// mantissa and saturates at 6 (checked against the threshold form on every binary32 value from
+// 2^-10 to 2^6 and on zeros, subnormals and values up to the largest finite one). It keeps the
+// sign of a negative value that rounds to zero (code 8); fp4_clear_negzero turns those into 0.
+__device__ __forceinline__ uint32_t fp4_clear_negzero(uint32_t w) {
+  const uint32_t m = w & 0x77777777u;                 // magnitudes; m + 7 carries into bit 3 iff m != 0
+  return m | (w & (m + 0x77777777u) & 0x88888888u);
+}
+__device__ __forceinline__ uint32_t codes_fp4_4(float a, float b, float c, float d, float s) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a * s, b * s, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c * s, d * s, 1.0f, 1);
+  return fp4_clear_negzero(w & 0xFFFFu);
+}
+__device__ __forceinline__ uint32_t codes_fp4_8(const float (&v)[8], float s) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0] * s, v[1] * s, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * s, v[3] * s, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * s, v[5] * s, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * s, v[7] * s, 1.0f, 3);
+  return fp4_clear_negzero(w);
 }
 __device__ __forceinline__ uint32_t code_int8(float v, float s) {
   return (uint32_t)bl_roundclip(v * s, -128.f, 127.f) & 0xFFu;
 }
-// INT4 code -> its exact FP6 E3M2 bit pattern (sign bit 5, exponent bias 3, 2 mantissa bits).
-// Magnitudes 0..8 encode as 00 0C 10 12 14 15 16 17 18 (five bits each, packed in one constant).
+// INT4 code c = RoundClip(v * s, -8, 7) -> its exact FP6 E3M2 bit pattern (sign bit 5, exponent bias
+// 3, 2 mantissa bits), read off the binary32 form of the rounded value: for |c| >= 1 the E3M2
+// exponent and mantissa are the binary32 exponent - 124 and its top two mantissa bits, so the
+// pattern is (|bits| >> 21) - 496; c = 0 gives 0 (the + 0 turns a -0 into +0).
 __device__ __forceinline__ uint32_t code_e3m2(float v, float s) {
-  const int c = bl_roundclip(v * s, -8.f, 7.f);
-  const uint32_t a = (uint32_t)(c < 0 ? -c : c);
-  constexpr unsigned long long MAG = (0x00ull) | (0x0Cull << 5) | (0x10ull << 10) | (0x12ull << 15) |
-                                     (0x14ull << 20) | (0x15ull << 25) | (0x16ull << 30) | (0x17ull << 35) |
-                                     (0x18ull << 40);
-  return (uint32_t)((MAG >> (5 * a)) & 31ull) | (c < 0 ? 0x20u : 0u);
+  const float r = fminf(fmaxf(__builtin_rintf(v * s), -8.f), 7.f) + 0.0f;
+  const uint32_t b = bl_f2u(r);
+  const int mag = (int)((b & 0x7FFFFFFFu) >> 21) - 496;
+  return (uint32_t)(mag > 0 ? mag : 0) | ((b >> 26) & 0x20u);
 }
+
 // Store the 4 codes (24 bits, code j at bits 6j) of elements 256g + 4 lane .. +3 of row m into the
 // tiled E3M2 layout (16 rows x 128 codes per 1536-byte tile, 96 bytes per row, code k at bits 6k):
 // four lanes make 12 bytes, written as three dwords.
@@ -265,8 +281,7 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
 #pragma unroll
       for (int g = 0; g < NGMAX; ++g)
         if (g < NG) {
-          const uint32_t c = code_fp4(v[g][0], s) | (code_fp4(v[g][1], s) << 4) |
-                             (code_fp4(v[g][2], s) << 8) | (code_fp4(v[g][3], s) << 12);
+          const uint32_t c = codes_fp4_4(v[g][0], v[g][1], v[g][2], v[g][3], s);
           crow[64 * g] = (uint16_t)c;
         }
       if (lane == 0) scale[row] = dscale;
@@ -647,10 +662,12 @@ __global__ __launch_bounds__(256) void k_quant_blk(const void* __restrict__ x, i
         reinterpret_cast<uint32_t*>(codes + (long)row * (K >> 1))[ch] = w;
       } else {
         // 8 codes x 6 bits; a thread pair (chunks 2i, 2i+1 of a 128-code group) writes 12 bytes
-        unsigned long long v48 = 0ull;
+        uint32_t e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v48 |= (unsigned long long)code_e3m2(v[c][j], s) << (6 * j);
-        const uint32_t lo = (uint32_t)v48, hi = (uint32_t)(v48 >> 32);
+        for (int j = 0; j < 8; ++j) e[j] = code_e3m2(v[c][j], s);
+        // the 48 bits (code j at bits 6 j) as two words
+        const uint32_t lo = e[0] | (e[1] << 6) | (e[2] << 12) | (e[3] << 18) | (e[4] << 24) | (e[5] << 30);
+        const uint32_t hi = (e[5] >> 2) | (e[6] << 4) | (e[7] << 10);
         const uint32_t plo = __shfl_xor(lo, 1, 64);
         const int k = 8 * ch;
         const long tile = (long)(row >> 4) * (K >> 7) + (k >> 7);
@@ -673,9 +690,7 @@ __global__ __launch_bounds__(256) void k_quant_blk(const void* __restrict__ x, i
     for (int c = 0; c < NCH; ++c) {
       const int ch = t + 256 * c;
       if (ch >= nch) continue;
-      uint32_t w = 0u;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) w |= code_fp4(v[c][j], s) << (4 * j);
+      const uint32_t w = codes_fp4_8(v[c], s);
       reinterpret_cast<uint32_t*>(codes + (long)row * (K >> 1))[ch] = w;
     }
     if (t == 0) scale[row] = dscale;
@@ -778,8 +793,7 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
       for (int g = 0; g < NG; ++g) {
         float v[4];
         load4<IN_F32>(x, base + 256 * g, v);
-        crow[64 * g] = (uint16_t)(code_fp4(v[0], s) | (code_fp4(v[1], s) << 4) |
-                                   (code_fp4(v[2], s) << 8) | (code_fp4(v[3], s) << 12));
+        crow[64 * g] = (uint16_t)codes_fp4_4(v[0], v[1], v[2], v[3], s);
       }
       if (lane == 0) scale[row] = dscale;
     } else {

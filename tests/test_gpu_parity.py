@@ -123,6 +123,55 @@ def test_quantize_fp4_pow2(M, K, f32):
     np.testing.assert_array_equal(host(scale), d)
 
 
+FP4_TIES = [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6), (6.0, 7)]
+
+
+def fp4_boundary_row(K, f32):
+    """A row whose largest magnitude is 6, so that the power-of-two FP4 scale is exactly 1 and every
+    element reaches the E2M1 rounding unchanged: the grid midpoints (ties) and the maximum, their
+    neighbours one unit in the last place away, the negatives of all of them, negative values that
+    round to zero, -0 and subnormals. Returns the row and the positions of the ties and of their
+    negatives."""
+    vals, pos = [], []
+    for t, _ in FP4_TIES:
+        pos.append(len(vals))
+        if f32:
+            near = [np.nextafter(np.float32(t), np.float32(0)), np.nextafter(np.float32(t), np.float32(7))]
+        else:
+            b = int(to_bf16_bits(np.array([t]))[0])
+            near = list(x_f32(np.array([b - 1, b + 1], np.uint16)))
+        vals += [t] + [v for v in near if abs(v) <= 6.0]
+    n = len(vals)
+    vals += [-v for v in vals]
+    vals += [-0.0, -1e-30, -0.1, -0.25, 2.0 ** -130, -(2.0 ** -130)]
+    row = np.zeros(K)
+    row[:len(vals)] = vals
+    return row, pos, [n + p for p in pos], 2 * n
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_quantize_fp4_rounding_boundaries(f32):
+    """E2M1 rounding at every tie and next to it: nearest, ties to the even mantissa, negative
+    values that round to zero give code 0."""
+    torch_cuda()
+    K = 256
+    row, pos, neg, tail = fp4_boundary_row(K, f32)
+    rows = np.stack([row, row[::-1].copy()])
+    x = rows.astype(np.float32) if f32 else to_bf16_bits(rows)
+    nib, _, d, _ = O.quant_fp4(x_f32(x), EPS, pow2=True)
+    np.testing.assert_array_equal(d, np.ones(2, np.float32))
+    # the oracle against the rule itself at the ties, at their negatives and at the signed zeros
+    for (t, code), p, q in zip(FP4_TIES, pos, neg):
+        assert nib[0, p] == code, (t, nib[0, p])
+        assert nib[0, q] == (code | 8 if code else 0), (-t, nib[0, q])
+    np.testing.assert_array_equal(nib[0, tail:tail + 6], np.zeros(6, np.uint8))
+    for fmt, pow2 in (("fp4_pow2", True), ("fp4", False)):
+        codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), fmt, eps=EPS)
+        nib_o, _, d_o, _ = O.quant_fp4(x_f32(x), EPS, pow2=pow2)
+        np.testing.assert_array_equal(nibbles(host(codes)), nib_o)
+        np.testing.assert_array_equal(host(scale), d_o)
+
+
 @pytest.mark.parametrize("fmt", ["int4", "int4_e3m2", "fp4", "fp4_pow2", "int8"])
 @pytest.mark.parametrize("f32", [False, True])
 @pytest.mark.parametrize("M,K", [(1, 256), (7, 768), (33, 4096), (130, 1024), (5, 8192)])
