@@ -144,8 +144,10 @@ __device__ inline double bl_limbs_to_double(const uint32_t (&L)[12]) {
   return ldexp((double)mant, P - 52 - 149);
 }
 
-__device__ inline double bl_bins_to_double_block(const unsigned long long* bins, unsigned long long* lds,
-                                                 double* out) {
+// Block-parallel first half of the conversion: the bins (256 exponents) added into twelve 64-bit
+// sums of 32-bit limb pieces (units of 2^-149, not yet carried) in lds[0..11]. Every thread of the
+// block calls it; lds holds the sums when it returns.
+__device__ inline void bl_bins_to_limb_sums_block(const unsigned long long* bins, unsigned long long* lds) {
   const int t = threadIdx.x;
   if (t < 12) lds[t] = 0ull;
   __syncthreads();
@@ -159,17 +161,26 @@ __device__ inline double bl_bins_to_double_block(const unsigned long long* bins,
     atomicAdd(&lds[w + 2], (unsigned long long)(uint32_t)(bit ? (b >> (64 - bit)) : 0ull));
   }
   __syncthreads();
-  if (t == 0) {
-    uint32_t L[12];
-    unsigned long long carry = 0ull;
+}
+
+// Second half: carries through the limb sums (each below 2^63 minus the incoming carry), then the
+// correctly rounded double of the 384-bit integer.
+__device__ inline double bl_limb_sums_to_double(const unsigned long long* sums) {
+  uint32_t L[12];
+  unsigned long long carry = 0ull;
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      const unsigned long long v = lds[i] + carry;
-      L[i] = (uint32_t)v;
-      carry = v >> 32;
-    }
-    *out = bl_limbs_to_double(L);
+  for (int i = 0; i < 12; ++i) {
+    const unsigned long long v = sums[i] + carry;
+    L[i] = (uint32_t)v;
+    carry = v >> 32;
   }
+  return bl_limbs_to_double(L);
+}
+
+__device__ inline double bl_bins_to_double_block(const unsigned long long* bins, unsigned long long* lds,
+                                                 double* out) {
+  bl_bins_to_limb_sums_block(bins, lds);
+  if (threadIdx.x == 0) *out = bl_limb_sums_to_double(lds);
   __syncthreads();
   return *out;
 }

@@ -879,7 +879,7 @@ __device__ __forceinline__ float round_down_f32(double d) {        // d >= 0, d 
 }
 
 constexpr int kTensorBlocks = 512;     // blocks of the tensor-wide reduction
-constexpr int kTensorCopies = 64;      // global copies of the bins (block b adds into copy b % 64)
+constexpr int kTensorLimbs = 12;       // 64-bit limb sums per block slot
 
 template <int IN_F32>
 __device__ __forceinline__ void load8(const void* __restrict__ x, long off, float (&o)[8]) {
@@ -915,18 +915,15 @@ __device__ __forceinline__ void wave_bins_add(unsigned long long* bins, float v,
   }
 }
 
-__global__ void k_tensor_clear(unsigned long long* __restrict__ gbins) {
-  for (int i = threadIdx.x; i < kTensorCopies * 256; i += blockDim.x) gbins[i] = 0ull;
-}
-
-// Each block adds its exact bins into global copy blockIdx % 64 (SUM) or writes its maximum to
-// slot blockIdx (the blocks sharing a copy are few, so the atomics seldom wait on each other).
+// Each block writes its exact total as twelve limb sums to slot blockIdx (SUM), or its maximum;
+// every slot is rewritten on every call, so the workspace needs no clearing.
 // Threads walk 8-element chunks of the row-major tensor with a grid stride.
 template <int IN_F32, bool SUM>
 __global__ __launch_bounds__(256) void k_tensor_reduce(const void* __restrict__ x, int M, int K, long ldx,
-                                                       unsigned long long* __restrict__ gbins,
+                                                       unsigned long long* __restrict__ gslot,
                                                        uint32_t* __restrict__ gmax) {
   __shared__ unsigned long long bins[SUM ? 256 : 1];
+  __shared__ unsigned long long limbs[SUM ? kTensorLimbs : 1];
   __shared__ uint32_t wmax[4];
   const int t = threadIdx.x, lane = t & 63;
   if constexpr (SUM) {
@@ -960,7 +957,6 @@ __global__ __launch_bounds__(256) void k_tensor_reduce(const void* __restrict__ 
       if (col >= KO) { col -= KO; ++row; }
     }
   }
-  const int copy = blockIdx.x % kTensorCopies;
   if constexpr (SUM) {
     AbsSum acc = accs[0];
 #pragma unroll
@@ -991,8 +987,8 @@ __global__ __launch_bounds__(256) void k_tensor_reduce(const void* __restrict__ 
     wave_bins_add(bins, mid, lane);
     wave_bins_add(bins, lo, lane);
     __syncthreads();
-    const unsigned long long b = bins[t];
-    if (b) atomicAdd(&gbins[copy * 256 + t], b);
+    bl_bins_to_limb_sums_block(bins, limbs);
+    if (t < kTensorLimbs) gslot[blockIdx.x * kTensorLimbs + t] = limbs[t];
   } else {
     mx = bl_wave_max_u(mx);
     if (lane == 0) wmax[t >> 6] = mx;
@@ -1005,29 +1001,27 @@ __global__ __launch_bounds__(256) void k_tensor_reduce(const void* __restrict__ 
   }
 }
 
-// one value for every row: beta (SUM, from the bins) or gamma (the maximum); 1024 threads
+// one value for every row: beta (SUM, from the blocks' limb sums) or gamma (the maximum); 1024 threads
 template <bool SUM>
-__global__ __launch_bounds__(1024) void k_tensor_scale(const unsigned long long* __restrict__ gbins,
+__global__ __launch_bounds__(1024) void k_tensor_scale(const unsigned long long* __restrict__ gslot,
                                                        const uint32_t* __restrict__ gmax, int M, double count,
                                                        float* __restrict__ rowval) {
-  __shared__ unsigned long long part[4][256];
-  __shared__ unsigned long long bins[256];
-  __shared__ unsigned long long limbs[12];
-  __shared__ double total;
+  __shared__ unsigned long long limbs[kTensorLimbs];
   __shared__ uint32_t wmax[16];
   __shared__ float val;
   const int t = threadIdx.x;
   if constexpr (SUM) {
-    const int e = t & 255, grp = t >> 8;
-    unsigned long long b = 0ull;
-#pragma unroll
-    for (int k = grp; k < kTensorCopies; k += 4) b += gbins[k * 256 + e];
-    part[grp][e] = b;
+    // thread (g, i) adds limb i of slots g, g + 64, ...; every sum stays below 2^49 + 2^40
+    if (t < kTensorLimbs) limbs[t] = 0ull;
     __syncthreads();
-    if (t < 256) bins[t] = part[0][t] + part[1][t] + part[2][t] + part[3][t];
+    if (t < kTensorLimbs * 64) {
+      const int i = t % kTensorLimbs, g = t / kTensorLimbs;
+      unsigned long long b = 0ull;
+      for (int k = g; k < kTensorBlocks; k += 64) b += gslot[k * kTensorLimbs + i];
+      atomicAdd(&limbs[i], b);
+    }
     __syncthreads();
-    const double S = bl_bins_to_double_block(bins, limbs, &total);
-    if (t == 0) val = (float)(S / count);
+    if (t == 0) val = (float)(bl_limb_sums_to_double(limbs) / count);
   } else {
     uint32_t m = 0u;
     for (int k = t; k < kTensorBlocks; k += 1024) m = gmax[k] > m ? gmax[k] : m;
@@ -1115,22 +1109,21 @@ hipError_t bl_launch_quantize(const void* x, int in_f32, int M, int K, long ldx,
 
 hipError_t bl_launch_quantize_per_tensor(const void* x, int in_f32, int M, int K, long ldx, int fmt, float eps,
                                          void* ws, void* codes, float* scale, hipStream_t st) {
-  // workspace: 64 copies of the 256 bins (uint64), 512 block maxima (uint32), then the M row values
+  // workspace: 512 block slots of 12 limb sums (uint64), 512 block maxima (uint32), then the M row values
   uint8_t* w = static_cast<uint8_t*>(ws);
-  unsigned long long* gbins = reinterpret_cast<unsigned long long*>(w);
-  uint32_t* gmax = reinterpret_cast<uint32_t*>(w + (size_t)kTensorCopies * 256 * 8);
-  float* rowval = reinterpret_cast<float*>(w + (size_t)kTensorCopies * 256 * 8 + (size_t)kTensorBlocks * 4);
+  unsigned long long* gslot = reinterpret_cast<unsigned long long*>(w);
+  uint32_t* gmax = reinterpret_cast<uint32_t*>(w + (size_t)kTensorBlocks * kTensorLimbs * 8);
+  float* rowval = reinterpret_cast<float*>(w + (size_t)kTensorBlocks * kTensorLimbs * 8 + (size_t)kTensorBlocks * 4);
   const bool sum = (fmt == BL_ACT_INT4 || fmt == BL_ACT_INT4_E3M2);
   const dim3 grid(kTensorBlocks), block(256);
   if (sum) {
-    hipLaunchKernelGGL(k_tensor_clear, dim3(1), dim3(1024), 0, st, gbins);
-    if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, true>), grid, block, 0, st, x, M, K, ldx, gbins, gmax);
-    else hipLaunchKernelGGL((k_tensor_reduce<0, true>), grid, block, 0, st, x, M, K, ldx, gbins, gmax);
-    hipLaunchKernelGGL((k_tensor_scale<true>), dim3(1), dim3(1024), 0, st, gbins, gmax, M, (double)M * K, rowval);
+    if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, true>), grid, block, 0, st, x, M, K, ldx, gslot, gmax);
+    else hipLaunchKernelGGL((k_tensor_reduce<0, true>), grid, block, 0, st, x, M, K, ldx, gslot, gmax);
+    hipLaunchKernelGGL((k_tensor_scale<true>), dim3(1), dim3(1024), 0, st, gslot, gmax, M, (double)M * K, rowval);
   } else {
-    if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, false>), grid, block, 0, st, x, M, K, ldx, gbins, gmax);
-    else hipLaunchKernelGGL((k_tensor_reduce<0, false>), grid, block, 0, st, x, M, K, ldx, gbins, gmax);
-    hipLaunchKernelGGL((k_tensor_scale<false>), dim3(1), dim3(1024), 0, st, gbins, gmax, M, (double)M * K, rowval);
+    if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, false>), grid, block, 0, st, x, M, K, ldx, gslot, gmax);
+    else hipLaunchKernelGGL((k_tensor_reduce<0, false>), grid, block, 0, st, x, M, K, ldx, gslot, gmax);
+    hipLaunchKernelGGL((k_tensor_scale<false>), dim3(1), dim3(1024), 0, st, gslot, gmax, M, (double)M * K, rowval);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

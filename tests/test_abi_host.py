@@ -191,7 +191,7 @@ def test_glu_conditional_validation(kw, status):
     (dict(x=None), 1), (dict(codes=None), 1), (dict(scale=None), 1), (dict(ws=None), 1),
     (dict(dt=7), 1), (dict(fmt=9), 1), (dict(eps=0.0), 1), (dict(M=0), 2), (dict(K=100, ldx=100), 2),
     (dict(ldx=128), 1), (dict(wsb=100), 4), (dict(x=P_MIS), 3), (dict(ws=P_MIS), 3), (dict(ldx=260), 3),
-    (dict(M=1 << 20, K=4096, ldx=4096, wsb=1 << 24), 2), (dict(M=300000, wsb=1 << 20), 4), (dict(wsb=133120), 4),
+    (dict(M=1 << 20, K=4096, ldx=4096, wsb=1 << 24), 2), (dict(M=300000, wsb=1 << 20), 4), (dict(wsb=51200), 4),
 ])
 def test_quantize_per_tensor_validation(kw, status):
     a = dict(x=P, dt=0, M=4, K=256, ldx=256, fmt=0, eps=1e-5, ws=P, wsb=1 << 21, codes=P, scale=P)
@@ -199,7 +199,7 @@ def test_quantize_per_tensor_validation(kw, status):
     st = tw.library().bitlinear_quantize_act_per_tensor(a["x"], a["dt"], a["M"], a["K"], a["ldx"], a["fmt"], a["eps"],
                                                         a["ws"], a["wsb"], a["codes"], a["scale"], None)
     assert st == status
-    assert tw.bitlinear_quantize_per_tensor_workspace_bytes(4) >= 64 * 256 * 8 + 512 * 4 + 16
+    assert tw.bitlinear_quantize_per_tensor_workspace_bytes(4) >= 512 * 12 * 8 + 512 * 4 + 16
 
 
 @needs_lib
