@@ -8,7 +8,7 @@
 hipError_t bl_launch_quantize(const void* x, int in_f32, int M, int K, long ldx, int fmt, int keep, float eps,
                               const float* hint, void* codes, float* scale, uint32_t* mask, hipStream_t st);
 
-// per-tensor scale variant; ws: 64 copies of 256 uint64 bins, 512 uint32 block maxima, then M floats
+// per-tensor scale variant; ws: 512 block slots of 12 uint64 limb sums, 512 uint32 block maxima, then M floats
 constexpr size_t bl_quantize_per_tensor_ws_bytes(long M) { return (size_t)512 * 12 * 8 + 512 * 4 + 4 * (size_t)M; }
 hipError_t bl_launch_quantize_per_tensor(const void* x, int in_f32, int M, int K, long ldx, int fmt, float eps,
                                          void* ws, void* codes, float* scale, hipStream_t st);
