@@ -47,12 +47,6 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 
 // ----------------------------------------------------------------------------- A storage per format
 constexpr int NST = 4;   // stage buffers (three steps in flight)
-#ifndef I8_ROWSTORE
-#define I8_ROWSTORE 1    // int8-core GEMM: whole-row output stores through LDS (1) or direct (0)
-#endif
-#ifndef MX_BM
-#define MX_BM 128        // FP6/FP4 GEMM block rows: 128 (two blocks per CU) or 256 (one)
-#endif
 
 template <int FMT>
 struct AFmt {
@@ -262,25 +256,24 @@ __device__ __forceinline__ void store_subtile_rows(float* __restrict__ Y, long l
   __builtin_amdgcn_wave_barrier();                 // the region is rewritten by the next subtile
 }
 
-template <int FMT, int EPI, int BM0>
+template <int FMT, int EPI>
 struct CfgMx {
   static constexpr bool GLU = (EPI == BL_EPI_RELU2_GLU);
   static constexpr int NB = GLU ? 2 : 1;
-  // 4 waves (2 x 2). BM0 = 256: 256 x 256 block, one block per CU (128 KB of LDS for E3M2);
-  // BM0 = 128: 128 x 256 block, two blocks per CU (at most 80 KB of LDS and 256 registers each).
+  // 4 waves (2 x 2), 128 x 256 block, two blocks per CU (at most 80 KB of LDS and 256 registers
+  // per lane each), so one block's loads, LDS reads and epilogue overlap the other's MFMAs.
   static constexpr int NW = 4, WGM = 2, WGN = 2;
-  static constexpr int BM = BM0, BN = GLU ? 128 : 256;
+  static constexpr int BM = 128, BN = GLU ? 128 : 256;
   static constexpr int SM = BM / WGM / 16, SN = BN / WGN / 16;
-  static constexpr int OCC = BM0 == 128 ? 2 : 1;
   using Plan = StagePlan<FMT, BM, BN, NB, NW>;
 };
 
-template <int FMT, int EPI, int BM0>
-__global__ __launch_bounds__(256, (BM0 == 128 ? 2 : 1)) void k_gemm_mx(
+template <int FMT, int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm_mx(
     const uint8_t* __restrict__ A, const float* __restrict__ ascale, int M, int K, const uint8_t* __restrict__ W,
     const float* __restrict__ walpha, const uint8_t* __restrict__ W2, const float* __restrict__ w2alpha, int N,
     float* __restrict__ Y, long ldy, const float* R, long ldr, float* __restrict__ rowmax) {
-  using C = CfgMx<FMT, EPI, BM0>;
+  using C = CfgMx<FMT, EPI>;
   using F = AFmt<FMT>;
   using P = typename C::Plan;
   constexpr int NB = C::NB, SM = C::SM, SN = C::SN, BM = C::BM;
@@ -581,7 +574,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_i8(const uint8_t* __restrict__ 
       }
     }
     float rmax = 0.f;
-    if constexpr (EPI == BL_EPI_RELU2_GLU || I8_ROWSTORE == 0) {
+    if constexpr (EPI == BL_EPI_RELU2_GLU) {
 #pragma unroll
       for (int t = 0; t < SN; ++t) {
         const int n = nw0 + 16 * t;
@@ -616,9 +609,9 @@ hipError_t launch(const bl_mm_args& a, hipStream_t st) {
   const uint8_t* W = static_cast<const uint8_t*>(a.W);
   const uint8_t* W2 = static_cast<const uint8_t*>(a.W2);
   if constexpr (FMT == BL_ACT_FP4_E2M1 || FMT == BL_ACT_INT4_E3M2) {
-    using C = CfgMx<FMT, EPI, MX_BM>;
+    using C = CfgMx<FMT, EPI>;
     const int ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
-    hipLaunchKernelGGL((k_gemm_mx<FMT, EPI, MX_BM>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A, a.ascale, a.M, a.K,
+    hipLaunchKernelGGL((k_gemm_mx<FMT, EPI>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A, a.ascale, a.M, a.K,
                        W, a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
   } else {
     // 128 x 256 tiles when they give every CU at least two blocks, 128 x 128 tiles otherwise
