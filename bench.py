@@ -182,6 +182,9 @@ def main():
     uWrs = [uWr] + [uWr.clone() for _ in range(ROTATE_GLU - 1)]
     dgs = {m: torch.empty((m, F["N"]), dtype=torch.float32, device=dev) for m in D["Ms"]}
     dhs = {m: torch.empty((m, F["N"]), dtype=torch.float32, device=dev) for m in D["Ms"]}
+    # decode A8: INT8 codes of the first M rows of the FFN's h against the down projection
+    d8Ws = [dW] + [dW.clone() for _ in range(ROTATE - 1)]
+    d8ys = {m: torch.empty((m, F["K"]), dtype=torch.float32, device=dev) for m in D["Ms"]}
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
@@ -209,6 +212,13 @@ def main():
                 tw.bitlinear_gemv_decode_glu_conditional(dcs[m], dss[m], D["K"], gWs[r], gA, uWrs[r], uA, F["N"],
                                                          gate=dgs[m], h=dhs[m])
         cond_graphs[m] = g
+    a8_graphs = {}
+    for m in D["Ms"]:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for r in range(ROTATE):
+                tw.bitlinear_gemv_decode("int8", fhc[:m], fhs[:m], F["N"], d8Ws[r], dA, F["K"], y=d8ys[m])
+        a8_graphs[m] = g
     torch.cuda.synchronize()
 
     names = ["quant_int4_e3m2_prefill", "gemm_a4_int4_fp6_prefill", "quant_int4_prefill", "gemm_a4_int4_i8_prefill",
@@ -217,7 +227,8 @@ def main():
              "quant_int4_e3m2_ffn", "gemm_a4_glu_ffn", "quant_int8_h", "gemm_a8_down", "quant_topk_int8_attn",
              "gemm_a8_oproj_residual", "kv_quant_q4_rope", "kv_quant_k3_rope_bos", "kv_quant_v3_bos"] + \
         [f"decode_m{m}_graph" for m in D["Ms"]] + \
-        [f"decode_glu_m{m}_graph" for m in D["Ms"]] + [f"decode_glu_cond_m{m}_graph" for m in D["Ms"]]
+        [f"decode_glu_m{m}_graph" for m in D["Ms"]] + [f"decode_glu_cond_m{m}_graph" for m in D["Ms"]] + \
+        [f"decode_a8_m{m}_graph" for m in D["Ms"]]
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -261,6 +272,8 @@ def main():
             glu_graphs[m].replay(); mark()
         for m in D["Ms"]:
             cond_graphs[m].replay(); mark()
+        for m in D["Ms"]:
+            a8_graphs[m].replay(); mark()
         return evs
 
     if args.copy_calibration:
@@ -288,6 +301,11 @@ def main():
     gemv_us = {m: times[f"decode_m{m}_graph"] / ROTATE for m in D["Ms"]}     # includes the tiny quantize
     glu_us = {m: times[f"decode_glu_m{m}_graph"] / ROTATE_GLU for m in D["Ms"]}
     cond_us = {m: times[f"decode_glu_cond_m{m}_graph"] / ROTATE_GLU for m in D["Ms"]}
+    a8_us = {m: times[f"decode_a8_m{m}_graph"] / ROTATE for m in D["Ms"]}
+    # 32-wide K slices of the down weights that the A8 GEMV reads (some of the M rows nonzero there)
+    a8_live = {m: int((fhc[:m].view(torch.int8).view(m, F["N"] // 32, 32) != 0).any(dim=2).any(dim=0).sum().item())
+               for m in D["Ms"]}
+    peaks = measured_peaks(torch, dev)
     # live up rows of the conditional projection (channels whose gate is positive in some row)
     live = {m: int((dgs[m] > 0).any(dim=0).sum().item()) for m in D["Ms"]}
 
@@ -380,6 +398,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(value, 2), "peak": FP4_PEAK_TOPS, "unit": "TFLOP/s",
                 "frac": round(value / FP4_PEAK_TOPS, 4), "traffic": measured_traffic(),
                 "frac_of_int8_peak": round(value / INT8_PEAK_TOPS, 4),
+                "frac_of_measured_peak": round(value / peaks["mfma_fp6_fp4_tops"], 4),
                 "kernel": "k_gemm_mx<INT4_E3M2,NONE>: INT4 codes on FP6 x FP4 matrix cores "
                           "(prefill_qkv M=4096 K=4096 N=12288)",
                 "avg_kernel_us": round(head_us, 3),
@@ -399,6 +418,12 @@ def main():
             "us": round(cond_us[m], 3), "gbs": round(gbs(b_cond, cond_us[m]), 1),
             "frac_hbm": round(gbs(b_cond, cond_us[m]) / HBM_PEAK_GBS, 4),
             "live_up_rows": round(live[m] / F["N"], 4), "speedup_vs_fused": round(glu_us[m] / cond_us[m], 3)}
+
+    for m in D["Ms"]:
+        b8 = a8_live[m] * 32 * F["K"] / 4 + m * F["N"] + 4 * m + 4 + 4 * m * F["K"]
+        decode[f"a8_m{m}"] = {"us": round(a8_us[m], 3), "gbs": round(gbs(b8, a8_us[m]), 1),
+                              "frac_hbm": round(gbs(b8, a8_us[m]) / HBM_PEAK_GBS, 4),
+                              "live_k_slices": round(a8_live[m] / (F["N"] // 32), 4)}
 
     sparsity = {"ffn_h_zero_codes": round(1 - nnz_h / (F["M"] * F["N"]), 4),
                 "attn_zero_codes": round(1 - nnz_attn / (A["M"] * A["K"]), 4)}
@@ -426,6 +451,7 @@ def main():
                            "(Q4/K3/V3 of the prefill QKV output), decode M=1/4/8",
                    "global_batch": P["M"], "seq_len": None, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "measured_peaks": peaks,
         "decode_gemv": decode,
         "kernels": kern,
         "sparsity": sparsity,
@@ -433,6 +459,38 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_peaks(torch, dev):
+    """What this GPU sustains, beside the datasheet peaks: a 256 MiB device-to-device copy (bytes read
+    plus written per second) and the library's FP6 x FP4 matrix-core-only loop in the GEMM's wave
+    shape (two 256-thread blocks per CU), each the best of three timed runs after a warm-up."""
+    import ternary_weight_quantized_amd as tw
+
+    def best_us(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3)
+        return best
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    copy_us = best_us(lambda: dst.copy_(src))
+    del src, dst
+    blocks = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 4000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    mfma_us = best_us(lambda: tw.bitlinear_calibrate_mfma(blocks, iters, out=out))
+    return {"hbm_copy_gbs": round(2 * (256 << 20) / (copy_us * 1e-6) / 1e9, 1),
+            "mfma_fp6_fp4_tops": round(blocks * iters * 8388608 / (mfma_us * 1e-6) / 1e12, 1),
+            "how": "256 MiB device copy (read + write bytes); FP6 x FP4 MFMA-only loop, "
+                   f"{blocks} blocks x 4 waves x {iters} x 32 MFMAs 16x16x128; best of 3 after a warm-up"}
 
 
 def cpu_baseline(rows, min_seconds=10.0, max_reps=30):

@@ -285,6 +285,18 @@ bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, in
                                 const int32_t* d_bos_slot, int64_t n_bos_slots, void* d_bos_codes,
                                 float* d_bos_scale, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_calibrate_mfma: a measurement aid, not part of the BitLinear path. Runs a matrix-core-only
+ * loop in the shape of the FP6 x FP4 GEMM's K loop (256-thread blocks, two per CU, 32 independent
+ * fp32 accumulators per wave, v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales): every block
+ * performs iters * 4 waves * 32 MFMAs of 2 * 16 * 16 * 128 ops, i.e. 8388608 * iters ops. Timing
+ * it (HIP events) gives the FP6/FP4 rate this GPU sustains, beside the datasheet peak.
+ *   blocks  1 .. 65536 (2 * number of CUs fills the part once);  iters >= 0.
+ *   d_out   out, blocks * 256 float32 (the accumulator sums; their values carry no meaning).
+ * Errors: NULL d_out -> INVALID_ARGUMENT; blocks or iters out of range -> UNSUPPORTED_SHAPE.
+ * ------------------------------------------------------------------------------------------- */
+bl_status bitlinear_calibrate_mfma(int32_t blocks, int32_t iters, float* d_out, void* stream);
+
 const char* bitlinear_status_string(int32_t status);
 int32_t bitlinear_abi_version(void);
 

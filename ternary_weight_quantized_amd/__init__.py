@@ -26,7 +26,7 @@ EXPORTED = (
     "bitlinear_pack_workspace_bytes", "bitlinear_gemm_w158a4", "bitlinear_gemm_w158a8_sparse",
     "bitlinear_gemv_decode", "bitlinear_gemv_decode_glu_conditional", "bitlinear_status_string",
     "bitlinear_abi_version", "bitlinear_quantize_act_per_tensor", "bitlinear_quantize_per_tensor_workspace_bytes",
-    "bitlinear_kv_quantize",
+    "bitlinear_kv_quantize", "bitlinear_calibrate_mfma",
 )
 
 
@@ -73,6 +73,8 @@ def _lib():
         lib.bitlinear_kv_quantize.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, i64, i32, f32, vp, vp, vp, i64,
                                               vp, vp, vp]
         lib.bitlinear_kv_quantize.restype = i32
+        lib.bitlinear_calibrate_mfma.argtypes = [i32, i32, vp, vp]
+        lib.bitlinear_calibrate_mfma.restype = i32
         lib.bitlinear_quantize_act_per_tensor.argtypes = [vp, i32, i64, i64, i64, i32, f32, vp, sz, vp, vp, vp]
         lib.bitlinear_quantize_act_per_tensor.restype = i32
         lib.bitlinear_quantize_per_tensor_workspace_bytes.argtypes = [i64]
@@ -198,6 +200,17 @@ def bitlinear_kv_quantize(x, H, D, bits, eps=1e-5, pos=None, cos=None, sin=None,
                                       _ptr(bos_codes), _ptr(bos_scale), _stream(stream))
     _check(st, "bitlinear_kv_quantize")
     return codes, scale, bos_codes, bos_scale
+
+
+def bitlinear_calibrate_mfma(blocks, iters, out=None, stream=None):
+    """Measurement aid (not part of the BitLinear path): FP6 x FP4 matrix-core-only loop of
+    blocks * iters * 8388608 ops in the GEMM's wave shape. Returns the (meaningless) sums buffer."""
+    import torch
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = _lib().bitlinear_calibrate_mfma(blocks, iters, _ptr(out), _stream(stream))
+    _check(st, "bitlinear_calibrate_mfma")
+    return out
 
 
 def bitlinear_packed_bytes(N, K):

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitlinear.so")
-SOURCES = ["api.hip", "quantize.hip", "pack.hip", "gemm.hip", "gemv.hip", "kvcache.hip"]
+SOURCES = ["api.hip", "quantize.hip", "pack.hip", "gemm.hip", "gemv.hip", "kvcache.hip", "calib.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

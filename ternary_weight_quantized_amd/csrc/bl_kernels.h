@@ -76,3 +76,6 @@ struct bl_kv_args {
   float* bos_scale;       // [nslots][H]
 };
 hipError_t bl_launch_kv_quant(const bl_kv_args& a, hipStream_t st);
+
+// measurement aid: FP6 x FP4 matrix-core loop (blocks x 256 threads, out[blocks * 256])
+hipError_t bl_launch_calib_mfma(int blocks, int iters, float* out, hipStream_t st);

@@ -1,0 +1,47 @@
+// Measurement aid, not part of the BitLinear path: the sustained FP6 x FP4 matrix-core rate of the
+// part in the shape of the GEMM's K loop (two 4-wave blocks per CU, 32 independent 16x16 fp32
+// accumulators per wave, v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales), so that a kernel's
+// MFMA roofline can be read against what this machine sustains as well as against the datasheet.
+// The operands change every iteration (one VALU op per subtile) so the loop is not a constant
+// repeat; the accumulators are summed into out[] so that no MFMA is dead code.
+#include "bl_common.h"
+#include "bl_kernels.h"
+
+namespace {
+
+__global__ __launch_bounds__(256, 2) void k_calib_mfma(int iters, float* __restrict__ out) {
+  v8i a = {(int)(threadIdx.x * 2654435761u), (int)(blockIdx.x * 40503u), 0x5A5A5A5A, 0x3C3C3C3C, 0x12345678,
+           0x0F0F0F0F, 0, 0};
+  v8i b[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    b[t] = v8i{(int)(0x4C4C4C4Cu ^ (t * 0x01010101u)), (int)(threadIdx.x * 77u), 0x44444444, 0x0C0C0C0C, 0, 0, 0, 0};
+  v4f c[4][8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) c[s][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v8i as = a;
+      as[0] ^= i * 0x9E3779B9 + s;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        c[s][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[t], as, c[s][t], 4, 3, 0, 127, 0, 127);
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sum += c[s][t][0] + c[s][t][1] + c[s][t][2] + c[s][t][3];
+  out[(long)blockIdx.x * 256 + threadIdx.x] = sum;
+}
+
+}  // namespace
+
+hipError_t bl_launch_calib_mfma(int blocks, int iters, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_calib_mfma, dim3(blocks), dim3(256), 0, st, iters, out);
+  return hipGetLastError();
+}

@@ -3,8 +3,9 @@
 // "BitNet a4.8: 4-bit Activations for 1-bit LLMs" (architecture write-up), section 3.4: the same
 // products as the GEMMs (Y = Q(X) Q_w(W)^T with INT4 or INT8 activations) for a few tokens.
 //
-// One 512-thread block owns 16 output columns (one packed tile row, n-group G) and splits the K
-// tiles over its eight waves; a wave issues all loads of a chunk of four K tiles at once (the
+// One block owns 16 output columns (one packed tile row, n-group G) and splits the K tiles over
+// its waves (eight; sixteen when K is long, e.g. the 11008-wide down projection, whose 4096 output
+// columns give only 256 blocks); a wave issues all loads of a chunk of four or six K tiles at once (the
 // activation slices first, then its 8-byte share of each 512-byte weight tile, so a wave reads
 // whole tiles, fully coalesced) and feeds each tile to the matrix cores as soon as it has landed.
 // The tile words go to 16x16x64 int8 MFMAs directly; the M token rows occupy the first M of the 16
@@ -49,7 +50,7 @@ __device__ __forceinline__ v4i expand_a_int8(uint4 q) {
 // One chunk of up to CH K tiles starting at kt0 (kt0 < kt_end). FULL chunks load unconditionally, so
 // the compiler can wait for each tile separately; the ragged last chunk clamps its addresses and
 // drops the tiles past kt_end.
-template <bool A8, int NB, bool FULL>
+template <bool A8, int NB, bool FULL, int CH = 4>
 __device__ __forceinline__ void chunk(const uint8_t* arp, const uint8_t* const (&wp)[2], long wstep, int kt0,
                                       int kt_end, int g, v4i (&acc)[NB][2]) {
   constexpr int AV = A8 ? 2 : 1;              // 16-byte activation vectors per lane and tile
@@ -102,8 +103,8 @@ __device__ __forceinline__ void chunk(const uint8_t* arp, const uint8_t* const (
   }
 }
 
-template <int FMT, int EPI>
-__global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
+template <int FMT, int EPI, int CHN, int NWV>
+__global__ __launch_bounds__(NWV * 64) void k_gemv(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
                                                      int M, int K, const uint8_t* __restrict__ W,
                                                      const float* __restrict__ walpha,
                                                      const uint8_t* __restrict__ W2,
@@ -112,12 +113,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* __restrict__
                                                      float* __restrict__ rowmax) {
   constexpr bool A8 = (FMT == BL_ACT_INT8);
   constexpr int NB = (EPI == BL_EPI_RELU2_GLU) ? 2 : 1;
-  __shared__ v4i red[NB][WAVES - 1][64];
+  __shared__ v4i red[NB][NWV - 1][64];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = blockIdx.x;
   const int KT = K >> 7, NG = N >> 4;            // 128-wide weight tiles along K, 16-row groups
-  const int per = (KT + WAVES - 1) / WAVES;
+  const int per = (KT + NWV - 1) / NWV;
   const int kt_begin = wave * per;
   const int kt_end = min(KT, kt_begin + per);
   const int r = lane & 15, g = lane >> 4;
@@ -141,9 +142,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* __restrict__
   v4i acc[NB][2];
 #pragma unroll
   for (int mtx = 0; mtx < NB; ++mtx) acc[mtx][0] = acc[mtx][1] = v4i{0, 0, 0, 0};
-  for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CH) {
-    if (kt0 + CH <= kt_end) chunk<A8, NB, true>(arp, wp, wstep, kt0, kt_end, g, acc);
-    else chunk<A8, NB, false>(arp, wp, wstep, kt0, kt_end, g, acc);
+  for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CHN) {
+    if (kt0 + CHN <= kt_end) chunk<A8, NB, true, CHN>(arp, wp, wstep, kt0, kt_end, g, acc);
+    else chunk<A8, NB, false, CHN>(arp, wp, wstep, kt0, kt_end, g, acc);
   }
 
   // exact int32 reduction of the eight K partitions
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* __restrict__
 #pragma unroll
   for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
-    for (int w = 0; w < WAVES - 1; ++w) acc[mtx][0] += red[mtx][w][lane];
+    for (int w = 0; w < NWV - 1; ++w) acc[mtx][0] += red[mtx][w][lane];
 
   constexpr int SHIFT = A8 ? 6 : 10;
 #pragma unroll
@@ -189,12 +190,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(const uint8_t* __restrict__
   }
 }
 
+template <int FMT, int EPI, int CHN, int NWV>
+hipError_t launch_w(const bl_mm_args& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_gemv<FMT, EPI, CHN, NWV>), dim3(a.N / 16), dim3(NWV * 64), 0, st,
+                     static_cast<const uint8_t*>(a.A), a.ascale, a.M, a.K, static_cast<const uint8_t*>(a.W),
+                     a.walpha, static_cast<const uint8_t*>(a.W2), a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
+  return hipGetLastError();
+}
+// eight waves with one chunk of up to four tiles each when K allows it (K <= 4096), else sixteen
+// waves with chunks of four or six tiles (K <= 12288 in one chunk per wave)
 template <int FMT, int EPI>
 hipError_t launch(const bl_mm_args& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemv<FMT, EPI>), dim3(a.N / 16), dim3(WAVES * 64), 0, st, static_cast<const uint8_t*>(a.A),
-                     a.ascale, a.M, a.K, static_cast<const uint8_t*>(a.W), a.walpha,
-                     static_cast<const uint8_t*>(a.W2), a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
-  return hipGetLastError();
+  const int KT = a.K >> 7;
+  if ((KT + WAVES - 1) / WAVES <= CH) return launch_w<FMT, EPI, CH, WAVES>(a, st);
+  if ((KT + 15) / 16 <= 4) return launch_w<FMT, EPI, 4, 16>(a, st);
+  return launch_w<FMT, EPI, 6, 16>(a, st);
 }
 
 template <int FMT>

@@ -251,3 +251,13 @@ def test_packed_rows_decoder_roundtrip_and_positions():
         bit = 4 * q if q < 8 else 4 * (q - 8) + 2
         assert words[n * 512 // 16 + k // 16] == (3 << bit)
         assert np.count_nonzero(words) == 1
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), 1), (dict(blocks=0), 2), (dict(blocks=65537), 2), (dict(iters=-1), 2),
+])
+def test_calibrate_mfma_validation(kw, status):
+    a = dict(blocks=512, iters=10, out=P)
+    a.update(kw)
+    assert tw.library().bitlinear_calibrate_mfma(a["blocks"], a["iters"], a["out"], None) == status

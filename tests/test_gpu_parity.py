@@ -363,7 +363,7 @@ def test_gemm_a8_residual_and_relu2(M, N, K):
 # ----------------------------------------------------------------------------- decode
 @pytest.mark.parametrize("fmt", ["int4", "int8"])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8])
-@pytest.mark.parametrize("N,K", [(48, 512), (1024, 4096), (64, 11008)])
+@pytest.mark.parametrize("N,K", [(48, 512), (1024, 4096), (64, 11008), (32, 8192), (48, 12800)])
 def test_decode(fmt, M, N, K):
     torch_cuda()
     x = make_x(6000 + M + K, M, K, special=False)

@@ -132,6 +132,32 @@ def test_ffn_7b_sampled():
     assert 0.45 < hz < 0.55                       # ReLU^2 zeroes the non-positive gate half
 
 
+@pytest.mark.parametrize("M", [1, 8])
+def test_decode_a8_ffn_full(M):
+    """Decode FFN of the first M tokens of the 7B FFN workload as the benchmark runs it: the fused
+    ReLU^2 GLU decode product of their INT4 codes (with row maxima), INT8 codes of h, and the INT8
+    down-projection decode product; every output against the oracle."""
+    torch = torch_cuda()
+    wl = WORKLOADS["ffn_7b"]
+    inp = workload_inputs("ffn_7b")
+    K, N = wl["K"], wl["N"]
+    tg, ag, pg, dag = weights(inp["w_gate"])
+    tu, au, pu, dau = weights(inp["w_up"])
+    td, ad, pd, dad = weights(inp["w_down"])
+    xb = inp["x"][:M]
+    codes, scale, _ = tw.bitlinear_quantize_act(dev_bf16(xb), "int4", eps=EPS)
+    rowmax = torch.zeros(M, dtype=torch.float32, device="cuda")
+    h = tw.bitlinear_gemv_decode("int4", codes, scale, K, pg, dag, N, up_packed=pu, up_alpha=dau, row_absmax=rowmax)
+    hc, hs, _ = tw.bitlinear_quantize_act(h, "int8", eps=EPS, row_absmax_hint=rowmax)
+    y = tw.bitlinear_gemv_decode("int8", hc, hs, N, pd, dad, K)
+    ref = O.ffn_ref(bf16_bits_to_f32(xb), tg, ag, tu, au, td, ad, EPS)
+    np.testing.assert_array_equal(host(h).view(np.uint32), ref["h"].view(np.uint32))
+    np.testing.assert_array_equal(host(rowmax), ref["h_absmax"])
+    np.testing.assert_array_equal(int8_values(host(hc)), ref["h_codes"])
+    np.testing.assert_array_equal(host(hs), ref["h_dscale"])
+    assert_y_close(host(y), ref["acc_d"], ref["h_dscale"], ad)
+
+
 def test_attn_out_sampled():
     torch_cuda()
     wl = WORKLOADS["attn_out"]
