@@ -78,8 +78,8 @@ def bf16_dev(torch, bits):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
-              "(the path shards by tokens or output columns without communication; see the design notes).",
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path would shard by "
+              "tokens or output columns without communication, and only one GPU's share is measured here.",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
