@@ -363,13 +363,16 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
 // owns the 8-element chunks t, t + 256, ... (one 16-byte load each). The threshold key T (the
 // largest 15-bit magnitude key with count(key >= T) >= keep) comes from two radix passes over LDS
 // histograms, 16 copies (thread t adds to copy t % 16, so a wave's 64 increments spread over 16
-// copies): exponents (key >> 7), then the mantissas of the keys whose exponent is T's. Bin counts
+// copies): exponents (key >> 7), then the mantissas of the keys whose exponent is T's. Copies are
+// interleaved in groups of four (bin b of copy 4g + i is word 4b + i of group g), so one 16-byte
+// read returns a bin of four copies and the clears are 16-byte stores. Bin counts
 // are summed over the copies, scanned in descending key order across the block, and the bin where
 // the running count reaches keep gives the next digit. Ties at T are ranked by index with one block
 // scan of the per-thread tie counts of every chunk. Codes: RN32(x * s) is rounded to an integer by
 // adding 1.5 * 2^23 (round to nearest even; |x * s| < 127.5 always, so no clamping is needed) and
 // its low byte is the two's-complement code. A 32-element mask word comes from 4 neighbouring threads.
 constexpr int TK_COPIES = 16, TK_STRIDE = 264;     // 256 bins + 8 pad words per copy
+constexpr int TK_GROUP = 4 * TK_STRIDE;            // words per group of four interleaved copies
 
 // Inclusive scan of one int per thread over the 256-thread block; returns (inclusive, total).
 __device__ __forceinline__ int2 tk_block_scan(int v, int* wtot, int t) {
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
                                                   float eps, const float* __restrict__ hint,
                                                   uint8_t* __restrict__ codes, float* __restrict__ scale,
                                                   uint32_t* __restrict__ mask) {
-  __shared__ uint32_t hist[TK_COPIES * TK_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[TK_COPIES * TK_STRIDE];
   __shared__ int wtot[4];
   __shared__ int wtot_v[NCH][4];
   __shared__ uint32_t wmax[4];
@@ -439,24 +442,33 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
   uint32_t T = all ? 0u : 0x8000u;                 // 0x8000: above every key (keep == 0)
   int need = 0;
   if (!all && keep > 0) {                          // block-uniform
-    uint32_t* hc = hist + (t & (TK_COPIES - 1)) * TK_STRIDE;
-    for (int i = t; i < TK_COPIES * TK_STRIDE; i += 256) hist[i] = 0u;
+    uint32_t* hc = hist + ((t & (TK_COPIES - 1)) >> 2) * TK_GROUP + (t & 3);   // bin b at hc[4 b]
+    uint4* hist4 = reinterpret_cast<uint4*>(hist);
+    for (int i = t; i < TK_COPIES * TK_STRIDE / 4; i += 256) hist4[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
+    // total of bin b over the 16 copies: four 16-byte reads
+    auto bin_total = [&](int b) -> int {
+      int n = 0;
+#pragma unroll
+      for (int g = 0; g < TK_COPIES / 4; ++g) {
+        const uint4 q = hist4[(g * TK_GROUP >> 2) + b];
+        n += (int)(q.x + q.y + q.z + q.w);
+      }
+      return n;
+    };
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       if (t + 256 * c < nch) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) atomicAdd(&hc[key(c, j) >> 7], 1u);
+        for (int j = 0; j < 8; ++j) atomicAdd(&hc[4 * (key(c, j) >> 7)], 1u);
       }
     __syncthreads();
     // pass 1: thread t owns exponent bin 255 - t (descending keys)
-    int cnt = 0;
-#pragma unroll
-    for (int k = 0; k < TK_COPIES; ++k) cnt += (int)hist[k * TK_STRIDE + 255 - t];
+    int cnt = bin_total(255 - t);
     int2 sc = tk_block_scan(cnt, wtot, t);
     if (sc.x - cnt < keep && keep <= sc.x) { sel[0] = 255 - t; sel[1] = sc.x - cnt; }
     // clear the mantissa bins (every thread has read its exponent bin above)
-    for (int i = t; i < TK_COPIES * 128; i += 256) hist[(i >> 7) * TK_STRIDE + (i & 127)] = 0u;
+    for (int i = t; i < TK_COPIES * 128 / 4; i += 256) hist4[((i >> 7) * TK_GROUP >> 2) + (i & 127)] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
     const uint32_t e = (uint32_t)sel[0];
     const int above = sel[1];
@@ -466,16 +478,12 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint32_t k = key(c, j);
-          if ((k >> 7) == e) atomicAdd(&hc[k & 127u], 1u);
+          if ((k >> 7) == e) atomicAdd(&hc[4 * (k & 127u)], 1u);
         }
       }
     __syncthreads();
     // pass 2: thread t < 128 owns mantissa bin 127 - t
-    cnt = 0;
-    if (t < 128) {
-#pragma unroll
-      for (int k = 0; k < TK_COPIES; ++k) cnt += (int)hist[k * TK_STRIDE + 127 - t];
-    }
+    cnt = t < 128 ? bin_total(127 - t) : 0;
     sc = tk_block_scan(cnt, wtot, t);
     const int ex = above + sc.x - cnt;
     if (t < 128 && ex < keep && keep <= above + sc.x) { sel[0] = 127 - t; sel[1] = ex; }
