@@ -22,6 +22,8 @@
  *  * Activations X are row-major [M, K] (tokens x features) with row stride ldx elements.
  *    Weights W are [N, K] as in a linear layer; outputs Y = X W^T are row-major [M, N], row stride ldy.
  *  * Shapes: K % 256 == 0, N % 16 == 0, M >= 1 (any value, ragged tiles are masked); M*K, N*K < 2^31.
+ *    The matmuls (GEMM, GEMV, conditional GLU) take K <= 2^18 - 256 = 261888: the int8-core INT4
+ *    path keeps 1024 * sum(c t) in int32, which stays exact up to there (all paths do).
  *  * Alignment: code buffers, packed weights, x, y and the residual must be 16-byte aligned;
  *    ldx*elem_size, ldy*4 and ldr*4 must be multiples of 16 bytes.
  *  * Inputs are finite (no NaN or Inf). eps must be finite and > 0.

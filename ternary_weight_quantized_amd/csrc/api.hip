@@ -10,6 +10,10 @@ namespace {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0u; }
 inline bool eps_ok(float eps) { return std::isfinite(eps) && eps > 0.0f; }
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
+// Longest reduction the matmuls accept. The int8-core INT4 path holds 1024 * sum(c t) in int32
+// (|c| <= 8, |t| <= 1), so K * 8 * 1024 must stay below 2^31; the INT8 path (64 * 127 per term) and
+// the fp32 sums of the FP6 / FP4 paths (exact below 2^24) have more room.
+constexpr int64_t kMaxMatmulK = ((int64_t)1 << 18) - 256;
 
 bl_status hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
@@ -20,7 +24,7 @@ bl_status check_mm(int32_t fmt, const void* codes, const float* scale, int64_t M
   if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8 && fmt != BL_ACT_INT4_E3M2)
     return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1 || N < 1) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (K % 256 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (K % 256 != 0 || N % 16 != 0 || K > kMaxMatmulK) return BL_ERR_UNSUPPORTED_SHAPE;
   if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ldy < N) return BL_ERR_INVALID_ARGUMENT;
   if (!aligned16(codes) || !aligned16(packed) || !aligned16(y) || (ldy * 4) % 16 != 0) return BL_ERR_MISALIGNED;

@@ -103,6 +103,7 @@ def _mm(name, **kw):
 MM_CASES = [
     (dict(codes=None), 1), (dict(scale=None), 1), (dict(packed=None), 1), (dict(alpha=None), 1), (dict(y=None), 1),
     (dict(K=128), 2), (dict(N=24), 2), (dict(M=0), 2), (dict(ldy=16), 1), (dict(ldy=33), 3),
+    (dict(K=262144), 2), (dict(M=1, N=16, K=1 << 20), 2),          # beyond the exact-accumulation K
     (dict(codes=P_MIS), 3), (dict(packed=P_MIS), 3), (dict(y=P_MIS), 3),
     (dict(epi=tw.bl_epilogue(1, None, 32, None, None, None)), 1),
     (dict(epi=tw.bl_epilogue(1, 4096, 8, None, None, None)), 1),
