@@ -456,3 +456,42 @@ def test_glu_conditional(M, N, K):
     np.testing.assert_array_equal(host(rowmax), r["h_absmax"])
     full = tw.bitlinear_gemv_decode("int4", codes, scale, K, pg, dag, N, up_packed=pu, up_alpha=dau)
     np.testing.assert_array_equal(host(full), host(h))
+
+
+# ----------------------------------------------------------------------------- longest accepted K
+MAXK = 261888      # 2^18 - 256: the longest reduction the matmul entry points accept
+
+
+@pytest.mark.parametrize("kind,fmt", [("gemm", "int4"), ("gemm", "int4_e3m2"), ("gemm", "fp4"), ("a8", "int8"),
+                                      ("gemv", "int4"), ("gemv", "int8")])
+def test_matmul_extreme_codes_at_longest_k(kind, fmt):
+    """Every activation code at its largest magnitude against all -1 weights at the longest accepted
+    K: the int32 sums of the int8-core paths (1024 * 8 * K for INT4 nibbles, 64 * 127 * K for INT8)
+    and the fp32 sums of the FP6 / FP4 paths stay exact, and the outputs equal the oracle's."""
+    torch = torch_cuda()
+    K, N = MAXK, 16
+    M = 8 if kind == "gemv" else 20
+    w = -np.ones((N, K), dtype=np.float32)
+    t, a = O.ternarize(w, EPS)
+    packed, alpha = tw.bitlinear_pack_ternary(torch.from_numpy(w).cuda(), EPS)
+    assert alpha.item() == a
+    rows, nbytes = tw.codes_shape(fmt, M, K)
+    if fmt == "int4_e3m2":
+        # E3M2 of -8 is 0b111000; four 6-bit codes fill three bytes (0x38, 0x8E, 0xE3, little endian)
+        pat = np.frombuffer(bytes([0x38, 0x8E, 0xE3]) * (rows * nbytes // 3), dtype=np.uint8)
+        codes = torch.from_numpy(pat.reshape(rows, nbytes).copy()).cuda()
+    else:
+        fill = {"int4": 0x88, "fp4": 0xFF, "int8": 0x81}[fmt]      # nibbles -8, E2M1 -6, int8 -127
+        codes = torch.full((rows, nbytes), fill, dtype=torch.uint8, device="cuda")
+    cval, unit = {"int4": (-8, 1.0), "int4_e3m2": (-8, 1.0), "fp4": (-12, 0.5), "int8": (-127, 1.0)}[fmt]
+    scale = torch.ones(M, dtype=torch.float32, device="cuda")
+    if kind == "gemm":
+        y = tw.bitlinear_gemm_w158a4(fmt, codes, scale, K, packed, alpha, N)
+    elif kind == "a8":
+        y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, alpha, N)
+    else:
+        y = tw.bitlinear_gemv_decode(fmt, codes, scale, K, packed, alpha, N)
+    c = np.full((M, K), cval, dtype=np.int64)
+    ref = O.dequant_f32(O.gemm_int(c, t), np.ones(M, dtype=np.float32), a, unit)
+    assert float(ref[0, 0]) == -cval * K * unit                    # the sum at the bound, held exactly
+    np.testing.assert_array_equal(host(y).view(np.uint32), ref.view(np.uint32))
