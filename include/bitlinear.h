@@ -293,7 +293,7 @@ bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, in
  * fp32 accumulators per wave, v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales): every block
  * performs iters * 4 waves * 32 MFMAs of 2 * 16 * 16 * 128 ops, i.e. 8388608 * iters ops. Timing
  * it (HIP events) gives the FP6/FP4 rate this GPU sustains, beside the datasheet peak.
- *   blocks  1 .. 65536 (2 * number of CUs fills the part once);  iters >= 0.
+ *   blocks  1 .. 65536 (2 * number of CUs fills the part once);  iters 0 .. 2^20.
  *   d_out   out, blocks * 256 float32 (the accumulator sums; their values carry no meaning).
  * Errors: NULL d_out -> INVALID_ARGUMENT; blocks or iters out of range -> UNSUPPORTED_SHAPE.
  * ------------------------------------------------------------------------------------------- */

@@ -248,7 +248,8 @@ bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, in
 
 bl_status bitlinear_calibrate_mfma(int32_t blocks, int32_t iters, float* d_out, void* stream) {
   if (!d_out) return BL_ERR_INVALID_ARGUMENT;
-  if (blocks < 1 || blocks > 65536 || iters < 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  // at most 2^20 steps (about half a second on a full part): a measurement, not a long-running load
+  if (blocks < 1 || blocks > 65536 || iters < 0 || iters > (1 << 20)) return BL_ERR_UNSUPPORTED_SHAPE;
   return hip_status(bl_launch_calib_mfma(blocks, iters, d_out, static_cast<hipStream_t>(stream)));
 }
 

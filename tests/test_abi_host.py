@@ -257,6 +257,7 @@ def test_packed_rows_decoder_roundtrip_and_positions():
 @needs_lib
 @pytest.mark.parametrize("kw,status", [
     (dict(out=None), 1), (dict(blocks=0), 2), (dict(blocks=65537), 2), (dict(iters=-1), 2),
+    (dict(iters=(1 << 20) + 1), 2),
 ])
 def test_calibrate_mfma_validation(kw, status):
     a = dict(blocks=512, iters=10, out=P)
