@@ -196,3 +196,28 @@ def test_decode_glu_conditional_full(M):
     np.testing.assert_array_equal(host(h).view(np.uint32), r["h"].view(np.uint32))
     np.testing.assert_array_equal(host(rowmax), r["h_absmax"])
     print(f"decode glu conditional M={M}: live up rows {r['live'].size / N:.3f}")
+
+
+@pytest.mark.parametrize("fmt", ["int4_e3m2", "int4", "fp4"])
+def test_largest_index_space_sampled(fmt):
+    """The largest M the 2^31-element limits allow at K = 256 (M*K and M*N just below 2^31): 64-bit
+    row offsets in the quantizer, the E3M2 tiles and the GEMM epilogue; sampled rows, including the
+    last one, against the oracle."""
+    torch = torch_cuda()
+    from synth import latent_weights
+    K, N = 256, 240
+    M = ((1 << 31) - 1) // K                     # 8388607 rows: M*K = 2^31 - 256, M*N = 2013265680
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    x = torch.randn((M, K), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    t, alpha, packed, a = weights(latent_weights(77, N, K))
+    codes, scale, _ = tw.bitlinear_quantize_act(x, fmt, eps=EPS)
+    y = tw.bitlinear_gemm_w158a4(fmt, codes, scale, K, packed, a, N)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, n=40, seed=11)
+    rows_t = torch.from_numpy(rows).cuda()
+    xs = x[rows_t].float().cpu().numpy()
+    ref = O.bitlinear_a4(xs, t, alpha, EPS, fmt="fp4" if fmt == "fp4" else "int4")
+    np.testing.assert_array_equal(scale[rows_t].cpu().numpy(), ref["dscale"])
+    assert_y_close(y[rows_t].cpu().numpy(), ref["acc"], ref["dscale"], alpha, 0.5 if fmt == "fp4" else 1.0)
+    del x, codes, scale, y
+    torch.cuda.empty_cache()
