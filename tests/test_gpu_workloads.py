@@ -221,3 +221,29 @@ def test_largest_index_space_sampled(fmt):
     assert_y_close(y[rows_t].cpu().numpy(), ref["acc"], ref["dscale"], alpha, 0.5 if fmt == "fp4" else 1.0)
     del x, codes, scale, y
     torch.cuda.empty_cache()
+
+
+def test_largest_index_space_topk_a8_sampled():
+    """Top-K INT8 quantization and the A8 GEMM with residual at M*K and M*N just below 2^31 (bf16
+    rows of 4096, keep 2048): sampled rows, including the last one, against the oracle."""
+    torch = torch_cuda()
+    from synth import latent_weights
+    K, N, keep = 4096, 4096, 2048
+    M = ((1 << 31) - 1) // K                     # 524287 rows
+    gen = torch.Generator(device="cuda").manual_seed(4321)
+    x = torch.randn((M, K), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    r = torch.randn((M, N), generator=gen, device="cuda", dtype=torch.float32)
+    t, alpha, packed, a = weights(latent_weights(78, N, K))
+    codes, scale, mask = tw.bitlinear_quantize_act(x, "int8", topk_keep=keep, eps=EPS, want_mask=True)
+    y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, residual=r)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, n=24, seed=12)
+    rows_t = torch.from_numpy(rows).cuda()
+    res = r[rows_t].cpu().numpy()
+    ref = O.oproj_ref(x[rows_t].float().cpu().numpy(), t, alpha, res, keep, EPS)
+    np.testing.assert_array_equal(mask_bits(mask[rows_t].cpu().numpy(), K), ref["mask"])
+    np.testing.assert_array_equal(int8_values(codes[rows_t].cpu().numpy()), ref["codes"])
+    np.testing.assert_array_equal(scale[rows_t].cpu().numpy(), ref["dscale"])
+    assert_y_close(y[rows_t].cpu().numpy(), ref["acc"], ref["dscale"], alpha, residual=res)
+    del x, r, codes, scale, mask, y
+    torch.cuda.empty_cache()
