@@ -132,3 +132,39 @@ def test_kv_cache_full(part, bits, rope):
         got = unpack_kv(host(bcodes), H, D, 4)[slots[rows][b]]
         np.testing.assert_array_equal(got, ref["bos_u"][b])
         np.testing.assert_array_equal(host(bscale)[slots[rows][b]], ref["bos_dscale"][b])
+
+
+def test_kv_quantize_largest_index_space_sampled():
+    """3-bit K heads with RoPE and BOS records at T*H*D just below 2^31 (32 heads of 128, bf16):
+    sampled tokens, including the last one and both BOS tokens, against the oracle."""
+    torch = torch_cuda()
+    H, D, P = 32, 128, 4096
+    T = ((1 << 31) - 1) // (H * D)               # 524287 tokens
+    gen = torch.Generator(device="cuda").manual_seed(99)
+    x = torch.randn((T, H * D), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    pos = (np.arange(T, dtype=np.int64) % P).astype(np.int32)
+    pos[-1] = 0                                   # tokens 0 and T-1 start sequences
+    bos = pos == 0
+    bos_rows = np.flatnonzero(bos)
+    slots = np.full(T, -1, np.int32)
+    slots[0], slots[-1] = 0, 1                    # records for the first and the last BOS token only
+    cos, sin = rope_tables(P, D)
+    codes, scale, bcodes, bscale = tw.bitlinear_kv_quantize(x, H, D, 3, eps=EPS, pos=dev_i32(pos), cos=dev_f32(cos),
+                                                            sin=dev_f32(sin), bos_slot=dev_i32(slots),
+                                                            n_bos_slots=2)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.choice(T, 16, replace=False), [0, P, T - 1]]))
+    rows_t = torch.from_numpy(rows).cuda()
+    xs = x[rows_t].float().cpu().numpy().reshape(len(rows), H, D)
+    ref = O.kv_cache_quant(xs, 3, EPS, pos=pos[rows], cos=cos, sin=sin, bos=bos[rows])
+    np.testing.assert_array_equal(unpack_kv(codes[rows_t].cpu().numpy(), H, D, 3), ref["u"])
+    np.testing.assert_array_equal(scale[rows_t].cpu().numpy(), ref["dscale"])
+    got = unpack_kv(host(bcodes), H, D, 4)
+    first, last = int(np.flatnonzero(rows == 0)[0]), int(np.flatnonzero(rows == T - 1)[0])
+    np.testing.assert_array_equal(got[0], ref["bos_u"][first])
+    np.testing.assert_array_equal(got[1], ref["bos_u"][last])
+    np.testing.assert_array_equal(host(bscale), ref["bos_dscale"][[first, last]])
+    assert len(bos_rows) > 2                      # BOS tokens without a slot write no record
+    del x, codes, scale
+    torch.cuda.empty_cache()
