@@ -249,8 +249,12 @@ def dequant(acc, dscale, alpha, acc_unit: float = 1.0):
 def dequant_f32(acc, dscale, alpha, acc_unit: float = 1.0):
     """float32 dequantization in a fixed order: RN32(RN32(acc * acc_unit) * RN32(dscale * alpha)).
 
-    Used where the result decides later codes (the ReLU^2 GLU intermediate).
-    acc*acc_unit is exact (|acc| < 2^24, acc_unit a power of two).
+    Reading R10 of Y = Q(X) Q_w(W)^T ([A4], [SP]): the integer sum is scaled by the product of the
+    two scales, each step one IEEE binary32 rounding. Used where the result decides later codes
+    (the ReLU^2 GLU intermediate) and as the bit pattern the GPU outputs are graded against.
+    RN32(acc) is exact for |acc| <= 2^24 (INT4 and FP4 sums always are); INT8 sums at long K
+    (127 K up to 3.3e7) can exceed it and are then rounded to nearest even, like the kernels'
+    int32 -> float32 conversion. acc_unit is 1 or 0.5, so the scaling by it is exact.
     """
     sc = (np.asarray(dscale, dtype=np.float32) * F32(alpha)).astype(np.float32)
     a = (np.asarray(acc).astype(np.float32) * F32(acc_unit)).astype(np.float32)

@@ -309,6 +309,92 @@ def test_fp4_gemm_counts_half_units():
     np.testing.assert_allclose(r["y"], ref, rtol=1e-12, atol=1e-300)
 
 
+# ----------------------------------------------------------------------------- fixed-order fp32 epilogue
+def rn32(q: Fraction) -> Fraction:
+    """IEEE binary32 round-to-nearest-even of an exact rational, in integer arithmetic (subnormals
+    included; the values used here never overflow)."""
+    if q == 0:
+        return Fraction(0)
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()       # 2^e <= a < 2^(e+1) after the fix-up
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * quantum
+    assert r < Fraction(2) ** 128
+    return r if q > 0 else -r
+
+
+def epilogue_exact(acc, d, alpha, unit):
+    """RN32(RN32(acc * unit) * RN32(d * alpha)), every step rounded from the exact rational."""
+    a = rn32(Fraction(int(acc)) * Fraction(unit))
+    sc = rn32(Fraction(float(d)) * Fraction(float(alpha)))
+    return rn32(a * sc)
+
+
+@pytest.mark.parametrize("case", read_cases("epilogue_hand.txt"))
+def test_dequant_f32_hand_cases(case):
+    acc, d, alpha, unit, y = case
+    got = O.dequant_f32(np.array([[int(scalar(acc))]]), np.float32([scalar(d)]), F32(scalar(alpha)), scalar(unit))
+    assert got.dtype == np.float32 and float(got[0, 0]) == scalar(y)
+
+
+def test_rn32_helper_against_float32_conversion():
+    """The rational rounding helper agrees with numpy's float64 -> float32 conversion (a single IEEE
+    rounding of an exact double) on doubles of every range, ties and subnormals included."""
+    rng = np.random.default_rng(31)
+    v = rng.standard_normal(3000) * np.exp2(rng.integers(-150, 120, 3000).astype(np.float64))
+    ties = (np.float32(rng.standard_normal(500)).astype(np.float64) * (1 + 2.0 ** -24))   # halfway cases
+    for x in np.concatenate([v, ties, [2.0 ** -149 * 1.5, 2.0 ** -149 * 0.5, 2.0 ** -149 * 2.5]]):
+        assert float(rn32(Fraction(float(x)))) == float(np.float32(x)), x
+
+
+def test_dequant_f32_is_the_fixed_order_rounding():
+    """dequant_f32 rounds exactly three times, in the stated order, on accumulators of every size
+    the matmuls produce (beyond 2^24 for INT8 at long K, where RN32(acc) itself rounds), for both
+    accumulator units; plausible mistakes (scales multiplied in another order, one rounding,
+    alpha or the unit dropped) disagree with it on this set."""
+    rng = np.random.default_rng(17)
+    n = 600
+    mags = np.concatenate([rng.integers(0, 64, n // 4), rng.integers(0, 1 << 14, n // 4),
+                           rng.integers((1 << 24) - 64, (1 << 24) + 64, n // 4),
+                           rng.integers(1 << 24, 127 * 261888 + 1, n - 3 * (n // 4))])
+    acc = mags * rng.choice([-1, 1], n)
+    d = (rng.random(n) * np.exp2(rng.integers(-20, 4, n).astype(np.float64))).astype(np.float32)
+    alpha = (rng.random(n) * np.exp2(rng.integers(-8, 2, n).astype(np.float64))).astype(np.float32)
+    other = {"order": 0, "once": 0, "no_alpha": 0, "no_unit": 0}
+    for unit in (1.0, 0.5):
+        for i in range(n):
+            got = O.dequant_f32(np.array([[int(acc[i])]]), d[i:i + 1], alpha[i], unit)[0, 0]
+            want = epilogue_exact(acc[i], d[i], alpha[i], unit)
+            assert Fraction(float(got)) == want, (int(acc[i]), float(d[i]), float(alpha[i]), unit)
+            A, D, Al, U = Fraction(int(acc[i])), Fraction(float(d[i])), Fraction(float(alpha[i])), Fraction(unit)
+            other["order"] += rn32(rn32(rn32(A * U) * D) * Al) != want
+            other["once"] += rn32(A * U * D * Al) != want
+            other["no_alpha"] += rn32(rn32(A * U) * rn32(D)) != want
+            other["no_unit"] += unit != 1.0 and rn32(rn32(A) * rn32(D * Al)) != want
+    assert all(v > 0 for v in other.values()), other
+
+
+def test_dequant_f32_agrees_with_float64_dequant():
+    """Three roundings of 2^-24 each: |dequant_f32 - dequant| <= 2^-22 |dequant| in the normal range."""
+    rng = np.random.default_rng(19)
+    acc = rng.integers(-127 * 261888, 127 * 261888 + 1, (64, 48))
+    d = (rng.random(64) * 0.05 + 1e-3).astype(np.float32)
+    alpha = F32(0.0159576)
+    for unit in (1.0, 0.5):
+        y32 = O.dequant_f32(acc, d, alpha, unit).astype(np.float64)
+        y64 = O.dequant(acc, d, alpha, unit)
+        assert np.all(np.abs(y32 - y64) <= 2.0 ** -22 * np.abs(y64))
+
+
 @pytest.mark.parametrize("case", read_cases("relu2_hand.txt"))
 def test_relu2_hand_cases(case):
     g, u, h = case
@@ -377,9 +463,18 @@ def test_oproj_residual():
     t, a = O.ternarize(latent_weights(52, 64, 128))
     res = normal(53, 4 * 64).reshape(4, 64).astype(np.float32)
     r = O.oproj_ref(x, t, a, res, keep=64)
-    r0 = O.bitlinear_a8(x, t, a, keep=64)
-    np.testing.assert_array_equal(r["y"], r0["y"] + res.astype(np.float64))
     assert np.all(r["mask"].sum(axis=1) == 64)
+    # against a float64 matmul of the dequantized, masked INT8 codes plus the residual
+    xq = r["codes"].astype(np.float64) * r["dscale"].astype(np.float64)[:, None]
+    wq = t.astype(np.float64) * float(a)
+    ref = xq @ wq.T + res.astype(np.float64)
+    bound = 1e-12 * (np.abs(xq) @ np.abs(wq).T + np.abs(res))        # cancellation-aware
+    assert np.all(np.abs(r["y"] - ref) <= bound)
+    # the residual really enters: an all-zero input row returns the residual row exactly
+    x0 = x.copy()
+    x0[1] = 0
+    r0 = O.oproj_ref(x0, t, a, res, keep=64)
+    np.testing.assert_array_equal(r0["y"][1], res[1].astype(np.float64))
 
 
 def test_generators_are_deterministic_and_gaussian():
