@@ -21,8 +21,9 @@
  *    is enqueued and no output is touched. BL_ERR_HIP reports a failed launch (hipGetLastError).
  *  * Activations X are row-major [M, K] (tokens x features) with row stride ldx elements.
  *    Weights W are [N, K] as in a linear layer; outputs Y = X W^T are row-major [M, N], row stride ldy.
- *  * Shapes: K % 256 == 0, N % 16 == 0, M >= 1 (any value, ragged tiles are masked); M*K, N*K < 2^31.
- *    The matmuls (GEMM, GEMV, conditional GLU) take K <= 2^18 - 256 = 261888: the int8-core INT4
+ *  * Shapes: K % 128 == 0 (one packed weight tile and one matrix-core step are 128 wide),
+ *    N % 16 == 0, M >= 1 (any value, ragged tiles are masked); M*K, N*K < 2^31.
+ *    The matmuls (GEMM, GEMV, conditional GLU) take K <= 2^18 - 128 = 262016: the int8-core INT4
  *    path keeps 1024 * sum(c t) in int32, which stays exact up to there (all paths do).
  *  * Alignment: code buffers, packed weights, x, y and the residual must be 16-byte aligned;
  *    ldx*elem_size, ldy*4 and ldr*4 must be multiples of 16 bytes.
@@ -45,7 +46,7 @@ extern "C" {
 typedef enum {
   BL_OK = 0,
   BL_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad enum, eps <= 0, ld too small, keep out of range */
-  BL_ERR_UNSUPPORTED_SHAPE = 2,  /* K % 256, N % 16, M > 8 for decode, size limits */
+  BL_ERR_UNSUPPORTED_SHAPE = 2,  /* K % 128, N % 16, M > 8 for decode, size limits */
   BL_ERR_MISALIGNED = 3,         /* a pointer or row stride breaks the 16-byte rule */
   BL_ERR_WORKSPACE_TOO_SMALL = 4,
   BL_ERR_HIP = 5
@@ -57,6 +58,19 @@ typedef enum {
 } bl_act_format;
 typedef enum { BL_IN_BF16 = 0, BL_IN_F32 = 1 } bl_in_dtype;
 typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_epi_kind;
+
+/* Operations, for bitlinear_workspace_size. */
+typedef enum {
+  BL_OP_QUANTIZE_ACT = 0, BL_OP_QUANTIZE_ACT_PER_TENSOR = 1, BL_OP_PACK_TERNARY = 2, BL_OP_PACK_TERNARY_ROWS = 3,
+  BL_OP_GEMM_W158A4 = 4, BL_OP_GEMM_W158A8_SPARSE = 5, BL_OP_GEMV_DECODE = 6, BL_OP_GEMV_DECODE_GLU_CONDITIONAL = 7,
+  BL_OP_KV_QUANTIZE = 8
+} bl_op;
+
+/* bitlinear_workspace_size: bytes of caller workspace the operation `op` needs for an [M, K] input and
+ * N outputs (N and K are accepted for every op; only the per-tensor quantizer depends on M). 0 for the
+ * operations that take no workspace; SIZE_MAX for an unknown op. Equals
+ * bitlinear_quantize_per_tensor_workspace_bytes(M) and bitlinear_pack_workspace_bytes() for those ops. */
+size_t bitlinear_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K);
 
 /*
  * Quantized activation codes (written by bitlinear_quantize_act, read by the matmul entry points):
@@ -109,8 +123,9 @@ typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_e
  *   d_x          [M, K] input, bf16 (in_dtype BL_IN_BF16) or float32 (BL_IN_F32), row stride ldx >= K.
  *                INT4 and FP4 accept bf16 and float32; INT8 accepts both.
  *   fmt          bl_act_format of the output.
- *   topk_keep    INT8 only: number of survivors per row in [0, K]; < 0 disables the mask.
- *                Must be < 0 for the 4-bit formats.
+ *   topk_keep    INT8 only: number of survivors per row in [0, K]; ANY NEGATIVE VALUE disables the mask
+ *                (every entry kept). 0 is not "off": it keeps nothing, so every code is 0. K keeps every
+ *                entry, like a negative value. Must be negative for the 4-bit formats.
  *   eps          > 0.
  *   d_row_absmax_hint  optional [M] float32 equal to max_k |x[m, k]| bit for bit (for instance the
  *                row_absmax output of the ReLU^2 GLU epilogue); INT8/FP4 then skip their max pass.

@@ -17,6 +17,9 @@ BL_OK = 0
 BL_ACT_INT4, BL_ACT_FP4_E2M1, BL_ACT_INT8, BL_ACT_INT4_E3M2, BL_ACT_FP4_E2M1_POW2 = 0, 1, 2, 3, 4
 BL_IN_BF16, BL_IN_F32 = 0, 1
 BL_EPI_NONE, BL_EPI_RESIDUAL, BL_EPI_RELU2_GLU = 0, 1, 2
+OPS = {"quantize_act": 0, "quantize_act_per_tensor": 1, "pack_ternary": 2, "pack_ternary_rows": 3,
+       "gemm_w158a4": 4, "gemm_w158a8_sparse": 5, "gemv_decode": 6, "gemv_decode_glu_conditional": 7,
+       "kv_quantize": 8}
 
 FORMATS = {"int4": BL_ACT_INT4, "fp4": BL_ACT_FP4_E2M1, "int8": BL_ACT_INT8, "int4_e3m2": BL_ACT_INT4_E3M2,
            "fp4_pow2": BL_ACT_FP4_E2M1_POW2}
@@ -26,7 +29,7 @@ EXPORTED = (
     "bitlinear_pack_workspace_bytes", "bitlinear_gemm_w158a4", "bitlinear_gemm_w158a8_sparse",
     "bitlinear_gemv_decode", "bitlinear_gemv_decode_glu_conditional", "bitlinear_status_string",
     "bitlinear_abi_version", "bitlinear_quantize_act_per_tensor", "bitlinear_quantize_per_tensor_workspace_bytes",
-    "bitlinear_kv_quantize", "bitlinear_calibrate_mfma",
+    "bitlinear_kv_quantize", "bitlinear_calibrate_mfma", "bitlinear_workspace_size",
 )
 
 
@@ -68,6 +71,8 @@ def _lib():
         lib.bitlinear_packed_bytes.restype = sz
         lib.bitlinear_pack_workspace_bytes.argtypes = []
         lib.bitlinear_pack_workspace_bytes.restype = sz
+        lib.bitlinear_workspace_size.argtypes = [i32, i64, i64, i64]
+        lib.bitlinear_workspace_size.restype = sz
         lib.bitlinear_pack_ternary.argtypes = [vp, i64, i64, f32, vp, vp, vp, sz, vp]
         lib.bitlinear_pack_ternary.restype = i32
         lib.bitlinear_kv_quantize.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, i64, i32, f32, vp, vp, vp, i64,
@@ -219,6 +224,11 @@ def bitlinear_packed_bytes(N, K):
 
 def bitlinear_pack_workspace_bytes():
     return int(_lib().bitlinear_pack_workspace_bytes())
+
+
+def bitlinear_workspace_size(op, M, N, K):
+    """Workspace bytes of an operation (name from OPS or the bl_op value); SIZE_MAX for an unknown op."""
+    return int(_lib().bitlinear_workspace_size(OPS[op] if isinstance(op, str) else int(op), M, N, K))
 
 
 def _pack(fn_name, w, eps, packed, alpha, workspace, stream):

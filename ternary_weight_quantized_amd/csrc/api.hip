@@ -2,6 +2,7 @@
 // Nothing is enqueued when validation fails; the library never allocates device memory.
 #include <cmath>
 #include <cstdint>
+#include <cstddef>
 
 #include "bl_kernels.h"
 
@@ -13,7 +14,7 @@ constexpr int64_t kMaxElems = (int64_t)1 << 31;
 // Longest reduction the matmuls accept. The int8-core INT4 path holds 1024 * sum(c t) in int32
 // (|c| <= 8, |t| <= 1), so K * 8 * 1024 must stay below 2^31; the INT8 path (64 * 127 per term) and
 // the fp32 sums of the FP6 / FP4 paths (exact below 2^24) have more room.
-constexpr int64_t kMaxMatmulK = ((int64_t)1 << 18) - 256;
+constexpr int64_t kMaxMatmulK = ((int64_t)1 << 18) - 128;
 
 bl_status hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
@@ -24,7 +25,7 @@ bl_status check_mm(int32_t fmt, const void* codes, const float* scale, int64_t M
   if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8 && fmt != BL_ACT_INT4_E3M2)
     return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1 || N < 1) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (K % 256 != 0 || N % 16 != 0 || K > kMaxMatmulK) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (K % 128 != 0 || N % 16 != 0 || K > kMaxMatmulK) return BL_ERR_UNSUPPORTED_SHAPE;
   if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ldy < N) return BL_ERR_INVALID_ARGUMENT;
   if (!aligned16(codes) || !aligned16(packed) || !aligned16(y) || (ldy * 4) % 16 != 0) return BL_ERR_MISALIGNED;
@@ -80,6 +81,26 @@ size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
 
 size_t bitlinear_pack_workspace_bytes(void) { return 256 * sizeof(unsigned long long); }
 
+size_t bitlinear_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K) {
+  (void)N; (void)K;
+  switch (op) {
+    case BL_OP_QUANTIZE_ACT:
+    case BL_OP_GEMM_W158A4:
+    case BL_OP_GEMM_W158A8_SPARSE:
+    case BL_OP_GEMV_DECODE:
+    case BL_OP_GEMV_DECODE_GLU_CONDITIONAL:
+    case BL_OP_KV_QUANTIZE:
+      return 0;
+    case BL_OP_QUANTIZE_ACT_PER_TENSOR:
+      return bitlinear_quantize_per_tensor_workspace_bytes(M);
+    case BL_OP_PACK_TERNARY:
+    case BL_OP_PACK_TERNARY_ROWS:
+      return bitlinear_pack_workspace_bytes();
+    default:
+      return SIZE_MAX;
+  }
+}
+
 bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, int64_t K, int64_t ldx, int32_t fmt,
                                  int32_t topk_keep, float eps, const float* d_row_absmax_hint, void* d_codes,
                                  float* d_scale, uint32_t* d_mask, void* stream) {
@@ -90,7 +111,7 @@ bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, i
     return BL_ERR_INVALID_ARGUMENT;
   if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (K % 256 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (K % 128 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
   if (M * K >= kMaxElems || M * ldx >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ldx < K) return BL_ERR_INVALID_ARGUMENT;
   if (fmt != BL_ACT_INT8 && (topk_keep >= 0 || d_mask)) return BL_ERR_INVALID_ARGUMENT;
@@ -108,32 +129,50 @@ size_t bitlinear_quantize_per_tensor_workspace_bytes(int64_t M) {
   return bl_quantize_per_tensor_ws_bytes((long)M);
 }
 
-bl_status bitlinear_quantize_act_per_tensor(const void* d_x, int32_t in_dtype, int64_t M, int64_t K, int64_t ldx,
-                                            int32_t fmt, float eps, void* d_workspace, size_t ws_bytes,
-                                            void* d_codes, float* d_scale, void* stream) {
-  if (!d_x || !d_codes || !d_scale || !d_workspace) return BL_ERR_INVALID_ARGUMENT;
+}  // extern "C"
+
+namespace {
+
+// Validation of the per-tensor quantizer's arguments other than the workspace.
+bl_status check_per_tensor(const void* d_x, int32_t in_dtype, int64_t M, int64_t K, int64_t ldx, int32_t fmt,
+                           float eps, const void* d_codes, const float* d_scale) {
+  if (!d_x || !d_codes || !d_scale) return BL_ERR_INVALID_ARGUMENT;
   if (in_dtype != BL_IN_BF16 && in_dtype != BL_IN_F32) return BL_ERR_INVALID_ARGUMENT;
   if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8 && fmt != BL_ACT_INT4_E3M2 &&
       fmt != BL_ACT_FP4_E2M1_POW2)
     return BL_ERR_INVALID_ARGUMENT;
   if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (K % 256 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (K % 128 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
   if (M * K >= kMaxElems || M * ldx >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ldx < K) return BL_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < bitlinear_quantize_per_tensor_workspace_bytes(M)) return BL_ERR_WORKSPACE_TOO_SMALL;
   const int64_t esz = in_dtype == BL_IN_F32 ? 4 : 2;
-  if (!aligned16(d_x) || !aligned16(d_codes) || !aligned16(d_workspace) || (ldx * esz) % 16 != 0)
-    return BL_ERR_MISALIGNED;
+  if (!aligned16(d_x) || !aligned16(d_codes) || (ldx * esz) % 16 != 0) return BL_ERR_MISALIGNED;
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bl_status bitlinear_quantize_act_per_tensor(const void* d_x, int32_t in_dtype, int64_t M, int64_t K, int64_t ldx,
+                                            int32_t fmt, float eps, void* d_workspace, size_t ws_bytes,
+                                            void* d_codes, float* d_scale, void* stream) {
+  if (!d_workspace) return BL_ERR_INVALID_ARGUMENT;
+  const bl_status s = check_per_tensor(d_x, in_dtype, M, K, ldx, fmt, eps, d_codes, d_scale);
+  if (s != BL_OK) return s;
+  if (ws_bytes < bitlinear_quantize_per_tensor_workspace_bytes(M)) return BL_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(d_workspace)) return BL_ERR_MISALIGNED;
   return hip_status(bl_launch_quantize_per_tensor(d_x, in_dtype == BL_IN_F32, (int)M, (int)K, (long)ldx, fmt, eps,
                                                   d_workspace, d_codes, d_scale, static_cast<hipStream_t>(stream)));
 }
+
 
 bl_status bitlinear_pack_ternary(const float* d_w, int64_t N, int64_t K, float eps, void* d_packed, float* d_alpha,
                                  void* d_workspace, size_t ws_bytes, void* stream) {
   if (!d_w || !d_packed || !d_alpha || !d_workspace) return BL_ERR_INVALID_ARGUMENT;
   if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
-  if (N < 1 || K < 1 || K % 256 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (N < 1 || K < 1 || K % 128 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
   if (N * K >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ws_bytes < bitlinear_pack_workspace_bytes()) return BL_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(d_w) || !aligned16(d_packed) || !aligned16(d_workspace)) return BL_ERR_MISALIGNED;
@@ -145,7 +184,7 @@ bl_status bitlinear_pack_ternary_rows(const float* d_w, int64_t N, int64_t K, fl
                                       float* d_alpha, void* d_workspace, size_t ws_bytes, void* stream) {
   if (!d_w || !d_packed || !d_alpha || !d_workspace) return BL_ERR_INVALID_ARGUMENT;
   if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
-  if (N < 1 || K < 1 || K % 256 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (N < 1 || K < 1 || K % 128 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
   if (N * K >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ws_bytes < bitlinear_pack_workspace_bytes()) return BL_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(d_w) || !aligned16(d_packed) || !aligned16(d_workspace)) return BL_ERR_MISALIGNED;

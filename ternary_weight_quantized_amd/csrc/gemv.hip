@@ -49,17 +49,18 @@ __device__ __forceinline__ v4i expand_a_int8(uint4 q) {
 
 // One chunk of up to CH K tiles starting at kt0 (kt0 < kt_end). FULL chunks load unconditionally, so
 // the compiler can wait for each tile separately; the ragged last chunk clamps its addresses and
-// drops the tiles past kt_end.
+// drops the tiles past kt_end. Offsets are 32-bit: N K / 4 < 2^29 bytes of weights, M K < 2^22
+// bytes of codes.
 template <bool A8, int NB, bool FULL, int CH = 4>
-__device__ __forceinline__ void chunk(const uint8_t* arp, const uint8_t* const (&wp)[2], long wstep, int kt0,
+__device__ __forceinline__ void chunk(const uint8_t* arp, const uint8_t* const (&wp)[2], uint32_t wstep, int kt0,
                                       int kt_end, int g, v4i (&acc)[NB][2]) {
   constexpr int AV = A8 ? 2 : 1;              // 16-byte activation vectors per lane and tile
-  constexpr long ABYTES = A8 ? 128 : 64;      // activation bytes per row and tile
+  constexpr uint32_t ABYTES = A8 ? 128 : 64;  // activation bytes per row and tile
   uint4 at[CH][AV];
   uint2 wt[NB][CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int kt = FULL ? kt0 + c : min(kt0 + c, kt_end - 1);
+    const uint32_t kt = FULL ? kt0 + c : min(kt0 + c, kt_end - 1);
 #pragma unroll
     for (int v = 0; v < AV; ++v) at[c][v] = *reinterpret_cast<const uint4*>(arp + kt * ABYTES + 16 * v);
   }
@@ -77,14 +78,14 @@ __device__ __forceinline__ void chunk(const uint8_t* arp, const uint8_t* const (
     for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
       for (int c = 0; c < CH; ++c)
-        wt[mtx][c] = live[c] ? *reinterpret_cast<const uint2*>(wp[mtx] + (long)(kt0 + c) * wstep) : make_uint2(0u, 0u);
+        wt[mtx][c] = live[c] ? *reinterpret_cast<const uint2*>(wp[mtx] + (uint32_t)(kt0 + c) * wstep) : make_uint2(0u, 0u);
   } else {
 #pragma unroll
     for (int mtx = 0; mtx < NB; ++mtx)
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const int kt = FULL ? kt0 + c : min(kt0 + c, kt_end - 1);
-        wt[mtx][c] = *reinterpret_cast<const uint2*>(wp[mtx] + (long)kt * wstep);
+        const uint32_t kt = FULL ? kt0 + c : min(kt0 + c, kt_end - 1);
+        wt[mtx][c] = *reinterpret_cast<const uint2*>(wp[mtx] + kt * wstep);
       }
   }
 #pragma unroll
@@ -123,21 +124,26 @@ __global__ __launch_bounds__(NWV * 64) void k_gemv(const uint8_t* __restrict__ A
   const int kt_end = min(KT, kt_begin + per);
   const int r = lane & 15, g = lane >> 4;
   const int n = 16 * G + r;
-  const long arow = A8 ? K : (K >> 1);
-  const uint8_t* arp = A + (long)min(r, M - 1) * arow + (A8 ? 32 * g : 16 * g);
-  const uint8_t* const wp[2] = {W + (long)G * 512 + lane * 8, (NB > 1 ? W2 : W) + (long)G * 512 + lane * 8};
-  const long wstep = (long)NG * 512;
+  const uint32_t arow = A8 ? K : (K >> 1);
+  const uint8_t* arp = A + (uint32_t)min(r, M - 1) * arow + (A8 ? 32 * g : 16 * g);
+  const uint32_t woff = (uint32_t)G * 512u + (uint32_t)lane * 8u;
+  const uint8_t* const wp[2] = {W + woff, (NB > 1 ? W2 : W) + woff};
+  const uint32_t wstep = (uint32_t)NG * 512u;
 
-  // everything the epilogue reads, fetched before the weight stream (rows past M repeat row M-1)
-  float ds[4], res[4];
+  // what the epilogue reads, fetched by the epilogue wave only, before its weight stream (rows past
+  // M repeat row M-1; the other waves only stream weights and hand over partial sums)
+  float ds[4] = {0.f, 0.f, 0.f, 0.f}, res[4] = {0.f, 0.f, 0.f, 0.f};
+  float alpha = 0.f, alpha2 = 0.f;
+  if (wave == 0) {
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int m = min(4 * g + v, M - 1);
-    ds[v] = ascale[m];
-    if constexpr (EPI == BL_EPI_RESIDUAL) res[v] = R[(long)m * ldr + n];
+    for (int v = 0; v < 4; ++v) {
+      const int m = min(4 * g + v, M - 1);
+      ds[v] = ascale[m];
+      if constexpr (EPI == BL_EPI_RESIDUAL) res[v] = R[(long)m * ldr + n];
+    }
+    alpha = *walpha;
+    if constexpr (EPI == BL_EPI_RELU2_GLU) alpha2 = *w2alpha;
   }
-  const float alpha = *walpha;
-  const float alpha2 = (EPI == BL_EPI_RELU2_GLU) ? *w2alpha : 0.f;
 
   v4i acc[NB][2];
 #pragma unroll
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemv(const uint8_t* __restrict__ A
     else chunk<A8, NB, false, CHN>(arp, wp, wstep, kt0, kt_end, g, acc);
   }
 
-  // exact int32 reduction of the eight K partitions
+  // exact int32 reduction of the K partitions
 #pragma unroll
   for (int mtx = 0; mtx < NB; ++mtx) acc[mtx][0] += acc[mtx][1];
   if (wave > 0) {
@@ -267,8 +273,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_glu_cond_fused(const uint8_t* __
   const int r = lane & 15, g4 = lane >> 4;
   const long arow = K >> 1;
   const uint8_t* arp = A + (long)min(r, M - 1) * arow + 16 * g4;
-  const uint8_t* const wp[2] = {Wg + (long)G * 512 + lane * 8, Wg + (long)G * 512 + lane * 8};
-  const long wstep = (long)NG * 512;
+  const uint8_t* const wp[2] = {Wg + (uint32_t)G * 512u + (uint32_t)lane * 8u, Wg + (uint32_t)G * 512u + (uint32_t)lane * 8u};
+  const uint32_t wstep = (uint32_t)NG * 512u;
   float ds[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) ds[v] = ascale[min(4 * g4 + v, M - 1)];

@@ -12,9 +12,10 @@
 //  - k_topk_blk: INT8 with the Top-K mask for bf16 rows of up to 8192 elements, one block per row.
 //  - k_quant_res / k_quant_stream: the remaining cases (float32 rows with a Top-K mask, longer
 //    rows). One wave64 owns one token row, four rows per block; a lane owns four consecutive
-//    elements of every 256-element group (group g, elements 256g + 4*lane .. +3). Rows of up to
-//    4096 elements stay in registers between the reduction and the quantization ("resident");
-//    longer rows are read again from global memory ("streaming").
+//    elements of every 256-element group (group g, elements 256g + 4*lane .. +3; when K % 256 ==
+//    128 the last group is half, lanes 32..63 hold nothing). k_quant_res (INT8 with Top-K of float32
+//    rows of up to 4096 elements) keeps the row in registers between the threshold search and the
+//    codes ("resident"); k_quant_stream reads longer rows again from global memory ("streaming").
 //  - k_tensor_*: the statistics of the per-tensor variant.
 #include <algorithm>
 
@@ -142,13 +143,15 @@ __device__ __forceinline__ uint32_t code_e3m2(float v, float s) {
 
 // Store the 4 codes (24 bits, code j at bits 6j) of elements 256g + 4 lane .. +3 of row m into the
 // tiled E3M2 layout (16 rows x 128 codes per 1536-byte tile, 96 bytes per row, code k at bits 6k):
-// four lanes make 12 bytes, written as three dwords.
-__device__ __forceinline__ void store_e3m2(uint8_t* __restrict__ codes, int m, int K, int g, int lane, uint32_t v24) {
+// four lanes make 12 bytes, written as three dwords. Every lane takes part in the shuffle; only lanes
+// holding elements (ok, whole groups of four) store.
+__device__ __forceinline__ void store_e3m2(uint8_t* __restrict__ codes, int m, int K, int g, int lane, uint32_t v24,
+                                           bool ok) {
   const uint32_t nxt = __shfl_down(v24, 1, 64);
   const int i = lane & 3, q = lane >> 2;
   const uint32_t w = i == 0 ? (v24 | (nxt << 24)) : i == 1 ? ((v24 >> 8) | (nxt << 16)) : ((v24 >> 16) | (nxt << 8));
   const long tile = (long)(m >> 4) * (K >> 7) + 2 * g + (q >> 3);
-  if (i < 3) *reinterpret_cast<uint32_t*>(codes + tile * 1536 + (m & 15) * 96 + 12 * (q & 7) + 4 * i) = w;
+  if (i < 3 && ok) *reinterpret_cast<uint32_t*>(codes + tile * 1536 + (m & 15) * 96 + 12 * (q & 7) + 4 * i) = w;
 }
 
 // FP4 scales from the row maximum gamma. MinMax (BL_ACT_FP4_E2M1): the maximum maps to 6,
@@ -185,177 +188,123 @@ __device__ __forceinline__ uint32_t topk_threshold(int keep, int lo_bit, CountFn
 
 // Mask word assembly: lane holds a nibble for elements 4*lane..4*lane+3 of a 256-group; eight
 // lanes make one 32-bit word (bit k % 32 of word k / 32).
-__device__ __forceinline__ void store_mask_nibble(uint32_t* __restrict__ mrow, int g, int lane, uint32_t nib) {
+__device__ __forceinline__ void store_mask_nibble(uint32_t* __restrict__ mrow, int g, int lane, uint32_t nib,
+                                                  bool ok) {
   uint32_t w = nib << (4 * (lane & 7));
   w |= __shfl_xor(w, 1, 64);
   w |= __shfl_xor(w, 2, 64);
   w |= __shfl_xor(w, 4, 64);
-  if ((lane & 7) == 0) mrow[8 * g + (lane >> 3)] = w;
+  if ((lane & 7) == 0 && ok) mrow[8 * g + (lane >> 3)] = w;
 }
 
-// ============================================================================ resident kernels
-template <int FMT, int IN_F32, int NGMAX>
+// ============================================================================ resident kernel
+// INT8 with a Top-K mask for float32 rows of up to 4096 elements (the only case the block-per-row
+// kernels do not take at that length): one wave per row, the row held in registers between the
+// threshold search and the codes. Group g holds elements 256 g + 4 lane .. +3; when K % 256 == 128
+// the last group is a half group whose lanes 32..63 hold nothing (zeros, excluded from the ties and
+// from every store).
+template <int IN_F32, int NGMAX>
 __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, int M, int K, long ldx,
                                                    int keep, float eps, const float* __restrict__ hint,
                                                    uint8_t* __restrict__ codes, float* __restrict__ scale,
                                                    uint32_t* __restrict__ mask) {
-  __shared__ unsigned long long bins[(FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2) ? 4 : 1][256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
   if (row >= M) return;                         // wave-uniform; no block barriers below
-  const int NG = K >> 8;
+  const int NG = (K + 255) >> 8;
   const long base = (long)row * ldx + 4 * lane;
   float v[NGMAX][4];
+  bool ok[NGMAX];
+#pragma unroll
+  for (int g = 0; g < NGMAX; ++g) {
+    ok[g] = g < NG && 256 * g + 4 * lane < K;
+    if (ok[g]) load4<IN_F32>(x, base + 256 * g, v[g]);
+    else v[g][0] = v[g][1] = v[g][2] = v[g][3] = 0.0f;
+  }
+  // gamma = max |x| over the whole row (exact)
+  float gamma;
+  if (hint) {
+    gamma = hint[row];
+  } else {
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t b = bl_f2u(v[g][j]) & 0x7FFFFFFFu;
+        mx = b > mx ? b : mx;
+      }
+    gamma = bl_u2f(bl_wave_max_u(mx));
+  }
+  const float s = 127.0f / (gamma + eps);
+  const bool all = keep < 0 || keep >= K;
+  const bool none = keep == 0;
+  float Tf = 0.0f;
+  int need = 0;
+  if (!all && !none) {
+    // every candidate threshold is > 0, so the zeros of missing lanes never count
+    auto count_ge = [&](float c) {
+      int n = 0;
+#pragma unroll
+      for (int g = 0; g < NGMAX; ++g)
+        if (g < NG) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) n += __popcll(__ballot(fabsf(v[g][j]) >= c));
+        }
+      return n;
+    };
+    Tf = bl_u2f(topk_threshold(keep, IN_F32 ? 0 : 16, count_ge));
+    int greater = 0;
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g)
+      if (g < NG) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) greater += __popcll(__ballot(fabsf(v[g][j]) > Tf));
+      }
+    need = keep - greater;                    // >= 1 ties at T survive, lowest index first
+  }
+  uint32_t* crow = reinterpret_cast<uint32_t*>(codes + (long)row * K) + lane;
+  uint32_t* mrow = mask ? mask + (long)row * (K >> 5) : nullptr;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int tie_base = 0;
 #pragma unroll
   for (int g = 0; g < NGMAX; ++g)
-    if (g < NG) load4<IN_F32>(x, base + 256 * g, v[g]);
-
-  if constexpr (FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2) {
-    float beta;
-    if (hint) {
-      beta = hint[row];                           // a given beta (per-tensor variant)
-    } else {
-      AbsSum acc;
+    if (g < NG) {
+      uint32_t keepbits;
+      if (all) {
+        keepbits = 0xFu;
+      } else if (none) {
+        keepbits = 0u;
+      } else {
+        uint32_t gt = 0u, eq = 0u;
+        int before = 0, tot = 0;
 #pragma unroll
-      for (int g = 0; g < NGMAX; ++g)
-        if (g < NG) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc.add(v[g][j]);
+        for (int j = 0; j < 4; ++j) {
+          const float a = fabsf(v[g][j]);
+          gt |= (a > Tf ? 1u : 0u) << j;
+          const bool t = ok[g] && a == Tf;
+          eq |= (t ? 1u : 0u) << j;
+          const unsigned long long bal = __ballot(t);
+          before += __popcll(bal & lt);
+          tot += __popcll(bal);
         }
-      double S = bl_wave_sum_d(acc.s);
-      const uint32_t ex = wave_max_exps(acc.exps());
-      const uint32_t emax = exps_emax(ex), emin = exps_emin(ex);
-      if (!sum_is_exact<IN_F32>(emax, emin, K)) {
-        unsigned long long* b = bins[wave];
-        bins_clear(b, lane);
+        // rank of this lane's ties = ties of earlier groups + of lower lanes + of lower j
+        int rank = tie_base + before;
+        uint32_t kb = gt;
 #pragma unroll
-        for (int g = 0; g < NGMAX; ++g)
-          if (g < NG) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bins_add(b, v[g][j]);
-          }
-        S = bins_finish(b, lane);
+        for (int j = 0; j < 4; ++j)
+          if ((eq >> j) & 1u) { kb |= (rank < need ? 1u : 0u) << j; ++rank; }
+        keepbits = kb;
+        tie_base += tot;
       }
-      beta = (float)(S / (double)K);
+      uint32_t c = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((keepbits >> j) & 1u) c |= code_int8(v[g][j], s) << (8 * j);
+      if (ok[g]) crow[64 * g] = c;
+      if (mrow) store_mask_nibble(mrow, g, lane, keepbits, ok[g]);
     }
-    const float s = bl_u2f(BL_SQRT7_BITS) / (beta + eps);
-    if constexpr (FMT == BL_ACT_INT4) {
-      uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
-#pragma unroll
-      for (int g = 0; g < NGMAX; ++g)
-        if (g < NG) {
-          const uint32_t c = code_int4(v[g][0], s) | (code_int4(v[g][1], s) << 4) |
-                             (code_int4(v[g][2], s) << 8) | (code_int4(v[g][3], s) << 12);
-          crow[64 * g] = (uint16_t)c;
-        }
-    } else {
-#pragma unroll
-      for (int g = 0; g < NGMAX; ++g)
-        if (g < NG)
-          store_e3m2(codes, row, K, g, lane, code_e3m2(v[g][0], s) | (code_e3m2(v[g][1], s) << 6) |
-                                                 (code_e3m2(v[g][2], s) << 12) | (code_e3m2(v[g][3], s) << 18));
-    }
-    if (lane == 0) scale[row] = beta / bl_u2f(BL_SQRT7_BITS);
-  } else {
-    // gamma = max |x| over the whole row (exact); FP4 and INT8 share it.
-    float gamma;
-    if (hint) {
-      gamma = hint[row];
-    } else {
-      uint32_t mx = 0u;
-#pragma unroll
-      for (int g = 0; g < NGMAX; ++g)
-        if (g < NG) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t b = bl_f2u(v[g][j]) & 0x7FFFFFFFu;
-            mx = b > mx ? b : mx;
-          }
-        }
-      gamma = bl_u2f(bl_wave_max_u(mx));
-    }
-    if constexpr (FMT == BL_ACT_FP4_E2M1 || FMT == BL_ACT_FP4_E2M1_POW2) {
-      float s, dscale;
-      fp4_scales<FMT == BL_ACT_FP4_E2M1_POW2>(gamma, eps, &s, &dscale);
-      uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
-#pragma unroll
-      for (int g = 0; g < NGMAX; ++g)
-        if (g < NG) {
-          const uint32_t c = codes_fp4_4(v[g][0], v[g][1], v[g][2], v[g][3], s);
-          crow[64 * g] = (uint16_t)c;
-        }
-      if (lane == 0) scale[row] = dscale;
-    } else {
-      const float s = 127.0f / (gamma + eps);
-      const bool all = keep < 0 || keep >= K;
-      const bool none = keep == 0;
-      float Tf = 0.0f;
-      int need = 0;
-      if (!all && !none) {
-        auto count_ge = [&](float c) {
-          int n = 0;
-#pragma unroll
-          for (int g = 0; g < NGMAX; ++g)
-            if (g < NG) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) n += __popcll(__ballot(fabsf(v[g][j]) >= c));
-            }
-          return n;
-        };
-        Tf = bl_u2f(topk_threshold(keep, IN_F32 ? 0 : 16, count_ge));
-        int greater = 0;
-#pragma unroll
-        for (int g = 0; g < NGMAX; ++g)
-          if (g < NG) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) greater += __popcll(__ballot(fabsf(v[g][j]) > Tf));
-          }
-        need = keep - greater;                    // >= 1 ties at T survive, lowest index first
-      }
-      uint32_t* crow = reinterpret_cast<uint32_t*>(codes + (long)row * K) + lane;
-      uint32_t* mrow = mask ? mask + (long)row * (K >> 5) : nullptr;
-      const unsigned long long lt = (1ull << lane) - 1ull;
-      int tie_base = 0;
-#pragma unroll
-      for (int g = 0; g < NGMAX; ++g)
-        if (g < NG) {
-          uint32_t keepbits;
-          if (all) {
-            keepbits = 0xFu;
-          } else if (none) {
-            keepbits = 0u;
-          } else {
-            uint32_t gt = 0u, eq = 0u;
-            int before = 0, tot = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float a = fabsf(v[g][j]);
-              gt |= (a > Tf ? 1u : 0u) << j;
-              const bool t = (a == Tf);
-              eq |= (t ? 1u : 0u) << j;
-              const unsigned long long bal = __ballot(t);
-              before += __popcll(bal & lt);
-              tot += __popcll(bal);
-            }
-            // rank of this lane's ties = ties of earlier groups + of lower lanes + of lower j
-            int rank = tie_base + before;
-            uint32_t kb = gt;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if ((eq >> j) & 1u) { kb |= (rank < need ? 1u : 0u) << j; ++rank; }
-            keepbits = kb;
-            tie_base += tot;
-          }
-          uint32_t c = 0u;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if ((keepbits >> j) & 1u) c |= code_int8(v[g][j], s) << (8 * j);
-          crow[64 * g] = c;
-          if (mrow) store_mask_nibble(mrow, g, lane, keepbits);
-        }
-      if (lane == 0) scale[row] = gamma / 127.0f;
-    }
-  }
+  if (lane == 0) scale[row] = gamma / 127.0f;
 }
 
 // ============================================================================ Top-K, block per row
@@ -731,8 +680,13 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
   if (row >= M) return;
-  const int NG = K >> 8;
+  const int NG = (K + 255) >> 8;                  // the last group is half when K % 256 == 128
   const long base = (long)row * ldx + 4 * lane;
+  // elements 256 g + 4 lane .. +3, or zeros for the lanes past the end of a half group
+  auto load = [&](int g, float (&v)[4]) {
+    if (256 * g + 4 * lane < K) load4<IN_F32>(x, base + 256 * g, v);
+    else v[0] = v[1] = v[2] = v[3] = 0.0f;
+  };
 
   if constexpr (FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2) {
     float beta;
@@ -742,7 +696,7 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
       AbsSum acc;
       for (int g = 0; g < NG; ++g) {
         float v[4];
-        load4<IN_F32>(x, base + 256 * g, v);
+        load(g, v);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc.add(v[j]);
       }
@@ -754,7 +708,7 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
         bins_clear(b, lane);
         for (int g = 0; g < NG; ++g) {
           float v[4];
-          load4<IN_F32>(x, base + 256 * g, v);
+          load(g, v);
 #pragma unroll
           for (int j = 0; j < 4; ++j) bins_add(b, v[j]);
         }
@@ -765,15 +719,17 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
     const float s = bl_u2f(BL_SQRT7_BITS) / (beta + eps);
     for (int g = 0; g < NG; ++g) {
       float v[4];
-      load4<IN_F32>(x, base + 256 * g, v);
+      load(g, v);
       if constexpr (FMT == BL_ACT_INT4) {
         uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;
-        crow[64 * g] = (uint16_t)(code_int4(v[0], s) | (code_int4(v[1], s) << 4) |
-                                   (code_int4(v[2], s) << 8) | (code_int4(v[3], s) << 12));
+        if (256 * g + 4 * lane < K)
+          crow[64 * g] = (uint16_t)(code_int4(v[0], s) | (code_int4(v[1], s) << 4) |
+                                     (code_int4(v[2], s) << 8) | (code_int4(v[3], s) << 12));
       } else {
         store_e3m2(codes, row, K, g, lane,
                    code_e3m2(v[0], s) | (code_e3m2(v[1], s) << 6) | (code_e3m2(v[2], s) << 12) |
-                       (code_e3m2(v[3], s) << 18));
+                       (code_e3m2(v[3], s) << 18),
+                   256 * g + 4 * lane < K);
       }
     }
     if (lane == 0) scale[row] = beta / bl_u2f(BL_SQRT7_BITS);
@@ -785,7 +741,7 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
       uint32_t mx = 0u;
       for (int g = 0; g < NG; ++g) {
         float v[4];
-        load4<IN_F32>(x, base + 256 * g, v);
+        load(g, v);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t b = bl_f2u(v[j]) & 0x7FFFFFFFu;
@@ -800,8 +756,9 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
       uint16_t* crow = reinterpret_cast<uint16_t*>(codes + (long)row * (K >> 1)) + lane;   // 2 bytes per lane per group
       for (int g = 0; g < NG; ++g) {
         float v[4];
-        load4<IN_F32>(x, base + 256 * g, v);
-        crow[64 * g] = (uint16_t)codes_fp4_4(v[0], v[1], v[2], v[3], s);
+        load(g, v);
+        const uint32_t c = codes_fp4_4(v[0], v[1], v[2], v[3], s);
+        if (256 * g + 4 * lane < K) crow[64 * g] = (uint16_t)c;
       }
       if (lane == 0) scale[row] = dscale;
     } else {
@@ -815,7 +772,7 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
           int n = 0;
           for (int g = 0; g < NG; ++g) {
             float v[4];
-            load4<IN_F32>(x, base + 256 * g, v);
+            load(g, v);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float a = fabsf(v[j]);
@@ -833,7 +790,7 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
       int tie_base = 0;
       for (int g = 0; g < NG; ++g) {
         float v[4];
-        load4<IN_F32>(x, base + 256 * g, v);
+        load(g, v);
         uint32_t keepbits;
         if (all) {
           keepbits = 0xFu;
@@ -846,7 +803,7 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
           for (int j = 0; j < 4; ++j) {
             const float a = fabsf(v[j]);
             gt |= (a > Tf ? 1u : 0u) << j;
-            const bool t = (a == Tf);
+            const bool t = 256 * g + 4 * lane < K && a == Tf;   // zeros past the end never tie
             eq |= (t ? 1u : 0u) << j;
             const unsigned long long bal = __ballot(t);
             before += __popcll(bal & lt);
@@ -864,8 +821,8 @@ __global__ __launch_bounds__(256) void k_quant_stream(const void* __restrict__ x
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if ((keepbits >> j) & 1u) c |= code_int8(v[j], s) << (8 * j);
-        crow[64 * g] = c;
-        if (mrow) store_mask_nibble(mrow, g, lane, keepbits);
+        if (256 * g + 4 * lane < K) crow[64 * g] = c;
+        if (mrow) store_mask_nibble(mrow, g, lane, keepbits, 256 * g + 4 * lane < K);
       }
       if (lane == 0) scale[row] = gamma / 127.0f;
     }
@@ -1050,7 +1007,6 @@ template <int FMT, int IN_F32>
 hipError_t launch_fmt(const void* x, int M, int K, long ldx, int keep, float eps, const float* hint,
                       uint8_t* codes, float* scale, uint32_t* mask, hipStream_t st) {
   const dim3 grid((M + 3) / 4), block(256);
-  const int NG = K >> 8;
   // no Top-K mask: one block per row
   const bool plain = FMT != BL_ACT_INT8 || (mask == nullptr && (keep < 0 || keep >= K));
   if (plain && K <= 16384) {
@@ -1063,9 +1019,10 @@ hipError_t launch_fmt(const void* x, int M, int K, long ldx, int keep, float eps
       hipLaunchKernelGGL((k_quant_blk<FMT, IN_F32, 8>), dim3(M), block, 0, st, x, M, K, ldx, eps, hint, codes, scale);
     return hipGetLastError();
   }
-  if constexpr (FMT == BL_ACT_INT8 && !IN_F32) {
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
-    if (K <= 8192) {
+  if constexpr (FMT == BL_ACT_INT8) {
+    if (!IN_F32 && K <= 8192) {
+      // Top-K of bf16 rows: one block per row
+      const uint16_t* xb = static_cast<const uint16_t*>(x);
       const int per = (K / 8 + 255) / 256;
       if (per <= 1)
         hipLaunchKernelGGL((k_topk_blk<1>), dim3(M), block, 0, st, xb, M, K, ldx, keep, eps, hint, codes, scale, mask);
@@ -1075,22 +1032,24 @@ hipError_t launch_fmt(const void* x, int M, int K, long ldx, int keep, float eps
         hipLaunchKernelGGL((k_topk_blk<4>), dim3(M), block, 0, st, xb, M, K, ldx, keep, eps, hint, codes, scale, mask);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_quant_stream<FMT, IN_F32>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
-                       mask);
-  } else {
-    if (NG <= 4)
-      hipLaunchKernelGGL((k_quant_res<FMT, IN_F32, 4>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
-                         mask);
-    else if (NG <= 8)
-      hipLaunchKernelGGL((k_quant_res<FMT, IN_F32, 8>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
-                         mask);
-    else if (NG <= 16)
-      hipLaunchKernelGGL((k_quant_res<FMT, IN_F32, 16>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
-                         mask);
-    else
-      hipLaunchKernelGGL((k_quant_stream<FMT, IN_F32>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
-                         mask);
+    if (IN_F32 && K <= 4096) {
+      // Top-K of float32 rows: one wave per row, the row in registers
+      const int NG = (K + 255) >> 8;
+      if (NG <= 4)
+        hipLaunchKernelGGL((k_quant_res<IN_F32, 4>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
+                           mask);
+      else if (NG <= 8)
+        hipLaunchKernelGGL((k_quant_res<IN_F32, 8>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
+                           mask);
+      else
+        hipLaunchKernelGGL((k_quant_res<IN_F32, 16>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
+                           mask);
+      return hipGetLastError();
+    }
   }
+  // every other case (rows longer than the block kernels take): one wave per row, streaming
+  hipLaunchKernelGGL((k_quant_stream<FMT, IN_F32>), grid, block, 0, st, x, M, K, ldx, keep, eps, hint, codes, scale,
+                     mask);
   return hipGetLastError();
 }
 

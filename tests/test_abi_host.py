@@ -54,6 +54,22 @@ def test_version_and_status_strings():
     assert tw.bitlinear_pack_workspace_bytes() >= 2048
 
 
+@needs_lib
+def test_workspace_size_query():
+    """One query for every operation: the per-op helpers' values where a workspace is taken, 0 where
+    none is, SIZE_MAX for an unknown op."""
+    for M in (1, 8, 4096, 1 << 20):
+        assert tw.bitlinear_workspace_size("quantize_act_per_tensor", M, 0, 4096) == \
+            tw.bitlinear_quantize_per_tensor_workspace_bytes(M)
+    for op in ("pack_ternary", "pack_ternary_rows"):
+        assert tw.bitlinear_workspace_size(op, 0, 11008, 4096) == tw.bitlinear_pack_workspace_bytes()
+    for op in ("quantize_act", "gemm_w158a4", "gemm_w158a8_sparse", "gemv_decode", "gemv_decode_glu_conditional",
+               "kv_quantize"):
+        assert tw.bitlinear_workspace_size(op, 4096, 12288, 4096) == 0
+    assert tw.bitlinear_workspace_size(99, 1, 1, 128) == 2 ** 64 - 1
+    assert tw.bitlinear_workspace_size(-1, 1, 1, 128) == 2 ** 64 - 1
+
+
 def _q(**kw):
     a = dict(x=P, dt=0, M=4, K=256, ldx=256, fmt=0, keep=-1, eps=1e-5, hint=None, codes=P, scale=P, mask=None)
     a.update(kw)
@@ -65,7 +81,7 @@ def _q(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), 1), (dict(codes=None), 1), (dict(scale=None), 1),
     (dict(dt=7), 1), (dict(fmt=9), 1), (dict(eps=0.0), 1), (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1),
-    (dict(M=0), 2), (dict(K=0), 2), (dict(K=100, ldx=100), 2), (dict(K=384, ldx=384), 2),
+    (dict(M=0), 2), (dict(K=0), 2), (dict(K=100, ldx=100), 2), (dict(K=320, ldx=320), 2),
     (dict(ldx=128), 1), (dict(fmt=0, keep=3), 1), (dict(fmt=1, mask=P), 1), (dict(fmt=2, keep=257), 1),
     (dict(fmt=4, keep=3), 1), (dict(fmt=4, mask=P), 1), (dict(fmt=5), 1),
     (dict(x=P_MIS), 3), (dict(codes=P_MIS), 3), (dict(ldx=260), 3), (dict(fmt=2, keep=5, mask=P_MIS), 3),
@@ -102,8 +118,8 @@ def _mm(name, **kw):
 
 MM_CASES = [
     (dict(codes=None), 1), (dict(scale=None), 1), (dict(packed=None), 1), (dict(alpha=None), 1), (dict(y=None), 1),
-    (dict(K=128), 2), (dict(N=24), 2), (dict(M=0), 2), (dict(ldy=16), 1), (dict(ldy=33), 3),
-    (dict(K=262144), 2), (dict(M=1, N=16, K=1 << 20), 2),          # beyond the exact-accumulation K
+    (dict(K=192), 2), (dict(K=64), 2), (dict(N=24), 2), (dict(M=0), 2), (dict(ldy=16), 1), (dict(ldy=33), 3),
+    (dict(K=262144), 2), (dict(K=262016 + 128), 2), (dict(M=1, N=16, K=1 << 20), 2),   # beyond the exact-accumulation K
     (dict(codes=P_MIS), 3), (dict(packed=P_MIS), 3), (dict(y=P_MIS), 3),
     (dict(epi=tw.bl_epilogue(1, None, 32, None, None, None)), 1),
     (dict(epi=tw.bl_epilogue(1, 4096, 8, None, None, None)), 1),
@@ -175,7 +191,7 @@ def test_pack_rows_validation(kw, status):
 @needs_lib
 @pytest.mark.parametrize("kw,status", [
     (dict(codes=None), 1), (dict(up=None), 1), (dict(upa=None), 1), (dict(h=None), 1), (dict(gate=None), 1),
-    (dict(M=9), 2), (dict(K=128), 2), (dict(N=24), 2),
+    (dict(M=9), 2), (dict(K=192), 2), (dict(N=24), 2),
     (dict(ldh=16), 1), (dict(ldg=16), 1), (dict(up=P_MIS), 3), (dict(h=P_MIS), 3), (dict(ldh=33), 3),
 ])
 def test_glu_conditional_validation(kw, status):
@@ -263,3 +279,4 @@ def test_calibrate_mfma_validation(kw, status):
     a = dict(blocks=512, iters=10, out=P)
     a.update(kw)
     assert tw.library().bitlinear_calibrate_mfma(a["blocks"], a["iters"], a["out"], None) == status
+

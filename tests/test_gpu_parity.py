@@ -62,7 +62,7 @@ def packed_weights(seed, N, K, sigma=0.02):
 
 
 # ----------------------------------------------------------------------------- pack
-@pytest.mark.parametrize("N,K", [(16, 256), (48, 768), (160, 4096), (2048, 2048)])
+@pytest.mark.parametrize("N,K", [(16, 256), (32, 384), (48, 768), (160, 4096), (2048, 2048)])
 def test_pack_ternary(N, K):
     torch_cuda()
     w, codes, alpha, packed, a = packed_weights(100 + N, N, K)
@@ -70,7 +70,7 @@ def test_pack_ternary(N, K):
     np.testing.assert_array_equal(unpack_ternary(host(packed), N, K), codes)
 
 
-@pytest.mark.parametrize("N,K", [(16, 256), (48, 768), (160, 4096)])
+@pytest.mark.parametrize("N,K", [(16, 256), (32, 384), (48, 768), (160, 4096)])
 def test_pack_ternary_rows(N, K):
     torch_cuda()
     w = latent_weights(150 + N, N, K)
@@ -96,7 +96,9 @@ def test_pack_ternary_wide_exponents_and_zero():
 
 
 # ----------------------------------------------------------------------------- quantizers
-QSHAPES = [(1, 256), (7, 768), (64, 2048), (33, 4096), (9, 4352), (6, 11008)]
+# K = 384 and 16512 are odd multiples of 128 (a half 256-group at the end); 16512 and 32768 take the
+# streaming kernels (rows longer than 16384)
+QSHAPES = [(1, 256), (6, 384), (7, 768), (64, 2048), (33, 4096), (9, 4352), (6, 11008), (6, 16512), (2, 32768)]
 
 
 @pytest.mark.parametrize("fmt", ["int4", "int4_e3m2"])
@@ -174,7 +176,7 @@ def test_quantize_fp4_rounding_boundaries(f32):
 
 @pytest.mark.parametrize("fmt", ["int4", "int4_e3m2", "fp4", "fp4_pow2", "int8"])
 @pytest.mark.parametrize("f32", [False, True])
-@pytest.mark.parametrize("M,K", [(1, 256), (7, 768), (33, 4096), (130, 1024), (5, 8192)])
+@pytest.mark.parametrize("M,K", [(1, 256), (9, 640), (7, 768), (33, 4096), (130, 1024), (5, 8192)])
 def test_quantize_per_tensor(M, K, f32, fmt):
     """One scale for the whole tensor: codes bit-exact, the scale repeated in every row."""
     torch = torch_cuda()
@@ -268,7 +270,7 @@ def test_quantize_is_deterministic():
 
 
 # ----------------------------------------------------------------------------- GEMMs
-GSHAPES = [(1, 16, 256), (200, 272, 512), (129, 144, 768), (64, 2048, 2048)]
+GSHAPES = [(1, 16, 256), (37, 80, 384), (200, 272, 512), (129, 144, 768), (64, 2048, 2048)]
 
 
 def _quant(x, fmt, keep=-1):
@@ -363,7 +365,8 @@ def test_gemm_a8_residual_and_relu2(M, N, K):
 # ----------------------------------------------------------------------------- decode
 @pytest.mark.parametrize("fmt", ["int4", "int8"])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8])
-@pytest.mark.parametrize("N,K", [(48, 512), (1024, 4096), (64, 11008), (32, 8192), (48, 12800)])
+@pytest.mark.parametrize("N,K", [(80, 384), (48, 512), (1024, 4096), (64, 11008), (32, 8192), (48, 12800),
+                                 (32, 16512)])
 def test_decode(fmt, M, N, K):
     torch_cuda()
     x = make_x(6000 + M + K, M, K, special=False)
@@ -434,7 +437,7 @@ def test_decode_matches_gemm():
 
 # ----------------------------------------------------------------------------- conditional up projection
 @pytest.mark.parametrize("M", [1, 3, 8])
-@pytest.mark.parametrize("N,K", [(16, 256), (48, 768), (80, 4352), (1024, 4096)])
+@pytest.mark.parametrize("N,K", [(16, 256), (48, 384), (48, 768), (80, 4352), (1024, 4096)])
 def test_glu_conditional(M, N, K):
     """Gate first, up only where the gate is positive: gate, h (bit patterns, +0 where g <= 0) and
     the row maxima equal the oracle's; h equals the fused GLU decode as numbers."""
@@ -459,7 +462,7 @@ def test_glu_conditional(M, N, K):
 
 
 # ----------------------------------------------------------------------------- longest accepted K
-MAXK = 261888      # 2^18 - 256: the longest reduction the matmul entry points accept
+MAXK = 262016      # 2^18 - 128: the longest reduction the matmul entry points accept
 
 
 @pytest.mark.parametrize("kind,fmt", [("gemm", "int4"), ("gemm", "int4_e3m2"), ("gemm", "fp4"), ("a8", "int8"),
@@ -495,3 +498,29 @@ def test_matmul_extreme_codes_at_longest_k(kind, fmt):
     ref = O.dequant_f32(O.gemm_int(c, t), np.ones(M, dtype=np.float32), a, unit)
     assert float(ref[0, 0]) == -cval * K * unit                    # the sum at the bound, held exactly
     np.testing.assert_array_equal(host(y).view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["a8", "gemv"])
+def test_a8_sums_beyond_float32_integers(kind):
+    """INT8 codes near 127 against +1 weights at the longest accepted K: the exact sums (about 3.2e7)
+    are mostly not float32 integers, so the epilogue's RN32(acc) really rounds; outputs equal the
+    oracle's fixed-order float32 epilogue bit for bit."""
+    torch = torch_cuda()
+    K, N = MAXK, 16
+    M = 8 if kind == "gemv" else 20
+    rng = np.random.default_rng(77)
+    c = rng.integers(100, 128, (M, K)).astype(np.int8)
+    w = np.where(rng.random((N, K)) < 0.1, -1.0, 1.0).astype(np.float32)     # mostly +1: sums near 2.6e7
+    t, a = O.ternarize(w, EPS)
+    packed, alpha = tw.bitlinear_pack_ternary(torch.from_numpy(w).cuda(), EPS)
+    assert alpha.item() == a
+    codes = torch.from_numpy(c.view(np.uint8)).cuda()
+    d = (rng.random(M) * 0.01 + 1e-3).astype(np.float32)
+    scale = dev_f32(d)
+    if kind == "a8":
+        y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, alpha, N)
+    else:
+        y = tw.bitlinear_gemv_decode("int8", codes, scale, K, packed, alpha, N)
+    acc = O.gemm_int(c.astype(np.int64), t)
+    assert np.abs(acc).min() > 2 ** 24 and np.mean(acc != acc.astype(np.float32).astype(np.int64)) > 0.25
+    assert_y_close(host(y), acc, d, a)
