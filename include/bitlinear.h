@@ -154,6 +154,26 @@ bl_status bitlinear_quantize_act_per_tensor(const void* d_x, int32_t in_dtype, i
                                             void* d_codes, float* d_scale, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * bitlinear_quantize_act_per_tensor_noalloc: bitlinear_quantize_act_per_tensor for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc): no workspace argument; the call allocates nothing and uses a fixed scratch array the
+ * library keeps on each device it runs on (bitlinear_noalloc_scratch_bytes() bytes, held until the
+ * process ends), which holds the workspace of at most BITLINEAR_NOALLOC_MAX_M rows.
+ *   Arguments, results and other errors as for bitlinear_quantize_act_per_tensor (the outputs are
+ *   identical to it); M > BITLINEAR_NOALLOC_MAX_M -> BL_ERR_WORKSPACE_TOO_SMALL, nothing enqueued.
+ *   The scratch array's address on a device is looked up on the first call made with that device
+ *   current (BL_ERR_HIP if the lookup fails). Every call rewrites all of the scratch it reads, so
+ *   what a previous call left there does not matter; but all calls on one device share the one
+ *   array, so calls that overlap on one device (concurrent streams or host threads) race and give
+ *   undefined results: serialize them.
+ * ------------------------------------------------------------------------------------------- */
+#define BITLINEAR_NOALLOC_MAX_M 65536
+size_t bitlinear_noalloc_scratch_bytes(void);
+bl_status bitlinear_quantize_act_per_tensor_noalloc(const void* d_x, int32_t in_dtype, int64_t M, int64_t K,
+                                                    int64_t ldx, int32_t fmt, float eps, void* d_codes,
+                                                    float* d_scale, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * bitlinear_pack_ternary: absmean ternary quantizer of a latent weight matrix (section 3.4,
  * "Ternary Weight Quantization (BitLinear)", paper Eq. 2) and 2-bit packing.
  *   alpha = RN32(RN64(sum |w|) / (N K)) with the sum exact over the whole tensor;

@@ -30,7 +30,9 @@ EXPORTED = (
     "bitlinear_gemv_decode", "bitlinear_gemv_decode_glu_conditional", "bitlinear_status_string",
     "bitlinear_abi_version", "bitlinear_quantize_act_per_tensor", "bitlinear_quantize_per_tensor_workspace_bytes",
     "bitlinear_kv_quantize", "bitlinear_calibrate_mfma", "bitlinear_workspace_size",
+    "bitlinear_quantize_act_per_tensor_noalloc", "bitlinear_noalloc_scratch_bytes",
 )
+NOALLOC_MAX_M = 65536
 
 
 class BitlinearError(RuntimeError):
@@ -83,6 +85,10 @@ def _lib():
         lib.bitlinear_quantize_act_per_tensor.argtypes = [vp, i32, i64, i64, i64, i32, f32, vp, sz, vp, vp, vp]
         lib.bitlinear_quantize_act_per_tensor.restype = i32
         lib.bitlinear_quantize_per_tensor_workspace_bytes.argtypes = [i64]
+        lib.bitlinear_quantize_act_per_tensor_noalloc.argtypes = [vp, i32, i64, i64, i64, i32, f32, vp, vp, vp]
+        lib.bitlinear_quantize_act_per_tensor_noalloc.restype = i32
+        lib.bitlinear_noalloc_scratch_bytes.argtypes = []
+        lib.bitlinear_noalloc_scratch_bytes.restype = sz
         lib.bitlinear_quantize_per_tensor_workspace_bytes.restype = sz
         lib.bitlinear_pack_ternary_rows.argtypes = [vp, i64, i64, f32, vp, vp, vp, sz, vp]
         lib.bitlinear_pack_ternary_rows.restype = i32
@@ -174,6 +180,27 @@ def bitlinear_quantize_act_per_tensor(x, fmt, eps=1e-5, codes=None, scale=None, 
     st = _lib().bitlinear_quantize_act_per_tensor(_ptr(x), in_dtype, M, K, x.stride(0), f, float(eps), _ptr(workspace),
                                                   workspace.numel(), _ptr(codes), _ptr(scale), _stream(stream))
     _check(st, "bitlinear_quantize_act_per_tensor")
+    return codes, scale
+
+
+def bitlinear_noalloc_scratch_bytes():
+    return int(_lib().bitlinear_noalloc_scratch_bytes())
+
+
+def bitlinear_quantize_act_per_tensor_noalloc(x, fmt, eps=1e-5, codes=None, scale=None, stream=None):
+    """The per-tensor quantizer without a workspace (the library's fixed scratch; M <= NOALLOC_MAX_M).
+    Returns (codes, scale f32 [M]); pass codes and scale to allocate nothing at all."""
+    import torch
+    f = _fmt(fmt)
+    M, K = x.shape
+    in_dtype = {torch.bfloat16: BL_IN_BF16, torch.float32: BL_IN_F32}[x.dtype]
+    if codes is None:
+        codes = torch.empty(codes_shape(f, M, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    st = _lib().bitlinear_quantize_act_per_tensor_noalloc(_ptr(x), in_dtype, M, K, x.stride(0), f, float(eps),
+                                                          _ptr(codes), _ptr(scale), _stream(stream))
+    _check(st, "bitlinear_quantize_act_per_tensor_noalloc")
     return codes, scale
 
 

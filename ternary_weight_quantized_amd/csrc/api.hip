@@ -1,6 +1,7 @@
 // C-ABI layer: host-side argument validation, then kernel launches on the caller's stream.
 // Nothing is enqueued when validation fails; the library never allocates device memory.
 #include <cmath>
+#include <mutex>
 #include <cstdint>
 #include <cstddef>
 
@@ -151,6 +152,34 @@ bl_status check_per_tensor(const void* d_x, int32_t in_dtype, int64_t M, int64_t
   return BL_OK;
 }
 
+// Scratch of the allocation-free per-tensor quantizer: one fixed array per device, the workspace of
+// at most BITLINEAR_NOALLOC_MAX_M rows. Host code never uses the array's name as an address: each
+// device's address comes from hipGetSymbolAddress, looked up once per device on its first call.
+constexpr size_t kNoallocScratchBytes = bl_quantize_per_tensor_ws_bytes(BITLINEAR_NOALLOC_MAX_M);
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];          // device address of `scratch` on each device (null: not looked up)
+
+// Address of the current device's scratch array, looked up (once per device) with that device current.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,6 +196,20 @@ bl_status bitlinear_quantize_act_per_tensor(const void* d_x, int32_t in_dtype, i
                                                   d_workspace, d_codes, d_scale, static_cast<hipStream_t>(stream)));
 }
 
+size_t bitlinear_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+bl_status bitlinear_quantize_act_per_tensor_noalloc(const void* d_x, int32_t in_dtype, int64_t M, int64_t K,
+                                                    int64_t ldx, int32_t fmt, float eps, void* d_codes,
+                                                    float* d_scale, void* stream) {
+  const bl_status s = check_per_tensor(d_x, in_dtype, M, K, ldx, fmt, eps, d_codes, d_scale);
+  if (s != BL_OK) return s;
+  if (M > BITLINEAR_NOALLOC_MAX_M) return BL_ERR_WORKSPACE_TOO_SMALL;   // beyond the fixed scratch
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return BL_ERR_HIP;
+  // every workspace slot is rewritten by the call (nothing needs clearing); no allocation happens
+  return hip_status(bl_launch_quantize_per_tensor(d_x, in_dtype == BL_IN_F32, (int)M, (int)K, (long)ldx, fmt, eps,
+                                                  ws, d_codes, d_scale, static_cast<hipStream_t>(stream)));
+}
 
 bl_status bitlinear_pack_ternary(const float* d_w, int64_t N, int64_t K, float eps, void* d_packed, float* d_alpha,
                                  void* d_workspace, size_t ws_bytes, void* stream) {

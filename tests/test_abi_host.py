@@ -280,3 +280,23 @@ def test_calibrate_mfma_validation(kw, status):
     a.update(kw)
     assert tw.library().bitlinear_calibrate_mfma(a["blocks"], a["iters"], a["out"], None) == status
 
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(scale=None), 1), (dict(dt=7), 1), (dict(fmt=9), 1),
+    (dict(eps=0.0), 1), (dict(M=0), 2), (dict(K=100, ldx=100), 2), (dict(ldx=128), 1), (dict(x=P_MIS), 3),
+    (dict(ldx=260), 3), (dict(M=(1 << 16) + 1), 4), (dict(M=1 << 20, K=4096, ldx=4096), 2),
+])
+def test_quantize_per_tensor_noalloc_validation(kw, status):
+    """Every rejection happens on the host, before the scratch array is looked up (no GPU here)."""
+    a = dict(x=P, dt=0, M=4, K=256, ldx=256, fmt=0, eps=1e-5, codes=P, scale=P)
+    a.update(kw)
+    st = tw.library().bitlinear_quantize_act_per_tensor_noalloc(a["x"], a["dt"], a["M"], a["K"], a["ldx"], a["fmt"],
+                                                                a["eps"], a["codes"], a["scale"], None)
+    assert st == status
+
+
+@needs_lib
+def test_noalloc_scratch_size():
+    assert tw.bitlinear_noalloc_scratch_bytes() == tw.bitlinear_quantize_per_tensor_workspace_bytes(tw.NOALLOC_MAX_M)
+    assert tw.bitlinear_noalloc_scratch_bytes() < 1 << 20
