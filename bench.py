@@ -185,6 +185,26 @@ def main():
     # decode A8: INT8 codes of the first M rows of the FFN's h against the down projection
     d8Ws = [dW] + [dW.clone() for _ in range(ROTATE - 1)]
     d8ys = {m: torch.empty((m, F["K"]), dtype=torch.float32, device=dev) for m in D["Ms"]}
+    # Structured-sparsity variants of the two A8 inputs, labelled as such: the i.i.d. codes with a seeded half
+    # of their 16-row x 128-column slices (the granularity whose matrix-core work the A8 GEMM skips) set to
+    # zero, e.g. channels dead for a group of tokens. For h that gives about 84% zero codes, the pages'
+    # figure for the 7B down-projection input; the Top-K codes go from 50% to about 75%. The h codes are
+    # computed once here.
+    tw.bitlinear_quantize_act(fx, "int4_e3m2", eps=EPS, codes=fc, scale=fs)
+    tw.bitlinear_gemm_w158a4("int4_e3m2", fc, fs, F["K"], gW, gA, F["N"], y=fh, up_packed=uW, up_alpha=uA,
+                             row_absmax=frm)
+    tw.bitlinear_quantize_act(fh, "int8", eps=EPS, row_absmax_hint=frm, codes=fhc, scale=fhs)
+    tw.bitlinear_quantize_act(ax, "int8", topk_keep=A["keep"], eps=EPS, codes=ac, scale=as_, mask=am)
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(4242)
+
+    def slice_mask(M_, K_, p_zero):
+        keep = (torch.rand((M_ // 16, K_ // 128), generator=gen) >= p_zero).to(torch.uint8)
+        return keep.repeat_interleave(16, 0).repeat_interleave(128, 1).to(dev)
+    fhc_s = fhc * slice_mask(F["M"], F["N"], 0.5)
+    ac_s = ac * slice_mask(A["M"], A["K"], 0.5)
+    fy_s = torch.empty_like(fy)
+    ay_s = torch.empty_like(ay)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
@@ -212,6 +232,16 @@ def main():
                 tw.bitlinear_gemv_decode_glu_conditional(dcs[m], dss[m], D["K"], gWs[r], gA, uWrs[r], uA, F["N"],
                                                          gate=dgs[m], h=dhs[m])
         cond_graphs[m] = g
+    # ceilings of a launch that streams one packed matrix: a plain read of the 11.27 MB weights (24 copies,
+    # the same rotation) and a launch that reads 16 bytes
+    read_sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    read_graph, launch_graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(read_graph, stream=side):
+        for r in range(ROTATE):
+            tw.bitlinear_calibrate_read(dWs[r], read_sink)
+    with torch.cuda.graph(launch_graph, stream=side):
+        for r in range(ROTATE):
+            tw.bitlinear_calibrate_read(dWs[r], read_sink, nbytes=16)
     a8_graphs = {}
     for m in D["Ms"]:
         g = torch.cuda.CUDAGraph()
@@ -225,7 +255,8 @@ def main():
              "quant_fp4_prefill", "gemm_a4_fp4_prefill", "quant_fp4_pow2_prefill",
              "quant_int4_per_tensor_prefill",
              "quant_int4_e3m2_ffn", "gemm_a4_glu_ffn", "quant_int8_h", "gemm_a8_down", "quant_topk_int8_attn",
-             "gemm_a8_oproj_residual", "kv_quant_q4_rope", "kv_quant_k3_rope_bos", "kv_quant_v3_bos"] + \
+             "gemm_a8_oproj_residual", "gemm_a8_down_structured", "gemm_a8_oproj_residual_structured",
+             "kv_quant_q4_rope", "kv_quant_k3_rope_bos", "kv_quant_v3_bos"] + \
         [f"decode_m{m}_graph" for m in D["Ms"]] + \
         [f"decode_glu_m{m}_graph" for m in D["Ms"]] + [f"decode_glu_cond_m{m}_graph" for m in D["Ms"]] + \
         [f"decode_a8_m{m}_graph" for m in D["Ms"]]
@@ -259,6 +290,8 @@ def main():
         tw.bitlinear_gemm_w158a8_sparse(fhc, fhs, F["N"], dW, dA, F["K"], y=fy); mark()
         tw.bitlinear_quantize_act(ax, "int8", topk_keep=A["keep"], eps=EPS, codes=ac, scale=as_, mask=am); mark()
         tw.bitlinear_gemm_w158a8_sparse(ac, as_, A["K"], oW, oA, A["N"], y=ay, residual=ar); mark()
+        tw.bitlinear_gemm_w158a8_sparse(fhc_s, fhs, F["N"], dW, dA, F["K"], y=fy_s); mark()
+        tw.bitlinear_gemm_w158a8_sparse(ac_s, as_, A["K"], oW, oA, A["N"], y=ay_s, residual=ar); mark()
         tw.bitlinear_kv_quantize(py4[:, :kH * kD], kH, kD, 4, eps=EPS, pos=kpos, cos=kcos, sin=ksin,
                                  codes=kq_c, scale=kq_s); mark()
         tw.bitlinear_kv_quantize(py4[:, kH * kD:2 * kH * kD], kH, kD, 3, eps=EPS, pos=kpos, cos=kcos, sin=ksin,
@@ -306,6 +339,23 @@ def main():
     a8_live = {m: int((fhc[:m].view(torch.int8).view(m, F["N"] // 32, 32) != 0).any(dim=2).any(dim=0).sum().item())
                for m in D["Ms"]}
     peaks = measured_peaks(torch, dev)
+
+    def graph_us(g, reps=20):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps / ROTATE
+    read_us, launch_us = graph_us(read_graph), graph_us(launch_graph)
+    peaks["decode_read_floor_us"] = round(read_us, 3)
+    peaks["decode_read_floor_gbs"] = round(D["N"] * D["K"] / 4 / (read_us * 1e-6) / 1e9, 1)
+    peaks["launch_floor_us"] = round(launch_us, 3)
+    peaks["how_floors"] = ("graph of 24 plain streaming reads of one packed 11008x4096 matrix (11.27 MB, the "
+                           "decode rotation), and of 24 launches reading 16 bytes; microseconds per launch")
     # live up rows of the conditional projection (channels whose gate is positive in some row)
     live = {m: int((dgs[m] > 0).any(dim=0).sum().item()) for m in D["Ms"]}
 
@@ -316,6 +366,8 @@ def main():
     h_codes = fhc.view(torch.int8)
     nnz_h = int((h_codes != 0).sum().item())
     nnz_attn = int((ac.view(torch.int8) != 0).sum().item())
+    nnz_h_s = int((fhc_s.view(torch.int8) != 0).sum().item())
+    nnz_attn_s = int((ac_s.view(torch.int8) != 0).sum().item())
     ops_down_alg = 2.0 * F["K"] * nnz_h
     ops_down_dense = 2.0 * F["M"] * F["N"] * F["K"]
     ops_oproj_alg = 2.0 * A["N"] * nnz_attn
@@ -368,7 +420,22 @@ def main():
                                        tops=tops(ops_oproj_alg, times["gemm_a8_oproj_residual"]),
                                        dense_tops=tops(ops_oproj_dense, times["gemm_a8_oproj_residual"]),
                                        peak=INT8_PEAK_TOPS),
+        "gemm_a8_down_structured": dict(us=times["gemm_a8_down_structured"], bound="mfma",
+                                        tops=tops(2.0 * F["K"] * nnz_h_s, times["gemm_a8_down_structured"]),
+                                        dense_tops=tops(ops_down_dense, times["gemm_a8_down_structured"]),
+                                        peak=INT8_PEAK_TOPS, input="structured sparsity (labelled variant)"),
+        "gemm_a8_oproj_residual_structured": dict(us=times["gemm_a8_oproj_residual_structured"], bound="mfma",
+                                                  tops=tops(2.0 * A["N"] * nnz_attn_s,
+                                                            times["gemm_a8_oproj_residual_structured"]),
+                                                  dense_tops=tops(ops_oproj_dense,
+                                                                  times["gemm_a8_oproj_residual_structured"]),
+                                                  peak=INT8_PEAK_TOPS, input="structured sparsity (labelled variant)"),
     }
+    for name, codes_t in (("gemm_a8_down", fhc), ("gemm_a8_oproj_residual", ac), ("gemm_a8_down_structured", fhc_s),
+                          ("gemm_a8_oproj_residual_structured", ac_s)):
+        z, zs = zero_slices(torch, codes_t)
+        kern[name]["zero_16x128_slices"] = round(z, 4)
+        kern[name]["skipped_16x128_slices"] = round(zs, 4)
     kv_rec = kT * kH
 
     def kv_bytes(bits, rope, bos):
@@ -404,7 +471,8 @@ def main():
                 "avg_kernel_us": round(head_us, 3),
                 "algorithmic": f"2*M*N*K = {ops_prefill:.4g} ops per launch"}
     decode = {f"m{m}": {"us": round(gemv_us[m], 3), "gbs": round(gbs(dec_bytes(m), gemv_us[m]), 1),
-                        "frac_hbm": round(gbs(dec_bytes(m), gemv_us[m]) / HBM_PEAK_GBS, 4)} for m in D["Ms"]}
+                        "frac_hbm": round(gbs(dec_bytes(m), gemv_us[m]) / HBM_PEAK_GBS, 4),
+                        "frac_read_floor": round(read_us / gemv_us[m], 4)} for m in D["Ms"]}
     glu_w = F["N"] * F["K"] / 4
 
     def glu_bytes(m, rows_up):
@@ -426,7 +494,9 @@ def main():
                               "live_k_slices": round(a8_live[m] / (F["N"] // 32), 4)}
 
     sparsity = {"ffn_h_zero_codes": round(1 - nnz_h / (F["M"] * F["N"]), 4),
-                "attn_zero_codes": round(1 - nnz_attn / (A["M"] * A["K"]), 4)}
+                "attn_zero_codes": round(1 - nnz_attn / (A["M"] * A["K"]), 4),
+                "ffn_h_zero_codes_structured": round(1 - nnz_h_s / (F["M"] * F["N"]), 4),
+                "attn_zero_codes_structured": round(1 - nnz_attn_s / (A["M"] * A["K"]), 4)}
 
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
@@ -461,6 +531,16 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def zero_slices(torch, codes):
+    """Fractions of the 16-row x 128-column slices of INT8 codes that are all zero, and of those the A8 GEMM
+    skips (every 16-row subtile except the first of each 64-row wave strip, which also expands the weights)."""
+    c = codes.view(torch.int8)
+    M_, K_ = c.shape
+    z = (c[: M_ // 16 * 16].view(M_ // 16, 16, K_ // 128, 128) != 0).any(dim=3).any(dim=1).logical_not()
+    skippable = (torch.arange(M_ // 16, device=c.device) % 4 != 0)[:, None]
+    return float(z.float().mean().item()), float((z & skippable).float().mean().item())
+
+
 def measured_peaks(torch, dev):
     """What this GPU sustains, beside the datasheet peaks: a 256 MiB device-to-device copy (bytes read
     plus written per second) and the library's FP6 x FP4 matrix-core-only loop in the GEMM's wave
@@ -493,30 +573,52 @@ def measured_peaks(torch, dev):
                    f"{blocks} blocks x 4 waves x {iters} x 32 MFMAs 16x16x128; best of 3 after a warm-up"}
 
 
-def cpu_baseline(rows, min_seconds=10.0, max_reps=30):
-    """The oracle as it stands, on the first `rows` tokens of the prefill workload (quantize + exact
-    integer GEMM + dequantization), repeated until about `min_seconds` of CPU work has been timed;
-    the weights are ternarized beforehand (offline in the method)."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(rows, rows_single=256, min_seconds=10.0, min_seconds_single=6.0, max_reps=30):
+    """The oracle as it stands (its integer GEMM is a float64 BLAS matmul of the codes), on the first
+    `rows` tokens of the prefill workload with all the threads BLAS uses, and on `rows_single` tokens
+    with one thread (quantize + exact integer GEMM + dequantization), each repeated until about
+    `min_seconds` of CPU work has been timed; the weights are ternarized beforehand (offline in the
+    method)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle as O
     from synth import WORKLOADS, bf16_bits_to_f32, workload_inputs
     P = WORKLOADS["prefill_qkv"]
     inp = workload_inputs("prefill_qkv")
     t, alpha = O.ternarize(inp["w"], EPS)
-    x = bf16_bits_to_f32(inp["x"][:rows])
-    reps, dt = 0, 0.0
-    while reps < max_reps and (reps == 0 or dt < min_seconds):
-        t0 = time.perf_counter()
-        O.bitlinear_a4(x, t, alpha, EPS)
-        dt += time.perf_counter() - t0
-        reps += 1
-    ops = 2.0 * rows * P["N"] * P["K"] * reps
+
+    def run(nrows, min_s):
+        x = bf16_bits_to_f32(inp["x"][:nrows])
+        reps, dt = 0, 0.0
+        while reps < max_reps and (reps == 0 or dt < min_s):
+            t0 = time.perf_counter()
+            O.bitlinear_a4(x, t, alpha, EPS)
+            dt += time.perf_counter() - t0
+            reps += 1
+        return 2.0 * nrows * P["N"] * P["K"] * reps / dt / 1e12, reps, dt
+
+    v_all, reps, dt = run(rows, min_seconds)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle.bitlinear_a4 (INT4) on {rows} of the 4096 prefill tokens, N=12288, K=4096, "
-                      f"{reps} passes: {dt:.2f} s", "host_cpus": os.cpu_count()}
+    with threadpool_limits(limits=1):
+        v_one, reps1, dt1 = run(rows_single, min_seconds_single)
+    return {"value": round(v_all, 5), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle.bitlinear_a4 (INT4; its integer GEMM is a BLAS float64 matmul of the codes) on "
+                      f"{rows} of the 4096 prefill tokens, N=12288, K=4096, {reps} passes: {dt:.2f} s",
+            "single_thread": {"value": round(v_one, 5), "unit": "TOPS", "cores": 1,
+                              "sample": f"the same on {rows_single} tokens, one BLAS thread, {reps1} passes: "
+                                        f"{dt1:.2f} s"},
+            "host_cpu": host_cpu_model(), "host_cpus": os.cpu_count()}
 
 
 if __name__ == "__main__":

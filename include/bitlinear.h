@@ -334,6 +334,16 @@ bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, in
  * ------------------------------------------------------------------------------------------- */
 bl_status bitlinear_calibrate_mfma(int32_t blocks, int32_t iters, float* d_out, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_calibrate_read: a measurement aid, not part of the BitLinear path. A plain streaming read
+ * of `bytes` bytes at d_src (16 bytes per lane, one load per lane), the ceiling for a kernel that
+ * reads the same bytes once per launch, e.g. a decode GEMV streaming one packed weight matrix.
+ *   bytes   a multiple of 16, 16 .. 2^31 - 16.   d_src 16-byte aligned.
+ *   d_sink  one uint32 the kernel may write (its value carries no meaning).
+ * Errors: NULL pointers -> INVALID_ARGUMENT; bytes out of range -> UNSUPPORTED_SHAPE; alignment -> MISALIGNED.
+ * ------------------------------------------------------------------------------------------- */
+bl_status bitlinear_calibrate_read(const void* d_src, int64_t bytes, uint32_t* d_sink, void* stream);
+
 const char* bitlinear_status_string(int32_t status);
 int32_t bitlinear_abi_version(void);
 

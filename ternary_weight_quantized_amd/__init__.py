@@ -29,7 +29,7 @@ EXPORTED = (
     "bitlinear_pack_workspace_bytes", "bitlinear_gemm_w158a4", "bitlinear_gemm_w158a8_sparse",
     "bitlinear_gemv_decode", "bitlinear_gemv_decode_glu_conditional", "bitlinear_status_string",
     "bitlinear_abi_version", "bitlinear_quantize_act_per_tensor", "bitlinear_quantize_per_tensor_workspace_bytes",
-    "bitlinear_kv_quantize", "bitlinear_calibrate_mfma", "bitlinear_workspace_size",
+    "bitlinear_kv_quantize", "bitlinear_calibrate_mfma", "bitlinear_calibrate_read", "bitlinear_workspace_size",
     "bitlinear_quantize_act_per_tensor_noalloc", "bitlinear_noalloc_scratch_bytes",
 )
 NOALLOC_MAX_M = 65536
@@ -81,6 +81,8 @@ def _lib():
                                               vp, vp, vp]
         lib.bitlinear_kv_quantize.restype = i32
         lib.bitlinear_calibrate_mfma.argtypes = [i32, i32, vp, vp]
+        lib.bitlinear_calibrate_read.argtypes = [vp, i64, vp, vp]
+        lib.bitlinear_calibrate_read.restype = i32
         lib.bitlinear_calibrate_mfma.restype = i32
         lib.bitlinear_quantize_act_per_tensor.argtypes = [vp, i32, i64, i64, i64, i32, f32, vp, sz, vp, vp, vp]
         lib.bitlinear_quantize_act_per_tensor.restype = i32
@@ -232,6 +234,12 @@ def bitlinear_kv_quantize(x, H, D, bits, eps=1e-5, pos=None, cos=None, sin=None,
                                       _ptr(bos_codes), _ptr(bos_scale), _stream(stream))
     _check(st, "bitlinear_kv_quantize")
     return codes, scale, bos_codes, bos_scale
+
+
+def bitlinear_calibrate_read(src, sink, nbytes=None, stream=None):
+    """Measurement aid: one plain streaming read of src (a device tensor, nbytes of it); sink: >= 4 bytes."""
+    b = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(_lib().bitlinear_calibrate_read(_ptr(src), b, _ptr(sink), _stream(stream)), "bitlinear_calibrate_read")
 
 
 def bitlinear_calibrate_mfma(blocks, iters, out=None, stream=None):

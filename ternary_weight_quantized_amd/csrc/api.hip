@@ -328,6 +328,13 @@ bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, in
   return hip_status(bl_launch_kv_quant(a, static_cast<hipStream_t>(stream)));
 }
 
+bl_status bitlinear_calibrate_read(const void* d_src, int64_t bytes, uint32_t* d_sink, void* stream) {
+  if (!d_src || !d_sink) return BL_ERR_INVALID_ARGUMENT;
+  if (bytes < 16 || bytes % 16 != 0 || bytes >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(d_src)) return BL_ERR_MISALIGNED;
+  return hip_status(bl_launch_calib_read(d_src, (long)bytes, d_sink, static_cast<hipStream_t>(stream)));
+}
+
 bl_status bitlinear_calibrate_mfma(int32_t blocks, int32_t iters, float* d_out, void* stream) {
   if (!d_out) return BL_ERR_INVALID_ARGUMENT;
   // at most 2^20 steps (about half a second on a full part): a measurement, not a long-running load

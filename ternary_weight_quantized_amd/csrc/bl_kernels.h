@@ -79,3 +79,5 @@ hipError_t bl_launch_kv_quant(const bl_kv_args& a, hipStream_t st);
 
 // measurement aid: FP6 x FP4 matrix-core loop (blocks x 256 threads, out[blocks * 256])
 hipError_t bl_launch_calib_mfma(int blocks, int iters, float* out, hipStream_t st);
+// measurement aid: plain streaming read of `bytes` bytes (16 per lane); sink: one uint32, never read back
+hipError_t bl_launch_calib_read(const void* p, long bytes, void* sink, hipStream_t st);

@@ -39,7 +39,27 @@ __global__ __launch_bounds__(256, 2) void k_calib_mfma(int iters, float* __restr
   out[(long)blockIdx.x * 256 + threadIdx.x] = sum;
 }
 
+// Measurement aid: a plain streaming read of `bytes` bytes (16 per lane, one load per lane, 256-lane
+// blocks: the fastest of the read shapes measured for an 11 MB buffer), the ceiling a decode GEMV
+// reading the same bytes per launch can reach. Each lane folds its 16 bytes into one word, and a
+// word is written only when it equals a value the data never produces, so the loads stay live.
+__global__ __launch_bounds__(256) void k_calib_read(const uint8_t* __restrict__ p, long bytes,
+                                                    uint32_t* __restrict__ sink) {
+  const long off = ((long)blockIdx.x * 256 + threadIdx.x) * 16;
+  if (off + 16 > bytes) return;
+  const uint4 v = *reinterpret_cast<const uint4*>(p + off);
+  const uint32_t f = v.x ^ v.y ^ v.z ^ v.w;
+  if (f == 0xA5C3E1F7u && v.x == 0x0F1E2D3Cu) sink[0] = f;
+}
+
 }  // namespace
+
+hipError_t bl_launch_calib_read(const void* p, long bytes, void* sink, hipStream_t st) {
+  const long blocks = (bytes / 16 + 255) / 256;
+  hipLaunchKernelGGL(k_calib_read, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, st,
+                     static_cast<const uint8_t*>(p), bytes, static_cast<uint32_t*>(sink));
+  return hipGetLastError();
+}
 
 hipError_t bl_launch_calib_mfma(int blocks, int iters, float* out, hipStream_t st) {
   hipLaunchKernelGGL(k_calib_mfma, dim3(blocks), dim3(256), 0, st, iters, out);

@@ -1,11 +1,17 @@
-"""Minimal driver for hardware-counter runs of one BitLinear GEMM (no graphs, few launches).
+"""Minimal driver for hardware-counter runs of the BitLinear kernels (few launches, no benchmark loop).
 
     python -m ternary_weight_quantized_amd.profile_run --gemm fp6 --reps 3 --copy-calibration
+    python -m ternary_weight_quantized_amd.profile_run --decode --copy-calibration
+    python -m ternary_weight_quantized_amd.profile_run --a8 --reps 3
 
-quantizes the prefill workload (M=4096, K=4096, N=12288, seeded synthetic bf16 activations and
-latent weights) and launches the selected GEMM `reps` times. With --copy-calibration a 256 MiB
-device-to-device copy runs first; its FETCH_SIZE and WRITE_SIZE readings give the factor that
-turns those counters into bytes.
+--gemm quantizes the prefill workload (M=4096, K=4096, N=12288, seeded synthetic bf16 activations and
+latent weights) and launches the selected W1.58A4 GEMM `reps` times. --decode launches, each over 24
+rotating copies of its weights (as the benchmark's graphs do): the INT4 decode GEMV of 1 token
+(11008x4096), the fused gate+up ReLU^2 GLU decode GEMV of 1 token (12 copies of both 11008x4096
+matrices) and the INT8 decode GEMV of one row of the FFN's h codes against the 4096x11008 down
+projection. --a8 launches the two W1.58A8 GEMMs of the FFN (down) and attention-output workloads.
+With --copy-calibration a 256 MiB device-to-device copy runs first; its FETCH_SIZE and WRITE_SIZE
+readings give the factor that turns those counters into bytes.
 """
 from __future__ import annotations
 
@@ -21,27 +27,95 @@ EPS = 1e-5
 FORMATS = {"fp6": "int4_e3m2", "int4": "int4", "fp4": "fp4"}
 
 
+def dev_bf16(torch, bits):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
 def main():
     p = argparse.ArgumentParser()
-    p.add_argument("--gemm", choices=sorted(FORMATS), default="fp6")
+    p.add_argument("--gemm", choices=sorted(FORMATS), default=None)
+    p.add_argument("--decode", action="store_true")
+    p.add_argument("--a8", action="store_true")
     p.add_argument("--reps", type=int, default=3)
     p.add_argument("--copy-calibration", action="store_true")
     args = p.parse_args()
+    if not (args.gemm or args.decode or args.a8):
+        args.gemm = "fp6"
 
-    import numpy as np
     import torch
 
     import ternary_weight_quantized_amd as tw
     from synth import WORKLOADS, workload_inputs
 
     tw.library()
-    P = WORKLOADS["prefill_qkv"]
-    inp = workload_inputs("prefill_qkv")
-    x = torch.from_numpy(np.ascontiguousarray(inp["x"]).view(np.int16)).view(torch.bfloat16).cuda()
-    packed, alpha = tw.bitlinear_pack_ternary(torch.from_numpy(inp["w"]).cuda(), EPS)
-    fmt = FORMATS[args.gemm]
-    codes, scale, _ = tw.bitlinear_quantize_act(x, fmt, eps=EPS)
-    y = torch.empty((P["M"], P["N"]), dtype=torch.float32, device="cuda")
+
+    def pack(w):
+        return tw.bitlinear_pack_ternary(torch.from_numpy(w).cuda(), EPS)
+
+    work = []
+    if args.gemm:
+        P = WORKLOADS["prefill_qkv"]
+        inp = workload_inputs("prefill_qkv")
+        x = dev_bf16(torch, inp["x"])
+        packed, alpha = pack(inp["w"])
+        fmt = FORMATS[args.gemm]
+        codes, scale, _ = tw.bitlinear_quantize_act(x, fmt, eps=EPS)
+        y = torch.empty((P["M"], P["N"]), dtype=torch.float32, device="cuda")
+        work.append((f"{args.reps} x {fmt} GEMM M={P['M']} K={P['K']} N={P['N']}",
+                     lambda: [tw.bitlinear_gemm_w158a4(fmt, codes, scale, P["K"], packed, alpha, P["N"], y=y)
+                              for _ in range(args.reps)]))
+    if args.decode or args.a8:
+        F = WORKLOADS["ffn_7b"]
+        fin = workload_inputs("ffn_7b")
+        gW, gA = pack(fin["w_gate"])
+        uW, uA = pack(fin["w_up"])
+        dW, dA = pack(fin["w_down"])
+        fx = dev_bf16(torch, fin["x"])
+        del fin
+        fc, fs, _ = tw.bitlinear_quantize_act(fx, "int4_e3m2", eps=EPS)
+        frm = torch.empty(F["M"], dtype=torch.float32, device="cuda")
+        fh = tw.bitlinear_gemm_w158a4("int4_e3m2", fc, fs, F["K"], gW, gA, F["N"], up_packed=uW, up_alpha=uA,
+                                      row_absmax=frm)
+        fhc, fhs, _ = tw.bitlinear_quantize_act(fh, "int8", eps=EPS, row_absmax_hint=frm)
+    if args.decode:
+        D = WORKLOADS["decode_a4"]
+        din = workload_inputs("decode_a4")
+        w0, a0 = pack(din["w"])
+        dc, ds, _ = tw.bitlinear_quantize_act(dev_bf16(torch, din["x"][:1]), "int4", eps=EPS)
+        dWs = [w0] + [w0.clone() for _ in range(23)]
+        gWs = [gW] + [gW.clone() for _ in range(11)]
+        uWs = [uW] + [uW.clone() for _ in range(11)]
+        d8Ws = [dW] + [dW.clone() for _ in range(23)]
+        y1 = torch.empty((1, D["N"]), dtype=torch.float32, device="cuda")
+        h1 = torch.empty((1, F["N"]), dtype=torch.float32, device="cuda")
+        y8 = torch.empty((1, F["K"]), dtype=torch.float32, device="cuda")
+
+        def decode():
+            for r in range(24):
+                tw.bitlinear_gemv_decode("int4", dc, ds, D["K"], dWs[r], a0, D["N"], y=y1)
+            for r in range(12):
+                tw.bitlinear_gemv_decode("int4", dc, ds, D["K"], gWs[r], gA, F["N"], y=h1, up_packed=uWs[r],
+                                         up_alpha=uA)
+            for r in range(24):
+                tw.bitlinear_gemv_decode("int8", fhc[:1], fhs[:1], F["N"], d8Ws[r], dA, F["K"], y=y8)
+        work.append(("decode: 24 INT4 GEMV M=1, 12 fused GLU GEMV M=1, 24 INT8 GEMV M=1", decode))
+    if args.a8:
+        A = WORKLOADS["attn_out"]
+        ain = workload_inputs("attn_out")
+        ax = dev_bf16(torch, ain["x"])
+        ar = torch.from_numpy(ain["residual"]).cuda()
+        oW, oA = pack(ain["w"])
+        del ain
+        ac, as_, _ = tw.bitlinear_quantize_act(ax, "int8", topk_keep=A["keep"], eps=EPS)
+        fy = torch.empty((F["M"], F["K"]), dtype=torch.float32, device="cuda")
+        ay = torch.empty((A["M"], A["N"]), dtype=torch.float32, device="cuda")
+
+        def a8():
+            for _ in range(args.reps):
+                tw.bitlinear_gemm_w158a8_sparse(fhc, fhs, F["N"], dW, dA, F["K"], y=fy)
+                tw.bitlinear_gemm_w158a8_sparse(ac, as_, A["K"], oW, oA, A["N"], y=ay, residual=ar)
+        work.append((f"{args.reps} x (A8 down 2048x11008x4096, A8 o_proj+residual 8192x4096x4096)", a8))
     torch.cuda.synchronize()
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
@@ -50,10 +124,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.reps):
-        tw.bitlinear_gemm_w158a4(fmt, codes, scale, P["K"], packed, alpha, P["N"], y=y)
-    torch.cuda.synchronize()
-    print(f"profile_run: {args.reps} x {fmt} GEMM M={P['M']} K={P['K']} N={P['N']}", flush=True)
+    for name, fn in work:
+        fn()
+        torch.cuda.synchronize()
+        print(f"profile_run: {name}", flush=True)
 
 
 if __name__ == "__main__":

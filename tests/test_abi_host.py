@@ -300,3 +300,14 @@ def test_quantize_per_tensor_noalloc_validation(kw, status):
 def test_noalloc_scratch_size():
     assert tw.bitlinear_noalloc_scratch_bytes() == tw.bitlinear_quantize_per_tensor_workspace_bytes(tw.NOALLOC_MAX_M)
     assert tw.bitlinear_noalloc_scratch_bytes() < 1 << 20
+
+
+@needs_lib
+def test_calibrate_read_validation():
+    lib = tw.library()
+    assert lib.bitlinear_calibrate_read(None, 1024, P, None) == 1
+    assert lib.bitlinear_calibrate_read(P, 1024, None, None) == 1
+    for b in (0, 8, 1000, 1 << 31):
+        assert lib.bitlinear_calibrate_read(P, b, P, None) == 2
+    assert lib.bitlinear_calibrate_read(P_MIS, 1024, P, None) == 3
+

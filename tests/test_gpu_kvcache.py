@@ -121,7 +121,10 @@ def test_kv_cache_full(part, bits, rope):
         kw.update(bos_slot=dev_i32(slots), n_bos_slots=int(bos.sum()))
     codes, scale, bcodes, bscale = tw.bitlinear_kv_quantize(qkv[:, off:off + H * D], H, D, bits, eps=EPS, **kw)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.random.default_rng(3).choice(T, 40, replace=False), [0, 1023, 1024, T - 1]]))
+    rng = np.random.default_rng(3)
+    per_block = np.arange(0, T, 128) + rng.integers(0, 128, (T + 127) // 128)          # one token per 128
+    rows = np.unique(np.concatenate([rng.choice(T, 256, replace=False), per_block[per_block < T],
+                                     [0, 1023, 1024, T - 1]]))
     xs = inp["qkv"][rows, off:off + H * D].reshape(len(rows), H, D)
     ref = O.kv_cache_quant(xs, bits, EPS, pos=pos[rows] if rope else None, cos=inp["cos"] if rope else None,
                            sin=inp["sin"] if rope else None, bos=bos[rows] if bits == 3 else None)

@@ -17,9 +17,12 @@ pytestmark = pytest.mark.gpu
 EPS = 1e-5
 
 
-def sample_rows(M, n=24, seed=0):
+def sample_rows(M, n=256, seed=0, tile=128):
+    """A seeded sample of at least min(n, M) rows: one random row in every 128-row tile of the GEMMs'
+    blocks (the ragged last tile included), n random rows, and the first and last row."""
     rng = np.random.default_rng(seed)
-    rows = set(rng.choice(M, size=min(n, M), replace=False).tolist()) | {0, M - 1}
+    per_tile = [t * tile + int(rng.integers(0, min(tile, M - t * tile))) for t in range((M + tile - 1) // tile)]
+    rows = set(per_tile) | set(rng.choice(M, size=min(n, M), replace=False).tolist()) | {0, M - 1}
     return np.array(sorted(rows))
 
 
@@ -213,7 +216,7 @@ def test_largest_index_space_sampled(fmt):
     codes, scale, _ = tw.bitlinear_quantize_act(x, fmt, eps=EPS)
     y = tw.bitlinear_gemm_w158a4(fmt, codes, scale, K, packed, a, N)
     torch.cuda.synchronize()
-    rows = sample_rows(M, n=40, seed=11)
+    rows = sample_rows(M, n=64, seed=11, tile=1 << 16)
     rows_t = torch.from_numpy(rows).cuda()
     xs = x[rows_t].float().cpu().numpy()
     ref = O.bitlinear_a4(xs, t, alpha, EPS, fmt="fp4" if fmt == "fp4" else "int4")
@@ -237,7 +240,7 @@ def test_largest_index_space_topk_a8_sampled():
     codes, scale, mask = tw.bitlinear_quantize_act(x, "int8", topk_keep=keep, eps=EPS, want_mask=True)
     y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, residual=r)
     torch.cuda.synchronize()
-    rows = sample_rows(M, n=24, seed=12)
+    rows = sample_rows(M, n=64, seed=12, tile=1 << 16)
     rows_t = torch.from_numpy(rows).cuda()
     res = r[rows_t].cpu().numpy()
     ref = O.oproj_ref(x[rows_t].float().cpu().numpy(), t, alpha, res, keep, EPS)
