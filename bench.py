@@ -166,6 +166,11 @@ def main():
     kkb_s = torch.empty((knslots, kH), dtype=torch.float32, device=dev)
     kvb_c = torch.empty_like(kkb_c)
     kvb_s = torch.empty_like(kkb_s)
+    # the same records from the QKV GEMM with the KV quantizer fused into its epilogue (no fp32 output)
+    kv_fused = {"codes": [torch.empty_like(kq_c), torch.empty_like(kk_c), torch.empty_like(kv_c)],
+                "scale": [torch.empty_like(kq_s), torch.empty_like(kk_s), torch.empty_like(kv_s)],
+                "bos_codes": [None, torch.empty_like(kkb_c), torch.empty_like(kvb_c)],
+                "bos_scale": [None, torch.empty_like(kkb_s), torch.empty_like(kvb_s)]}
 
     D = WORKLOADS["decode_a4"]
     din = workload_inputs("decode_a4")
@@ -256,7 +261,7 @@ def main():
              "quant_int4_per_tensor_prefill",
              "quant_int4_e3m2_ffn", "gemm_a4_glu_ffn", "quant_int8_h", "gemm_a8_down", "quant_topk_int8_attn",
              "gemm_a8_oproj_residual", "gemm_a8_down_structured", "gemm_a8_oproj_residual_structured",
-             "kv_quant_q4_rope", "kv_quant_k3_rope_bos", "kv_quant_v3_bos"] + \
+             "kv_quant_q4_rope", "kv_quant_k3_rope_bos", "kv_quant_v3_bos", "gemm_a4_qkv_kv_fused"] + \
         [f"decode_m{m}_graph" for m in D["Ms"]] + \
         [f"decode_glu_m{m}_graph" for m in D["Ms"]] + [f"decode_glu_cond_m{m}_graph" for m in D["Ms"]] + \
         [f"decode_a8_m{m}_graph" for m in D["Ms"]]
@@ -299,6 +304,9 @@ def main():
                                  bos_scale=kkb_s); mark()
         tw.bitlinear_kv_quantize(py4[:, 2 * kH * kD:], kH, kD, 3, eps=EPS, bos_slot=kslot, n_bos_slots=knslots,
                                  codes=kv_c, scale=kv_s, bos_codes=kvb_c, bos_scale=kvb_s); mark()
+        tw.bitlinear_gemm_w158a4_kv("int4_e3m2", pc6, ps6, P["K"], pW, pA, P["N"], kH, bits=(4, 3, 3), eps=EPS,
+                                    pos=kpos, cos=kcos, sin=ksin, bos_slot=kslot, n_bos_slots=knslots,
+                                    out=kv_fused); mark()
         for m in D["Ms"]:
             graphs[m].replay(); mark()
         for m in D["Ms"]:
@@ -449,6 +457,14 @@ def main():
     for n, bits, rope, bos in (("kv_quant_q4_rope", 4, True, False), ("kv_quant_k3_rope_bos", 3, True, True),
                                ("kv_quant_v3_bos", 3, False, True)):
         kern[n] = dict(us=times[n], bound="hbm", gbs=gbs(kv_bytes(bits, rope, bos), times[n]))
+    unfused = times["gemm_a4_int4_fp6_prefill"] + sum(times[n] for n in ("kv_quant_q4_rope", "kv_quant_k3_rope_bos",
+                                                                          "kv_quant_v3_bos"))
+    kern["gemm_a4_qkv_kv_fused"] = dict(us=times["gemm_a4_qkv_kv_fused"], bound="mfma",
+                                        tops=tops(ops_prefill, times["gemm_a4_qkv_kv_fused"]), peak=FP4_PEAK_TOPS,
+                                        unfused_us=round(unfused, 3),
+                                        speedup_vs_unfused=round(unfused / times["gemm_a4_qkv_kv_fused"], 3),
+                                        what="INT4-on-FP6 QKV GEMM with RoPE and the Q4/K3/V3 (+BOS) KV quantizer "
+                                             "in its epilogue, no fp32 output; unfused = GEMM + three KV kernels")
     for m in D["Ms"]:
         kern[f"decode_m{m}"] = dict(us=gemv_us[m], bound="hbm", gbs=gbs(dec_bytes(m), gemv_us[m]))
     for k in kern.values():

@@ -335,6 +335,42 @@ bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, in
 bl_status bitlinear_calibrate_mfma(int32_t blocks, int32_t iters, float* d_out, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * bitlinear_gemm_w158a4_kv: the QKV projection of a prefill with the KV-cache quantizer of section 3.4,
+ * "Low-Bit KV Cache Quantization" (Table 3), fused into its epilogue: Y = Q_4bit(X) Q_w(W_qkv)^T as
+ * bitlinear_gemm_w158a4 computes it (fmt BL_ACT_INT4_E3M2 or BL_ACT_FP4_E2M1), and from each row's
+ * fp32 values, exactly as bitlinear_kv_quantize computes them from that fp32 output:
+ *   columns [p H 128, (p+1) H 128) are part p = Q, K, V (head size D = 128, N = 3 H 128);
+ *   RoPE (when d_cos is given) on Q and K, never on V; per (token, head) absmax codes of bits[p]
+ *   bits in the KV record layout above (d_codes[p] [M][H][16 bits[p]] bytes, d_scale[p] [M][H]);
+ *   with d_bos_slot, parts with 3 bits also get the 4-bit records of BOS tokens in
+ *   d_bos_codes[p] [n_bos_slots][H][64] and d_bos_scale[p] [n_bos_slots][H] (the other parts' BOS
+ *   pointers are ignored). The outputs equal bitlinear_gemm_w158a4 followed by three
+ *   bitlinear_kv_quantize calls on the Q, K and V columns of Y, bit for bit.
+ *   d_y        NULL: the fp32 projection is not stored (its 4 M N bytes never reach memory); else Y as
+ *              bitlinear_gemm_w158a4 writes it (row stride ldy).
+ * Errors: as for bitlinear_gemm_w158a4 and bitlinear_kv_quantize; N != 3 H 128 -> UNSUPPORTED_SHAPE;
+ * other formats -> INVALID_ARGUMENT.
+ * ------------------------------------------------------------------------------------------- */
+typedef struct {
+  int64_t H;                 /* heads per part */
+  float eps;
+  int32_t bits[3];           /* Q, K, V: 3 or 4 */
+  void* d_codes[3];
+  float* d_scale[3];
+  const int32_t* d_pos;      /* [M] positions (with d_cos) */
+  const float* d_cos;        /* [P][64] (or NULL: no RoPE) */
+  const float* d_sin;
+  int64_t P;
+  const int32_t* d_bos_slot; /* optional [M]: slot >= 0 marks a BOS token */
+  int64_t n_bos_slots;
+  void* d_bos_codes[3];
+  float* d_bos_scale[3];
+} bl_kv_epilogue;
+bl_status bitlinear_gemm_w158a4_kv(int32_t fmt, const void* d_codes, const float* d_scale, int64_t M, int64_t K,
+                                   const void* d_packed, const float* d_alpha, int64_t N, float* d_y, int64_t ldy,
+                                   const bl_kv_epilogue* h_kv, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * bitlinear_calibrate_read: a measurement aid, not part of the BitLinear path. A plain streaming read
  * of `bytes` bytes at d_src (16 bytes per lane, one load per lane), the ceiling for a kernel that
  * reads the same bytes once per launch, e.g. a decode GEMV streaming one packed weight matrix.

@@ -30,7 +30,7 @@ EXPORTED = (
     "bitlinear_gemv_decode", "bitlinear_gemv_decode_glu_conditional", "bitlinear_status_string",
     "bitlinear_abi_version", "bitlinear_quantize_act_per_tensor", "bitlinear_quantize_per_tensor_workspace_bytes",
     "bitlinear_kv_quantize", "bitlinear_calibrate_mfma", "bitlinear_calibrate_read", "bitlinear_workspace_size",
-    "bitlinear_quantize_act_per_tensor_noalloc", "bitlinear_noalloc_scratch_bytes",
+    "bitlinear_quantize_act_per_tensor_noalloc", "bitlinear_noalloc_scratch_bytes", "bitlinear_gemm_w158a4_kv",
 )
 NOALLOC_MAX_M = 65536
 
@@ -52,6 +52,24 @@ class bl_epilogue(ctypes.Structure):
         ("d_up_packed", ctypes.c_void_p),
         ("d_up_alpha", ctypes.c_void_p),
         ("d_row_absmax", ctypes.c_void_p),
+    ]
+
+
+class bl_kv_epilogue(ctypes.Structure):
+    _fields_ = [
+        ("H", ctypes.c_int64),
+        ("eps", ctypes.c_float),
+        ("bits", ctypes.c_int32 * 3),
+        ("d_codes", ctypes.c_void_p * 3),
+        ("d_scale", ctypes.c_void_p * 3),
+        ("d_pos", ctypes.c_void_p),
+        ("d_cos", ctypes.c_void_p),
+        ("d_sin", ctypes.c_void_p),
+        ("P", ctypes.c_int64),
+        ("d_bos_slot", ctypes.c_void_p),
+        ("n_bos_slots", ctypes.c_int64),
+        ("d_bos_codes", ctypes.c_void_p * 3),
+        ("d_bos_scale", ctypes.c_void_p * 3),
     ]
 
 
@@ -100,6 +118,9 @@ def _lib():
         for name in ("bitlinear_gemm_w158a4", "bitlinear_gemv_decode"):
             getattr(lib, name).argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, i64, ep, vp]
             getattr(lib, name).restype = i32
+        lib.bitlinear_gemm_w158a4_kv.argtypes = [i32, vp, vp, i64, i64, vp, vp, i64, vp, i64,
+                                                 ctypes.POINTER(bl_kv_epilogue), vp]
+        lib.bitlinear_gemm_w158a4_kv.restype = i32
         lib.bitlinear_gemm_w158a8_sparse.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, i64, ep, vp]
         lib.bitlinear_gemm_w158a8_sparse.restype = i32
         lib.bitlinear_status_string.argtypes = [i32]
@@ -319,6 +340,47 @@ def bitlinear_gemm_w158a4(fmt, codes, scale, K, packed, alpha, N, y=None, residu
     """Y [M, N] = Q_4bit(X) Q_w(W)^T with an optional epilogue (residual or ReLU^2 GLU with W_up)."""
     return _mm("bitlinear_gemm_w158a4", fmt, codes, scale, scale.shape[0], K, packed, alpha, N, y, residual,
                up_packed, up_alpha, row_absmax, stream)
+
+
+def bitlinear_gemm_w158a4_kv(fmt, codes, scale, K, packed, alpha, N, H, bits=(4, 3, 3), eps=1e-5, pos=None, cos=None,
+                             sin=None, bos_slot=None, n_bos_slots=0, y=None, want_y=False, out=None, stream=None):
+    """QKV projection with the KV-cache quantizer in its epilogue (head size 128, N = 3 H 128).
+
+    Returns dict(y (or None), codes=[q, k, v], scale=[q, k, v], bos_codes=[...], bos_scale=[...]);
+    `out` may give preallocated buffers under the same keys."""
+    import torch
+    f = _fmt(fmt)
+    M = scale.shape[0]
+    dev = codes.device
+    if want_y and y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    out = dict(out or {})
+    if "codes" not in out:
+        out["codes"] = [torch.empty((M, H * 16 * b), dtype=torch.uint8, device=dev) for b in bits]
+        out["scale"] = [torch.empty((M, H), dtype=torch.float32, device=dev) for _ in bits]
+    if bos_slot is not None and "bos_codes" not in out:
+        out["bos_codes"] = [torch.empty((n_bos_slots, H * 64), dtype=torch.uint8, device=dev) if b == 3 else None
+                            for b in bits]
+        out["bos_scale"] = [torch.empty((n_bos_slots, H), dtype=torch.float32, device=dev) if b == 3 else None
+                            for b in bits]
+    e = bl_kv_epilogue()
+    e.H, e.eps = H, float(eps)
+    for p in range(3):
+        e.bits[p] = bits[p]
+        e.d_codes[p] = out["codes"][p].data_ptr()
+        e.d_scale[p] = out["scale"][p].data_ptr()
+        if bos_slot is not None and out["bos_codes"][p] is not None:
+            e.d_bos_codes[p] = out["bos_codes"][p].data_ptr()
+            e.d_bos_scale[p] = out["bos_scale"][p].data_ptr()
+    if cos is not None:
+        e.d_pos, e.d_cos, e.d_sin, e.P = pos.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0]
+    if bos_slot is not None:
+        e.d_bos_slot, e.n_bos_slots = bos_slot.data_ptr(), n_bos_slots
+    st = _lib().bitlinear_gemm_w158a4_kv(f, _ptr(codes), _ptr(scale), M, K, _ptr(packed), _ptr(alpha), N, _ptr(y),
+                                         N if y is None else y.stride(0), ctypes.byref(e), _stream(stream))
+    _check(st, "bitlinear_gemm_w158a4_kv")
+    out["y"] = y
+    return out
 
 
 def bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, alpha, N, y=None, residual=None, up_packed=None,

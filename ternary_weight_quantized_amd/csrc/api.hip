@@ -21,15 +21,17 @@ bl_status hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP
 
 // Validation shared by the three matmul entry points.
 bl_status check_mm(int32_t fmt, const void* codes, const float* scale, int64_t M, int64_t K, const void* packed,
-                   const float* alpha, int64_t N, const float* y, int64_t ldy, const bl_epilogue* epi) {
-  if (!codes || !scale || !packed || !alpha || !y) return BL_ERR_INVALID_ARGUMENT;
+                   const float* alpha, int64_t N, const float* y, int64_t ldy, const bl_epilogue* epi,
+                   bool y_optional = false) {
+  if (!codes || !scale || !packed || !alpha || (!y && !y_optional)) return BL_ERR_INVALID_ARGUMENT;
   if (fmt != BL_ACT_INT4 && fmt != BL_ACT_FP4_E2M1 && fmt != BL_ACT_INT8 && fmt != BL_ACT_INT4_E3M2)
     return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1 || N < 1) return BL_ERR_UNSUPPORTED_SHAPE;
   if (K % 128 != 0 || N % 16 != 0 || K > kMaxMatmulK) return BL_ERR_UNSUPPORTED_SHAPE;
   if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (ldy < N) return BL_ERR_INVALID_ARGUMENT;
-  if (!aligned16(codes) || !aligned16(packed) || !aligned16(y) || (ldy * 4) % 16 != 0) return BL_ERR_MISALIGNED;
+  if (y && ldy < N) return BL_ERR_INVALID_ARGUMENT;
+  if (!aligned16(codes) || !aligned16(packed)) return BL_ERR_MISALIGNED;
+  if (y && (!aligned16(y) || (ldy * 4) % 16 != 0)) return BL_ERR_MISALIGNED;
   if (epi) {
     if (epi->kind == BL_EPI_RESIDUAL) {
       if (!epi->d_residual) return BL_ERR_INVALID_ARGUMENT;
@@ -296,6 +298,52 @@ bl_status bitlinear_gemv_decode_glu_conditional(const void* d_codes, const float
   u.G = d_gate; u.ldg = (long)ldg; u.Wup = d_up_rows; u.upalpha = d_up_alpha;
   u.H = d_h; u.ldh = (long)ldh; u.rowmax = d_row_absmax;
   return hip_status(bl_launch_glu_conditional_fused(u, d_gate_packed, d_gate_alpha, st));
+}
+
+bl_status bitlinear_gemm_w158a4_kv(int32_t fmt, const void* d_codes, const float* d_scale, int64_t M, int64_t K,
+                                   const void* d_packed, const float* d_alpha, int64_t N, float* d_y, int64_t ldy,
+                                   const bl_kv_epilogue* h_kv, void* stream) {
+  if (!h_kv) return BL_ERR_INVALID_ARGUMENT;
+  if (fmt != BL_ACT_INT4_E3M2 && fmt != BL_ACT_FP4_E2M1) return BL_ERR_INVALID_ARGUMENT;
+  // the matmul checks (a null y is allowed: the fp32 projection is then not stored)
+  const bl_status s = check_mm(fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, nullptr, true);
+  if (s != BL_OK) return s;
+  const bl_kv_epilogue& k = *h_kv;
+  if (k.H < 1 || N != 3 * k.H * 128) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (!eps_ok(k.eps)) return BL_ERR_INVALID_ARGUMENT;
+  bool any3 = false;
+  for (int p = 0; p < 3; ++p) {
+    if (k.bits[p] != 3 && k.bits[p] != 4) return BL_ERR_INVALID_ARGUMENT;
+    if (!k.d_codes[p] || !k.d_scale[p]) return BL_ERR_INVALID_ARGUMENT;
+    if (!aligned16(k.d_codes[p])) return BL_ERR_MISALIGNED;
+    any3 = any3 || k.bits[p] == 3;
+  }
+  if ((k.d_cos == nullptr) != (k.d_sin == nullptr)) return BL_ERR_INVALID_ARGUMENT;
+  if (k.d_cos && (!k.d_pos || k.P < 1)) return BL_ERR_INVALID_ARGUMENT;
+  if (k.d_cos && (!aligned16(k.d_cos) || !aligned16(k.d_sin))) return BL_ERR_MISALIGNED;
+  if (k.d_cos && k.P * 128 >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (k.d_bos_slot) {
+    if (!any3 || k.n_bos_slots < 1) return BL_ERR_INVALID_ARGUMENT;
+    if (k.n_bos_slots * k.H * 128 >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+    for (int p = 0; p < 3; ++p) {
+      if (k.bits[p] != 3) continue;
+      if (!k.d_bos_codes[p] || !k.d_bos_scale[p]) return BL_ERR_INVALID_ARGUMENT;
+      if (!aligned16(k.d_bos_codes[p])) return BL_ERR_MISALIGNED;
+    }
+  }
+  bl_mm_args a = make_args(fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, d_y ? ldy : N, nullptr);
+  bl_kv_epi e{};
+  e.H = (int)k.H; e.eps = k.eps;
+  for (int p = 0; p < 3; ++p) {
+    e.bits[p] = k.bits[p];
+    e.codes[p] = static_cast<uint8_t*>(k.d_codes[p]);
+    e.scale[p] = k.d_scale[p];
+    e.bos_codes[p] = static_cast<uint8_t*>(k.d_bos_codes[p]);
+    e.bos_scale[p] = k.d_bos_scale[p];
+  }
+  e.pos = k.d_pos; e.cos = k.d_cos; e.sin = k.d_sin; e.P = (int)k.P;
+  e.bos_slot = k.d_bos_slot; e.nslots = (int)k.n_bos_slots;
+  return hip_status(bl_launch_gemm_kv(a, e, static_cast<hipStream_t>(stream)));
 }
 
 bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, int64_t H, int64_t D, int64_t ldx,

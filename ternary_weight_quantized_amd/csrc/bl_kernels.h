@@ -35,6 +35,27 @@ struct bl_mm_args {
 };
 
 hipError_t bl_launch_gemm(const bl_mm_args& a, hipStream_t st);
+
+// KV-cache epilogue of the QKV projection (FP6 / FP4 GEMM, head size 128): parts 0, 1, 2 = Q, K, V
+// columns [p H 128, (p+1) H 128); RoPE (cos != null) on Q and K; absmax codes per (token, head);
+// 4-bit BOS records of 3-bit parts for tokens with bos_slot[t] in [0, nslots).
+constexpr int BL_EPI_KV = 3;        // internal epilogue kind of the fused entry point
+struct bl_kv_epi {
+  int H;
+  float eps;
+  int bits[3];
+  uint8_t* codes[3];
+  float* scale[3];
+  const int* pos;
+  const float* cos;
+  const float* sin;
+  int P;
+  const int* bos_slot;
+  int nslots;
+  uint8_t* bos_codes[3];
+  float* bos_scale[3];
+};
+hipError_t bl_launch_gemm_kv(const bl_mm_args& a, const bl_kv_epi& kv, hipStream_t st);
 hipError_t bl_launch_gemv(const bl_mm_args& a, hipStream_t st);
 hipError_t bl_launch_fill_zero(float* p, long n, hipStream_t st);
 

@@ -268,11 +268,122 @@ struct CfgMx {
   using Plan = StagePlan<FMT, BM, BN, NB, NW>;
 };
 
+// ---------------------------------------------------------------------------- fused KV-cache epilogue
+// One wave's 128-column strip of a 128 x 256 tile is exactly one head of 128 (strips start at
+// multiples of 128), and lane (r, g) holds columns 16 t + 4 g + v (t < 8, v < 4) of row r: the
+// rotate-half partner i + 64 of column i = 16 t + 4 g + v (t < 4) is column 16 (t + 4) + 4 g + v of
+// the same lane, and the head's absmax is a maximum over the four lanes r, r + 16, r + 32, r + 48.
+// Codes, scales and BOS records are written exactly as the stand-alone KV quantizer writes them.
+// u = RoundClip(RN32(x s), -Qp-1, Qp) + 2^(b-1) of four values, b bits apart. |x| <= gamma gives
+// |RN32(x s)| < Qp + 1/2, so the clip never acts; adding C = 1.5 2^23 + 2^(b-1) rounds to an integer
+// (ties to even, like rint: C is even) and leaves rint(x s) + 2^(b-1) in the low mantissa bits.
+template <int BITS>
+__device__ __forceinline__ uint32_t kv_code4(const float (&x)[4], float s) {
+  constexpr float C = 12582912.0f + (float)(1 << (BITS - 1));
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  uint32_t r = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r |= (bl_f2u(x[j] * s + C) & MASK) << (BITS * j);
+  return r;
+}
+
+// the head record of one row: 4 bits per code (64 bytes) or 3 bits (48 bytes); the lane's codes of
+// tile t are codes 16 t + 4 g .. + 3; lanes g and g ^ 1 (lane ^ 16) combine their pieces
+template <int BITS>
+__device__ __forceinline__ void kv_store_head(uint8_t* __restrict__ rec, const float (&x)[8][4], float s, int g,
+                                              bool ok) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t mine = kv_code4<BITS>(x[t], s);
+    const uint32_t other = __shfl_xor(mine, 16, 64);
+    if (ok && (g & 1) == 0) {
+      if constexpr (BITS == 4) {
+        *reinterpret_cast<uint32_t*>(rec + 8 * t + 2 * g) = mine | (other << 16);       // codes 16t+4g .. +7
+      } else {
+        const uint32_t v24 = mine | (other << 12);                                        // 8 codes, 3 bytes
+        uint8_t* b = rec + 6 * t + 3 * (g >> 1);
+        if (g == 0) {
+          *reinterpret_cast<uint16_t*>(b) = (uint16_t)v24;
+          b[2] = (uint8_t)(v24 >> 16);
+        } else {
+          b[0] = (uint8_t)v24;
+          *reinterpret_cast<uint16_t*>(b + 1) = (uint16_t)(v24 >> 8);
+        }
+      }
+    }
+  }
+}
+
+// The lane's RoPE table entries of one row (columns 16 t + 4 g .. + 3, t < 4), for the row's position
+// (clamped into the table, so that no position reads outside it).
+__device__ __forceinline__ void kv_rope_tables(const bl_kv_epi& kv, int p, int g, float4 (&cs)[4], float4 (&sn)[4]) {
+  p = p < 0 ? 0 : (p >= kv.P ? kv.P - 1 : p);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    cs[t] = *reinterpret_cast<const float4*>(kv.cos + (long)p * 64 + 16 * t + 4 * g);
+    sn[t] = *reinterpret_cast<const float4*>(kv.sin + (long)p * 64 + 16 * t + 4 * g);
+  }
+}
+
+// o: the fp32 outputs of one row of the wave's strip (exactly the values the plain epilogue stores);
+// cs, sn: the row's RoPE table entries (used for Q and K when the tables are given); slot: the row's
+// BOS slot (or -1)
+__device__ __forceinline__ void kv_epilogue_row(const bl_kv_epi& kv, int m, bool mok, int nstrip, float (&o)[8][4],
+                                                int g, const float4 (&cs)[4], const float4 (&sn)[4], int slot) {
+  const int HD = kv.H * 128;
+  const int part = nstrip / HD;
+  const int h = (nstrip - part * HD) >> 7;
+  const bool rope = kv.cos != nullptr && part < 2;
+  if (rope) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float4 c = cs[t], sv = sn[t];
+      const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float a = o[t][v], b = o[t + 4][v];
+        o[t][v] = a * cc[v] - b * ss[v];
+        o[t + 4][v] = b * cc[v] + a * ss[v];
+      }
+    }
+  }
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t u = bl_f2u(o[t][v]) & 0x7FFFFFFFu;
+      mx = u > mx ? u : mx;
+    }
+  uint32_t q = __shfl_xor(mx, 16, 64);
+  mx = q > mx ? q : mx;
+  q = __shfl_xor(mx, 32, 64);
+  mx = q > mx ? q : mx;
+  const float gamma = bl_u2f(mx);
+  const float den = gamma + kv.eps;
+  const long rec = (long)m * kv.H + h;
+  if (kv.bits[part] == 4) {
+    kv_store_head<4>(kv.codes[part] + rec * 64, o, 7.0f / den, g, mok);
+    if (mok && g == 0) kv.scale[part][rec] = gamma / 7.0f;
+  } else {
+    kv_store_head<3>(kv.codes[part] + rec * 48, o, 3.0f / den, g, mok);
+    if (mok && g == 0) kv.scale[part][rec] = gamma / 3.0f;
+    if (kv.bos_slot) {                                       // uniform over the launch
+      const bool wr = mok && slot >= 0 && slot < kv.nslots;
+      if (__ballot(wr) != 0ull) {
+        const long brec = (long)(wr ? slot : 0) * kv.H + h;
+        kv_store_head<4>(kv.bos_codes[part] + brec * 64, o, 7.0f / den, g, wr);
+        if (wr && g == 0) kv.bos_scale[part][brec] = gamma / 7.0f;
+      }
+    }
+  }
+}
+
 template <int FMT, int EPI>
 __global__ __launch_bounds__(256, 2) void k_gemm_mx(
     const uint8_t* __restrict__ A, const float* __restrict__ ascale, int M, int K, const uint8_t* __restrict__ W,
     const float* __restrict__ walpha, const uint8_t* __restrict__ W2, const float* __restrict__ w2alpha, int N,
-    float* __restrict__ Y, long ldy, const float* R, long ldr, float* __restrict__ rowmax) {
+    float* __restrict__ Y, long ldy, const float* R, long ldr, float* __restrict__ rowmax, const bl_kv_epi kv) {
   using C = CfgMx<FMT, EPI>;
   using F = AFmt<FMT>;
   using P = typename C::Plan;
@@ -314,6 +425,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx(
 #pragma unroll
   for (int s = 0; s < SM; ++s) dsv[s] = ascale[min(m0 + wm * SM * 16 + 16 * s + r16, M - 1)];
   const float alpha = *walpha;
+  // KV epilogue: the rows' positions and BOS slots, fetched before the K loop as well
+  int kvpos[SM], kvslot[SM];
+  if constexpr (EPI == BL_EPI_KV) {
+#pragma unroll
+    for (int s = 0; s < SM; ++s) {
+      const int m = min(m0 + wm * SM * 16 + 16 * s + r16, M - 1);
+      kvpos[s] = kv.cos ? kv.pos[m] : 0;
+      kvslot[s] = kv.bos_slot ? kv.bos_slot[m] : -1;
+    }
+  }
   const float alpha2 = C::GLU ? *w2alpha : 0.f;
 
   P plan;
@@ -389,11 +510,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx(
   // fp32 epilogue: the matrix-core sum is 2*sum(c t) (E3M2) or sum(2e t) = sum(doubled code * t)
   // (E2M1); x 0.5 is exact and gives sum(c t), respectively the half-unit count of the oracle.
   const int nw0 = n0 + wn * SN * 16 + 4 * g4;
+  // KV epilogue: each subtile's RoPE table rows are fetched while the previous subtile is processed
+  float4 kcs[2][4], ksn[2][4];
+  if constexpr (EPI == BL_EPI_KV) {
+    if (kv.cos) kv_rope_tables(kv, kvpos[0], g4, kcs[0], ksn[0]);
+  }
 #pragma unroll
   for (int s = 0; s < SM; ++s) {
     const int m = m0 + wm * SM * 16 + 16 * s + r16;
     const bool mok = m < M;
     const float sc = dsv[s] * alpha, sc2 = dsv[s] * alpha2;
+    if constexpr (EPI == BL_EPI_KV) {
+      if (kv.cos && s + 1 < SM) kv_rope_tables(kv, kvpos[s + 1], g4, kcs[(s + 1) & 1], ksn[(s + 1) & 1]);
+    }
     float4 res[SN];
     if constexpr (EPI == BL_EPI_RESIDUAL) {
 #pragma unroll
@@ -416,6 +545,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx(
       for (int t = 0; t < SN; ++t) {
         const int n = nw0 + 16 * t;
         if (mok && n < N) *reinterpret_cast<float4*>(Y + (long)m * ldy + n) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+      }
+    } else if constexpr (EPI == BL_EPI_KV) {
+      static_assert(SN == 8, "one head of 128 per wave strip");
+      const int nstrip = n0 + wn * SN * 16;
+      if (nstrip < N) {                                      // wave-uniform: a whole strip or none
+        if (Y)
+          store_subtile_rows<SN>(Y, ldy, M, N, m0 + wm * SM * 16 + 16 * s, nstrip, o,
+                                 reinterpret_cast<float*>(smem) + wave * (16 * (16 * SN + 4)), lane);
+        kv_epilogue_row(kv, m, mok, nstrip, o, g4, kcs[s & 1], ksn[s & 1], kvslot[s]);
       }
     } else {
       // whole-row stores through the wave's LDS region
@@ -612,7 +750,7 @@ hipError_t launch(const bl_mm_args& a, hipStream_t st) {
     using C = CfgMx<FMT, EPI>;
     const int ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
     hipLaunchKernelGGL((k_gemm_mx<FMT, EPI>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A, a.ascale, a.M, a.K,
-                       W, a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
+                       W, a.walpha, W2, a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax, bl_kv_epi{});
   } else {
     // 128 x 256 tiles when they give every CU at least two blocks, 128 x 128 tiles otherwise
     using C2 = CfgI8<FMT, EPI, 256>;
@@ -647,6 +785,23 @@ __global__ void k_fill_zero(float* p, long n) {
 
 hipError_t bl_launch_fill_zero(float* p, long n, hipStream_t st) {
   hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t bl_launch_gemm_kv(const bl_mm_args& a, const bl_kv_epi& kv, hipStream_t st) {
+  const uint8_t* A = static_cast<const uint8_t*>(a.A);
+  const uint8_t* W = static_cast<const uint8_t*>(a.W);
+  if (a.fmt == BL_ACT_INT4_E3M2) {
+    using C = CfgMx<BL_ACT_INT4_E3M2, BL_EPI_KV>;
+    const int ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
+    hipLaunchKernelGGL((k_gemm_mx<BL_ACT_INT4_E3M2, BL_EPI_KV>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A,
+                       a.ascale, a.M, a.K, W, a.walpha, nullptr, nullptr, a.N, a.Y, a.ldy, nullptr, 0L, nullptr, kv);
+  } else {
+    using C = CfgMx<BL_ACT_FP4_E2M1, BL_EPI_KV>;
+    const int ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
+    hipLaunchKernelGGL((k_gemm_mx<BL_ACT_FP4_E2M1, BL_EPI_KV>), dim3(ntm * ntn), dim3(C::NW * 64), 0, st, A,
+                       a.ascale, a.M, a.K, W, a.walpha, nullptr, nullptr, a.N, a.Y, a.ldy, nullptr, 0L, nullptr, kv);
+  }
   return hipGetLastError();
 }
 

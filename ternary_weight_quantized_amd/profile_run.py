@@ -9,7 +9,8 @@ latent weights) and launches the selected W1.58A4 GEMM `reps` times. --decode la
 rotating copies of its weights (as the benchmark's graphs do): the INT4 decode GEMV of 1 token
 (11008x4096), the fused gate+up ReLU^2 GLU decode GEMV of 1 token (12 copies of both 11008x4096
 matrices) and the INT8 decode GEMV of one row of the FFN's h codes against the 4096x11008 down
-projection. --a8 launches the two W1.58A8 GEMMs of the FFN (down) and attention-output workloads.
+projection. --a8 launches the two W1.58A8 GEMMs of the FFN (down) and attention-output workloads; --kv the
+prefill QKV GEMM with the KV-cache quantizer fused into its epilogue (Q4 RoPE, K3 RoPE + BOS, V3 + BOS).
 With --copy-calibration a 256 MiB device-to-device copy runs first; its FETCH_SIZE and WRITE_SIZE
 readings give the factor that turns those counters into bytes.
 """
@@ -37,10 +38,11 @@ def main():
     p.add_argument("--gemm", choices=sorted(FORMATS), default=None)
     p.add_argument("--decode", action="store_true")
     p.add_argument("--a8", action="store_true")
+    p.add_argument("--kv", action="store_true", help="the prefill QKV GEMM with the fused KV-cache epilogue")
     p.add_argument("--reps", type=int, default=3)
     p.add_argument("--copy-calibration", action="store_true")
     args = p.parse_args()
-    if not (args.gemm or args.decode or args.a8):
+    if not (args.gemm or args.decode or args.a8 or args.kv):
         args.gemm = "fp6"
 
     import torch
@@ -64,6 +66,30 @@ def main():
         y = torch.empty((P["M"], P["N"]), dtype=torch.float32, device="cuda")
         work.append((f"{args.reps} x {fmt} GEMM M={P['M']} K={P['K']} N={P['N']}",
                      lambda: [tw.bitlinear_gemm_w158a4(fmt, codes, scale, P["K"], packed, alpha, P["N"], y=y)
+                              for _ in range(args.reps)]))
+    if args.kv:
+        P = WORKLOADS["prefill_qkv"]
+        KV = WORKLOADS["kv_cache"]
+        import numpy as np
+        from synth import rope_tables
+        inp = workload_inputs("prefill_qkv")
+        kx = dev_bf16(torch, inp["x"])
+        kW, kA = pack(inp["w"])
+        kc, ks, _ = tw.bitlinear_quantize_act(kx, "int4_e3m2", eps=EPS)
+        H = P["N"] // 384
+        pos_np = (np.arange(P["M"]) % KV["seq_len"]).astype(np.int32)
+        bos = pos_np == 0
+        kpos = torch.from_numpy(pos_np).cuda()
+        kslot = torch.from_numpy(np.where(bos, np.cumsum(bos) - 1, -1).astype(np.int32)).cuda()
+        c_np, s_np = rope_tables(KV["seq_len"], 128)
+        kcos, ksin = torch.from_numpy(c_np).cuda(), torch.from_numpy(s_np).cuda()
+        kv_out = tw.bitlinear_gemm_w158a4_kv("int4_e3m2", kc, ks, P["K"], kW, kA, P["N"], H, bits=(4, 3, 3), eps=EPS,
+                                             pos=kpos, cos=kcos, sin=ksin, bos_slot=kslot,
+                                             n_bos_slots=int(bos.sum()))
+        work.append((f"{args.reps} x fused QKV + KV GEMM M={P['M']} K={P['K']} N={P['N']}",
+                     lambda: [tw.bitlinear_gemm_w158a4_kv("int4_e3m2", kc, ks, P["K"], kW, kA, P["N"], H,
+                                                          bits=(4, 3, 3), eps=EPS, pos=kpos, cos=kcos, sin=ksin,
+                                                          bos_slot=kslot, n_bos_slots=int(bos.sum()), out=kv_out)
                               for _ in range(args.reps)]))
     if args.decode or args.a8:
         F = WORKLOADS["ffn_7b"]

@@ -311,3 +311,38 @@ def test_calibrate_read_validation():
         assert lib.bitlinear_calibrate_read(P, b, P, None) == 2
     assert lib.bitlinear_calibrate_read(P_MIS, 1024, P, None) == 3
 
+
+
+def _kvmm(**kw):
+    a = dict(fmt=3, codes=P, scale=P, M=4, K=256, packed=P, alpha=P, N=384, y=None, ldy=384, H=1, eps=1e-5,
+             bits=(4, 3, 3), c=(P, P, P), s=(P, P, P), pos=None, cos=None, sin=None, Pn=0, bos=None, ns=0,
+             bc=(None, None, None), bs=(None, None, None))
+    a.update(kw)
+    e = tw.bl_kv_epilogue()
+    e.H, e.eps, e.P, e.n_bos_slots = a["H"], a["eps"], a["Pn"], a["ns"]
+    for i in range(3):
+        e.bits[i] = a["bits"][i]
+        e.d_codes[i] = a["c"][i].value if a["c"][i] is not None else None
+        e.d_scale[i] = a["s"][i].value if a["s"][i] is not None else None
+        e.d_bos_codes[i] = a["bc"][i].value if a["bc"][i] is not None else None
+        e.d_bos_scale[i] = a["bs"][i].value if a["bs"][i] is not None else None
+    for f in ("pos", "cos", "sin", "bos"):
+        setattr(e, {"pos": "d_pos", "cos": "d_cos", "sin": "d_sin", "bos": "d_bos_slot"}[f],
+                a[f].value if a[f] is not None else None)
+    return tw.library().bitlinear_gemm_w158a4_kv(a["fmt"], a["codes"], a["scale"], a["M"], a["K"], a["packed"],
+                                                 a["alpha"], a["N"], a["y"], a["ldy"], ctypes.byref(e), None)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=0), 1), (dict(fmt=2), 1), (dict(codes=None), 1), (dict(N=256), 2), (dict(H=2), 2), (dict(H=0), 2),
+    (dict(bits=(4, 5, 3)), 1), (dict(c=(P, None, P)), 1), (dict(s=(None, P, P)), 1), (dict(c=(P, P_MIS, P)), 3),
+    (dict(eps=0.0), 1), (dict(cos=P), 1), (dict(cos=P, sin=P), 1), (dict(cos=P, sin=P, pos=P), 1),
+    (dict(cos=P_MIS, sin=P, pos=P, Pn=8), 3), (dict(bos=P), 1), (dict(bos=P, ns=1), 1),
+    (dict(bos=P, ns=1, bits=(4, 4, 4), bc=(P, P, P), bs=(P, P, P)), 1),
+    (dict(bos=P, ns=1, bc=(None, P_MIS, P), bs=(None, P, P)), 3),
+    (dict(y=P, ldy=100), 1), (dict(y=P_MIS), 3), (dict(K=192), 2), (dict(M=0), 2),
+])
+def test_gemm_kv_validation(kw, status):
+    """Every rejection of the fused QKV + KV entry point happens on the host (no GPU here)."""
+    assert _kvmm(**kw) == status

@@ -171,3 +171,117 @@ def test_kv_quantize_largest_index_space_sampled():
     assert len(bos_rows) > 2                      # BOS tokens without a slot write no record
     del x, codes, scale
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- KV quantizer fused into the QKV GEMM
+def _qkv_case(seed, M, H, K, fmt, rope, bos_tokens):
+    """INT4 codes of bf16 rows and ternary QKV weights [3 H 128, K]; positions with BOS tokens at the
+    given indices (positions restart there), RoPE tables of 64 positions."""
+    from synth import latent_weights
+    N = 3 * H * 128
+    xb = activations_bf16(seed, M, K)
+    w = latent_weights(seed + 1, N, K)
+    t, alpha = O.ternarize(w, EPS)
+    packed, a = tw.bitlinear_pack_ternary(dev_f32(w), EPS)
+    codes, scale, _ = tw.bitlinear_quantize_act(dev_bf16(xb), fmt, eps=EPS)
+    pos = (np.arange(M) % 64).astype(np.int32)
+    bos = np.zeros(M, bool)
+    bos[list(bos_tokens)] = True
+    slots = np.where(bos, np.cumsum(bos) - 1, -1).astype(np.int32)
+    cos, sin = rope_tables(64, 128)
+    return dict(xb=xb, t=t, alpha=alpha, packed=packed, a=a, codes=codes, scale=scale, pos=pos, bos=bos, slots=slots,
+                nslots=int(bos.sum()), cos=cos, sin=sin, N=N)
+
+
+@pytest.mark.parametrize("fmt", ["int4_e3m2", "fp4"])
+@pytest.mark.parametrize("bits", [(4, 3, 3), (4, 4, 4), (3, 3, 3)])
+@pytest.mark.parametrize("rope,bos,want_y", [(True, True, False), (False, False, True), (True, False, True)])
+@pytest.mark.parametrize("M,H,K", [(1, 1, 256), (37, 2, 384), (200, 3, 512)])
+def test_qkv_kv_fused(M, H, K, fmt, bits, rope, bos, want_y):
+    """The fused QKV + KV-cache epilogue equals the GEMM followed by the stand-alone KV quantizer,
+    bit for bit (codes, scales, BOS records, and Y when it is written), and the oracle (the fixed-order
+    fp32 epilogue, then RoPE and absmax codes)."""
+    torch = torch_cuda()
+    c = _qkv_case(8100 + M + H + K, M, H, K, fmt, rope, [0] if bos else [])
+    N = c["N"]
+    kw = dict(pos=dev_i32(c["pos"]), cos=dev_f32(c["cos"]), sin=dev_f32(c["sin"])) if rope else {}
+    bkw = dict(bos_slot=dev_i32(c["slots"]), n_bos_slots=c["nslots"]) if bos and 3 in bits else {}
+    r = tw.bitlinear_gemm_w158a4_kv(fmt, c["codes"], c["scale"], K, c["packed"], c["a"], N, H, bits=bits, eps=EPS,
+                                    want_y=want_y, **kw, **bkw)
+    y = tw.bitlinear_gemm_w158a4(fmt, c["codes"], c["scale"], K, c["packed"], c["a"], N)
+    torch.cuda.synchronize()
+    if want_y:
+        np.testing.assert_array_equal(host(r["y"]).view(np.uint32), host(y).view(np.uint32))
+    else:
+        assert r["y"] is None
+    # the oracle: exact integer accumulators, fixed-order fp32 epilogue, then the KV quantizer
+    if fmt == "fp4":
+        ref = O.bitlinear_a4(bf16_bits_to_f32(c["xb"]), c["t"], c["alpha"], EPS, fmt="fp4")
+        y32 = O.dequant_f32(ref["acc"], ref["dscale"], c["alpha"], 0.5)
+    else:
+        ref = O.bitlinear_a4(bf16_bits_to_f32(c["xb"]), c["t"], c["alpha"], EPS)
+        y32 = O.dequant_f32(ref["acc"], ref["dscale"], c["alpha"])
+    np.testing.assert_array_equal(host(y).view(np.uint32), y32.view(np.uint32))
+    for p in range(3):
+        b = bits[p]
+        cols = slice(p * H * 128, (p + 1) * H * 128)
+        use_rope = rope and p < 2
+        o = O.kv_cache_quant(y32[:, cols].reshape(M, H, 128), b, EPS, pos=c["pos"] if use_rope else None,
+                             cos=c["cos"] if use_rope else None, sin=c["sin"] if use_rope else None,
+                             bos=c["bos"] if (bkw and b == 3) else None)
+        np.testing.assert_array_equal(unpack_kv(host(r["codes"][p]), H, 128, b), o["u"])
+        np.testing.assert_array_equal(host(r["scale"][p]), o["dscale"])
+        # the unfused path on the same Y gives the same records
+        kc, ks, kbc, kbs = tw.bitlinear_kv_quantize(y[:, cols], H, 128, b, eps=EPS, **(kw if use_rope else {}),
+                                                    **(bkw if b == 3 else {}))
+        np.testing.assert_array_equal(host(r["codes"][p]), host(kc))
+        np.testing.assert_array_equal(host(r["scale"][p]), host(ks))
+        if bkw and b == 3:
+            sl = c["slots"][c["bos"]]
+            np.testing.assert_array_equal(unpack_kv(host(r["bos_codes"][p]), H, 128, 4)[sl], o["bos_u"][c["bos"]])
+            np.testing.assert_array_equal(host(r["bos_scale"][p])[sl], o["bos_dscale"][c["bos"]])
+            np.testing.assert_array_equal(host(r["bos_codes"][p]), host(kbc))
+            np.testing.assert_array_equal(host(r["bos_scale"][p]), host(kbs))
+
+
+def test_qkv_kv_fused_full():
+    """The prefill workload as the benchmark runs the fused path: M=4096, K=4096, 32 heads per part,
+    Q at 4 bits with RoPE, K at 3 bits with RoPE and BOS records, V at 3 bits with BOS records, no fp32
+    output; every record equals the unfused path (GEMM, then the stand-alone quantizer) and sampled
+    tokens equal the oracle."""
+    torch = torch_cuda()
+    wl = WORKLOADS["prefill_qkv"]
+    inp = workload_inputs("prefill_qkv")
+    M, K, N = wl["M"], wl["K"], wl["N"]
+    H = N // 384
+    t, alpha = O.ternarize(inp["w"], EPS)
+    packed, a = tw.bitlinear_pack_ternary(dev_f32(inp["w"]), EPS)
+    codes, scale, _ = tw.bitlinear_quantize_act(dev_bf16(inp["x"]), "int4_e3m2", eps=EPS)
+    pos = (np.arange(M) % 1024).astype(np.int32)
+    bos = pos == 0
+    slots = np.where(bos, np.cumsum(bos) - 1, -1).astype(np.int32)
+    cos, sin = rope_tables(1024, 128)
+    kw = dict(pos=dev_i32(pos), cos=dev_f32(cos), sin=dev_f32(sin))
+    bkw = dict(bos_slot=dev_i32(slots), n_bos_slots=int(bos.sum()))
+    r = tw.bitlinear_gemm_w158a4_kv("int4_e3m2", codes, scale, K, packed, a, N, H, bits=(4, 3, 3), eps=EPS, **kw, **bkw)
+    y = tw.bitlinear_gemm_w158a4("int4_e3m2", codes, scale, K, packed, a, N)
+    for p, b in enumerate((4, 3, 3)):
+        cols = slice(p * H * 128, (p + 1) * H * 128)
+        kc, ks, kbc, kbs = tw.bitlinear_kv_quantize(y[:, cols], H, 128, b, eps=EPS, **(kw if p < 2 else {}),
+                                                    **(bkw if b == 3 else {}))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(r["codes"][p]), host(kc))
+        np.testing.assert_array_equal(host(r["scale"][p]), host(ks))
+        if b == 3:
+            np.testing.assert_array_equal(host(r["bos_codes"][p]), host(kbc))
+            np.testing.assert_array_equal(host(r["bos_scale"][p]), host(kbs))
+    rng = np.random.default_rng(21)
+    rows = np.unique(np.concatenate([rng.choice(M, 64, replace=False), np.arange(0, M, 128), [0, 1024, M - 1]]))
+    ref = O.bitlinear_a4(bf16_bits_to_f32(inp["x"][rows]), t, alpha, EPS)
+    y32 = O.dequant_f32(ref["acc"], ref["dscale"], alpha)
+    for p, b in enumerate((4, 3, 3)):
+        cols = slice(p * H * 128, (p + 1) * H * 128)
+        o = O.kv_cache_quant(y32[:, cols].reshape(len(rows), H, 128), b, EPS, pos=pos[rows] if p < 2 else None,
+                             cos=cos if p < 2 else None, sin=sin if p < 2 else None, bos=bos[rows] if b == 3 else None)
+        np.testing.assert_array_equal(unpack_kv(host(r["codes"][p])[rows], H, 128, b), o["u"])
+        np.testing.assert_array_equal(host(r["scale"][p])[rows], o["dscale"])
