@@ -8,6 +8,10 @@
 // columns give only 256 blocks); a wave issues all loads of a chunk of four or six K tiles at once (the
 // activation slices first, then its 8-byte share of each 512-byte weight tile, so a wave reads
 // whole tiles, fully coalesced) and feeds each tile to the matrix cores as soon as it has landed.
+// INT4 codes that fit in 32 KiB (M K / 2 bytes) are instead copied once per block into LDS with
+// direct-to-LDS loads, issued before the weight loads; one barrier after the first chunk's weight
+// loads publishes them, and the waves read their activation tiles from LDS rather than each
+// loading them through the vector memory path.
 // The tile words go to 16x16x64 int8 MFMAs directly; the M token rows occupy the first M of the 16
 // MFMA rows and the other rows repeat row M-1 (their outputs are never stored), which keeps every
 // load unconditional. The eight partial int32 tiles are summed exactly in LDS. The per-token scales,
@@ -104,8 +108,57 @@ __device__ __forceinline__ void chunk(const uint8_t* arp, const uint8_t* const (
   }
 }
 
-template <int FMT, int EPI, int CHN, int NWV>
-__global__ __launch_bounds__(NWV * 64) void k_gemv(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
+// Register cap of the eight-wave INT4 GLU: at most 80 VGPRs leave room for three blocks of eight
+// waves per CU, so the 688 blocks of an 11008-wide FFN are resident at once instead of in two rounds.
+// LDS copy of the INT4 codes of the M token rows (M K / 2 bytes), taken when they fit: one 16-byte
+// direct-to-LDS load per lane, piece i = NWV 64 j + 64 wave + lane of the contiguous rows, instead of
+// every wave of every block loading its activation tiles through the vector memory path.
+constexpr int ALDS_BYTES = 32768;
+template <int NWV>
+__device__ __forceinline__ void stage_codes_lds(const uint8_t* __restrict__ A, uint32_t nbytes, uint8_t* acodes,
+                                                int wave, int lane) {
+  const uint32_t npc = nbytes >> 4;
+  for (uint32_t i0 = 64u * wave; i0 < npc; i0 += NWV * 64) {
+    if (i0 + lane < npc)
+      __builtin_amdgcn_global_load_lds(A + 16u * (i0 + lane), (__attribute__((address_space(3))) void*)(acodes + 16u * i0),
+                                       16, 0, 0);
+  }
+}
+
+// Weights of one chunk of up to CH K tiles from kt0 (kt0 < kt_end; tiles past kt_end repeat the last).
+template <int NB, int CH = 4>
+__device__ __forceinline__ void load_w_chunk(const uint8_t* const (&wp)[2], uint32_t wstep, int kt0, int kt_end,
+                                             uint2 (&wt)[NB][CH]) {
+#pragma unroll
+  for (int mtx = 0; mtx < NB; ++mtx)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) wt[mtx][c] = *reinterpret_cast<const uint2*>(wp[mtx] + (uint32_t)min(kt0 + c, kt_end - 1) * wstep);
+}
+// Matrix-core work of that chunk with the INT4 codes read from an LDS copy of the rows (alds: this
+// lane's row and 16-byte column offset). FULL chunks run straight through, so the reads issue together.
+template <int NB, bool FULL, int CH = 4>
+__device__ __forceinline__ void mfma_chunk_lds(const uint8_t* alds, const uint2 (&wt)[NB][CH], int kt0, int kt_end,
+                                               v4i (&acc)[NB][2]) {
+  uint4 at[CH];                                 // all reads first (tiles past kt_end repeat the last)
+#pragma unroll
+  for (int c = 0; c < CH; ++c) at[c] = *reinterpret_cast<const uint4*>(alds + (uint32_t)min(kt0 + c, kt_end - 1) * 64u);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if (!FULL && kt0 + c >= kt_end) break;
+    const uint4 a = at[c];
+#pragma unroll
+    for (int mtx = 0; mtx < NB; ++mtx) {
+      acc[mtx][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_a_int4(a.x, a.y), expand_w_i8(wt[mtx][c].x), acc[mtx][0], 0, 0, 0);
+      acc[mtx][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand_a_int4(a.z, a.w), expand_w_i8(wt[mtx][c].y), acc[mtx][1], 0, 0, 0);
+    }
+  }
+}
+
+template <int FMT, int EPI, int NWV>
+constexpr int kGluWaves = (NWV == 8 && EPI == BL_EPI_RELU2_GLU && FMT != BL_ACT_INT8) ? 6 : 1;
+
+template <int FMT, int EPI, int CHN, int NWV, bool ALDS>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(kGluWaves<FMT, EPI, NWV>))) void k_gemv(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
                                                      int M, int K, const uint8_t* __restrict__ W,
                                                      const float* __restrict__ walpha,
                                                      const uint8_t* __restrict__ W2,
@@ -114,7 +167,9 @@ __global__ __launch_bounds__(NWV * 64) void k_gemv(const uint8_t* __restrict__ A
                                                      float* __restrict__ rowmax) {
   constexpr bool A8 = (FMT == BL_ACT_INT8);
   constexpr int NB = (EPI == BL_EPI_RELU2_GLU) ? 2 : 1;
+  static_assert(!ALDS || FMT == BL_ACT_INT4, "LDS-staged codes are INT4 only");
   __shared__ v4i red[NB][NWV - 1][64];
+  __shared__ __attribute__((aligned(16))) uint8_t acodes[ALDS ? ALDS_BYTES : 16];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = blockIdx.x;
@@ -129,6 +184,7 @@ __global__ __launch_bounds__(NWV * 64) void k_gemv(const uint8_t* __restrict__ A
   const uint32_t woff = (uint32_t)G * 512u + (uint32_t)lane * 8u;
   const uint8_t* const wp[2] = {W + woff, (NB > 1 ? W2 : W) + woff};
   const uint32_t wstep = (uint32_t)NG * 512u;
+  if constexpr (ALDS) stage_codes_lds<NWV>(A, (uint32_t)M * arow, acodes, wave, lane);
 
   // what the epilogue reads, fetched by the epilogue wave only, before its weight stream (rows past
   // M repeat row M-1; the other waves only stream weights and hand over partial sums)
@@ -148,9 +204,22 @@ __global__ __launch_bounds__(NWV * 64) void k_gemv(const uint8_t* __restrict__ A
   v4i acc[NB][2];
 #pragma unroll
   for (int mtx = 0; mtx < NB; ++mtx) acc[mtx][0] = acc[mtx][1] = v4i{0, 0, 0, 0};
-  for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CHN) {
-    if (kt0 + CHN <= kt_end) chunk<A8, NB, true, CHN>(arp, wp, wstep, kt0, kt_end, g, acc);
-    else chunk<A8, NB, false, CHN>(arp, wp, wstep, kt0, kt_end, g, acc);
+  if constexpr (ALDS) {
+    // the first chunk's weights are in flight across the barrier that publishes the LDS codes
+    const uint8_t* alds = acodes + (uint32_t)min(r, M - 1) * arow + 16 * g;
+    uint2 wt[NB][CHN];
+    if (kt_begin < kt_end) load_w_chunk<NB, CHN>(wp, wstep, kt_begin, kt_end, wt);
+    __syncthreads();
+    for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CHN) {
+      if (kt0 != kt_begin) load_w_chunk<NB, CHN>(wp, wstep, kt0, kt_end, wt);
+      if (kt0 + CHN <= kt_end) mfma_chunk_lds<NB, true, CHN>(alds, wt, kt0, kt_end, acc);
+      else mfma_chunk_lds<NB, false, CHN>(alds, wt, kt0, kt_end, acc);
+    }
+  } else {
+    for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CHN) {
+      if (kt0 + CHN <= kt_end) chunk<A8, NB, true, CHN>(arp, wp, wstep, kt0, kt_end, g, acc);
+      else chunk<A8, NB, false, CHN>(arp, wp, wstep, kt0, kt_end, g, acc);
+    }
   }
 
   // exact int32 reduction of the K partitions
@@ -198,7 +267,9 @@ __global__ __launch_bounds__(NWV * 64) void k_gemv(const uint8_t* __restrict__ A
 
 template <int FMT, int EPI, int CHN, int NWV>
 hipError_t launch_w(const bl_mm_args& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemv<FMT, EPI, CHN, NWV>), dim3(a.N / 16), dim3(NWV * 64), 0, st,
+  const bool alds = FMT == BL_ACT_INT4 && (long)a.M * (a.K / 2) <= ALDS_BYTES;
+  hipLaunchKernelGGL((alds ? k_gemv<FMT, EPI, CHN, NWV, FMT == BL_ACT_INT4> : k_gemv<FMT, EPI, CHN, NWV, false>),
+                     dim3(a.N / 16), dim3(NWV * 64), 0, st,
                      static_cast<const uint8_t*>(a.A), a.ascale, a.M, a.K, static_cast<const uint8_t*>(a.W),
                      a.walpha, static_cast<const uint8_t*>(a.W2), a.w2alpha, a.N, a.Y, a.ldy, a.R, a.ldr, a.rowmax);
   return hipGetLastError();
@@ -245,24 +316,33 @@ __device__ __forceinline__ int dot_ternary_int4(uint4 w, uint4 a0, uint4 a1, int
   return acc + f - 4 * b;
 }
 
-// Fused form for one block per 16-channel group (the tile row of W_gate): phase 1 is the INT4 decode
-// GEMV of the gate (eight waves split K, exact int32 sum in LDS); the block then knows g for its 16
-// channels and M rows, and in phase 2 each wave takes two channels and, if the gate of a channel is
-// positive in some row, streams its row-major up weights (K/4 bytes; 16 bytes per lane and 64-wide
-// K slice) against the INT4 codes with v_dot8 (dot_ternary_int4 above). Rows of W_up whose channel
-// is dead in every row are never read. One launch, so the up loads of a block overlap the gate loads
-// of others.
-__global__ __launch_bounds__(WAVES * 64) void k_glu_cond_fused(const uint8_t* __restrict__ A,
-                                                               const float* __restrict__ ascale, int M, int K,
-                                                               const uint8_t* __restrict__ Wg,
-                                                               const float* __restrict__ galpha,
-                                                               const uint8_t* __restrict__ Wup,
-                                                               const float* __restrict__ upalpha, int N,
-                                                               float* __restrict__ Gout, long ldg,
-                                                               float* __restrict__ H, long ldh,
-                                                               float* __restrict__ rowmax) {
-  __shared__ v4i red[WAVES - 1][64];
-  __shared__ float gl[8][16];                   // g[row][channel] of the block
+// Sum of an int32 over the 64 lanes of a wave, returned wave-uniform: DPP exchanges inside each row
+// of 16 lanes (xor 1, xor 2, then the half-row and row mirrors), then the four row sums by readlane.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm(1, 0, 3, 2)
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm(2, 3, 0, 1)
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
+}
+
+// Fused form for one block per 16-channel group (the tile row of W_gate). At the start the block
+// copies the M rows of INT4 codes into LDS (direct-to-LDS loads, when they fit), then phase 1 is
+// the INT4 decode GEMV of the gate (eight waves split K, partial int32 tiles in LDS). After one
+// barrier each wave sums the partials of its own two channels (lanes 2 m + q: row m, channel
+// 2 wave + q), writes g, and if the gate of a channel is positive in some row streams that
+// channel's row-major up weights (K/4 bytes; 16 bytes per lane and 64-wide K slice) against the
+// codes in LDS with v_dot8 (dot_ternary_int4 above); the row sums are wave reductions by DPP.
+// Rows of W_up whose channel is dead in every row are never read. One launch, so the up loads of a
+// block overlap the gate loads of others; at most 80 VGPRs keep three blocks per CU resident.
+template <bool ALDS>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(6))) void k_glu_cond_fused(
+    const uint8_t* __restrict__ A, const float* __restrict__ ascale, int M, int K, const uint8_t* __restrict__ Wg,
+    const float* __restrict__ galpha, const uint8_t* __restrict__ Wup, const float* __restrict__ upalpha, int N,
+    float* __restrict__ Gout, long ldg, float* __restrict__ H, long ldh, float* __restrict__ rowmax) {
+  __shared__ v4i red[WAVES][64];
+  __shared__ __attribute__((aligned(16))) uint8_t acodes[ALDS ? ALDS_BYTES : 16];
   __shared__ float hmax[8][16];                 // |h| for the row maxima
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = blockIdx.x;
@@ -271,97 +351,97 @@ __global__ __launch_bounds__(WAVES * 64) void k_glu_cond_fused(const uint8_t* __
   const int kt_begin = wave * per;
   const int kt_end = min(KT, kt_begin + per);
   const int r = lane & 15, g4 = lane >> 4;
-  const long arow = K >> 1;
-  const uint8_t* arp = A + (long)min(r, M - 1) * arow + 16 * g4;
+  const uint32_t arow = (uint32_t)K >> 1;
+  if constexpr (ALDS) stage_codes_lds<WAVES>(A, (uint32_t)M * arow, acodes, wave, lane);
+  const uint8_t* arp = A + (uint32_t)min(r, M - 1) * arow + 16 * g4;
   const uint8_t* const wp[2] = {Wg + (uint32_t)G * 512u + (uint32_t)lane * 8u, Wg + (uint32_t)G * 512u + (uint32_t)lane * 8u};
   const uint32_t wstep = (uint32_t)NG * 512u;
-  float ds[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) ds[v] = ascale[min(4 * g4 + v, M - 1)];
-  const float alpha = *galpha;
+  // lanes 2 m + q < 2 M own (row m, channel 2 wave + q) from the handover on
+  const int om = lane >> 1, oq = lane & 1, och = 2 * wave + oq;
+  const bool owner = lane < 2 * M;
+  const float ods = ascale[min(om, M - 1)];
+  const float alpha = *galpha, ualpha = *upalpha;
 
   // ---- phase 1: gate projection of the block's 16 channels
   v4i acc[1][2];
   acc[0][0] = acc[0][1] = v4i{0, 0, 0, 0};
-  for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CH) {
-    if (kt0 + CH <= kt_end) chunk<false, 1, true>(arp, wp, wstep, kt0, kt_end, g4, acc);
-    else chunk<false, 1, false>(arp, wp, wstep, kt0, kt_end, g4, acc);
-  }
-  acc[0][0] += acc[0][1];
-  if (wave > 0) red[wave - 1][lane] = acc[0][0];
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 0; w < WAVES - 1; ++w) acc[0][0] += red[w][lane];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * g4 + v;
-      const float g = (float)(acc[0][0][v] >> 10) * (ds[v] * alpha);
-      if (m < 8) gl[m][r] = g;
-      if (m < M) Gout[(long)m * ldg + 16 * G + r] = g;
+  if constexpr (ALDS) {
+    // the first chunk's weights are in flight across the barrier that publishes the LDS codes
+    const uint8_t* alds = acodes + (uint32_t)min(r, M - 1) * arow + 16 * g4;
+    uint2 wt[1][CH];
+    if (kt_begin < kt_end) load_w_chunk<1>(wp, wstep, kt_begin, kt_end, wt);
+    __syncthreads();
+    for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CH) {
+      if (kt0 != kt_begin) load_w_chunk<1>(wp, wstep, kt0, kt_end, wt);
+      if (kt0 + CH <= kt_end) mfma_chunk_lds<1, true>(alds, wt, kt0, kt_end, acc);
+      else mfma_chunk_lds<1, false>(alds, wt, kt0, kt_end, acc);
+    }
+  } else {
+    for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CH) {
+      if (kt0 + CH <= kt_end) chunk<false, 1, true>(arp, wp, wstep, kt0, kt_end, g4, acc);
+      else chunk<false, 1, false>(arp, wp, wstep, kt0, kt_end, g4, acc);
     }
   }
+  red[wave][lane] = acc[0][0] + acc[0][1];
   __syncthreads();
 
-  // ---- phase 2: up projection of the live channels (two per wave)
-  const float ualpha = *upalpha;
-  const long wrow = K >> 2;
-  const int KC = K >> 6;
-  const int ch0 = 2 * wave;
-  bool live[2] = {false, false};
-  for (int m = 0; m < M; ++m) {
-    live[0] |= gl[m][ch0] > 0.f;
-    live[1] |= gl[m][ch0 + 1] > 0.f;
+  // ---- handover: g of the wave's two channels, exact int32 sum of the eight partial tiles (the
+  // value of row m, channel c sits in tile lane c + 16 (m / 4), component m % 4)
+  float g = 0.f;
+  if (owner) {
+    const int* rp = reinterpret_cast<const int*>(&red[0][och + 16 * (om >> 2)]) + (om & 3);
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s += rp[w * 64 * 4];
+    g = (float)(s >> 10) * (ods * alpha);
+    Gout[(long)om * ldg + 16 * G + och] = g;
   }
-  int uacc[2][8];
+  const unsigned long long pos = __ballot(owner && g > 0.f);
+  const bool live0 = (pos & 0x5555555555555555ull) != 0ull, live1 = (pos & 0xAAAAAAAAAAAAAAAAull) != 0ull;
+
+  // ---- phase 2: up projection of the live channels
+  int us[2][8];                                 // wave-uniform row sums
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int m = 0; m < 8; ++m) uacc[q][m] = 0;
-  if (live[0] || live[1]) {
-    const uint8_t* wr0 = Wup + (long)(16 * G + ch0) * wrow;
+    for (int m = 0; m < 8; ++m) us[q][m] = 0;
+  if (live0 || live1) {
+    const uint32_t wrow = (uint32_t)K >> 2;
+    const int KC = K >> 6;
+    const uint8_t* wr0 = Wup + (long)(16 * G + 2 * wave) * wrow;
+    int uacc[2][8];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) uacc[q][m] = 0;
     for (int c = lane; c < KC; c += 64) {
       // both weight rows first (only the live ones), then the codes of the M rows
-      uint4 w[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        w[q] = live[q] ? *reinterpret_cast<const uint4*>(wr0 + q * wrow + 16 * c) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 w0 = live0 ? *reinterpret_cast<const uint4*>(wr0 + 16u * c) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 w1 = live1 ? *reinterpret_cast<const uint4*>(wr0 + wrow + 16u * c) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         if (m >= M) break;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(A + (long)m * arow + 32 * c);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(A + (long)m * arow + 32 * c + 16);
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          if (live[q]) uacc[q][m] = dot_ternary_int4(w[q], a0, a1, uacc[q][m]);
+        const uint8_t* ap = (ALDS ? acodes : A) + (uint32_t)m * arow + 32u * c;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16);
+        if (live0) uacc[0][m] = dot_ternary_int4(w0, a0, a1, uacc[0][m]);
+        if (live1) uacc[1][m] = dot_ternary_int4(w1, a0, a1, uacc[1][m]);
       }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (!live[q]) continue;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        if (m >= M) break;
-        int v = uacc[q][m];
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
-        uacc[q][m] = v;
-      }
+    for (int m = 0; m < 8; ++m) {
+      if (m >= M) break;
+      if (live0) us[0][m] = wave_sum_i32(uacc[0][m]);
+      if (live1) us[1][m] = wave_sum_i32(uacc[1][m]);
     }
   }
-  if (lane < 2 * M) {
-    const int q = lane & 1, m = lane >> 1, ch = ch0 + q;
-    int u0 = 0, u1 = 0;
+  if (owner) {
+    int u = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u0 = (i == m) ? uacc[0][i] : u0;
-      u1 = (i == m) ? uacc[1][i] : u1;
-    }
-    const float um = (float)(q ? u1 : u0);
-    const float g = gl[m][ch];
-    const float h = g > 0.f ? (g * g) * (um * (ascale[m] * ualpha)) : 0.f;
-    H[(long)m * ldh + 16 * G + ch] = h;
-    hmax[m][ch] = fabsf(h);
+    for (int m = 0; m < 8; ++m) u = (m == om) ? (oq ? us[1][m] : us[0][m]) : u;
+    const float h = g > 0.f ? (g * g) * ((float)u * (ods * ualpha)) : 0.f;
+    H[(long)om * ldh + 16 * G + och] = h;
+    hmax[om][och] = fabsf(h);
   }
   if (rowmax) {
     __syncthreads();
@@ -383,8 +463,9 @@ hipError_t bl_launch_gemv(const bl_mm_args& a, hipStream_t st) {
 
 hipError_t bl_launch_glu_conditional_fused(const bl_upcond_args& a, const void* Wg, const float* galpha,
                                           hipStream_t st) {
-  hipLaunchKernelGGL(k_glu_cond_fused, dim3(a.N / 16), dim3(WAVES * 64), 0, st, static_cast<const uint8_t*>(a.A),
-                     a.ascale, a.M, a.K, static_cast<const uint8_t*>(Wg), galpha, static_cast<const uint8_t*>(a.Wup),
-                     a.upalpha, a.N, a.G, a.ldg, a.H, a.ldh, a.rowmax);
+  const bool alds = (long)a.M * (a.K / 2) <= ALDS_BYTES;
+  hipLaunchKernelGGL(alds ? k_glu_cond_fused<true> : k_glu_cond_fused<false>, dim3(a.N / 16), dim3(WAVES * 64), 0, st,
+                     static_cast<const uint8_t*>(a.A), a.ascale, a.M, a.K, static_cast<const uint8_t*>(Wg), galpha,
+                     static_cast<const uint8_t*>(a.Wup), a.upalpha, a.N, a.G, a.ldg, a.H, a.ldh, a.rowmax);
   return hipGetLastError();
 }
