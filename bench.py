@@ -583,10 +583,15 @@ def measured_peaks(torch, dev):
     iters = 4000
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     mfma_us = best_us(lambda: tw.bitlinear_calibrate_mfma(blocks, iters, out=out))
+    # thread 0 of every block: shader-clock ticks per 100 MHz real-time tick over its loop
+    clk = out.view(blocks, 256)[:, 0].double()
     return {"hbm_copy_gbs": round(2 * (256 << 20) / (copy_us * 1e-6) / 1e9, 1),
             "mfma_fp6_fp4_tops": round(blocks * iters * 8388608 / (mfma_us * 1e-6) / 1e12, 1),
-            "how": "256 MiB device copy (read + write bytes); FP6 x FP4 MFMA-only loop, "
-                   f"{blocks} blocks x 4 waves x {iters} x 32 MFMAs 16x16x128; best of 3 after a warm-up"}
+            "mfma_clock_ghz": round(float(clk.mean().item()) * 0.1, 3),
+            "how": "256 MiB device copy (read + write bytes); FP6 x FP4 MFMA-only loop on operands with the "
+                   "GEMM's statistics (ternary E2M1 weights, bell-shaped INT4 codes in E3M2, eight weight and four "
+                   f"activation sets alternating), {blocks} blocks x 4 waves x {iters} x 32 MFMAs 16x16x128, best of "
+                   "3 after a warm-up; the clock is the mean shader-clock rate over the blocks' loops"}
 
 
 def host_cpu_model():

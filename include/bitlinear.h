@@ -326,10 +326,15 @@ bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, in
  * bitlinear_calibrate_mfma: a measurement aid, not part of the BitLinear path. Runs a matrix-core-only
  * loop in the shape of the FP6 x FP4 GEMM's K loop (256-thread blocks, two per CU, 32 independent
  * fp32 accumulators per wave, v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales): every block
- * performs iters * 4 waves * 32 MFMAs of 2 * 16 * 16 * 128 ops, i.e. 8388608 * iters ops. Timing
- * it (HIP events) gives the FP6/FP4 rate this GPU sustains, beside the datasheet peak.
+ * performs iters * 4 waves * 32 MFMAs of 2 * 16 * 16 * 128 ops, i.e. 8388608 * iters ops. The
+ * operands have the GEMM's statistics (ternary weights as E2M1 0 / +2 / -2, bell-shaped INT4 codes
+ * in E3M2; eight weight and four activation sets alternate), since the sustained matrix-core rate
+ * depends on the operand bits. Timing it (HIP events) gives the FP6/FP4 rate this GPU sustains on
+ * such data, beside the datasheet peak.
  *   blocks  1 .. 65536 (2 * number of CUs fills the part once);  iters 0 .. 2^20.
- *   d_out   out, blocks * 256 float32 (the accumulator sums; their values carry no meaning).
+ *   d_out   out, blocks * 256 float32: element 256 b holds block b's shader-clock ticks per 100 MHz
+ *           real-time tick over its loop (x 0.1 = the clock in GHz); the other elements carry no
+ *           meaning.
  * Errors: NULL d_out -> INVALID_ARGUMENT; blocks or iters out of range -> UNSUPPORTED_SHAPE.
  * ------------------------------------------------------------------------------------------- */
 bl_status bitlinear_calibrate_mfma(int32_t blocks, int32_t iters, float* d_out, void* stream);

@@ -265,7 +265,9 @@ def bitlinear_calibrate_read(src, sink, nbytes=None, stream=None):
 
 def bitlinear_calibrate_mfma(blocks, iters, out=None, stream=None):
     """Measurement aid (not part of the BitLinear path): FP6 x FP4 matrix-core-only loop of
-    blocks * iters * 8388608 ops in the GEMM's wave shape. Returns the (meaningless) sums buffer."""
+    blocks * iters * 8388608 ops in the GEMM's wave shape, on operands with the GEMM's statistics.
+    Returns the buffer: element 256 b holds block b's shader-clock ticks per 100 MHz real-time tick
+    (x 0.1 = GHz); the other elements carry no meaning."""
     import torch
     if out is None:
         out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")

@@ -3,14 +3,19 @@
     python -m ternary_weight_quantized_amd.profile_run --gemm fp6 --reps 3 --copy-calibration
     python -m ternary_weight_quantized_amd.profile_run --decode --copy-calibration
     python -m ternary_weight_quantized_amd.profile_run --a8 --reps 3
+    python -m ternary_weight_quantized_amd.profile_run --quant --reps 3 --copy-calibration
 
 --gemm quantizes the prefill workload (M=4096, K=4096, N=12288, seeded synthetic bf16 activations and
 latent weights) and launches the selected W1.58A4 GEMM `reps` times. --decode launches, each over 24
 rotating copies of its weights (as the benchmark's graphs do): the INT4 decode GEMV of 1 token
 (11008x4096), the fused gate+up ReLU^2 GLU decode GEMV of 1 token (12 copies of both 11008x4096
-matrices) and the INT8 decode GEMV of one row of the FFN's h codes against the 4096x11008 down
+matrices), the gate-first conditional up projection of the same token (12 copies of the gate and of the
+row-major up matrix) and the INT8 decode GEMV of one row of the FFN's h codes against the 4096x11008 down
 projection. --a8 launches the two W1.58A8 GEMMs of the FFN (down) and attention-output workloads; --kv the
-prefill QKV GEMM with the KV-cache quantizer fused into its epilogue (Q4 RoPE, K3 RoPE + BOS, V3 + BOS).
+prefill QKV GEMM with the KV-cache quantizer fused into its epilogue (Q4 RoPE, K3 RoPE + BOS, V3 + BOS);
+--quant every activation quantizer of the workloads (prefill INT4 nibbles, E3M2, FP4, FP4 power-of-two and
+per-tensor INT4 of the 4096x4096 bf16 input; INT8 of an fp32 2048x11008 h with its row maxima; Top-K INT8
+of the 8192x4096 bf16 attention output) and the three KV quantizers of a 4096 x 3 x 32 x 128 fp32 QKV output.
 With --copy-calibration a 256 MiB device-to-device copy runs first; its FETCH_SIZE and WRITE_SIZE
 readings give the factor that turns those counters into bytes.
 """
@@ -39,10 +44,11 @@ def main():
     p.add_argument("--decode", action="store_true")
     p.add_argument("--a8", action="store_true")
     p.add_argument("--kv", action="store_true", help="the prefill QKV GEMM with the fused KV-cache epilogue")
+    p.add_argument("--quant", action="store_true", help="every activation and KV-cache quantizer of the workloads")
     p.add_argument("--reps", type=int, default=3)
     p.add_argument("--copy-calibration", action="store_true")
     args = p.parse_args()
-    if not (args.gemm or args.decode or args.a8 or args.kv):
+    if not (args.gemm or args.decode or args.a8 or args.kv or args.quant):
         args.gemm = "fp6"
 
     import torch
@@ -98,6 +104,9 @@ def main():
         uW, uA = pack(fin["w_up"])
         dW, dA = pack(fin["w_down"])
         fx = dev_bf16(torch, fin["x"])
+        uWr = None
+        if args.decode:
+            uWr, _ = tw.bitlinear_pack_ternary_rows(torch.from_numpy(fin["w_up"]).cuda(), EPS)
         del fin
         fc, fs, _ = tw.bitlinear_quantize_act(fx, "int4_e3m2", eps=EPS)
         frm = torch.empty(F["M"], dtype=torch.float32, device="cuda")
@@ -112,9 +121,11 @@ def main():
         dWs = [w0] + [w0.clone() for _ in range(23)]
         gWs = [gW] + [gW.clone() for _ in range(11)]
         uWs = [uW] + [uW.clone() for _ in range(11)]
+        uWrs = [uWr] + [uWr.clone() for _ in range(11)]
         d8Ws = [dW] + [dW.clone() for _ in range(23)]
         y1 = torch.empty((1, D["N"]), dtype=torch.float32, device="cuda")
         h1 = torch.empty((1, F["N"]), dtype=torch.float32, device="cuda")
+        g1 = torch.empty((1, F["N"]), dtype=torch.float32, device="cuda")
         y8 = torch.empty((1, F["K"]), dtype=torch.float32, device="cuda")
 
         def decode():
@@ -123,9 +134,12 @@ def main():
             for r in range(12):
                 tw.bitlinear_gemv_decode("int4", dc, ds, D["K"], gWs[r], gA, F["N"], y=h1, up_packed=uWs[r],
                                          up_alpha=uA)
+            for r in range(12):
+                tw.bitlinear_gemv_decode_glu_conditional(dc, ds, D["K"], gWs[r], gA, uWrs[r], uA, F["N"], gate=g1, h=h1)
             for r in range(24):
                 tw.bitlinear_gemv_decode("int8", fhc[:1], fhs[:1], F["N"], d8Ws[r], dA, F["K"], y=y8)
-        work.append(("decode: 24 INT4 GEMV M=1, 12 fused GLU GEMV M=1, 24 INT8 GEMV M=1", decode))
+        work.append(("decode: 24 INT4 GEMV M=1, 12 fused GLU GEMV M=1, 12 conditional GLU M=1, 24 INT8 GEMV M=1",
+                     decode))
     if args.a8:
         A = WORKLOADS["attn_out"]
         ain = workload_inputs("attn_out")
@@ -142,6 +156,43 @@ def main():
                 tw.bitlinear_gemm_w158a8_sparse(fhc, fhs, F["N"], dW, dA, F["K"], y=fy)
                 tw.bitlinear_gemm_w158a8_sparse(ac, as_, A["K"], oW, oA, A["N"], y=ay, residual=ar)
         work.append((f"{args.reps} x (A8 down 2048x11008x4096, A8 o_proj+residual 8192x4096x4096)", a8))
+    if args.quant:
+        import numpy as np
+        from synth import rope_tables
+        P = WORKLOADS["prefill_qkv"]
+        px = dev_bf16(torch, workload_inputs("prefill_qkv")["x"])
+        Fq = WORKLOADS["ffn_7b"]
+        # the FFN's h [2048, 11008] as float32, with its row maxima: any fp32 rows of that shape load the same bytes
+        qh = torch.from_numpy(np.random.default_rng(5).standard_normal((Fq["M"], Fq["N"]), dtype=np.float32)).cuda()
+        qrm = qh.abs().amax(dim=1).contiguous()
+        A = WORKLOADS["attn_out"]
+        qax = dev_bf16(torch, workload_inputs("attn_out")["x"])
+        KV = WORKLOADS["kv_cache"]
+        kT, kH, kD = KV["T"], KV["H"], KV["D"]
+        # the QKV projection output [4096, 3 * 32 * 128] in float32 (any values: the kernels read all of it)
+        qkv = torch.from_numpy(np.random.default_rng(6).standard_normal((kT, 3 * kH * kD), dtype=np.float32)).cuda()
+        kpos_np = (np.arange(kT) % KV["seq_len"]).astype(np.int32)
+        kpos = torch.from_numpy(kpos_np).cuda()
+        kbos = kpos_np == 0
+        kslot = torch.from_numpy(np.where(kbos, np.cumsum(kbos) - 1, -1).astype(np.int32)).cuda()
+        c_np, s_np = rope_tables(KV["seq_len"], kD)
+        kcos, ksin = torch.from_numpy(c_np).cuda(), torch.from_numpy(s_np).cuda()
+        pws = torch.empty(tw.bitlinear_quantize_per_tensor_workspace_bytes(P["M"]), dtype=torch.uint8, device="cuda")
+
+        def quant():
+            for _ in range(args.reps):
+                for fmt in ("int4", "int4_e3m2", "fp4", "fp4_pow2"):
+                    tw.bitlinear_quantize_act(px, fmt, eps=EPS)
+                tw.bitlinear_quantize_act_per_tensor(px, "int4", eps=EPS, workspace=pws)
+                tw.bitlinear_quantize_act(qh, "int8", eps=EPS, row_absmax_hint=qrm)
+                tw.bitlinear_quantize_act(qax, "int8", topk_keep=A["keep"], eps=EPS)
+                tw.bitlinear_kv_quantize(qkv[:, :kH * kD], kH, kD, 4, eps=EPS, pos=kpos, cos=kcos, sin=ksin)
+                tw.bitlinear_kv_quantize(qkv[:, kH * kD:2 * kH * kD], kH, kD, 3, eps=EPS, pos=kpos, cos=kcos, sin=ksin,
+                                         bos_slot=kslot, n_bos_slots=int(kbos.sum()))
+                tw.bitlinear_kv_quantize(qkv[:, 2 * kH * kD:], kH, kD, 3, eps=EPS, bos_slot=kslot,
+                                         n_bos_slots=int(kbos.sum()))
+        work.append((f"{args.reps} x every quantizer (prefill INT4/E3M2/FP4/FP4 pow2/per-tensor, INT8 h, Top-K INT8, "
+                     "KV Q4/K3/V3)", quant))
     torch.cuda.synchronize()
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
