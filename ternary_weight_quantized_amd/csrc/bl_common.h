@@ -20,26 +20,53 @@ __device__ __forceinline__ float bl_bf16lo(uint32_t w) { return __uint_as_float(
 __device__ __forceinline__ float bl_bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ------------------------------------------------------------------ wave reductions (wave64)
+// DPP exchanges inside each row of 16 lanes (xor 1, xor 2, the half-row mirror
+// i <-> 7 - i of each 8 lanes, the row mirror i <-> 15 - i) leave every lane of a row holding the
+// row's result after four steps; readlane of lanes 0, 16, 32 and 48 then combines the four rows, so
+// the result is wave-uniform. Callers run with every lane of the wave active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t bl_dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t bl_wave_reduce_u(uint32_t v, Op op) {
+  v = op(v, bl_dpp<0xB1>(v));      // quad_perm(1, 0, 3, 2)
+  v = op(v, bl_dpp<0x4E>(v));      // quad_perm(2, 3, 0, 1)
+  v = op(v, bl_dpp<0x141>(v));     // row_half_mirror
+  v = op(v, bl_dpp<0x140>(v));     // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
 __device__ __forceinline__ float bl_wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return bl_u2f(bl_wave_reduce_u(bl_f2u(v), [](uint32_t a, uint32_t b) { return bl_f2u(fmaxf(bl_u2f(a), bl_u2f(b))); }));
 }
 __device__ __forceinline__ uint32_t bl_wave_max_u(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) { uint32_t t = __shfl_xor(v, o, 64); v = t > v ? t : v; }
-  return v;
+  return bl_wave_reduce_u(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ uint32_t bl_wave_min_u(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) { uint32_t t = __shfl_xor(v, o, 64); v = t < v ? t : v; }
-  return v;
+  return bl_wave_reduce_u(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
-// Sum of doubles; exact whenever every partial sum is representable (the callers check this).
+template <int CTRL>
+__device__ __forceinline__ double bl_dpp_d(double v) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const uint32_t lo = bl_dpp<CTRL>((uint32_t)u), hi = bl_dpp<CTRL>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ double bl_readlane_d(double v, int l) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+// Sum of doubles; exact whenever every partial sum is representable (the callers check this), so
+// the order of the additions does not matter.
 __device__ __forceinline__ double bl_wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += bl_dpp_d<0xB1>(v);
+  v += bl_dpp_d<0x4E>(v);
+  v += bl_dpp_d<0x141>(v);
+  v += bl_dpp_d<0x140>(v);
+  return (bl_readlane_d(v, 0) + bl_readlane_d(v, 16)) + (bl_readlane_d(v, 32) + bl_readlane_d(v, 48));
 }
 
 // ------------------------------------------------------------------ exact sums of |binary32| values

@@ -66,12 +66,9 @@ __device__ __forceinline__ uint32_t exps_emin(uint32_t p) { return 255u - (p & 0
 // packed (emax, 255 - emin) maximum over the wave: both halves at once
 __device__ __forceinline__ uint32_t wave_max_exps(uint32_t p) {
   typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t q = __shfl_xor(p, o, 64);
-    p = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, p), __builtin_bit_cast(us2, q)));
-  }
-  return p;
+  return bl_wave_reduce_u(p, [](uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b)));
+  });
 }
 
 // Exact-bins fallback for one wave: called only when the double sum might have rounded.
