@@ -146,7 +146,7 @@ bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, i
  *   tensor. scale[m] holds the same value for every row, so the matmuls take these codes unchanged.
  * Arguments as for bitlinear_quantize_act, plus d_workspace of at least
  * bitlinear_quantize_per_tensor_workspace_bytes(M) bytes (16-byte aligned; contents on entry do not
- * matter, the call overwrites it).
+ * matter, the call overwrites it); that query returns 0 for M <= 0 and SIZE_MAX for M >= 2^31.
  * ------------------------------------------------------------------------------------------- */
 size_t bitlinear_quantize_per_tensor_workspace_bytes(int64_t M);
 bl_status bitlinear_quantize_act_per_tensor(const void* d_x, int32_t in_dtype, int64_t M, int64_t K, int64_t ldx,
@@ -185,6 +185,8 @@ bl_status bitlinear_quantize_act_per_tensor_noalloc(const void* d_x, int32_t in_
  *   d_alpha      output, one float32 on the device.
  *   d_workspace  scratch of at least bitlinear_pack_workspace_bytes() bytes, 16-byte aligned; its
  *                contents on entry do not matter (the call clears what it uses).
+ * bitlinear_packed_bytes returns 0 for N or K <= 0 and SIZE_MAX when N * K is beyond every accepted
+ * shape (2^31 elements).
  * ------------------------------------------------------------------------------------------- */
 size_t bitlinear_packed_bytes(int64_t N, int64_t K);
 size_t bitlinear_pack_workspace_bytes(void);

@@ -16,6 +16,8 @@ constexpr int64_t kMaxElems = (int64_t)1 << 31;
 // (|c| <= 8, |t| <= 1), so K * 8 * 1024 must stay below 2^31; the INT8 path (64 * 127 per term) and
 // the fp32 sums of the FP6 / FP4 paths (exact below 2^24) have more room.
 constexpr int64_t kMaxMatmulK = ((int64_t)1 << 18) - 128;
+// a * b < kMaxElems for non-negative a and b, decided without forming a product that can overflow
+bool fits(int64_t a, int64_t b) { return a >= 0 && b >= 0 && (a == 0 || b <= (kMaxElems - 1) / a); }
 
 bl_status hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
@@ -28,15 +30,15 @@ bl_status check_mm(int32_t fmt, const void* codes, const float* scale, int64_t M
     return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1 || N < 1) return BL_ERR_UNSUPPORTED_SHAPE;
   if (K % 128 != 0 || N % 16 != 0 || K > kMaxMatmulK) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (!fits(M, K) || !fits(N, K) || !fits(M, N)) return BL_ERR_UNSUPPORTED_SHAPE;
   if (y && ldy < N) return BL_ERR_INVALID_ARGUMENT;
   if (!aligned16(codes) || !aligned16(packed)) return BL_ERR_MISALIGNED;
-  if (y && (!aligned16(y) || (ldy * 4) % 16 != 0)) return BL_ERR_MISALIGNED;
+  if (y && (!aligned16(y) || ldy % 4 != 0)) return BL_ERR_MISALIGNED;              // ldy * 4 bytes, a multiple of 16
   if (epi) {
     if (epi->kind == BL_EPI_RESIDUAL) {
       if (!epi->d_residual) return BL_ERR_INVALID_ARGUMENT;
       if (epi->ldr < N) return BL_ERR_INVALID_ARGUMENT;
-      if (!aligned16(epi->d_residual) || (epi->ldr * 4) % 16 != 0) return BL_ERR_MISALIGNED;
+      if (!aligned16(epi->d_residual) || epi->ldr % 4 != 0) return BL_ERR_MISALIGNED;
     } else if (epi->kind == BL_EPI_RELU2_GLU) {
       if (!epi->d_up_packed || !epi->d_up_alpha) return BL_ERR_INVALID_ARGUMENT;
       if (!aligned16(epi->d_up_packed)) return BL_ERR_MISALIGNED;
@@ -79,6 +81,7 @@ const char* bitlinear_status_string(int32_t s) {
 
 size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0) return 0;
+  if (!fits(N, K)) return SIZE_MAX;               // beyond every accepted shape
   return (size_t)(N * K / 4);
 }
 
@@ -115,12 +118,12 @@ bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, i
   if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1) return BL_ERR_UNSUPPORTED_SHAPE;
   if (K % 128 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (M * K >= kMaxElems || M * ldx >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ldx < K) return BL_ERR_INVALID_ARGUMENT;
+  if (!fits(M, K) || !fits(M, ldx)) return BL_ERR_UNSUPPORTED_SHAPE;
   if (fmt != BL_ACT_INT8 && (topk_keep >= 0 || d_mask)) return BL_ERR_INVALID_ARGUMENT;
   if (topk_keep > K) return BL_ERR_INVALID_ARGUMENT;
   const int64_t esz = in_dtype == BL_IN_F32 ? 4 : 2;
-  if (!aligned16(d_x) || !aligned16(d_codes) || (ldx * esz) % 16 != 0) return BL_ERR_MISALIGNED;
+  if (!aligned16(d_x) || !aligned16(d_codes) || ldx % (16 / esz) != 0) return BL_ERR_MISALIGNED;
   if (d_mask && !aligned16(d_mask)) return BL_ERR_MISALIGNED;
   const float* hint = (fmt == BL_ACT_INT4 || fmt == BL_ACT_INT4_E3M2) ? nullptr : d_row_absmax_hint;
   return hip_status(bl_launch_quantize(d_x, in_dtype == BL_IN_F32, (int)M, (int)K, (long)ldx, fmt, (int)topk_keep,
@@ -129,6 +132,7 @@ bl_status bitlinear_quantize_act(const void* d_x, int32_t in_dtype, int64_t M, i
 
 size_t bitlinear_quantize_per_tensor_workspace_bytes(int64_t M) {
   if (M <= 0) return 0;
+  if (M >= kMaxElems) return SIZE_MAX;            // beyond every accepted shape
   return bl_quantize_per_tensor_ws_bytes((long)M);
 }
 
@@ -147,10 +151,10 @@ bl_status check_per_tensor(const void* d_x, int32_t in_dtype, int64_t M, int64_t
   if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
   if (M < 1 || K < 1) return BL_ERR_UNSUPPORTED_SHAPE;
   if (K % 128 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (M * K >= kMaxElems || M * ldx >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ldx < K) return BL_ERR_INVALID_ARGUMENT;
+  if (!fits(M, K) || !fits(M, ldx)) return BL_ERR_UNSUPPORTED_SHAPE;
   const int64_t esz = in_dtype == BL_IN_F32 ? 4 : 2;
-  if (!aligned16(d_x) || !aligned16(d_codes) || (ldx * esz) % 16 != 0) return BL_ERR_MISALIGNED;
+  if (!aligned16(d_x) || !aligned16(d_codes) || ldx % (16 / esz) != 0) return BL_ERR_MISALIGNED;
   return BL_OK;
 }
 
@@ -218,7 +222,7 @@ bl_status bitlinear_pack_ternary(const float* d_w, int64_t N, int64_t K, float e
   if (!d_w || !d_packed || !d_alpha || !d_workspace) return BL_ERR_INVALID_ARGUMENT;
   if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
   if (N < 1 || K < 1 || K % 128 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (N * K >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (!fits(N, K)) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ws_bytes < bitlinear_pack_workspace_bytes()) return BL_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(d_w) || !aligned16(d_packed) || !aligned16(d_workspace)) return BL_ERR_MISALIGNED;
   return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace, false,
@@ -230,7 +234,7 @@ bl_status bitlinear_pack_ternary_rows(const float* d_w, int64_t N, int64_t K, fl
   if (!d_w || !d_packed || !d_alpha || !d_workspace) return BL_ERR_INVALID_ARGUMENT;
   if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
   if (N < 1 || K < 1 || K % 128 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (N * K >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (!fits(N, K)) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ws_bytes < bitlinear_pack_workspace_bytes()) return BL_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(d_w) || !aligned16(d_packed) || !aligned16(d_workspace)) return BL_ERR_MISALIGNED;
   return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace, true,
@@ -287,7 +291,7 @@ bl_status bitlinear_gemv_decode_glu_conditional(const void* d_codes, const float
   if (!d_up_rows || !d_up_alpha || !d_h) return BL_ERR_INVALID_ARGUMENT;
   if (ldh < N) return BL_ERR_INVALID_ARGUMENT;
   if (M > 8) return BL_ERR_UNSUPPORTED_SHAPE;
-  if (!aligned16(d_up_rows) || !aligned16(d_h) || (ldh * 4) % 16 != 0) return BL_ERR_MISALIGNED;
+  if (!aligned16(d_up_rows) || !aligned16(d_h) || ldh % 4 != 0) return BL_ERR_MISALIGNED;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (d_row_absmax) {
     const hipError_t e = bl_launch_fill_zero(d_row_absmax, (long)M, st);
@@ -309,7 +313,7 @@ bl_status bitlinear_gemm_w158a4_kv(int32_t fmt, const void* d_codes, const float
   const bl_status s = check_mm(fmt, d_codes, d_scale, M, K, d_packed, d_alpha, N, d_y, ldy, nullptr, true);
   if (s != BL_OK) return s;
   const bl_kv_epilogue& k = *h_kv;
-  if (k.H < 1 || N != 3 * k.H * 128) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (k.H < 1 || k.H > N / 384 || N != 3 * k.H * 128) return BL_ERR_UNSUPPORTED_SHAPE;
   if (!eps_ok(k.eps)) return BL_ERR_INVALID_ARGUMENT;
   bool any3 = false;
   for (int p = 0; p < 3; ++p) {
@@ -321,10 +325,10 @@ bl_status bitlinear_gemm_w158a4_kv(int32_t fmt, const void* d_codes, const float
   if ((k.d_cos == nullptr) != (k.d_sin == nullptr)) return BL_ERR_INVALID_ARGUMENT;
   if (k.d_cos && (!k.d_pos || k.P < 1)) return BL_ERR_INVALID_ARGUMENT;
   if (k.d_cos && (!aligned16(k.d_cos) || !aligned16(k.d_sin))) return BL_ERR_MISALIGNED;
-  if (k.d_cos && k.P * 128 >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (k.d_cos && !fits(k.P, 128)) return BL_ERR_UNSUPPORTED_SHAPE;
   if (k.d_bos_slot) {
     if (!any3 || k.n_bos_slots < 1) return BL_ERR_INVALID_ARGUMENT;
-    if (k.n_bos_slots * k.H * 128 >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
+    if (!fits(k.n_bos_slots, k.H * 128)) return BL_ERR_UNSUPPORTED_SHAPE;
     for (int p = 0; p < 3; ++p) {
       if (k.bits[p] != 3) continue;
       if (!k.d_bos_codes[p] || !k.d_bos_scale[p]) return BL_ERR_INVALID_ARGUMENT;
@@ -359,13 +363,13 @@ bl_status bitlinear_kv_quantize(const void* d_x, int32_t in_dtype, int64_t T, in
   if ((d_cos == nullptr) != (d_sin == nullptr)) return BL_ERR_INVALID_ARGUMENT;
   if (d_cos && (!d_pos || P < 1)) return BL_ERR_INVALID_ARGUMENT;
   if (d_bos_slot && (bits != 3 || !d_bos_codes || !d_bos_scale || n_bos_slots < 1)) return BL_ERR_INVALID_ARGUMENT;
-  if (T < 0 || H < 1) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (T < 0 || H < 1 || H >= kMaxElems) return BL_ERR_UNSUPPORTED_SHAPE;
   if (D != 64 && D != 128 && D != 256) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ldx < H * D) return BL_ERR_INVALID_ARGUMENT;
-  if (T * ldx >= kMaxElems || T * H * D >= kMaxElems || P * D >= kMaxElems || n_bos_slots * H * D >= kMaxElems)
+  if (!fits(T, ldx) || !fits(T, H * D) || (d_cos && !fits(P, D)) || (d_bos_slot && !fits(n_bos_slots, H * D)))
     return BL_ERR_UNSUPPORTED_SHAPE;
   const int64_t esz = in_dtype == BL_IN_F32 ? 4 : 2;
-  if (!aligned16(d_x) || (ldx * esz) % 16 != 0 || !aligned16(d_codes)) return BL_ERR_MISALIGNED;
+  if (!aligned16(d_x) || ldx % (16 / esz) != 0 || !aligned16(d_codes)) return BL_ERR_MISALIGNED;
   if (d_cos && (!aligned16(d_cos) || !aligned16(d_sin))) return BL_ERR_MISALIGNED;
   if (d_bos_slot && !aligned16(d_bos_codes)) return BL_ERR_MISALIGNED;
   bl_kv_args a{};
