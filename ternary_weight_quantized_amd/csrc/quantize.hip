@@ -535,9 +535,12 @@ __global__ __launch_bounds__(256) void k_quant_blk(const void* __restrict__ x, i
                                                    const float* __restrict__ hint, uint8_t* __restrict__ codes,
                                                    float* __restrict__ scale) {
   constexpr bool SUM = (FMT == BL_ACT_INT4 || FMT == BL_ACT_INT4_E3M2);
+  constexpr bool E3M2 = (FMT == BL_ACT_INT4_E3M2);
   __shared__ double wsum[4];
   __shared__ uint32_t wa[4], wb[4];
   __shared__ unsigned long long bins[SUM ? 256 : 1];
+  // E3M2: the row's 6-bit codes (3K/4 bytes, K <= 256 NCH) gathered before the tiled stores
+  __shared__ __attribute__((aligned(16))) uint8_t erow[E3M2 ? 256 * NCH * 6 : 16];
   __shared__ unsigned long long limbs[12];
   __shared__ double total;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -615,25 +618,32 @@ __global__ __launch_bounds__(256) void k_quant_blk(const void* __restrict__ x, i
         for (int j = 0; j < 8; ++j) w |= code_int4(v[c][j], s) << (4 * j);
         reinterpret_cast<uint32_t*>(codes + (long)row * (K >> 1))[ch] = w;
       } else {
-        // 8 codes x 6 bits; a thread pair (chunks 2i, 2i+1 of a 128-code group) writes 12 bytes
+        // 8 codes x 6 bits = 6 bytes at byte 6 ch of the LDS row (code k at bits 6 k)
         uint32_t e[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) e[j] = code_e3m2(v[c][j], s);
-        // the 48 bits (code j at bits 6 j) as two words
         const uint32_t lo = e[0] | (e[1] << 6) | (e[2] << 12) | (e[3] << 18) | (e[4] << 24) | (e[5] << 30);
         const uint32_t hi = (e[5] >> 2) | (e[6] << 4) | (e[7] << 10);
-        const uint32_t plo = __shfl_xor(lo, 1, 64);
-        const int k = 8 * ch;
-        const long tile = (long)(row >> 4) * (K >> 7) + (k >> 7);
-        uint8_t* base = codes + tile * 1536 + (row & 15) * 96 + 6 * ((k & 127) >> 3);
+        uint8_t* d = erow + 6 * ch;
         if ((ch & 1) == 0) {
-          uint32_t* d = reinterpret_cast<uint32_t*>(base);
-          d[0] = lo;
-          d[1] = (hi & 0xFFFFu) | (plo << 16);
+          *reinterpret_cast<uint32_t*>(d) = lo;
+          *reinterpret_cast<uint16_t*>(d + 4) = (uint16_t)hi;
         } else {
-          // own chunk starts 6 bytes into the pair: bytes 8..11 of the pair = own bits 16..47
-          *reinterpret_cast<uint32_t*>(base + 2) = (lo >> 16) | (hi << 16);
+          *reinterpret_cast<uint16_t*>(d) = (uint16_t)lo;
+          *reinterpret_cast<uint32_t*>(d + 2) = (lo >> 16) | (hi << 16);
         }
+      }
+    }
+    if constexpr (E3M2) {
+      // 16-byte pieces of the row to the tiles: piece p holds bytes 16 p .. 16 p + 15 of the row, inside
+      // the 96-byte row piece of K tile 16 p / 96 (16-row x 128-code tiles of 1536 bytes)
+      __syncthreads();
+      const int npc = (3 * K) >> 6;
+      const long tile0 = (long)(row >> 4) * (K >> 7);
+      for (int pc = t; pc < npc; pc += 256) {
+        const int kt = pc / 6, off = 16 * (pc - 6 * kt);
+        *reinterpret_cast<uint4*>(codes + (tile0 + kt) * 1536 + (row & 15) * 96 + off) =
+            *reinterpret_cast<const uint4*>(erow + 16 * pc);
       }
     }
     if (t == 0) scale[row] = beta / bl_u2f(BL_SQRT7_BITS);
