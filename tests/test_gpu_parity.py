@@ -125,6 +125,33 @@ def test_quantize_fp4_pow2(M, K, f32):
     np.testing.assert_array_equal(host(scale), d)
 
 
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("M,K", [(2049, 640), (2100, 8192)])
+def test_quantize_many_rows(M, K, f32):
+    """More rows than the part holds blocks at once (two rounds of blocks), at an odd multiple of 128
+    and at 8192: every plain format (INT4 nibbles and E3M2 tiles, FP4, FP4 power of two, INT8 with
+    and without the row-max hint) bit-exact over the whole tensor, special rows included."""
+    torch_cuda()
+    x = make_x(4500 + M + K, M, K, f32)
+    xf = x_f32(x)
+    c, d, _ = O.quant_int4(xf, EPS)
+    for fmt in ("int4", "int4_e3m2"):
+        codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), fmt, eps=EPS)
+        got = int4_values(host(codes)) if fmt == "int4" else e3m2_values(host(codes), M)
+        np.testing.assert_array_equal(got, c)
+        np.testing.assert_array_equal(host(scale), d)
+    for pow2 in (False, True):
+        codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), "fp4_pow2" if pow2 else "fp4", eps=EPS)
+        nib, _, d4, _ = O.quant_fp4(xf, EPS, pow2=pow2)
+        np.testing.assert_array_equal(nibbles(host(codes)), nib)
+        np.testing.assert_array_equal(host(scale), d4)
+    c8, _, d8, g8 = O.quant_int8(xf, EPS)
+    for hint in (None, dev_f32(g8)):
+        codes, scale, _ = tw.bitlinear_quantize_act(to_dev(x), "int8", eps=EPS, row_absmax_hint=hint)
+        np.testing.assert_array_equal(int8_values(host(codes)), c8)
+        np.testing.assert_array_equal(host(scale), d8)
+
+
 FP4_TIES = [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6), (6.0, 7)]
 
 
@@ -437,12 +464,12 @@ def test_decode_matches_gemm():
 
 # ----------------------------------------------------------------------------- conditional up projection
 @pytest.mark.parametrize("M", [1, 3, 8])
-@pytest.mark.parametrize("N,K", [(16, 256), (48, 384), (48, 768), (80, 4352), (1024, 4096), (32, 8320)])
+@pytest.mark.parametrize("N,K", [(16, 256), (48, 384), (48, 768), (80, 4352), (1024, 4096), (32, 8192), (32, 8320)])
 def test_glu_conditional(M, N, K):
     """Gate first, up only where the gate is positive: gate, h (bit patterns, +0 where g <= 0) and
     the row maxima equal the oracle's; h equals the fused GLU decode as numbers. K = 8320 with
-    M = 8 has more code bytes (33280) than the kernel stages in LDS and takes the global-load path;
-    M = 3 runs without the row maxima."""
+    M = 8 has more code bytes (33280) than the kernel stages in LDS and takes the global-load path,
+    K = 8192 with M = 8 exactly fills the 32 KiB stage; M = 3 runs without the row maxima."""
     torch = torch_cuda()
     x = make_x(7000 + M + K, M, K, special=False)
     wg = latent_weights(7100 + N, N, K)
