@@ -370,6 +370,35 @@ def test_gemm_a8_sparse(M, N, K, keep_frac):
     assert_y_close(host(y), O.gemm_int(c, t), d, alpha)
 
 
+@pytest.mark.parametrize("M,N,K,epi", [(130, 80, 1280, "none"), (300, 528, 768, "residual"), (64, 272, 2048, "relu2")])
+def test_gemm_a8_structured_zero_slices(M, N, K, epi):
+    """A seeded half of the 16-row x 128-column code slices set to zero (the structured-sparsity input
+    of the benchmark, at small sizes): in some K steps the first subtile of a 64-row wave strip is
+    zero while later ones are live, in others every subtile of a strip is zero; all epilogues."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(5600 + M + K)
+    x = x_f32(make_x(5600 + M, M, K, f32=True, special=False))
+    dead = rng.random(((M + 15) // 16, K // 128)) < 0.5
+    dead[0, 0], dead[1, 0], dead[2, 0], dead[3, 0] = True, False, True, False   # strip 0, step 0
+    x[np.repeat(np.repeat(dead, 16, 0), 128, 1)[:M]] = 0.0
+    _, t, alpha, packed, a = packed_weights(5700 + N, N, K)
+    codes, scale, c, d, _ = _quant(x, "int8", -1)
+    acc = O.gemm_int(c, t)
+    if epi == "none":
+        y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N)
+        assert_y_close(host(y), acc, d, alpha)
+    elif epi == "residual":
+        r = normal(5800, M * N).reshape(M, N).astype(np.float32)
+        y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, residual=dev_f32(r))
+        assert_y_close(host(y), acc, d, alpha, residual=r)
+    else:
+        _, tu, au, pu, dau = packed_weights(5900 + N, N, K)
+        h = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, up_packed=pu, up_alpha=dau)
+        h_ref = O.relu2_glu(O.dequant_f32(acc, d, alpha), O.dequant_f32(O.gemm_int(c, tu), d, au))
+        np.testing.assert_array_equal(host(h).view(np.uint32), h_ref.view(np.uint32))
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("M,N,K", [(200, 272, 512), (33, 64, 11008)])
 def test_gemm_a8_residual_and_relu2(M, N, K):
     torch = torch_cuda()
