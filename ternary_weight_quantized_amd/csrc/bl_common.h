@@ -47,6 +47,19 @@ __device__ __forceinline__ uint32_t bl_wave_max_u(uint32_t v) {
 __device__ __forceinline__ uint32_t bl_wave_min_u(uint32_t v) {
   return bl_wave_reduce_u(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
+// Inclusive prefix sum of an int over the 64 lanes of a wave: shifts right by 1, 2, 4 and 8 lanes
+// inside each row of 16 (a lane with no source adds 0), then the totals of the earlier rows (lanes
+// 15, 31, 47) read through readlane. Every lane of the wave must be active.
+__device__ __forceinline__ int bl_wave_incl_scan(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
 template <int CTRL>
 __device__ __forceinline__ double bl_dpp_d(double v) {
   const unsigned long long u = __builtin_bit_cast(unsigned long long, v);

@@ -320,15 +320,11 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
 constexpr int TK_COPIES = 16, TK_STRIDE = 264;     // 256 bins + 8 pad words per copy
 constexpr int TK_GROUP = 4 * TK_STRIDE;            // words per group of four interleaved copies
 
-// Inclusive scan of one int per thread over the 256-thread block; returns (inclusive, total).
+// Inclusive scan of one int per thread over the 256-thread block; returns (inclusive, total). The
+// caller places a barrier between this scan's reads of wtot and the next write of the same array.
 __device__ __forceinline__ int2 tk_block_scan(int v, int* wtot, int t) {
   const int lane = t & 63, wave = t >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
+  const int incl = bl_wave_incl_scan(v, lane);
   if (lane == 63) wtot[wave] = incl;
   __syncthreads();
   int off = 0, tot = 0;
@@ -337,7 +333,6 @@ __device__ __forceinline__ int2 tk_block_scan(int v, int* wtot, int t) {
     off += w < wave ? wtot[w] : 0;
     tot += wtot[w];
   }
-  __syncthreads();                                   // wtot may be reused by the next scan
   return make_int2(incl + off, tot);
 }
 
@@ -359,6 +354,13 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
   for (int c = 0; c < NCH; ++c)
     if (t + 256 * c < nch) w[c] = *reinterpret_cast<const uint4*>(x + (long)row * ldx + 8 * (t + 256 * c));
     else w[c] = make_uint4(0u, 0u, 0u, 0u);
+  const bool all = keep < 0 || keep >= K;
+  const bool search = !all && keep > 0;            // block-uniform
+  uint4* hist4 = reinterpret_cast<uint4*>(hist);
+  // the histogram is cleared while the row loads are in flight; the barrier of the row maximum (or
+  // the one below, with a given maximum) orders the clear before the first atomic
+  if (search)
+    for (int i = t; i < TK_COPIES * TK_STRIDE / 4; i += 256) hist4[i] = make_uint4(0u, 0u, 0u, 0u);
   auto key = [&](int c, int j) -> uint32_t {
     const uint32_t d = j < 2 ? w[c].x : j < 4 ? w[c].y : j < 6 ? w[c].z : w[c].w;
     return ((j & 1) ? (d >> 16) : d) & 0x7FFFu;
@@ -371,6 +373,7 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
   float gamma;
   if (hint) {
     gamma = hint[row];
+    if (search) __syncthreads();
   } else {
     uint32_t mx = 0u;
 #pragma unroll
@@ -383,15 +386,11 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
     gamma = bl_u2f(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])) << 16);
   }
   const float s = 127.0f / (gamma + eps);
-  const bool all = keep < 0 || keep >= K;
 
   uint32_t T = all ? 0u : 0x8000u;                 // 0x8000: above every key (keep == 0)
   int need = 0;
-  if (!all && keep > 0) {                          // block-uniform
+  if (search) {
     uint32_t* hc = hist + ((t & (TK_COPIES - 1)) >> 2) * TK_GROUP + (t & 3);   // bin b at hc[4 b]
-    uint4* hist4 = reinterpret_cast<uint4*>(hist);
-    for (int i = t; i < TK_COPIES * TK_STRIDE / 4; i += 256) hist4[i] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
     // total of bin b over the 16 copies: four 16-byte reads
     auto bin_total = [&](int b) -> int {
       int n = 0;
@@ -442,7 +441,7 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
   int rank[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) rank[c] = 0;
-  if (!all && keep > 0) {
+  if (search) {
     int tc[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -455,12 +454,7 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
     int incl[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      incl[c] = tc[c];
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl[c], d, 64);
-        if (lane >= d) incl[c] += o;
-      }
+      incl[c] = bl_wave_incl_scan(tc[c], lane);
       if (lane == 63) wtot_v[c][wave] = incl[c];
     }
     __syncthreads();
@@ -501,10 +495,10 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
     const uint32_t lo = __builtin_amdgcn_perm(rr[1], rr[0], 0x0C0C0400u) | __builtin_amdgcn_perm(rr[3], rr[2], 0x04000C0Cu);
     const uint32_t hi = __builtin_amdgcn_perm(rr[5], rr[4], 0x0C0C0400u) | __builtin_amdgcn_perm(rr[7], rr[6], 0x04000C0Cu);
     reinterpret_cast<uint2*>(codes + (long)row * K)[ch] = make_uint2(lo, hi);
-    if (mrow) {
+    if (mrow) {                                    // the four threads of a quad share one word
       uint32_t mw = kb << (8 * (t & 3));
-      mw |= __shfl_xor(mw, 1, 64);
-      mw |= __shfl_xor(mw, 2, 64);
+      mw |= bl_dpp<0xB1>(mw);                      // quad_perm(1, 0, 3, 2)
+      mw |= bl_dpp<0x4E>(mw);                      // quad_perm(2, 3, 0, 1)
       if ((t & 3) == 0) mrow[ch >> 2] = mw;
     }
   }

@@ -267,6 +267,21 @@ def test_quantize_int8_topk(M, K, f32, keep_frac):
     np.testing.assert_array_equal(host(scale), d)
 
 
+@pytest.mark.parametrize("M,K", [(5, 768), (33, 4096), (6, 8192)])
+def test_quantize_int8_topk_with_hint(M, K):
+    """Top-K of bf16 rows with the row maximum given: the same codes, mask and scales as the oracle
+    (the threshold search runs without the block's own max reduction)."""
+    torch_cuda()
+    x = make_x(3500 + M + K, M, K, False)
+    keep = K // 2
+    c, m, d, g = O.quant_int8(x_f32(x), EPS, keep)
+    codes, scale, mask = tw.bitlinear_quantize_act(to_dev(x), "int8", topk_keep=keep, eps=EPS, want_mask=True,
+                                                   row_absmax_hint=dev_f32(g))
+    np.testing.assert_array_equal(mask_bits(host(mask), K), m)
+    np.testing.assert_array_equal(int8_values(host(codes)), c)
+    np.testing.assert_array_equal(host(scale), d)
+
+
 def test_quantize_int8_hint_matches_max_pass():
     torch_cuda()
     x = make_x(77, 12, 11008, True)
