@@ -282,6 +282,24 @@ def test_quantize_int8_topk_with_hint(M, K):
     np.testing.assert_array_equal(host(scale), d)
 
 
+@pytest.mark.parametrize("M,K", [(4000, 768), (2500, 4096), (1700, 8192)])
+@pytest.mark.parametrize("keep_frac", [0.5, 1.0, 0.0, "one", "hint"])
+def test_quantize_int8_topk_many_rows(M, K, keep_frac):
+    """More bf16 rows than the device holds blocks of the Top-K kernel at once, so that every block
+    works through several rows (the next row's copy in flight while one is quantized): with and
+    without the threshold search (keep = K and keep = 0 skip it), and with a given row maximum."""
+    torch_cuda()
+    keep = 1 if keep_frac == "one" else K // 2 if keep_frac == "hint" else int(keep_frac * K)
+    x = make_x(3700 + M + K, M, K, False)
+    c, m, d, g = O.quant_int8(x_f32(x), EPS, keep)
+    hint = dev_f32(g) if keep_frac == "hint" else None
+    codes, scale, mask = tw.bitlinear_quantize_act(to_dev(x), "int8", topk_keep=keep, eps=EPS, want_mask=True,
+                                                   row_absmax_hint=hint)
+    np.testing.assert_array_equal(mask_bits(host(mask), K), m)
+    np.testing.assert_array_equal(int8_values(host(codes)), c)
+    np.testing.assert_array_equal(host(scale), d)
+
+
 def test_quantize_int8_hint_matches_max_pass():
     torch_cuda()
     x = make_x(77, 12, 11008, True)
