@@ -336,6 +336,20 @@ __device__ __forceinline__ int2 tk_block_scan(int v, int* wtot, int t) {
   return make_int2(incl + off, tot);
 }
 
+typedef unsigned short tk_u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ tk_u16x2 tk_pk(uint32_t v) { return __builtin_bit_cast(tk_u16x2, v); }
+__device__ __forceinline__ uint32_t tk_unpk(tk_u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+// Bits 15 and 31 of q0..q3 (one flag per 16-bit half; half h of q_i is element 2i + h of a chunk)
+// gathered into bit 2i + h of one byte.
+__device__ __forceinline__ uint32_t tk_fold(uint32_t q0, uint32_t q1, uint32_t q2, uint32_t q3) {
+  const uint32_t f = (q0 >> 15) | (q1 >> 13) | (q2 >> 11) | (q3 >> 9);   // bits 0,2,4,6 and 16,18,20,22
+  return (f | (f >> 15)) & 0xFFu;
+}
+// 0xFF in byte k where bit k of n (k < 4) is set, else 0x00 (v_perm selector 13 gives 0xFF, 12 gives 0)
+__device__ __forceinline__ uint32_t tk_byte_mask(uint32_t n) {
+  return __builtin_amdgcn_perm(0u, 0u, 0x0C0C0C0Cu + (((n & 0xFu) * 0x00204081u) & 0x01010101u));
+}
+
 template <int NCH>
 __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x, int M, int K, long ldx, int keep,
                                                   float eps, const float* __restrict__ hint,
@@ -361,25 +375,20 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
   // the one below, with a given maximum) orders the clear before the first atomic
   if (search)
     for (int i = t; i < TK_COPIES * TK_STRIDE / 4; i += 256) hist4[i] = make_uint4(0u, 0u, 0u, 0u);
-  auto key = [&](int c, int j) -> uint32_t {
-    const uint32_t d = j < 2 ? w[c].x : j < 4 ? w[c].y : j < 6 ? w[c].z : w[c].w;
-    return ((j & 1) ? (d >> 16) : d) & 0x7FFFu;
-  };
-  auto val = [&](int c, int j) -> float {
-    const uint32_t d = j < 2 ? w[c].x : j < 4 ? w[c].y : j < 6 ? w[c].z : w[c].w;
-    return bl_u2f((j & 1) ? (d & 0xFFFF0000u) : (d << 16));
-  };
+  // dword i of chunk c: elements 2i (low half) and 2i + 1 (high half)
+  auto dw = [&](int c, int i) -> uint32_t { return i == 0 ? w[c].x : i == 1 ? w[c].y : i == 2 ? w[c].z : w[c].w; };
 
   float gamma;
   if (hint) {
     gamma = hint[row];
     if (search) __syncthreads();
   } else {
-    uint32_t mx = 0u;
+    tk_u16x2 pm = tk_pk(0u);                       // packed maxima of the 15-bit keys
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mx = max(mx, key(c, j));       // padding chunks hold key 0
+      for (int i = 0; i < 4; ++i) pm = __builtin_elementwise_max(pm, tk_pk(dw(c, i) & 0x7FFF7FFFu));
+    uint32_t mx = max((uint32_t)pm.x, (uint32_t)pm.y);   // padding chunks hold key 0
     mx = bl_wave_max_u(mx);
     if (lane == 0) wmax[wave] = mx;
     __syncthreads();
@@ -401,11 +410,15 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
       }
       return n;
     };
+    // exponent bin of each key: bits 7..14 (low half) and 23..30 (high half) of a dword
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       if (t + 256 * c < nch) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) atomicAdd(&hc[4 * (key(c, j) >> 7)], 1u);
+        for (int i = 0; i < 4; ++i) {
+          atomicAdd(&hc[4 * __builtin_amdgcn_ubfe(dw(c, i), 7, 8)], 1u);
+          atomicAdd(&hc[4 * __builtin_amdgcn_ubfe(dw(c, i), 23, 8)], 1u);
+        }
       }
     __syncthreads();
     // pass 1: thread t owns exponent bin 255 - t (descending keys)
@@ -417,13 +430,19 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
     __syncthreads();
     const uint32_t e = (uint32_t)sel[0];
     const int above = sel[1];
+    // mantissa bin of each key whose exponent is e; every other key adds to bin 128 + its mantissa
+    // (bins 128..255 are not read in this pass), so no lane branches. Per 16-bit half: x = key ^
+    // (e << 7) is the mantissa when the exponent matches and at least 128 + the mantissa otherwise.
+    const uint32_t ee = (e << 7) | (e << 23);
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       if (t + 256 * c < nch) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t k = key(c, j);
-          if ((k >> 7) == e) atomicAdd(&hc[4 * (k & 127u)], 1u);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t x = (dw(c, i) & 0x7FFF7FFFu) ^ ee;
+          const uint32_t b = tk_unpk(__builtin_elementwise_min(tk_pk(x), tk_pk((x & 0x007F007Fu) | 0x00800080u)));
+          atomicAdd(&hc[4 * (b & 0xFFFFu)], 1u);
+          atomicAdd(&hc[4 * (b >> 16)], 1u);
         }
       }
     __syncthreads();
@@ -437,19 +456,31 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
     need = keep - sel[1];                          // >= 1 ties at T survive, lowest index first
   }
 
+  // per chunk: bit j of gt8 / eq8 says whether key j is above / equal to T (packed 16-bit
+  // differences T - key: bit 15 of a half is set exactly when key > T, and bit 15 of the difference
+  // minus one is set exactly when key >= T, since every key and T are below 2^15)
+  uint32_t gt8[NCH], eq8[NCH];
   // tie ranks in index order: chunk c of all threads, then chunk c + 1
   int rank[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) rank[c] = 0;
   if (search) {
+    const tk_u16x2 tp = tk_pk(T | (T << 16));
     int tc[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      tc[c] = 0;
-      if (t + 256 * c < nch) {
+      uint32_t g[4], q[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) tc[c] += key(c, j) == T ? 1 : 0;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t d = tk_unpk(tp - tk_pk(dw(c, i) & 0x7FFF7FFFu));
+        const uint32_t e = tk_unpk(tk_pk(d) - tk_pk(0x00010001u));
+        g[i] = d & 0x80008000u;
+        q[i] = e & ~d & 0x80008000u;
       }
+      const bool ok = t + 256 * c < nch;           // padding chunks hold no keys
+      gt8[c] = tk_fold(g[0], g[1], g[2], g[3]);
+      eq8[c] = ok ? tk_fold(q[0], q[1], q[2], q[3]) : 0u;
+      tc[c] = __popc(eq8[c]);
     }
     int incl[NCH];
 #pragma unroll
@@ -477,23 +508,27 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
   for (int c = 0; c < NCH; ++c) {
     const int ch = t + 256 * c;
     if (ch >= nch) continue;                       // whole groups of 4 threads drop out together
-    uint32_t kb = 0u;
-    int r = rank[c];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t k = key(c, j);
-      bool keepj = all || k > T;
-      if (!all && k == T) { keepj = r < need; ++r; }
-      kb |= (keepj ? 1u : 0u) << j;
+    uint32_t kb = all ? 0xFFu : 0u;                // bit j: element j of the chunk survives
+    if (search) {
+      // the ties of this chunk with ranks below need, lowest index first (most chunks have none)
+      uint32_t ke = eq8[c];
+      const int room = need - rank[c];
+      if (room <= 0) ke = 0u;
+      while (__popc(ke) > room) ke &= ~(0x80000000u >> __clz(ke));
+      kb = gt8[c] | ke;
     }
+    // codes of all eight elements, then the dropped ones cleared byte by byte
     uint32_t rr[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float y = ((kb >> j) & 1u) ? val(c, j) * s : 0.0f;
-      rr[j] = bl_f2u(y + 12582912.0f);             // low byte = rint(y) in two's complement
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t d = dw(c, i);
+      rr[2 * i] = bl_f2u(bl_u2f(d << 16) * s + 12582912.0f);             // low byte = rint(x s)
+      rr[2 * i + 1] = bl_f2u(bl_u2f(d & 0xFFFF0000u) * s + 12582912.0f);
     }
-    const uint32_t lo = __builtin_amdgcn_perm(rr[1], rr[0], 0x0C0C0400u) | __builtin_amdgcn_perm(rr[3], rr[2], 0x04000C0Cu);
-    const uint32_t hi = __builtin_amdgcn_perm(rr[5], rr[4], 0x0C0C0400u) | __builtin_amdgcn_perm(rr[7], rr[6], 0x04000C0Cu);
+    uint32_t lo = __builtin_amdgcn_perm(rr[1], rr[0], 0x0C0C0400u) | __builtin_amdgcn_perm(rr[3], rr[2], 0x04000C0Cu);
+    uint32_t hi = __builtin_amdgcn_perm(rr[5], rr[4], 0x0C0C0400u) | __builtin_amdgcn_perm(rr[7], rr[6], 0x04000C0Cu);
+    lo &= tk_byte_mask(kb);
+    hi &= tk_byte_mask(kb >> 4);
     reinterpret_cast<uint2*>(codes + (long)row * K)[ch] = make_uint2(lo, hi);
     if (mrow) {                                    // the four threads of a quad share one word
       uint32_t mw = kb << (8 * (t & 3));
