@@ -26,6 +26,9 @@ namespace {
 constexpr int WAVES = 8;
 constexpr int CH = 4;     // K tiles per chunk and wave
 
+// s_waitcnt immediate that waits for vector memory operations only, until at most n are outstanding
+constexpr int gemv_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 __device__ __forceinline__ v4i expand_w_i8(uint32_t w) {
   v4i r;
   r[0] = (int)((w << 6) & 0xC0C0C0C0u);
@@ -159,9 +162,9 @@ constexpr int kGluWaves = (NWV == 8 && EPI == BL_EPI_RELU2_GLU && FMT != BL_ACT_
 
 template <int FMT, int EPI, int CHN, int NWV, bool ALDS>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(kGluWaves<FMT, EPI, NWV>))) void k_gemv(const uint8_t* __restrict__ A, const float* __restrict__ ascale,
-                                                     int M, int K, const uint8_t* __restrict__ W,
+                                                     int M, int K, const uint8_t* W,
                                                      const float* __restrict__ walpha,
-                                                     const uint8_t* __restrict__ W2,
+                                                     const uint8_t* W2,
                                                      const float* __restrict__ w2alpha, int N,
                                                      float* __restrict__ Y, long ldy, const float* R, long ldr,
                                                      float* __restrict__ rowmax) {
@@ -171,7 +174,10 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(kGluWa
   __shared__ v4i red[NB][NWV - 1][64];
   __shared__ __attribute__((aligned(16))) uint8_t acodes[ALDS ? ALDS_BYTES : 16];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // (wave-uniform in a scalar register for the single-matrix kernel, whose first-chunk waits depend on
+  // a branch on it; the two-matrix one keeps the vector form, which needs fewer registers there)
+  const int lane = threadIdx.x & 63;
+  const int wave = NB == 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : (int)(threadIdx.x >> 6);
   const int G = blockIdx.x;
   const int KT = K >> 7, NG = N >> 4;            // 128-wide weight tiles along K, 16-row groups
   const int per = (KT + NWV - 1) / NWV;
@@ -181,10 +187,15 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(kGluWa
   const int n = 16 * G + r;
   const uint32_t arow = A8 ? K : (K >> 1);
   const uint8_t* arp = A + (uint32_t)min(r, M - 1) * arow + (A8 ? 32 * g : 16 * g);
+  // (the weight pointers are not __restrict__: their loads must stay where they are issued, ahead of
+  // the barrier below, which a load the compiler may treat as invariant need not)
   const uint32_t woff = (uint32_t)G * 512u + (uint32_t)lane * 8u;
   const uint8_t* const wp[2] = {W + woff, (NB > 1 ? W2 : W) + woff};
   const uint32_t wstep = (uint32_t)NG * 512u;
-  if constexpr (ALDS) stage_codes_lds<NWV>(A, (uint32_t)M * arow, acodes, wave, lane);
+  if constexpr (ALDS) {
+    stage_codes_lds<NWV>(A, (uint32_t)M * arow, acodes, wave, lane);
+    if constexpr (NB == 1) asm volatile("" ::: "memory");   // every later load is issued after the copy
+  }
 
   // what the epilogue reads, fetched by the epilogue wave only, before its weight stream (rows past
   // M repeat row M-1; the other waves only stream weights and hand over partial sums)
@@ -208,12 +219,33 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(kGluWa
     // the first chunk's weights are in flight across the barrier that publishes the LDS codes
     const uint8_t* alds = acodes + (uint32_t)min(r, M - 1) * arow + 16 * g;
     uint2 wt[NB][CHN];
-    if (kt_begin < kt_end) load_w_chunk<NB, CHN>(wp, wstep, kt_begin, kt_end, wt);
-    __syncthreads();
-    for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CHN) {
-      if (kt0 != kt_begin) load_w_chunk<NB, CHN>(wp, wstep, kt0, kt_end, wt);
-      if (kt0 + CHN <= kt_end) mfma_chunk_lds<NB, true, CHN>(alds, wt, kt0, kt_end, acc);
-      else mfma_chunk_lds<NB, false, CHN>(alds, wt, kt0, kt_end, acc);
+    if constexpr (NB == 1) {
+      // every wave issues the first chunk's CHN weight loads after the copy (a wave without K tiles
+      // loads valid, unused words), so the copy has landed once at most those are outstanding; the
+      // barrier does not wait for the weights, and each wave starts on a tile as soon as it arrives
+      const bool work = kt_begin < kt_end;
+      load_w_chunk<NB, CHN>(wp, wstep, work ? kt_begin : KT - 1, work ? kt_end : KT, wt);
+      __builtin_amdgcn_s_waitcnt(gemv_vmcnt(NB * CHN));
+      asm volatile("s_barrier" ::: "memory");
+      if (work) {
+        if (kt_begin + CHN <= kt_end) mfma_chunk_lds<NB, true, CHN>(alds, wt, kt_begin, kt_end, acc);
+        else mfma_chunk_lds<NB, false, CHN>(alds, wt, kt_begin, kt_end, acc);
+        for (int kt0 = kt_begin + CHN; kt0 < kt_end; kt0 += CHN) {
+          load_w_chunk<NB, CHN>(wp, wstep, kt0, kt_end, wt);
+          if (kt0 + CHN <= kt_end) mfma_chunk_lds<NB, true, CHN>(alds, wt, kt0, kt_end, acc);
+          else mfma_chunk_lds<NB, false, CHN>(alds, wt, kt0, kt_end, acc);
+        }
+      }
+    } else {
+      // two matrices: the scheme above needs more registers than the three-blocks-per-CU cap allows
+      // (it spills), so the barrier also waits for the first chunk's weights
+      if (kt_begin < kt_end) load_w_chunk<NB, CHN>(wp, wstep, kt_begin, kt_end, wt);
+      __syncthreads();
+      for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CHN) {
+        if (kt0 != kt_begin) load_w_chunk<NB, CHN>(wp, wstep, kt0, kt_end, wt);
+        if (kt0 + CHN <= kt_end) mfma_chunk_lds<NB, true, CHN>(alds, wt, kt0, kt_end, acc);
+        else mfma_chunk_lds<NB, false, CHN>(alds, wt, kt0, kt_end, acc);
+      }
     }
   } else {
     for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CHN) {

@@ -48,7 +48,7 @@ __device__ __forceinline__ uint32_t kv_codes4(const float v[4], float s) {
 template <int D>
 __device__ __forceinline__ void kv_store4(uint8_t* rec_base, int l, uint32_t a16, uint32_t b16, bool ok) {
   const uint32_t send = (l & 1) ? a16 : b16;
-  const uint32_t recv = __shfl_xor(send, 1, 64);
+  const uint32_t recv = bl_dpp<0xB1>(send);        // the pair partner (lane xor 1)
   if (!ok) return;
   if ((l & 1) == 0)
     *reinterpret_cast<uint32_t*>(rec_base + 2 * l) = a16 | (recv << 16);
@@ -122,11 +122,14 @@ __global__ __launch_bounds__(256) void k_kv_quant(const void* __restrict__ x, lo
     mx = ua > mx ? ua : mx;
     mx = ub > mx ? ub : mx;
   }
-#pragma unroll
-  for (int o = LPH / 2; o >= 1; o >>= 1) {
-    const uint32_t v = __shfl_xor(mx, o, 64);
-    mx = v > mx ? v : mx;
-  }
+  // head maximum over the LPH lanes of the group: DPP exchanges inside rows of 16 lanes (xor 1,
+  // xor 2, the mirror of each 8 lanes, the mirror of the row), then one shuffle across rows for D = 256
+  mx = max(mx, bl_dpp<0xB1>(mx));                  // quad_perm(1, 0, 3, 2)
+  mx = max(mx, bl_dpp<0x4E>(mx));                  // quad_perm(2, 3, 0, 1)
+  mx = max(mx, bl_dpp<0x141>(mx));                 // row_half_mirror
+  if constexpr (LPH >= 16) mx = max(mx, bl_dpp<0x140>(mx));   // row_mirror
+  if constexpr (LPH >= 32) mx = max(mx, (uint32_t)__shfl_xor(mx, 16, 64));
+  static_assert(LPH == 8 || LPH == 16 || LPH == 32, "head groups of 8, 16 or 32 lanes");
   const float gamma = bl_u2f(mx);
   const float den = gamma + eps;
 

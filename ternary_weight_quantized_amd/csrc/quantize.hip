@@ -308,7 +308,7 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
 // INT8 absmax with the Top-K mask for bf16 rows (K <= 8192), one 256-thread block per row. Thread t
 // owns the 8-element chunks t, t + 256, ... (one 16-byte load each). The threshold key T (the
 // largest 15-bit magnitude key with count(key >= T) >= keep) comes from two radix passes over LDS
-// histograms, 16 copies (thread t adds to copy t % 16, so a wave's 64 increments spread over 16
+// histograms, 8 copies (thread t adds to copy t % 8, so a wave's 64 increments spread over 8
 // copies): exponents (key >> 7), then the mantissas of the keys whose exponent is T's. Copies are
 // interleaved in groups of four (bin b of copy 4g + i is word 4b + i of group g), so one 16-byte
 // read returns a bin of four copies and the clears are 16-byte stores. Bin counts
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256) void k_quant_res(const void* __restrict__ x, i
 // scan of the per-thread tie counts of every chunk. Codes: RN32(x * s) is rounded to an integer by
 // adding 1.5 * 2^23 (round to nearest even; |x * s| < 127.5 always, so no clamping is needed) and
 // its low byte is the two's-complement code. A 32-element mask word comes from 4 neighbouring threads.
-constexpr int TK_COPIES = 16, TK_STRIDE = 264;     // 256 bins + 8 pad words per copy
+constexpr int TK_COPIES = 8, TK_STRIDE = 264;      // 256 bins + 8 pad words per copy
 constexpr int TK_GROUP = 4 * TK_STRIDE;            // words per group of four interleaved copies
 
 // Inclusive scan of one int per thread over the 256-thread block; returns (inclusive, total). The
