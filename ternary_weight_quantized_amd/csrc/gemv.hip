@@ -370,7 +370,7 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
 // block overlap the gate loads of others; at most 80 VGPRs keep three blocks per CU resident.
 template <bool ALDS>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(6))) void k_glu_cond_fused(
-    const uint8_t* __restrict__ A, const float* __restrict__ ascale, int M, int K, const uint8_t* __restrict__ Wg,
+    const uint8_t* __restrict__ A, const float* __restrict__ ascale, int M, int K, const uint8_t* Wg,
     const float* __restrict__ galpha, const uint8_t* __restrict__ Wup, const float* __restrict__ upalpha, int N,
     float* __restrict__ Gout, long ldg, float* __restrict__ H, long ldh, float* __restrict__ rowmax) {
   __shared__ v4i red[WAVES][64];
@@ -384,7 +384,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(6)))
   const int kt_end = min(KT, kt_begin + per);
   const int r = lane & 15, g4 = lane >> 4;
   const uint32_t arow = (uint32_t)K >> 1;
-  if constexpr (ALDS) stage_codes_lds<WAVES>(A, (uint32_t)M * arow, acodes, wave, lane);
+  if constexpr (ALDS) {
+    stage_codes_lds<WAVES>(A, (uint32_t)M * arow, acodes, wave, lane);
+    asm volatile("" ::: "memory");               // every later load is issued after the copy
+  }
   const uint8_t* arp = A + (uint32_t)min(r, M - 1) * arow + 16 * g4;
   const uint8_t* const wp[2] = {Wg + (uint32_t)G * 512u + (uint32_t)lane * 8u, Wg + (uint32_t)G * 512u + (uint32_t)lane * 8u};
   const uint32_t wstep = (uint32_t)NG * 512u;
@@ -398,15 +401,24 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(6)))
   v4i acc[1][2];
   acc[0][0] = acc[0][1] = v4i{0, 0, 0, 0};
   if constexpr (ALDS) {
-    // the first chunk's weights are in flight across the barrier that publishes the LDS codes
+    // every wave issues the first chunk's CH gate-weight loads after the copy (valid addresses also
+    // without a K tile), so the copy has landed once at most those are outstanding; the barrier
+    // that publishes it does not wait for the weights (the gate pointer is not __restrict__, so
+    // the compiler keeps these loads ahead of the barrier)
     const uint8_t* alds = acodes + (uint32_t)min(r, M - 1) * arow + 16 * g4;
     uint2 wt[1][CH];
-    if (kt_begin < kt_end) load_w_chunk<1>(wp, wstep, kt_begin, kt_end, wt);
-    __syncthreads();
-    for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CH) {
-      if (kt0 != kt_begin) load_w_chunk<1>(wp, wstep, kt0, kt_end, wt);
-      if (kt0 + CH <= kt_end) mfma_chunk_lds<1, true>(alds, wt, kt0, kt_end, acc);
-      else mfma_chunk_lds<1, false>(alds, wt, kt0, kt_end, acc);
+    const bool work = kt_begin < kt_end;
+    load_w_chunk<1>(wp, wstep, work ? kt_begin : KT - 1, work ? kt_end : KT, wt);
+    __builtin_amdgcn_s_waitcnt(gemv_vmcnt(CH));
+    asm volatile("s_barrier" ::: "memory");
+    if (work) {
+      if (kt_begin + CH <= kt_end) mfma_chunk_lds<1, true>(alds, wt, kt_begin, kt_end, acc);
+      else mfma_chunk_lds<1, false>(alds, wt, kt_begin, kt_end, acc);
+      for (int kt0 = kt_begin + CH; kt0 < kt_end; kt0 += CH) {
+        load_w_chunk<1>(wp, wstep, kt0, kt_end, wt);
+        if (kt0 + CH <= kt_end) mfma_chunk_lds<1, true>(alds, wt, kt0, kt_end, acc);
+        else mfma_chunk_lds<1, false>(alds, wt, kt0, kt_end, acc);
+      }
     }
   } else {
     for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CH) {
