@@ -300,6 +300,28 @@ def test_quantize_int8_topk_many_rows(M, K, keep_frac):
     np.testing.assert_array_equal(host(scale), d)
 
 
+@pytest.mark.parametrize("K", [768, 4096, 8192])
+def test_quantize_int8_topk_threshold_depth(K):
+    """Rows whose Top-K threshold lies 0 to 12 binary exponents below the row maximum: a few
+    elements near 3.0 set the maximum, the rest are N(0, 1) scaled by 2^-d. The threshold search
+    resolves thresholds near the maximum's exponent with small histograms and falls back to the
+    full search below that; both sides of that boundary must give the oracle's mask and codes."""
+    torch_cuda()
+    rng = np.random.default_rng(4242 + K)
+    rows = []
+    for d in range(0, 13):
+        r = rng.standard_normal(K) * 2.0 ** -d
+        r[rng.choice(K, 8, replace=False)] = 3.0 + rng.random(8)
+        rows.append(r)
+    x = to_bf16_bits(np.array(rows))
+    for keep in (K // 2, K // 8, K - 3):
+        c, m, d_, g = O.quant_int8(x_f32(x), EPS, keep)
+        codes, scale, mask = tw.bitlinear_quantize_act(to_dev(x), "int8", topk_keep=keep, eps=EPS, want_mask=True)
+        np.testing.assert_array_equal(mask_bits(host(mask), K), m)
+        np.testing.assert_array_equal(int8_values(host(codes)), c)
+        np.testing.assert_array_equal(host(scale), d_)
+
+
 def test_quantize_int8_hint_matches_max_pass():
     torch_cuda()
     x = make_x(77, 12, 11008, True)
