@@ -10,8 +10,8 @@
 //
 // One pass over HBM: a group of D/8 lanes holds one head, each lane 4 elements of the first half
 // and the 4 partner elements of the second half, so the rotation needs no data exchange; the head
-// max is a shuffle reduction inside the group; codes are packed with lane shuffles and written as
-// dwords.
+// max is a reduction inside the group (DPP row exchanges); codes are packed with lane exchanges and
+// written as dwords.
 #include "bl_common.h"
 #include "bl_kernels.h"
 

@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) void k_topk_blk(const uint16_t* __restrict__ x
   int need = 0;
   if (search) {
     uint32_t* hc = hist + ((t & (TK_COPIES - 1)) >> 2) * TK_GROUP + (t & 3);   // bin b at hc[4 b]
-    // total of bin b over the 16 copies: four 16-byte reads
+    // total of bin b over the copies: one 16-byte read per group of four
     auto bin_total = [&](int b) -> int {
       int n = 0;
 #pragma unroll
