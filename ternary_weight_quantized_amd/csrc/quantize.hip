@@ -880,6 +880,7 @@ __device__ __forceinline__ float round_down_f32(double d) {        // d >= 0, d 
 }
 
 constexpr int kTensorBlocks = 512;     // blocks of the tensor-wide reduction
+constexpr int kTensorThreads = 1024;   // threads per block: two blocks fill a CU's 32 wave slots
 constexpr int kTensorLimbs = 12;       // 64-bit limb sums per block slot
 
 template <int IN_F32>
@@ -895,40 +896,28 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, long off, floa
   }
 }
 
-// Adds one non-negative float per lane to the LDS bins, one atomic per distinct exponent of the
-// wave (lanes with equal exponents are summed first; 64 significands < 2^24 fit in 32 bits).
-// Called by all 64 lanes together.
-__device__ __forceinline__ void wave_bins_add(unsigned long long* bins, float v, int lane) {
+// Adds one non-negative float per lane to the LDS bins: its significand to the bin of its exponent,
+// one 64-bit LDS atomic per lane (integer sums, so their order does not matter). Lanes that share an
+// exponent are serialized by the LDS, which costs far less than merging them first with shuffles.
+__device__ __forceinline__ void lane_bins_add(unsigned long long* bins, float v) {
   uint32_t e, m;
   bl_bin_split(bl_f2u(v) & 0x7FFFFFFFu, &e, &m);
-  bool pending = m != 0u;
-  for (;;) {
-    const unsigned long long act = __ballot(pending);
-    if (act == 0ull) break;
-    const int leader = __ffsll((long long)act) - 1;
-    const uint32_t e0 = __shfl(e, leader, 64);
-    const bool mine = pending && e == e0;
-    uint32_t part = mine ? m : 0u;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-    if (lane == leader) atomicAdd(&bins[e0], (unsigned long long)part);
-    pending = pending && !mine;
-  }
+  if (m) atomicAdd(&bins[e], (unsigned long long)m);
 }
 
 // Each block writes its exact total as twelve limb sums to slot blockIdx (SUM), or its maximum;
 // every slot is rewritten on every call, so the workspace needs no clearing.
 // Threads walk 8-element chunks of the row-major tensor with a grid stride.
 template <int IN_F32, bool SUM>
-__global__ __launch_bounds__(256) void k_tensor_reduce(const void* __restrict__ x, int M, int K, long ldx,
+__global__ __launch_bounds__(kTensorThreads) void k_tensor_reduce(const void* __restrict__ x, int M, int K, long ldx,
                                                        unsigned long long* __restrict__ gslot,
                                                        uint32_t* __restrict__ gmax) {
   __shared__ unsigned long long bins[SUM ? 256 : 1];
   __shared__ unsigned long long limbs[SUM ? kTensorLimbs : 1];
-  __shared__ uint32_t wmax[4];
+  __shared__ uint32_t wmax[kTensorThreads / 64];
   const int t = threadIdx.x, lane = t & 63;
   if constexpr (SUM) {
-    bins[t] = 0ull;
+    if (t < 256) bins[t] = 0ull;
     __syncthreads();
   }
   uint32_t mx = 0u;
@@ -984,9 +973,9 @@ __global__ __launch_bounds__(256) void k_tensor_reduce(const void* __restrict__ 
         if (col >= KO) { col -= KO; ++row; }
       }
     }
-    wave_bins_add(bins, hi, lane);
-    wave_bins_add(bins, mid, lane);
-    wave_bins_add(bins, lo, lane);
+    lane_bins_add(bins, hi);
+    lane_bins_add(bins, mid);
+    lane_bins_add(bins, lo);
     __syncthreads();
     bl_bins_to_limb_sums_block(bins, limbs);
     if (t < kTensorLimbs) gslot[blockIdx.x * kTensorLimbs + t] = limbs[t];
@@ -996,7 +985,7 @@ __global__ __launch_bounds__(256) void k_tensor_reduce(const void* __restrict__ 
     __syncthreads();
     if (t == 0) {
       uint32_t m = wmax[0];
-      for (int w = 1; w < 4; ++w) m = wmax[w] > m ? wmax[w] : m;
+      for (int w = 1; w < kTensorThreads / 64; ++w) m = wmax[w] > m ? wmax[w] : m;
       gmax[blockIdx.x] = m;
     }
   }
@@ -1118,7 +1107,7 @@ hipError_t bl_launch_quantize_per_tensor(const void* x, int in_f32, int M, int K
   uint32_t* gmax = reinterpret_cast<uint32_t*>(w + (size_t)kTensorBlocks * kTensorLimbs * 8);
   float* rowval = reinterpret_cast<float*>(w + (size_t)kTensorBlocks * kTensorLimbs * 8 + (size_t)kTensorBlocks * 4);
   const bool sum = (fmt == BL_ACT_INT4 || fmt == BL_ACT_INT4_E3M2);
-  const dim3 grid(kTensorBlocks), block(256);
+  const dim3 grid(kTensorBlocks), block(kTensorThreads);
   if (sum) {
     if (in_f32) hipLaunchKernelGGL((k_tensor_reduce<1, true>), grid, block, 0, st, x, M, K, ldx, gslot, gmax);
     else hipLaunchKernelGGL((k_tensor_reduce<0, true>), grid, block, 0, st, x, M, K, ldx, gslot, gmax);
