@@ -286,12 +286,14 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(kGluWa
     if (m < M) Y[(long)m * ldy + n] = out;
     if constexpr (EPI == BL_EPI_RELU2_GLU) {
       if (rowmax) {
-        float a = fabsf(out);
-        a = fmaxf(a, __shfl_xor(a, 1, 64));
-        a = fmaxf(a, __shfl_xor(a, 2, 64));
-        a = fmaxf(a, __shfl_xor(a, 4, 64));
-        a = fmaxf(a, __shfl_xor(a, 8, 64));
-        if (r == 0 && m < M) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, bl_f2u(a));
+        // maximum of |h| over the 16 columns (lanes of one DPP row); non-negative floats order
+        // as their bit patterns
+        uint32_t a = bl_f2u(fabsf(out));
+        a = max(a, bl_dpp<0xB1>(a));               // quad_perm(1, 0, 3, 2)
+        a = max(a, bl_dpp<0x4E>(a));               // quad_perm(2, 3, 0, 1)
+        a = max(a, bl_dpp<0x141>(a));              // row_half_mirror
+        a = max(a, bl_dpp<0x140>(a));              // row_mirror
+        if (r == 0 && m < M) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, a);
       }
     }
   }
