@@ -174,8 +174,8 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(kGluWa
   __shared__ v4i red[NB][NWV - 1][64];
   __shared__ __attribute__((aligned(16))) uint8_t acodes[ALDS ? ALDS_BYTES : 16];
 
-  // (wave-uniform in a scalar register for the single-matrix kernel, whose first-chunk waits depend on
-  // a branch on it; the two-matrix one keeps the vector form, which needs fewer registers there)
+  // (the wave index sits in a scalar register in the single-matrix kernels, which measured faster
+  // that way; in the two-matrix one it needs registers the three-blocks-per-CU cap does not leave)
   const int lane = threadIdx.x & 63;
   const int wave = NB == 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : (int)(threadIdx.x >> 6);
   const int G = blockIdx.x;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(kGluWa
   const uint32_t wstep = (uint32_t)NG * 512u;
   if constexpr (ALDS) {
     stage_codes_lds<NWV>(A, (uint32_t)M * arow, acodes, wave, lane);
-    if constexpr (NB == 1) asm volatile("" ::: "memory");   // every later load is issued after the copy
+    asm volatile("" ::: "memory");   // every later load is issued after the copy
   }
 
   // what the epilogue reads, fetched by the epilogue wave only, before its weight stream (rows past
@@ -219,30 +219,19 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(kGluWa
     // the first chunk's weights are in flight across the barrier that publishes the LDS codes
     const uint8_t* alds = acodes + (uint32_t)min(r, M - 1) * arow + 16 * g;
     uint2 wt[NB][CHN];
-    if constexpr (NB == 1) {
-      // every wave issues the first chunk's CHN weight loads after the copy (a wave without K tiles
-      // loads valid, unused words), so the copy has landed once at most those are outstanding; the
-      // barrier does not wait for the weights, and each wave starts on a tile as soon as it arrives
-      const bool work = kt_begin < kt_end;
-      load_w_chunk<NB, CHN>(wp, wstep, work ? kt_begin : KT - 1, work ? kt_end : KT, wt);
-      __builtin_amdgcn_s_waitcnt(gemv_vmcnt(NB * CHN));
-      asm volatile("s_barrier" ::: "memory");
-      if (work) {
-        if (kt_begin + CHN <= kt_end) mfma_chunk_lds<NB, true, CHN>(alds, wt, kt_begin, kt_end, acc);
-        else mfma_chunk_lds<NB, false, CHN>(alds, wt, kt_begin, kt_end, acc);
-        for (int kt0 = kt_begin + CHN; kt0 < kt_end; kt0 += CHN) {
-          load_w_chunk<NB, CHN>(wp, wstep, kt0, kt_end, wt);
-          if (kt0 + CHN <= kt_end) mfma_chunk_lds<NB, true, CHN>(alds, wt, kt0, kt_end, acc);
-          else mfma_chunk_lds<NB, false, CHN>(alds, wt, kt0, kt_end, acc);
-        }
-      }
-    } else {
-      // two matrices: the scheme above needs more registers than the three-blocks-per-CU cap allows
-      // (it spills), so the barrier also waits for the first chunk's weights
-      if (kt_begin < kt_end) load_w_chunk<NB, CHN>(wp, wstep, kt_begin, kt_end, wt);
-      __syncthreads();
-      for (int kt0 = kt_begin; kt0 < kt_end; kt0 += CHN) {
-        if (kt0 != kt_begin) load_w_chunk<NB, CHN>(wp, wstep, kt0, kt_end, wt);
+    // every wave issues the first chunk's NB * CHN weight loads after the copy (a wave without K
+    // tiles loads valid, unused words), so the copy has landed once at most those are outstanding;
+    // the barrier does not wait for the weights, and each wave starts on a tile as soon as it arrives
+    // (the flag is made wave-uniform so that the compiler counts those loads exactly)
+    const bool work = __builtin_amdgcn_readfirstlane((int)(kt_begin < kt_end)) != 0;
+    load_w_chunk<NB, CHN>(wp, wstep, work ? kt_begin : KT - 1, work ? kt_end : KT, wt);
+    __builtin_amdgcn_s_waitcnt(gemv_vmcnt(NB * CHN));
+    asm volatile("s_barrier" ::: "memory");
+    if (work) {
+      if (kt_begin + CHN <= kt_end) mfma_chunk_lds<NB, true, CHN>(alds, wt, kt_begin, kt_end, acc);
+      else mfma_chunk_lds<NB, false, CHN>(alds, wt, kt_begin, kt_end, acc);
+      for (int kt0 = kt_begin + CHN; kt0 < kt_end; kt0 += CHN) {
+        load_w_chunk<NB, CHN>(wp, wstep, kt0, kt_end, wt);
         if (kt0 + CHN <= kt_end) mfma_chunk_lds<NB, true, CHN>(alds, wt, kt0, kt_end, acc);
         else mfma_chunk_lds<NB, false, CHN>(alds, wt, kt0, kt_end, acc);
       }
