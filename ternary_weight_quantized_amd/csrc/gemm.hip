@@ -287,31 +287,47 @@ __device__ __forceinline__ uint32_t kv_code4(const float (&x)[4], float s) {
   return r;
 }
 
-// the head record of one row: 4 bits per code (64 bytes) or 3 bits (48 bytes); the lane's codes of
-// tile t are codes 16 t + 4 g .. + 3; lanes g and g ^ 1 (lane ^ 16) combine their pieces
+// The head records of one 16-row subtile, assembled in the wave's LDS region and written as 16-byte
+// pieces (whole records, one store instruction per subtile). A record holds 128 codes, code k at
+// bits BITS k: 64 bytes for 4 bits, 48 for 3. Lane (r, g) holds codes 16 t + 4 g .. + 3 of row r
+// for each tile t: 4 bits make the 16-bit group at byte 8 t + 2 g of the record; 3 bits make the
+// 12-bit group at bit 48 t + 12 g, which is ORed into zeroed words (it may straddle two).
 template <int BITS>
-__device__ __forceinline__ void kv_store_head(uint8_t* __restrict__ rec, const float (&x)[8][4], float s, int g,
-                                              bool ok) {
+__device__ __forceinline__ void kv_stage_records(uint8_t* __restrict__ region, const float (&x)[8][4], float s, int r,
+                                                 int g, int lane) {
+  constexpr int RB = BITS * 16;                  // bytes per record
+  if constexpr (BITS == 3) {
+    if (lane < RB) reinterpret_cast<uint4*>(region)[lane] = make_uint4(0u, 0u, 0u, 0u);   // 16 records
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const uint32_t mine = kv_code4<BITS>(x[t], s);
-    const uint32_t other = __shfl_xor(mine, 16, 64);
-    if (ok && (g & 1) == 0) {
-      if constexpr (BITS == 4) {
-        *reinterpret_cast<uint32_t*>(rec + 8 * t + 2 * g) = mine | (other << 16);       // codes 16t+4g .. +7
-      } else {
-        const uint32_t v24 = mine | (other << 12);                                        // 8 codes, 3 bytes
-        uint8_t* b = rec + 6 * t + 3 * (g >> 1);
-        if (g == 0) {
-          *reinterpret_cast<uint16_t*>(b) = (uint16_t)v24;
-          b[2] = (uint8_t)(v24 >> 16);
-        } else {
-          b[0] = (uint8_t)v24;
-          *reinterpret_cast<uint16_t*>(b + 1) = (uint16_t)(v24 >> 8);
-        }
-      }
+    const uint32_t c = kv_code4<BITS>(x[t], s);
+    if constexpr (BITS == 4) {
+      *reinterpret_cast<uint16_t*>(region + r * RB + 8 * t + 2 * g) = (uint16_t)c;
+    } else {
+      const int o = 48 * t + 12 * g, sh = o & 31;
+      uint32_t* w = reinterpret_cast<uint32_t*>(region + r * RB) + (o >> 5);
+      atomicOr(w, c << sh);
+      if (sh > 20) atomicOr(w + 1, c >> (32 - sh));
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+// lane l < 16 RB / 16 writes piece l % (RB / 16) of record l / (RB / 16), the record of subtile row
+// l / (RB / 16), to dst(that row) when the row is stored (keep)
+template <int BITS, typename Dst, typename Keep>
+__device__ __forceinline__ void kv_write_records(const uint8_t* __restrict__ region, int lane, Dst dst, Keep keep) {
+  constexpr int RB = BITS * 16, PPR = RB / 16;
+  if (lane < 16 * PPR) {
+    const int rr = lane / PPR, pc = lane - PPR * (lane / PPR);
+    const uint4 q = *reinterpret_cast<const uint4*>(region + rr * RB + 16 * pc);
+    if (keep(rr)) *reinterpret_cast<uint4*>(dst(rr) + 16 * pc) = q;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();                 // the region is rewritten by the next records
 }
 
 // The lane's RoPE table entries of one row (columns 16 t + 4 g .. + 3, t < 4), for the row's position
@@ -327,9 +343,10 @@ __device__ __forceinline__ void kv_rope_tables(const bl_kv_epi& kv, int p, int g
 
 // o: the fp32 outputs of one row of the wave's strip (exactly the values the plain epilogue stores);
 // cs, sn: the row's RoPE table entries (used for Q and K when the tables are given); slot: the row's
-// BOS slot (or -1)
+// BOS slot (or -1); mrow0: the subtile's first row; region: the wave's LDS region
 __device__ __forceinline__ void kv_epilogue_row(const bl_kv_epi& kv, int m, bool mok, int nstrip, float (&o)[8][4],
-                                                int g, const float4 (&cs)[4], const float4 (&sn)[4], int slot) {
+                                                int g, const float4 (&cs)[4], const float4 (&sn)[4], int slot,
+                                                int mrow0, int M, uint8_t* __restrict__ region, int lane) {
   const int HD = kv.H * 128;
   const int part = nstrip / HD;
   const int h = (nstrip - part * HD) >> 7;
@@ -361,19 +378,30 @@ __device__ __forceinline__ void kv_epilogue_row(const bl_kv_epi& kv, int m, bool
   mx = q > mx ? q : mx;
   const float gamma = bl_u2f(mx);
   const float den = gamma + kv.eps;
+  const int r = lane & 15;
   const long rec = (long)m * kv.H + h;
+  auto row_ok = [&](int rr) { return mrow0 + rr < M; };
   if (kv.bits[part] == 4) {
-    kv_store_head<4>(kv.codes[part] + rec * 64, o, 7.0f / den, g, mok);
+    kv_stage_records<4>(region, o, 7.0f / den, r, g, lane);
+    uint8_t* base = kv.codes[part];
+    kv_write_records<4>(region, lane, [&](int rr) { return base + ((long)(mrow0 + rr) * kv.H + h) * 64; }, row_ok);
     if (mok && g == 0) kv.scale[part][rec] = gamma / 7.0f;
   } else {
-    kv_store_head<3>(kv.codes[part] + rec * 48, o, 3.0f / den, g, mok);
+    kv_stage_records<3>(region, o, 3.0f / den, r, g, lane);
+    uint8_t* base = kv.codes[part];
+    kv_write_records<3>(region, lane, [&](int rr) { return base + ((long)(mrow0 + rr) * kv.H + h) * 48; }, row_ok);
     if (mok && g == 0) kv.scale[part][rec] = gamma / 3.0f;
     if (kv.bos_slot) {                                       // uniform over the launch
       const bool wr = mok && slot >= 0 && slot < kv.nslots;
       if (__ballot(wr) != 0ull) {
-        const long brec = (long)(wr ? slot : 0) * kv.H + h;
-        kv_store_head<4>(kv.bos_codes[part] + brec * 64, o, 7.0f / den, g, wr);
-        if (wr && g == 0) kv.bos_scale[part][brec] = gamma / 7.0f;
+        // the rows' BOS slots go through LDS to the lanes that write their records
+        int* slots = reinterpret_cast<int*>(region + 1024);
+        if (lane < 16) slots[lane] = wr ? slot : -1;
+        kv_stage_records<4>(region, o, 7.0f / den, r, g, lane);
+        uint8_t* bbase = kv.bos_codes[part];
+        kv_write_records<4>(region, lane, [&](int rr) { return bbase + ((long)slots[rr] * kv.H + h) * 64; },
+                            [&](int rr) { return slots[rr] >= 0; });
+        if (wr && g == 0) kv.bos_scale[part][(long)slot * kv.H + h] = gamma / 7.0f;
       }
     }
   }
@@ -553,7 +581,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx(
         if (Y)
           store_subtile_rows<SN>(Y, ldy, M, N, m0 + wm * SM * 16 + 16 * s, nstrip, o,
                                  reinterpret_cast<float*>(smem) + wave * (16 * (16 * SN + 4)), lane);
-        kv_epilogue_row(kv, m, mok, nstrip, o, g4, kcs[s & 1], ksn[s & 1], kvslot[s]);
+        kv_epilogue_row(kv, m, mok, nstrip, o, g4, kcs[s & 1], ksn[s & 1], kvslot[s], m0 + wm * SM * 16 + 16 * s, M,
+                        reinterpret_cast<uint8_t*>(reinterpret_cast<float*>(smem) + wave * (16 * (16 * SN + 4))), lane);
       }
     } else {
       // whole-row stores through the wave's LDS region
