@@ -60,6 +60,15 @@ __device__ __forceinline__ int bl_wave_incl_scan(int v, int lane) {
   const int row = lane >> 4;
   return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
+// Maximum over the lanes l, l ^ 16, l ^ 32 and l ^ 48 of a wave (the four 16-lane rows at one
+// position). v_permlane16_swap with both operands v returns, in its two results, the values of the
+// lanes l and l ^ 16; v_permlane32_swap those of l and l ^ 32. Every lane must be active.
+__device__ __forceinline__ uint32_t bl_max_across_rows(uint32_t v) {
+  const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = p16[0] > p16[1] ? p16[0] : p16[1];
+  const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return p32[0] > p32[1] ? p32[0] : p32[1];
+}
 template <int CTRL>
 __device__ __forceinline__ double bl_dpp_d(double v) {
   const unsigned long long u = __builtin_bit_cast(unsigned long long, v);

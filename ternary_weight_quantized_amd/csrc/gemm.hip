@@ -372,10 +372,7 @@ __device__ __forceinline__ void kv_epilogue_row(const bl_kv_epi& kv, int m, bool
       const uint32_t u = bl_f2u(o[t][v]) & 0x7FFFFFFFu;
       mx = u > mx ? u : mx;
     }
-  uint32_t q = __shfl_xor(mx, 16, 64);
-  mx = q > mx ? q : mx;
-  q = __shfl_xor(mx, 32, 64);
-  mx = q > mx ? q : mx;
+  mx = bl_max_across_rows(mx);
   const float gamma = bl_u2f(mx);
   const float den = gamma + kv.eps;
   const int r = lane & 15;
@@ -591,9 +588,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mx(
     }
     if constexpr (EPI == BL_EPI_RELU2_GLU) {
       if (rowmax) {
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
-        if (g4 == 0 && mok) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, bl_f2u(rmax));
+        // |h| >= 0, so the maximum of the bit patterns is the maximum of the values
+        const uint32_t rb = bl_max_across_rows(bl_f2u(rmax));
+        if (g4 == 0 && mok) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, rb);
       }
     }
   }
@@ -761,9 +758,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_i8(const uint8_t* __restrict__ 
     }
     if constexpr (EPI == BL_EPI_RELU2_GLU) {
       if (rowmax) {
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
-        if (g4 == 0 && mok) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, bl_f2u(rmax));
+        // |h| >= 0, so the maximum of the bit patterns is the maximum of the values
+        const uint32_t rb = bl_max_across_rows(bl_f2u(rmax));
+        if (g4 == 0 && mok) atomicMax(reinterpret_cast<unsigned int*>(rowmax) + m, rb);
       }
     }
   }
