@@ -244,6 +244,46 @@ def test_qkv_kv_fused(M, H, K, fmt, bits, rope, bos, want_y):
             np.testing.assert_array_equal(host(r["bos_scale"][p]), host(kbs))
 
 
+@pytest.mark.parametrize("fmt", ["int4_e3m2", "fp4"])
+def test_qkv_kv_fused_many_bos(fmt):
+    """Several BOS tokens inside one 16-row subtile, in other subtiles and in the ragged last one
+    (M = 37): every BOS record and scale of the fused epilogue equals the stand-alone quantizer's
+    on the GEMM's output and the oracle's, and the plain records stay exact."""
+    torch = torch_cuda()
+    M, H, K = 37, 2, 384
+    c = _qkv_case(8700, M, H, K, fmt, True, [0, 3, 4, 15, 17, 18, 31, 32, 36])
+    N = c["N"]
+    kw = dict(pos=dev_i32(c["pos"]), cos=dev_f32(c["cos"]), sin=dev_f32(c["sin"]))
+    bkw = dict(bos_slot=dev_i32(c["slots"]), n_bos_slots=c["nslots"])
+    r = tw.bitlinear_gemm_w158a4_kv(fmt, c["codes"], c["scale"], K, c["packed"], c["a"], N, H, bits=(4, 3, 3),
+                                    eps=EPS, **kw, **bkw)
+    y = tw.bitlinear_gemm_w158a4(fmt, c["codes"], c["scale"], K, c["packed"], c["a"], N)
+    torch.cuda.synchronize()
+    # the oracle's Y: exact integer accumulators and the fixed-order fp32 epilogue
+    if fmt == "fp4":
+        ref = O.bitlinear_a4(bf16_bits_to_f32(c["xb"]), c["t"], c["alpha"], EPS, fmt="fp4")
+        y_ref = O.dequant_f32(ref["acc"], ref["dscale"], c["alpha"], 0.5)
+    else:
+        ref = O.bitlinear_a4(bf16_bits_to_f32(c["xb"]), c["t"], c["alpha"], EPS)
+        y_ref = O.dequant_f32(ref["acc"], ref["dscale"], c["alpha"])
+    np.testing.assert_array_equal(host(y).view(np.uint32), y_ref.view(np.uint32))
+    for p in range(3):
+        b = (4, 3, 3)[p]
+        cols = slice(p * H * 128, (p + 1) * H * 128)
+        use = kw if p < 2 else {}
+        kc, ks, kbc, kbs = tw.bitlinear_kv_quantize(y[:, cols], H, 128, b, eps=EPS, **use, **(bkw if b == 3 else {}))
+        np.testing.assert_array_equal(host(r["codes"][p]), host(kc))
+        np.testing.assert_array_equal(host(r["scale"][p]), host(ks))
+        if b == 3:
+            np.testing.assert_array_equal(host(r["bos_codes"][p]), host(kbc))
+            np.testing.assert_array_equal(host(r["bos_scale"][p]), host(kbs))
+            o = O.kv_cache_quant(y_ref[:, cols].reshape(M, H, 128), b, EPS, pos=c["pos"] if p < 2 else None, cos=c["cos"] if p < 2 else None,
+                                 sin=c["sin"] if p < 2 else None, bos=c["bos"])
+            sl = c["slots"][c["bos"]]
+            np.testing.assert_array_equal(unpack_kv(host(r["bos_codes"][p]), H, 128, 4)[sl], o["bos_u"][c["bos"]])
+            np.testing.assert_array_equal(host(r["bos_scale"][p])[sl], o["bos_dscale"][c["bos"]])
+
+
 def test_qkv_kv_fused_full():
     """The prefill workload as the benchmark runs the fused path: M=4096, K=4096, 32 heads per part,
     Q at 4 bits with RoPE, K at 3 bits with RoPE and BOS records, V at 3 bits with BOS records, no fp32
