@@ -13,7 +13,9 @@ One step = one pass of every hot-path operation over the synthetic workloads, in
                (12 rotating copies of both matrices)
 The headline value is the W1.58A4 INT4 prefill GEMM throughput in TOPS (2*M*N*K / average kernel time,
 HIP events on the launch stream); the decode GEMV bandwidth and every kernel's time and roofline
-fraction are reported beside it. The weights are ternarized and packed once, outside the timed region.
+fraction are reported beside it. The memory-bound quantizers are also timed back to back from a HIP
+graph over input copies larger than the last-level cache (us_graph), which leaves out the dispatch gap
+that the eager sequence's events include. The weights are ternarized and packed once, outside the timed region.
 """
 from __future__ import annotations
 
@@ -389,6 +391,66 @@ def main():
     peaks["launch_floor_us"] = round(launch_us, 3)
     peaks["how_floors"] = ("graph of 24 plain streaming reads of one packed 11008x4096 matrix (11.27 MB, the "
                            "decode rotation), and of 24 launches reading 16 bytes; microseconds per launch")
+    # The eager sequence times each call between events on the launch stream, so a short quantizer's
+    # figure there also holds the dispatch gap before it (every call is issued from Python). Here each
+    # memory-bound quantizer runs back to back from a HIP graph, every launch on its own HBM copy of its
+    # input, the copies together larger than the 256 MB last-level cache, so that no launch finds its
+    # input in a cache: microseconds per launch.
+    def spread(t, n=None):
+        n = n or max(2, -(-(320 << 20) // (t.numel() * t.element_size())))    # at least 320 MiB in all
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    def per_launch_us(calls, reps=10):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for c in calls:
+                c()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps / len(calls)
+        del g
+        return us
+
+    pxs, fxs, fhs_in, axs = spread(px), spread(fx), spread(fh), spread(ax)
+    kvxs = spread(py4, 6)          # six copies of the QKV output: five other 67 MB parts between two reads of one
+    kq, kk = slice(0, kH * kD), slice(kH * kD, 2 * kH * kD)
+    kvv = slice(2 * kH * kD, 3 * kH * kD)
+    qgraph = {
+        "quant_int4_e3m2_prefill": [lambda x=x: tw.bitlinear_quantize_act(x, "int4_e3m2", eps=EPS, codes=pc6, scale=ps6)
+                                    for x in pxs],
+        "quant_int4_prefill": [lambda x=x: tw.bitlinear_quantize_act(x, "int4", eps=EPS, codes=pc4, scale=ps4)
+                               for x in pxs],
+        "quant_fp4_prefill": [lambda x=x: tw.bitlinear_quantize_act(x, "fp4", eps=EPS, codes=pcf, scale=psf)
+                              for x in pxs],
+        "quant_fp4_pow2_prefill": [lambda x=x: tw.bitlinear_quantize_act(x, "fp4_pow2", eps=EPS, codes=pcp, scale=psp)
+                                   for x in pxs],
+        "quant_int4_per_tensor_prefill": [lambda x=x: tw.bitlinear_quantize_act_per_tensor(x, "int4", eps=EPS, codes=pct,
+                                                                                          scale=pst, workspace=pws)
+                                          for x in pxs],
+        "quant_int4_e3m2_ffn": [lambda x=x: tw.bitlinear_quantize_act(x, "int4_e3m2", eps=EPS, codes=fc, scale=fs)
+                                for x in fxs],
+        "quant_int8_h": [lambda x=x: tw.bitlinear_quantize_act(x, "int8", eps=EPS, row_absmax_hint=frm, codes=fhc,
+                                                               scale=fhs) for x in fhs_in],
+        "quant_topk_int8_attn": [lambda x=x: tw.bitlinear_quantize_act(x, "int8", topk_keep=A["keep"], eps=EPS, codes=ac,
+                                                                       scale=as_, mask=am) for x in axs],
+        "kv_quant_q4_rope": [lambda x=x: tw.bitlinear_kv_quantize(x[:, kq], kH, kD, 4, eps=EPS, pos=kpos, cos=kcos,
+                                                                  sin=ksin, codes=kq_c, scale=kq_s) for x in kvxs],
+        "kv_quant_k3_rope_bos": [lambda x=x: tw.bitlinear_kv_quantize(x[:, kk], kH, kD, 3, eps=EPS, pos=kpos, cos=kcos,
+                                                                      sin=ksin, bos_slot=kslot, n_bos_slots=knslots,
+                                                                      codes=kk_c, scale=kk_s, bos_codes=kkb_c,
+                                                                      bos_scale=kkb_s) for x in kvxs],
+        "kv_quant_v3_bos": [lambda x=x: tw.bitlinear_kv_quantize(x[:, kvv], kH, kD, 3, eps=EPS, bos_slot=kslot,
+                                                                 n_bos_slots=knslots, codes=kv_c, scale=kv_s,
+                                                                 bos_codes=kvb_c, bos_scale=kvb_s) for x in kvxs],
+    }
+    q_graph_us = {n: per_launch_us(c) for n, c in qgraph.items()}
+    del pxs, fxs, fhs_in, axs, kvxs, qgraph
     # live up rows of the conditional projection (channels whose gate is positive in some row)
     live = {m: int((dgs[m] > 0).any(dim=0).sum().item()) for m in D["Ms"]}
     live_sparse = int((dgsp > 0).any(dim=0).sum().item())
@@ -493,12 +555,17 @@ def main():
                                              "in its epilogue, no fp32 output; unfused = GEMM + three KV kernels")
     for m in D["Ms"]:
         kern[f"decode_m{m}"] = dict(us=gemv_us[m], bound="hbm", gbs=gbs(dec_bytes(m), gemv_us[m]))
+    for n, us in q_graph_us.items():
+        k = kern[n]
+        k["us_graph"] = us
+        k["gbs_graph"] = k["gbs"] * k["us"] / us                 # the same algorithmic bytes
+        k["frac_graph"] = round(k["gbs_graph"] / HBM_PEAK_GBS, 4)
     for k in kern.values():
         if "tops" in k:
             k["frac"] = round(k["tops"] / k["peak"], 4)
         else:
             k["frac"] = round(k["gbs"] / HBM_PEAK_GBS, 4)
-        for f in ("us", "tops", "dense_tops", "gbs"):
+        for f in ("us", "tops", "dense_tops", "gbs", "us_graph", "gbs_graph"):
             if f in k:
                 k[f] = round(k[f], 3)
 
