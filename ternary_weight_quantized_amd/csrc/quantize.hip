@@ -173,6 +173,38 @@ __device__ __forceinline__ uint32_t code_e3m2(float v, float s) {
   return (uint32_t)(mag > 0 ? mag : 0) | ((b >> 26) & 0x20u);
 }
 
+// The E3M2 patterns of the INT4 codes of two chunks of 8 values (p, then q) through one CDNA4
+// conversion: the rounded and clamped codes are exact E3M2 values, so v_cvt_scalef32_2xpk16_bf6_f32
+// at scale 1 writes their patterns. It places element i of its first operand at code 2i and element
+// i of its second at code 2i + 1 (an in-bounds probe of the instruction on the GPU showed this), so
+// the even and the odd elements go to the two operands; codes 16..31 are not used. A rounded -0
+// becomes +0 first (the conversion keeps the sign of zero). w[0] and the low half of w[1] hold p's
+// 48 bits, the high half of w[1] and w[2] q's (code k at bits 6 k).
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ void codes_e3m2_16(const float (&p)[8], const float (&q)[8], float s, uint32_t (&w)[3]) {
+  v16f_t a = __builtin_nondeterministic_value(a), b = __builtin_nondeterministic_value(b);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = __builtin_rintf(__builtin_amdgcn_fmed3f(p[2 * j] * s, -8.f, 7.f)) + 0.0f;
+    b[j] = __builtin_rintf(__builtin_amdgcn_fmed3f(p[2 * j + 1] * s, -8.f, 7.f)) + 0.0f;
+    a[4 + j] = __builtin_rintf(__builtin_amdgcn_fmed3f(q[2 * j] * s, -8.f, 7.f)) + 0.0f;
+    b[4 + j] = __builtin_rintf(__builtin_amdgcn_fmed3f(q[2 * j + 1] * s, -8.f, 7.f)) + 0.0f;
+  }
+  const auto o = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(a, b, 1.0f);
+  w[0] = o[0]; w[1] = o[1]; w[2] = o[2];
+}
+// 48 bits of 8 E3M2 codes (lo: bits 0..31, hi: bits 32..47) at byte 6 ch of an LDS row
+__device__ __forceinline__ void put_e3m2_48(uint8_t* erow, int ch, uint32_t lo, uint32_t hi) {
+  uint8_t* d = erow + 6 * ch;
+  if ((ch & 1) == 0) {
+    *reinterpret_cast<uint32_t*>(d) = lo;
+    *reinterpret_cast<uint16_t*>(d + 4) = (uint16_t)hi;
+  } else {
+    *reinterpret_cast<uint16_t*>(d) = (uint16_t)lo;
+    *reinterpret_cast<uint32_t*>(d + 2) = (lo >> 16) | (hi << 16);
+  }
+}
+
 // Store the 4 codes (24 bits, code j at bits 6j) of elements 256g + 4 lane .. +3 of row m into the
 // tiled E3M2 layout (16 rows x 128 codes per 1536-byte tile, 96 bytes per row, code k at bits 6k):
 // four lanes make 12 bytes, written as three dwords. Every lane takes part in the shuffle; only lanes
@@ -698,27 +730,36 @@ __global__ __launch_bounds__(256) void k_quant_blk(const void* __restrict__ x, i
   if constexpr (SUM) {
     const float beta = st_val;
     const float s = bl_u2f(BL_SQRT7_BITS) / (beta + eps);
+    if constexpr (FMT == BL_ACT_INT4) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int ch = t + 256 * c;
-      if (ch >= nch) continue;                                   // whole wave pairs drop out together
-      if constexpr (FMT == BL_ACT_INT4) {
+      for (int c = 0; c < NCH; ++c) {
+        const int ch = t + 256 * c;
+        if (ch >= nch) continue;                                 // whole wave pairs drop out together
         reinterpret_cast<uint32_t*>(codes + (long)row * (K >> 1))[ch] = codes_int4_8(v[c], s);
-      } else {
-        // 8 codes x 6 bits = 6 bytes at byte 6 ch of the LDS row (code k at bits 6 k)
+      }
+    } else if constexpr (NCH == 2) {
+      // chunks 0 and 1 (8 codes x 6 bits = 6 bytes each, at byte 6 ch of the LDS row) share one
+      // conversion (longer rows, whose extra operand registers would lower the occupancy, take the
+      // arithmetic form below)
+#pragma unroll
+      for (int c = 0; c < NCH; c += 2) {
+        const int ch = t + 256 * c;
+        if (ch >= nch) continue;
+        uint32_t w[3];
+        codes_e3m2_16(v[c], v[c + 1], s, w);
+        put_e3m2_48(erow, ch, w[0], w[1] & 0xFFFFu);
+        if (ch + 256 < nch) put_e3m2_48(erow, ch + 256, (w[1] >> 16) | (w[2] << 16), w[2] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int ch = t + 256 * c;
+        if (ch >= nch) continue;
         uint32_t e[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) e[j] = code_e3m2(v[c][j], s);
-        const uint32_t lo = e[0] | (e[1] << 6) | (e[2] << 12) | (e[3] << 18) | (e[4] << 24) | (e[5] << 30);
-        const uint32_t hi = (e[5] >> 2) | (e[6] << 4) | (e[7] << 10);
-        uint8_t* d = erow + 6 * ch;
-        if ((ch & 1) == 0) {
-          *reinterpret_cast<uint32_t*>(d) = lo;
-          *reinterpret_cast<uint16_t*>(d + 4) = (uint16_t)hi;
-        } else {
-          *reinterpret_cast<uint16_t*>(d) = (uint16_t)lo;
-          *reinterpret_cast<uint32_t*>(d + 2) = (lo >> 16) | (hi << 16);
-        }
+        put_e3m2_48(erow, ch, e[0] | (e[1] << 6) | (e[2] << 12) | (e[3] << 18) | (e[4] << 24) | (e[5] << 30),
+                    (e[5] >> 2) | (e[6] << 4) | (e[7] << 10));
       }
     }
     if constexpr (E3M2) {
