@@ -179,11 +179,16 @@ def main():
         kcos, ksin = torch.from_numpy(c_np).cuda(), torch.from_numpy(s_np).cuda()
         pws = torch.empty(tw.bitlinear_quantize_per_tensor_workspace_bytes(P["M"]), dtype=torch.uint8, device="cuda")
 
+        # every prefill quantizer reads its own copy of the rows, and each repetition streams about 530 MB,
+        # more than the 256 MB last-level cache holds, so no launch finds its input there (the per-tensor
+        # call's second pass re-reads the rows its first pass just read, as it does in use)
+        pxs = [px] + [px.clone() for _ in range(4)]
+
         def quant():
             for _ in range(args.reps):
-                for fmt in ("int4", "int4_e3m2", "fp4", "fp4_pow2"):
-                    tw.bitlinear_quantize_act(px, fmt, eps=EPS)
-                tw.bitlinear_quantize_act_per_tensor(px, "int4", eps=EPS, workspace=pws)
+                for i, fmt in enumerate(("int4", "int4_e3m2", "fp4", "fp4_pow2")):
+                    tw.bitlinear_quantize_act(pxs[i], fmt, eps=EPS)
+                tw.bitlinear_quantize_act_per_tensor(pxs[4], "int4", eps=EPS, workspace=pws)
                 tw.bitlinear_quantize_act(qh, "int8", eps=EPS, row_absmax_hint=qrm)
                 tw.bitlinear_quantize_act(qax, "int8", topk_keep=A["keep"], eps=EPS)
                 tw.bitlinear_kv_quantize(qkv[:, :kH * kD], kH, kD, 4, eps=EPS, pos=kpos, cos=kcos, sin=ksin)
