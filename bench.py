@@ -609,6 +609,25 @@ def main():
                               "frac_hbm": round(gbs(b8, a8_us[m]) / HBM_PEAK_GBS, 4),
                               "live_k_slices": round(a8_live[m] / (F["N"] // 32), 4)}
 
+    # whole BitLinear layers, quantizer and matmul together: consecutive launches on one stream, so the
+    # sum of their event intervals is the layer's time on the stream (dispatch gaps included)
+    def layer(parts, ops, what):
+        us = sum(times[n] for n in parts)
+        return {"us": round(us, 3), "tops": round(tops(ops, us), 2), "kernels": parts, "what": what}
+
+    layers = {
+        "prefill_qkv_int4_fp6": layer(["quant_int4_e3m2_prefill", "gemm_a4_int4_fp6_prefill"], ops_prefill,
+                                      "per-token INT4 (E3M2 layout) + W1.58A4 GEMM on FP6 x FP4 cores"),
+        "prefill_qkv_int4_int8core": layer(["quant_int4_prefill", "gemm_a4_int4_i8_prefill"], ops_prefill,
+                                           "per-token INT4 (nibbles) + W1.58A4 GEMM on int8 cores"),
+        "prefill_qkv_fp4": layer(["quant_fp4_prefill", "gemm_a4_fp4_prefill"], ops_prefill,
+                                 "per-token FP4 E2M1 + W1.58A4 GEMM on FP4 cores"),
+        "ffn_7b": layer(["quant_int4_e3m2_ffn", "gemm_a4_glu_ffn", "quant_int8_h", "gemm_a8_down"],
+                        ops_glu + ops_down_dense,
+                        "INT4 + gate/up GEMM with ReLU^2 GLU + INT8 of h + W1.58A8 down (dense-equivalent ops)"),
+        "attn_out": layer(["quant_topk_int8_attn", "gemm_a8_oproj_residual"], ops_oproj_dense,
+                          "Top-K 50% + INT8 + W1.58A8 o_proj with the residual (dense-equivalent ops)"),
+    }
     sparsity = {"ffn_h_zero_codes": round(1 - nnz_h / (F["M"] * F["N"]), 4),
                 "attn_zero_codes": round(1 - nnz_attn / (A["M"] * A["K"]), 4),
                 "ffn_h_zero_codes_structured": round(1 - nnz_h_s / (F["M"] * F["N"]), 4),
@@ -640,6 +659,7 @@ def main():
         "measured_peaks": peaks,
         "decode_gemv": decode,
         "kernels": kern,
+        "layers": layers,
         "sparsity": sparsity,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
