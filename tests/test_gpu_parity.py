@@ -201,6 +201,58 @@ def test_quantize_fp4_rounding_boundaries(f32):
         np.testing.assert_array_equal(host(scale), d_o)
 
 
+def int4_tie_row(K, seed):
+    """A float32 row whose probe elements land x s exactly on the INT4 rounding ties k + 1/2
+    (k = -9 .. 7, so -8.5 and 7.5 meet the clip too), with s = sqrt7 / (beta + eps) the row's scale,
+    each beside its neighbours one unit in the last place away, and values that round to -0, +0 and
+    -0 itself. The probes move beta only in its last bits, so placing them again until beta no
+    longer changes settles it. Returns the row and the number of probes that sit exactly on a tie."""
+    rng = np.random.default_rng(seed)
+    row = rng.standard_normal(K).astype(np.float32)
+    ties = [np.float32(k + 0.5) for k in range(-9, 8)]
+    f = np.float32
+
+    def scale(r):
+        _, _, beta = O.quant_int4(r[None], EPS)
+        return f(O.SQRT7_F32 / f(beta[0] + f(EPS)))
+
+    s = scale(row)
+    for _ in range(10):
+        j = 0
+        for t in ties:
+            x = f(t / s)
+            for _ in range(8):                      # walk to the float whose product is the tie
+                y = f(x * s)
+                if y == t:
+                    break
+                x = np.nextafter(x, f(np.inf) if (y < t) == (s > 0) else f(-np.inf))
+            row[j:j + 3] = [np.nextafter(x, f(-np.inf)), x, np.nextafter(x, f(np.inf))]
+            j += 3
+        row[j:j + 5] = [f(-0.2) / s, -1e-30, 0.0, -0.0, f(0.49) / s]
+        s_new = scale(row)
+        if s_new == s:
+            break
+        s = s_new
+    exact = sum(int(f(row[3 * i + 1] * s) == t) for i, t in enumerate(ties))
+    return row, exact
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int4_e3m2"])
+def test_quantize_int4_rounding_ties(fmt):
+    """INT4 rounding at every tie k + 1/2 of x s and next to it, the clip at -8 and 7, and values
+    that round to -0: half to even, and the nibble and E3M2 codes equal the oracle's."""
+    torch_cuda()
+    K = 512
+    rows = np.stack([int4_tie_row(K, 77 + i)[0] for i in range(3)])
+    exact = min(int4_tie_row(K, 77 + i)[1] for i in range(3))
+    assert exact >= 12, exact                       # the probes really sit on the ties
+    c, d, _ = O.quant_int4(rows, EPS)
+    codes, scale, _ = tw.bitlinear_quantize_act(dev_f32(rows), fmt, eps=EPS)
+    got = int4_values(host(codes)) if fmt == "int4" else e3m2_values(host(codes), 3)
+    np.testing.assert_array_equal(got, c)
+    np.testing.assert_array_equal(host(scale), d)
+
+
 @pytest.mark.parametrize("fmt", ["int4", "int4_e3m2", "fp4", "fp4_pow2", "int8"])
 @pytest.mark.parametrize("f32", [False, True])
 @pytest.mark.parametrize("M,K", [(1, 256), (9, 640), (7, 768), (33, 4096), (130, 1024), (5, 8192)])
