@@ -177,3 +177,58 @@ def test_random_kv_quantize(T, H, D, bits, rope, f32):
     if bits == 3 and bos.any():
         np.testing.assert_array_equal(unpack_kv(host(bcodes), H, D, 4), ref["bos_u"][bos])
         np.testing.assert_array_equal(host(bscale), ref["bos_dscale"][bos])
+
+
+QKVCASES = _draw(12, lambda i: (int(_R.integers(1, 400)), int(_R.integers(1, 5)), 128 * int(_R.integers(1, 24)),
+                                str(_R.choice(["int4_e3m2", "fp4"])),
+                                tuple(int(b) for b in _R.choice([3, 4], size=3)), bool(_R.integers(2)),
+                                float(_R.choice([0.0, 0.05, 0.3])), bool(_R.integers(2))))
+
+
+@pytest.mark.parametrize("M,H,K,fmt,bits,rope,p_bos,want_y", QKVCASES, ids=[_id(c) for c in QKVCASES])
+def test_random_qkv_kv_fused(M, H, K, fmt, bits, rope, p_bos, want_y):
+    """The QKV GEMM with the KV-cache quantizer in its epilogue: records, scales and BOS records equal
+    the oracle's (fixed-order fp32 epilogue, then RoPE and absmax codes) and the stand-alone
+    quantizer's on the GEMM's output; Y, when written, equals the plain GEMM's."""
+    from tests.test_gpu_kvcache import _qkv_case, dev_i32
+    torch = torch_cuda()
+    rng = np.random.default_rng(39000 + M + K)
+    bos_tokens = sorted(set([0] + np.flatnonzero(rng.random(M) < p_bos).tolist())) if p_bos > 0 else []
+    c = _qkv_case(39500 + M + H + K, M, H, K, fmt, rope, bos_tokens)
+    N = c["N"]
+    kw = dict(pos=dev_i32(c["pos"]), cos=dev_f32(c["cos"]), sin=dev_f32(c["sin"])) if rope else {}
+    with_bos = bool(bos_tokens) and 3 in bits
+    bkw = dict(bos_slot=dev_i32(c["slots"]), n_bos_slots=c["nslots"]) if with_bos else {}
+    r = tw.bitlinear_gemm_w158a4_kv(fmt, c["codes"], c["scale"], K, c["packed"], c["a"], N, H, bits=bits, eps=EPS,
+                                    want_y=want_y, **kw, **bkw)
+    y = tw.bitlinear_gemm_w158a4(fmt, c["codes"], c["scale"], K, c["packed"], c["a"], N)
+    torch.cuda.synchronize()
+    xf = x_f32(c["xb"])
+    if fmt == "fp4":
+        ref = O.bitlinear_a4(xf, c["t"], c["alpha"], EPS, fmt="fp4")
+        y32 = O.dequant_f32(ref["acc"], ref["dscale"], c["alpha"], 0.5)
+    else:
+        ref = O.bitlinear_a4(xf, c["t"], c["alpha"], EPS)
+        y32 = O.dequant_f32(ref["acc"], ref["dscale"], c["alpha"])
+    np.testing.assert_array_equal(host(y).view(np.uint32), y32.view(np.uint32))
+    if want_y:
+        np.testing.assert_array_equal(host(r["y"]).view(np.uint32), y32.view(np.uint32))
+    for p in range(3):
+        b = bits[p]
+        cols = slice(p * H * 128, (p + 1) * H * 128)
+        use_rope = rope and p < 2
+        o = O.kv_cache_quant(y32[:, cols].reshape(M, H, 128), b, EPS, pos=c["pos"] if use_rope else None,
+                             cos=c["cos"] if use_rope else None, sin=c["sin"] if use_rope else None,
+                             bos=c["bos"] if (with_bos and b == 3) else None)
+        np.testing.assert_array_equal(unpack_kv(host(r["codes"][p]), H, 128, b), o["u"])
+        np.testing.assert_array_equal(host(r["scale"][p]), o["dscale"])
+        kc, ks, kbc, kbs = tw.bitlinear_kv_quantize(y[:, cols], H, 128, b, eps=EPS, **(kw if use_rope else {}),
+                                                    **(bkw if b == 3 else {}))
+        np.testing.assert_array_equal(host(r["codes"][p]), host(kc))
+        np.testing.assert_array_equal(host(r["scale"][p]), host(ks))
+        if with_bos and b == 3:
+            sl = c["slots"][c["bos"]]
+            np.testing.assert_array_equal(unpack_kv(host(r["bos_codes"][p]), H, 128, 4)[sl], o["bos_u"][c["bos"]])
+            np.testing.assert_array_equal(host(r["bos_scale"][p])[sl], o["bos_dscale"][c["bos"]])
+            np.testing.assert_array_equal(host(r["bos_codes"][p]), host(kbc))
+            np.testing.assert_array_equal(host(r["bos_scale"][p]), host(kbs))
