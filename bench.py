@@ -96,8 +96,9 @@ def main():
     t_setup = time.time()
 
     # ------------------------------------------------------------------ inputs and packed weights
-    def pack(w):
-        return tw.bitlinear_pack_ternary(torch.from_numpy(w).to(dev), EPS)
+    def pack(w, a8=False):
+        f = tw.bitlinear_pack_ternary_a8 if a8 else tw.bitlinear_pack_ternary
+        return f(torch.from_numpy(w).to(dev), EPS)
 
     P = WORKLOADS["prefill_qkv"]
     pin = workload_inputs("prefill_qkv")
@@ -124,7 +125,7 @@ def main():
     gW, gA = pack(fin["w_gate"])
     uW, uA = pack(fin["w_up"])
     uWr, _ = tw.bitlinear_pack_ternary_rows(torch.from_numpy(fin["w_up"]).to(dev), EPS)
-    dW, dA = pack(fin["w_down"])
+    dW, dA = pack(fin["w_down"], a8=True)        # the INT8 matmuls take the A8 weight layout
     wg_latent = fin["w_gate"]            # kept for the gate-sparse decode input below
     del fin
     fc = torch.empty((F["M"], 3 * F["K"] // 4), dtype=torch.uint8, device=dev)
@@ -139,7 +140,7 @@ def main():
     ain = workload_inputs("attn_out")
     ax = bf16_dev(torch, ain["x"])
     ar = torch.from_numpy(ain["residual"]).to(dev)
-    oW, oA = pack(ain["w"])
+    oW, oA = pack(ain["w"], a8=True)
     del ain
     ac = torch.empty((A["M"], A["K"]), dtype=torch.uint8, device=dev)
     as_ = torch.empty(A["M"], dtype=torch.float32, device=dev)

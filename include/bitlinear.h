@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 1
+#define BITLINEAR_ABI_VERSION 2
 
 typedef enum {
   BL_OK = 0,
@@ -63,7 +63,7 @@ typedef enum { BL_EPI_NONE = 0, BL_EPI_RESIDUAL = 1, BL_EPI_RELU2_GLU = 2 } bl_e
 typedef enum {
   BL_OP_QUANTIZE_ACT = 0, BL_OP_QUANTIZE_ACT_PER_TENSOR = 1, BL_OP_PACK_TERNARY = 2, BL_OP_PACK_TERNARY_ROWS = 3,
   BL_OP_GEMM_W158A4 = 4, BL_OP_GEMM_W158A8_SPARSE = 5, BL_OP_GEMV_DECODE = 6, BL_OP_GEMV_DECODE_GLU_CONDITIONAL = 7,
-  BL_OP_KV_QUANTIZE = 8
+  BL_OP_KV_QUANTIZE = 8, BL_OP_PACK_TERNARY_A8 = 9
 } bl_op;
 
 /* bitlinear_workspace_size: bytes of caller workspace the operation `op` needs for an [M, K] input and
@@ -194,6 +194,21 @@ bl_status bitlinear_pack_ternary(const float* d_w, int64_t N, int64_t K, float e
                                  void* d_packed, float* d_alpha,
                                  void* d_workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * bitlinear_pack_ternary_a8: the same ternary quantizer (alpha and codes exactly as
+ * bitlinear_pack_ternary) for the weights of the matmuls with INT8 activations (section 3.4,
+ * sparsification: the attention output and FFN down projections), in the A8 tile layout: the
+ * tiles, lanes and words of the layout above, with weight kk0 + q (q = 0..15) of a word in bits
+ * [8 (q % 4) + 2 (q / 4), +2). Expanding such a word to int8 bytes gives the weights in the order
+ * of the INT8 codes in memory, so the INT8 matmuls feed the codes to the matrix cores unchanged.
+ * bitlinear_gemm_w158a8_sparse and bitlinear_gemv_decode with fmt BL_ACT_INT8 take weights in this
+ * layout (and only in it); every other matmul takes the layout of bitlinear_pack_ternary.
+ * Arguments, shapes and errors as for bitlinear_pack_ternary.
+ * ------------------------------------------------------------------------------------------- */
+bl_status bitlinear_pack_ternary_a8(const float* d_w, int64_t N, int64_t K, float eps,
+                                    void* d_packed, float* d_alpha,
+                                    void* d_workspace, size_t ws_bytes, void* stream);
+
 /* Epilogue of the matmul entry points (a HOST struct; the pointers in it are device pointers).
  *   acc      exact integer sum_k code_x * code_w (FP4: sum of doubled E2M1 codes; counted in halves)
  *   sc[m]    = RN32(scale[m] * alpha)
@@ -234,7 +249,8 @@ bl_status bitlinear_gemm_w158a4(int32_t fmt, const void* d_codes, const float* d
 /* ---------------------------------------------------------------------------------------------
  * bitlinear_gemm_w158a8_sparse: Y = (Q_INT8(X) . M) Q_w(W)^T (section 3.4, sparsification,
  * paper Eq. 1) for the attention output and FFN down projections. Codes are INT8 from
- * bitlinear_quantize_act (masked entries already 0). Matrix-core work on 64-wide K slices whose
+ * bitlinear_quantize_act (masked entries already 0); the weights (and W_up of the RELU2_GLU
+ * epilogue) come from bitlinear_pack_ternary_a8. Matrix-core work on 64-wide K slices whose
  * activation codes are all zero for a 16-row group is skipped. Arguments as for the A4 GEMM.
  * ------------------------------------------------------------------------------------------- */
 bl_status bitlinear_gemm_w158a8_sparse(const void* d_codes, const float* d_scale, int64_t M, int64_t K,
@@ -245,7 +261,8 @@ bl_status bitlinear_gemm_w158a8_sparse(const void* d_codes, const float* d_scale
  * bitlinear_gemv_decode: the same products for decode batches, 1 <= M <= 8, fmt INT4 or INT8.
  * Streams every packed weight tile once from HBM. With INT8 codes a lane skips the load of its
  * 32-wide K slice of a weight tile when the codes of all M rows are zero there. Arguments as for
- * the GEMMs.
+ * the GEMMs: weights from bitlinear_pack_ternary for fmt BL_ACT_INT4, from
+ * bitlinear_pack_ternary_a8 for fmt BL_ACT_INT8.
  * ------------------------------------------------------------------------------------------- */
 bl_status bitlinear_gemv_decode(int32_t fmt, const void* d_codes, const float* d_scale,
                                 int64_t M, int64_t K,

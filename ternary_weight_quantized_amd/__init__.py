@@ -19,13 +19,14 @@ BL_IN_BF16, BL_IN_F32 = 0, 1
 BL_EPI_NONE, BL_EPI_RESIDUAL, BL_EPI_RELU2_GLU = 0, 1, 2
 OPS = {"quantize_act": 0, "quantize_act_per_tensor": 1, "pack_ternary": 2, "pack_ternary_rows": 3,
        "gemm_w158a4": 4, "gemm_w158a8_sparse": 5, "gemv_decode": 6, "gemv_decode_glu_conditional": 7,
-       "kv_quantize": 8}
+       "kv_quantize": 8, "pack_ternary_a8": 9}
 
 FORMATS = {"int4": BL_ACT_INT4, "fp4": BL_ACT_FP4_E2M1, "int8": BL_ACT_INT8, "int4_e3m2": BL_ACT_INT4_E3M2,
            "fp4_pow2": BL_ACT_FP4_E2M1_POW2}
 
 EXPORTED = (
-    "bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_pack_ternary_rows", "bitlinear_packed_bytes",
+    "bitlinear_quantize_act", "bitlinear_pack_ternary", "bitlinear_pack_ternary_rows", "bitlinear_pack_ternary_a8",
+    "bitlinear_packed_bytes",
     "bitlinear_pack_workspace_bytes", "bitlinear_gemm_w158a4", "bitlinear_gemm_w158a8_sparse",
     "bitlinear_gemv_decode", "bitlinear_gemv_decode_glu_conditional", "bitlinear_status_string",
     "bitlinear_abi_version", "bitlinear_quantize_act_per_tensor", "bitlinear_quantize_per_tensor_workspace_bytes",
@@ -110,8 +111,9 @@ def _lib():
         lib.bitlinear_noalloc_scratch_bytes.argtypes = []
         lib.bitlinear_noalloc_scratch_bytes.restype = sz
         lib.bitlinear_quantize_per_tensor_workspace_bytes.restype = sz
-        lib.bitlinear_pack_ternary_rows.argtypes = [vp, i64, i64, f32, vp, vp, vp, sz, vp]
-        lib.bitlinear_pack_ternary_rows.restype = i32
+        for name in ("bitlinear_pack_ternary_rows", "bitlinear_pack_ternary_a8"):
+            getattr(lib, name).argtypes = [vp, i64, i64, f32, vp, vp, vp, sz, vp]
+            getattr(lib, name).restype = i32
         lib.bitlinear_gemv_decode_glu_conditional.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, i64, vp, i64, vp,
                                                               i64, vp, vp]
         lib.bitlinear_gemv_decode_glu_conditional.restype = i32
@@ -307,6 +309,11 @@ def _pack(fn_name, w, eps, packed, alpha, workspace, stream):
 def bitlinear_pack_ternary(w, eps=1e-5, packed=None, alpha=None, workspace=None, stream=None):
     """Ternarize and pack w [N, K] float32 (CUDA), tiled layout. Returns (packed uint8 [N*K/4], alpha f32 [1])."""
     return _pack("bitlinear_pack_ternary", w, eps, packed, alpha, workspace, stream)
+
+
+def bitlinear_pack_ternary_a8(w, eps=1e-5, packed=None, alpha=None, workspace=None, stream=None):
+    """Ternarize and pack w [N, K] float32 (CUDA), A8 tile layout (the weights of the INT8 matmuls)."""
+    return _pack("bitlinear_pack_ternary_a8", w, eps, packed, alpha, workspace, stream)
 
 
 def bitlinear_pack_ternary_rows(w, eps=1e-5, packed=None, alpha=None, workspace=None, stream=None):

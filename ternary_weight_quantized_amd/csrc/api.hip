@@ -101,6 +101,7 @@ size_t bitlinear_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K) {
       return bitlinear_quantize_per_tensor_workspace_bytes(M);
     case BL_OP_PACK_TERNARY:
     case BL_OP_PACK_TERNARY_ROWS:
+    case BL_OP_PACK_TERNARY_A8:
       return bitlinear_pack_workspace_bytes();
     default:
       return SIZE_MAX;
@@ -225,7 +226,19 @@ bl_status bitlinear_pack_ternary(const float* d_w, int64_t N, int64_t K, float e
   if (!fits(N, K)) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ws_bytes < bitlinear_pack_workspace_bytes()) return BL_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(d_w) || !aligned16(d_packed) || !aligned16(d_workspace)) return BL_ERR_MISALIGNED;
-  return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace, false,
+  return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace, BL_PACK_TILES,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_pack_ternary_a8(const float* d_w, int64_t N, int64_t K, float eps, void* d_packed, float* d_alpha,
+                                    void* d_workspace, size_t ws_bytes, void* stream) {
+  if (!d_w || !d_packed || !d_alpha || !d_workspace) return BL_ERR_INVALID_ARGUMENT;
+  if (!eps_ok(eps)) return BL_ERR_INVALID_ARGUMENT;
+  if (N < 1 || K < 1 || K % 128 != 0 || N % 16 != 0) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (!fits(N, K)) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (ws_bytes < bitlinear_pack_workspace_bytes()) return BL_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(d_w) || !aligned16(d_packed) || !aligned16(d_workspace)) return BL_ERR_MISALIGNED;
+  return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace, BL_PACK_TILES_A8,
                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -237,7 +250,7 @@ bl_status bitlinear_pack_ternary_rows(const float* d_w, int64_t N, int64_t K, fl
   if (!fits(N, K)) return BL_ERR_UNSUPPORTED_SHAPE;
   if (ws_bytes < bitlinear_pack_workspace_bytes()) return BL_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(d_w) || !aligned16(d_packed) || !aligned16(d_workspace)) return BL_ERR_MISALIGNED;
-  return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace, true,
+  return hip_status(bl_launch_pack(d_w, (int)N, (int)K, eps, d_packed, d_alpha, d_workspace, BL_PACK_ROWS,
                                    static_cast<hipStream_t>(stream)));
 }
 

@@ -13,8 +13,10 @@ constexpr size_t bl_quantize_per_tensor_ws_bytes(long M) { return (size_t)512 * 
 hipError_t bl_launch_quantize_per_tensor(const void* x, int in_f32, int M, int K, long ldx, int fmt, float eps,
                                          void* ws, void* codes, float* scale, hipStream_t st);
 
+// packed weight layouts of bl_launch_pack
+enum { BL_PACK_TILES = 0, BL_PACK_ROWS = 1, BL_PACK_TILES_A8 = 2 };
 hipError_t bl_launch_pack(const float* w, int N, int K, float eps, void* packed, float* alpha,
-                          void* ws, bool rows, hipStream_t st);
+                          void* ws, int layout, hipStream_t st);
 
 // Arguments shared by the GEMM and the decode GEMV.
 struct bl_mm_args {

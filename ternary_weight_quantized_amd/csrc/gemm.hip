@@ -145,12 +145,15 @@ __device__ __forceinline__ int a_off(int r, int b) {
   return r * F::ROW + 16 * slot + (b & 15);
 }
 
+// one packed word (16 weights) -> four dwords of int8 values 64 t: a standard word gives k 0 2 4 6,
+// 8 10 12 14, 1 3 5 7, 9 11 13 15 (the order of expand_a_int4), an A8 word k 0..3, 4..7, 8..11,
+// 12..15 (the order of the INT8 codes in memory)
 __device__ __forceinline__ v4i expand_w_i8(uint32_t w) {
   v4i r;
-  r[0] = (int)((w << 6) & 0xC0C0C0C0u);   // k 0 2 4 6
-  r[1] = (int)((w << 4) & 0xC0C0C0C0u);   // k 8 10 12 14
-  r[2] = (int)((w << 2) & 0xC0C0C0C0u);   // k 1 3 5 7
-  r[3] = (int)(w & 0xC0C0C0C0u);          // k 9 11 13 15
+  r[0] = (int)((w << 6) & 0xC0C0C0C0u);
+  r[1] = (int)((w << 4) & 0xC0C0C0C0u);
+  r[2] = (int)((w << 2) & 0xC0C0C0C0u);
+  r[3] = (int)(w & 0xC0C0C0C0u);
   return r;
 }
 __device__ __forceinline__ v4i expand_a_int4(uint32_t p0, uint32_t p1) {
@@ -161,14 +164,9 @@ __device__ __forceinline__ v4i expand_a_int4(uint32_t p0, uint32_t p1) {
   r[3] = (int)(p1 & 0xF0F0F0F0u);         // k 9 11 13 15
   return r;
 }
-__device__ __forceinline__ v4i expand_a_int8(uint4 q) {
-  v4i r;
-  r[0] = (int)__builtin_amdgcn_perm(q.y, q.x, 0x06040200u);  // bytes 0 2 4 6
-  r[1] = (int)__builtin_amdgcn_perm(q.w, q.z, 0x06040200u);  // 8 10 12 14
-  r[2] = (int)__builtin_amdgcn_perm(q.y, q.x, 0x07050301u);  // 1 3 5 7
-  r[3] = (int)__builtin_amdgcn_perm(q.w, q.z, 0x07050301u);  // 9 11 13 15
-  return r;
-}
+// 16 INT8 codes in memory order feed the MFMA as they are: the weights of these matmuls come in the
+// A8 word layout, whose expansion is in the same k order
+__device__ __forceinline__ v4i expand_a_int8(uint4 q) { return v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w}; }
 // two packed words (32 weights) -> four dwords of E2M1 nibbles in natural k order, value 2*t
 __device__ __forceinline__ v8i expand_w_fp4(uint32_t w0, uint32_t w1) {
   v8i r;

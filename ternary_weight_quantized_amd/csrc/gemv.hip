@@ -45,14 +45,9 @@ __device__ __forceinline__ v4i expand_a_int4(uint32_t p0, uint32_t p1) {
   r[3] = (int)(p1 & 0xF0F0F0F0u);
   return r;
 }
-__device__ __forceinline__ v4i expand_a_int8(uint4 q) {
-  v4i r;
-  r[0] = (int)__builtin_amdgcn_perm(q.y, q.x, 0x06040200u);
-  r[1] = (int)__builtin_amdgcn_perm(q.w, q.z, 0x06040200u);
-  r[2] = (int)__builtin_amdgcn_perm(q.y, q.x, 0x07050301u);
-  r[3] = (int)__builtin_amdgcn_perm(q.w, q.z, 0x07050301u);
-  return r;
-}
+// INT8 codes in memory order: the weights of the INT8 products come in the A8 word layout, whose
+// expansion (expand_w_i8) is in that k order
+__device__ __forceinline__ v4i expand_a_int8(uint4 q) { return v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w}; }
 
 // One chunk of up to CH K tiles starting at kt0 (kt0 < kt_end). FULL chunks load unconditionally, so
 // the compiler can wait for each tile separately; the ragged last chunk clamps its addresses and

@@ -8,8 +8,9 @@
 // significands are summed per exponent in 64-bit integers (LDS per block, then global atomics),
 // so the sum is independent of order; one thread turns the 256 bins into the correctly rounded
 // double of the exact total and divides by N*K. The pack kernel then writes one 32-bit word
-// (16 weights of one row) per thread in the tiled layout of the public header (16 x 128 tiles), or
-// in the row-major layout used by the gathered (conditional) up projection.
+// (16 weights of one row) per thread in the tiled layout of the public header (16 x 128 tiles, with
+// the field order of the 4-bit-activation matmuls or of the INT8 ones), or in the row-major layout
+// used by the gathered (conditional) up projection.
 #include "bl_common.h"
 #include "bl_kernels.h"
 
@@ -49,7 +50,18 @@ __global__ __launch_bounds__(256) void k_alpha(const unsigned long long* __restr
   if (threadIdx.x == 0) *alpha = (float)(S / count);
 }
 
+// Bit position of weight q (0..15) of a packed 32-bit word. Standard words (every matmul with 4-bit
+// activations): q < 8 at 4 q, q >= 8 at 4 (q - 8) + 2, so that masking the word with 0xCCCCCCCC after
+// shifting it by 2 or 0 gives the E2M1 nibbles of q = 0..7 and 8..15 in order. A8 words (the int8
+// matmuls with INT8 activations): q at 8 (q % 4) + 2 (q / 4), so that masking it with 0xC0C0C0C0
+// after shifting it by 6, 4, 2 or 0 gives the int8 bytes of q = 0..3, 4..7, 8..11 and 12..15 in
+// order, the order of the INT8 codes themselves.
+__device__ __forceinline__ int field_pos(int q, bool a8) {
+  return a8 ? 8 * (q & 3) + 2 * (q >> 2) : (q < 8 ? 4 * q : 4 * (q - 8) + 2);
+}
+
 // One thread per packed 32-bit word: tile (kt, G) of 16 rows x 128 columns, lane L = 16 g + r, word i.
+template <bool A8>
 __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int N, int K, float eps,
                                               const float* __restrict__ alpha, uint32_t* __restrict__ out) {
   const long wid = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -74,8 +86,7 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int N
       const int q = 4 * c + j;                                   // k offset inside the word
       const int code = bl_roundclip(vv[j] / den, -1.f, 1.f);     // IEEE division, half-even
       const uint32_t f = (uint32_t)code & 3u;                    // 0 -> 00, +1 -> 01, -1 -> 11
-      const int pos = q < 8 ? 4 * q : 4 * (q - 8) + 2;
-      word |= f << pos;
+      word |= f << field_pos(q, A8);
     }
   }
   out[wid] = word;
@@ -99,8 +110,7 @@ __global__ __launch_bounds__(256) void k_pack_rows(const float* __restrict__ w, 
     for (int j = 0; j < 4; ++j) {
       const int q = 4 * c + j;
       const int code = bl_roundclip(vv[j] / den, -1.f, 1.f);
-      const int pos = q < 8 ? 4 * q : 4 * (q - 8) + 2;
-      word |= ((uint32_t)code & 3u) << pos;
+      word |= ((uint32_t)code & 3u) << field_pos(q, false);
     }
   }
   out[wid] = word;
@@ -109,7 +119,7 @@ __global__ __launch_bounds__(256) void k_pack_rows(const float* __restrict__ w, 
 }  // namespace
 
 hipError_t bl_launch_pack(const float* w, int N, int K, float eps, void* packed, float* alpha,
-                          void* ws, bool rows, hipStream_t st) {
+                          void* ws, int layout, hipStream_t st) {
   unsigned long long* bins = static_cast<unsigned long long*>(ws);
   hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, st, bins, 256);
   const long n = (long)N * K;
@@ -118,11 +128,12 @@ hipError_t bl_launch_pack(const float* w, int N, int K, float eps, void* packed,
   hipLaunchKernelGGL(k_abs_bins, dim3((unsigned)blocks), dim3(256), 0, st, w, n, bins);
   hipLaunchKernelGGL(k_alpha, dim3(1), dim3(256), 0, st, bins, (double)n, alpha);
   const long nwords = n / 16;
-  if (rows)
-    hipLaunchKernelGGL(k_pack_rows, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st, w, N, K, eps, alpha,
-                       static_cast<uint32_t*>(packed));
+  const dim3 grid((unsigned)((nwords + 255) / 256));
+  if (layout == BL_PACK_ROWS)
+    hipLaunchKernelGGL(k_pack_rows, grid, dim3(256), 0, st, w, N, K, eps, alpha, static_cast<uint32_t*>(packed));
+  else if (layout == BL_PACK_TILES_A8)
+    hipLaunchKernelGGL((k_pack<true>), grid, dim3(256), 0, st, w, N, K, eps, alpha, static_cast<uint32_t*>(packed));
   else
-    hipLaunchKernelGGL(k_pack, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st, w, N, K, eps, alpha,
-                       static_cast<uint32_t*>(packed));
+    hipLaunchKernelGGL((k_pack<false>), grid, dim3(256), 0, st, w, N, K, eps, alpha, static_cast<uint32_t*>(packed));
   return hipGetLastError();
 }

@@ -58,8 +58,9 @@ def main():
 
     tw.library()
 
-    def pack(w):
-        return tw.bitlinear_pack_ternary(torch.from_numpy(w).cuda(), EPS)
+    def pack(w, a8=False):
+        f = tw.bitlinear_pack_ternary_a8 if a8 else tw.bitlinear_pack_ternary
+        return f(torch.from_numpy(w).cuda(), EPS)
 
     work = []
     if args.gemm:
@@ -102,7 +103,7 @@ def main():
         fin = workload_inputs("ffn_7b")
         gW, gA = pack(fin["w_gate"])
         uW, uA = pack(fin["w_up"])
-        dW, dA = pack(fin["w_down"])
+        dW, dA = pack(fin["w_down"], a8=True)       # the INT8 matmuls take the A8 weight layout
         fx = dev_bf16(torch, fin["x"])
         uWr = None
         if args.decode:
@@ -145,7 +146,7 @@ def main():
         ain = workload_inputs("attn_out")
         ax = dev_bf16(torch, ain["x"])
         ar = torch.from_numpy(ain["residual"]).cuda()
-        oW, oA = pack(ain["w"])
+        oW, oA = pack(ain["w"], a8=True)
         del ain
         ac, as_, _ = tw.bitlinear_quantize_act(ax, "int8", topk_keep=A["keep"], eps=EPS)
         fy = torch.empty((F["M"], F["K"]), dtype=torch.float32, device="cuda")

@@ -21,7 +21,7 @@ hipError_t bl_launch_quantize(const void*, int, int M, int K, long, int, int, fl
                               uint32_t*, hipStream_t) { note(M, K, -1); return hipSuccess; }
 hipError_t bl_launch_quantize_per_tensor(const void*, int, int M, int K, long, int, float, void*, void*, float*,
                                          hipStream_t) { note(M, K, -1); return hipSuccess; }
-hipError_t bl_launch_pack(const float*, int N, int K, float, void*, float*, void*, bool, hipStream_t) {
+hipError_t bl_launch_pack(const float*, int N, int K, float, void*, float*, void*, int, hipStream_t) {
   note(-1, K, N); return hipSuccess;
 }
 hipError_t bl_launch_gemm(const bl_mm_args& a, hipStream_t) { note(a.M, a.K, a.N); return hipSuccess; }
@@ -95,6 +95,10 @@ int main() {
   // ---- pack
   OK(bitlinear_pack_ternary(F, 32, 256, eps, P, F, P, bitlinear_pack_workspace_bytes(), nullptr));
   OK(bitlinear_pack_ternary_rows(F, 11008, 4096, eps, P, F, P, bitlinear_pack_workspace_bytes(), nullptr));
+  OK(bitlinear_pack_ternary_a8(F, 4096, 11008 & ~int64_t(127), eps, P, F, P, bitlinear_pack_workspace_bytes(), nullptr));
+  ERR(bitlinear_pack_ternary_a8(F, 24, 256, eps, P, F, P, bitlinear_pack_workspace_bytes(), nullptr), BL_ERR_UNSUPPORTED_SHAPE);
+  ERR(bitlinear_pack_ternary_a8(nullptr, 32, 256, eps, P, F, P, bitlinear_pack_workspace_bytes(), nullptr),
+      BL_ERR_INVALID_ARGUMENT);
   ERR(bitlinear_pack_ternary(F, 10, 256, eps, P, F, P, bitlinear_pack_workspace_bytes(), nullptr), BL_ERR_UNSUPPORTED_SHAPE);
   ERR(bitlinear_pack_ternary(F, BIG & ~int64_t(15), 256, eps, P, F, P, bitlinear_pack_workspace_bytes(), nullptr),
       BL_ERR_UNSUPPORTED_SHAPE);

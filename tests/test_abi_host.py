@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_version_and_status_strings():
-    assert tw.bitlinear_abi_version() == 1
+    assert tw.bitlinear_abi_version() == 2
     assert tw.bitlinear_status_string(0) == "ok"
     assert "argument" in tw.bitlinear_status_string(1)
     assert tw.bitlinear_packed_bytes(4096, 11008) == 4096 * 11008 // 4
@@ -61,7 +61,7 @@ def test_workspace_size_query():
     for M in (1, 8, 4096, 1 << 20):
         assert tw.bitlinear_workspace_size("quantize_act_per_tensor", M, 0, 4096) == \
             tw.bitlinear_quantize_per_tensor_workspace_bytes(M)
-    for op in ("pack_ternary", "pack_ternary_rows"):
+    for op in ("pack_ternary", "pack_ternary_rows", "pack_ternary_a8"):
         assert tw.bitlinear_workspace_size(op, 0, 11008, 4096) == tw.bitlinear_pack_workspace_bytes()
     for op in ("quantize_act", "gemm_w158a4", "gemm_w158a8_sparse", "gemv_decode", "gemv_decode_glu_conditional",
                "kv_quantize"):
@@ -148,12 +148,29 @@ def test_format_restrictions():
     assert _mm("bitlinear_gemm_w158a4", fmt=4) == 1          # FP4 power-of-two codes run as fmt 1
 
 
-def test_packed_layout_decoder_roundtrip():
+@pytest.mark.parametrize("a8", [False, True])
+def test_packed_layout_decoder_roundtrip(a8):
     rng = np.random.default_rng(0)
     codes = rng.integers(-1, 2, (48, 768)).astype(np.int8)
-    packed = pack_reference(codes)
+    packed = pack_reference(codes, a8)
     assert packed.size == 48 * 768 // 4
-    np.testing.assert_array_equal(unpack_ternary(packed, 48, 768), codes)
+    np.testing.assert_array_equal(unpack_ternary(packed, 48, 768, a8), codes)
+
+
+def test_a8_word_expands_in_code_order():
+    """The A8 word layout is the one whose int8 expansion (the word shifted left by 6, 4, 2, 0 and
+    masked with 0xC0C0C0C0) yields the 16 weights as bytes in k order, 64 t each, the order of
+    16 INT8 codes in memory; the standard layout yields k 0 2 4 6, 8 10 12 14, 1 3 5 7, 9 11 13 15."""
+    rng = np.random.default_rng(1)
+    for a8, order in ((True, list(range(16))), (False, [0, 2, 4, 6, 8, 10, 12, 14, 1, 3, 5, 7, 9, 11, 13, 15])):
+        for _ in range(20):
+            t = rng.integers(-1, 2, (16, 128)).astype(np.int8)
+            w = pack_reference(t, a8).view("<u4")[0]                 # row 0, k 0..15
+            out = []
+            for sh in (6, 4, 2, 0):
+                d = (int(w) << sh) & 0xC0C0C0C0
+                out += [np.int8(np.uint8((d >> (8 * b)) & 0xFF)) for b in range(4)]
+            np.testing.assert_array_equal(np.array(out, dtype=np.int64), 64 * t[0, order].astype(np.int64))
 
 
 def test_packed_layout_decoder_positions():

@@ -54,10 +54,12 @@ def to_dev(x):
     return dev_f32(x) if x.dtype == np.float32 else dev_bf16(x)
 
 
-def packed_weights(seed, N, K, sigma=0.02):
+def packed_weights(seed, N, K, sigma=0.02, a8=False):
+    """Latent weights, the oracle's ternary codes and alpha, and the library's packed weights: the
+    standard layout, or with a8 the layout of the matmuls with INT8 activations."""
     w = latent_weights(seed, N, K, sigma)
     codes, alpha = O.ternarize(w, EPS)
-    packed, a = tw.bitlinear_pack_ternary(dev_f32(w), EPS)
+    packed, a = (tw.bitlinear_pack_ternary_a8 if a8 else tw.bitlinear_pack_ternary)(dev_f32(w), EPS)
     return w, codes, alpha, packed, a
 
 
@@ -68,6 +70,20 @@ def test_pack_ternary(N, K):
     w, codes, alpha, packed, a = packed_weights(100 + N, N, K)
     assert host(a)[0] == alpha, (host(a)[0], alpha)
     np.testing.assert_array_equal(unpack_ternary(host(packed), N, K), codes)
+
+
+@pytest.mark.parametrize("N,K", [(16, 256), (32, 384), (48, 768), (160, 4096), (2048, 2048)])
+def test_pack_ternary_a8(N, K):
+    """The A8 tile layout holds the oracle's codes (decoded from the header's description) and the
+    same alpha as the standard layout."""
+    torch_cuda()
+    w, codes, alpha, packed, a = packed_weights(150 + N, N, K, a8=True)
+    assert host(a)[0] == alpha
+    np.testing.assert_array_equal(unpack_ternary(host(packed), N, K, a8=True), codes)
+    _, _, _, p_std, a_std = packed_weights(150 + N, N, K)
+    assert host(a_std)[0] == alpha
+    if N * K >= 16 * 256:
+        assert not np.array_equal(host(packed), host(p_std))       # the two layouts differ
 
 
 @pytest.mark.parametrize("N,K", [(16, 256), (32, 384), (48, 768), (160, 4096)])
@@ -470,7 +486,7 @@ def test_gemm_a8_sparse(M, N, K, keep_frac):
     torch_cuda()
     x = make_x(5000 + M, M, K, f32=True)
     x[M // 2:, : K // 2] = 0.0                      # whole zero K slices exercise the skip path
-    _, t, alpha, packed, a = packed_weights(5100 + N, N, K)
+    _, t, alpha, packed, a = packed_weights(5100 + N, N, K, a8=True)
     keep = -1 if keep_frac is None else int(keep_frac * K)
     codes, scale, c, d, _ = _quant(x, "int8", keep)
     y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N)
@@ -488,7 +504,7 @@ def test_gemm_a8_structured_zero_slices(M, N, K, epi):
     dead = rng.random(((M + 15) // 16, K // 128)) < 0.5
     dead[0, 0], dead[1, 0], dead[2, 0], dead[3, 0] = True, False, True, False   # strip 0, step 0
     x[np.repeat(np.repeat(dead, 16, 0), 128, 1)[:M]] = 0.0
-    _, t, alpha, packed, a = packed_weights(5700 + N, N, K)
+    _, t, alpha, packed, a = packed_weights(5700 + N, N, K, a8=True)
     codes, scale, c, d, _ = _quant(x, "int8", -1)
     acc = O.gemm_int(c, t)
     if epi == "none":
@@ -499,7 +515,7 @@ def test_gemm_a8_structured_zero_slices(M, N, K, epi):
         y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, residual=dev_f32(r))
         assert_y_close(host(y), acc, d, alpha, residual=r)
     else:
-        _, tu, au, pu, dau = packed_weights(5900 + N, N, K)
+        _, tu, au, pu, dau = packed_weights(5900 + N, N, K, a8=True)
         h = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, up_packed=pu, up_alpha=dau)
         h_ref = O.relu2_glu(O.dequant_f32(acc, d, alpha), O.dequant_f32(O.gemm_int(c, tu), d, au))
         np.testing.assert_array_equal(host(h).view(np.uint32), h_ref.view(np.uint32))
@@ -511,13 +527,13 @@ def test_gemm_a8_residual_and_relu2(M, N, K):
     torch = torch_cuda()
     x = make_x(5200 + M, M, K, f32=True, special=False)
     x[1] = 0.0
-    _, t, alpha, packed, a = packed_weights(5300 + N, N, K)
+    _, t, alpha, packed, a = packed_weights(5300 + N, N, K, a8=True)
     codes, scale, c, d, _ = _quant(x, "int8", K // 2)
     acc = O.gemm_int(c, t)
     r = normal(5400, M * N).reshape(M, N).astype(np.float32)
     y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, residual=dev_f32(r))
     assert_y_close(host(y), acc, d, alpha, residual=r)
-    _, tu, au, pu, dau = packed_weights(5500 + N, N, K)
+    _, tu, au, pu, dau = packed_weights(5500 + N, N, K, a8=True)
     rowmax = torch.zeros(M, dtype=torch.float32, device="cuda")
     h = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, up_packed=pu, up_alpha=dau, row_absmax=rowmax)
     h_ref = O.relu2_glu(O.dequant_f32(acc, d, alpha), O.dequant_f32(O.gemm_int(c, tu), d, au))
@@ -536,7 +552,7 @@ def test_decode(fmt, M, N, K):
     if fmt == "int8":
         x = x_f32(x)
         x[:, 256:1024] = 0.0                      # zero slices: their weight loads are skipped
-    _, t, alpha, packed, a = packed_weights(6100 + N, N, K)
+    _, t, alpha, packed, a = packed_weights(6100 + N, N, K, a8=fmt == "int8")
     codes, scale, c, d, _ = _quant(x, fmt, -1)
     y = tw.bitlinear_gemv_decode(fmt, codes, scale, K, packed, a, N)
     assert_y_close(host(y), O.gemm_int(c, t), d, alpha)
@@ -547,13 +563,13 @@ def test_decode_epilogues(fmt):
     torch = torch_cuda()
     M, N, K = 6, 96, 1024
     x = x_f32(make_x(6200, M, K, special=False))
-    _, t, alpha, packed, a = packed_weights(6300, N, K)
+    _, t, alpha, packed, a = packed_weights(6300, N, K, a8=fmt == "int8")
     codes, scale, c, d, _ = _quant(x, fmt, -1)
     acc = O.gemm_int(c, t)
     r = normal(6400, M * N).reshape(M, N).astype(np.float32)
     y = tw.bitlinear_gemv_decode(fmt, codes, scale, K, packed, a, N, residual=dev_f32(r))
     assert_y_close(host(y), acc, d, alpha, residual=r)
-    _, tu, au, pu, dau = packed_weights(6500, N, K)
+    _, tu, au, pu, dau = packed_weights(6500, N, K, a8=fmt == "int8")
     rowmax = torch.zeros(M, dtype=torch.float32, device="cuda")
     h = tw.bitlinear_gemv_decode(fmt, codes, scale, K, packed, a, N, up_packed=pu, up_alpha=dau, row_absmax=rowmax)
     h_ref = O.relu2_glu(O.dequant_f32(acc, d, alpha), O.dequant_f32(O.gemm_int(c, tu), d, au))
@@ -642,7 +658,8 @@ def test_matmul_extreme_codes_at_longest_k(kind, fmt):
     M = 8 if kind == "gemv" else 20
     w = -np.ones((N, K), dtype=np.float32)
     t, a = O.ternarize(w, EPS)
-    packed, alpha = tw.bitlinear_pack_ternary(torch.from_numpy(w).cuda(), EPS)
+    pack = tw.bitlinear_pack_ternary_a8 if fmt == "int8" else tw.bitlinear_pack_ternary
+    packed, alpha = pack(torch.from_numpy(w).cuda(), EPS)
     assert alpha.item() == a
     rows, nbytes = tw.codes_shape(fmt, M, K)
     if fmt == "int4_e3m2":
@@ -678,7 +695,7 @@ def test_a8_sums_beyond_float32_integers(kind):
     c = rng.integers(100, 128, (M, K)).astype(np.int8)
     w = np.where(rng.random((N, K)) < 0.1, -1.0, 1.0).astype(np.float32)     # mostly +1: sums near 2.6e7
     t, a = O.ternarize(w, EPS)
-    packed, alpha = tw.bitlinear_pack_ternary(torch.from_numpy(w).cuda(), EPS)
+    packed, alpha = tw.bitlinear_pack_ternary_a8(torch.from_numpy(w).cuda(), EPS)
     assert alpha.item() == a
     codes = torch.from_numpy(c.view(np.uint8)).cuda()
     d = (rng.random(M) * 0.01 + 1e-3).astype(np.float32)

@@ -84,7 +84,7 @@ def _quantized(x, fmt, keep=-1):
     return codes, scale, c, d, 1.0
 
 
-def _check_epilogue(call, epi, M, N, K, c, d, unit, t, alpha, seed):
+def _check_epilogue(call, epi, M, N, K, c, d, unit, t, alpha, seed, a8=False):
     """Run call(**kw) for the epilogue and compare with the oracle."""
     torch = torch_cuda()
     acc = O.gemm_int(c, t)
@@ -94,7 +94,7 @@ def _check_epilogue(call, epi, M, N, K, c, d, unit, t, alpha, seed):
         r = normal(seed, M * N).reshape(M, N).astype(np.float32)
         assert_y_close(host(call(residual=dev_f32(r))), acc, d, alpha, unit, residual=r)
     else:
-        _, tu, au, pu, dau = packed_weights(seed + 1, N, K)
+        _, tu, au, pu, dau = packed_weights(seed + 1, N, K, a8=a8)
         rowmax = torch.full((M,), 7.0, dtype=torch.float32, device="cuda")
         h = call(up_packed=pu, up_alpha=dau, row_absmax=rowmax)
         h_ref = O.relu2_glu(O.dequant_f32(acc, d, alpha, unit), O.dequant_f32(O.gemm_int(c, tu), d, au, unit))
@@ -116,10 +116,10 @@ def test_random_gemm_a4(M, N, K, fmt, epi):
 def test_random_gemm_a8(M, N, K, epi, keep):
     torch_cuda()
     x = make_x(33000 + M + K, M, K, f32=True, special=epi != "glu")
-    _, t, alpha, packed, a = packed_weights(33500 + N + K, N, K)
+    _, t, alpha, packed, a = packed_weights(33500 + N + K, N, K, a8=True)
     codes, scale, c, d, unit = _quantized(x, "int8", keep)
     _check_epilogue(lambda **kw: tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, **kw),
-                    epi, M, N, K, c, d, unit, t, alpha, 34000 + M)
+                    epi, M, N, K, c, d, unit, t, alpha, 34000 + M, a8=True)
 
 
 @pytest.mark.parametrize("M,N,K,fmt,epi", DCASES, ids=[_id(c) for c in DCASES])
@@ -128,10 +128,10 @@ def test_random_decode(M, N, K, fmt, epi):
     x = make_x(35000 + M + K, M, K, special=False)
     if fmt == "int8":
         x = x_f32(x)
-    _, t, alpha, packed, a = packed_weights(35500 + N + K, N, K)
+    _, t, alpha, packed, a = packed_weights(35500 + N + K, N, K, a8=fmt == "int8")
     codes, scale, c, d, unit = _quantized(x, fmt)
     _check_epilogue(lambda **kw: tw.bitlinear_gemv_decode(fmt, codes, scale, K, packed, a, N, **kw),
-                    epi, M, N, K, c, d, unit, t, alpha, 36000 + M)
+                    epi, M, N, K, c, d, unit, t, alpha, 36000 + M, a8=fmt == "int8")
 
 
 @pytest.mark.parametrize("M,N,K", CCASES, ids=[_id(c) for c in CCASES])

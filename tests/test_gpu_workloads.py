@@ -26,9 +26,11 @@ def sample_rows(M, n=256, seed=0, tile=128):
     return np.array(sorted(rows))
 
 
-def weights(w):
+def weights(w, a8=False):
+    """The oracle's codes and alpha, and the library's packed weights (a8: the layout of the matmuls
+    with INT8 activations)."""
     codes, alpha = O.ternarize(w, EPS)
-    packed, a = tw.bitlinear_pack_ternary(dev_f32(w), EPS)
+    packed, a = (tw.bitlinear_pack_ternary_a8 if a8 else tw.bitlinear_pack_ternary)(dev_f32(w), EPS)
     assert host(a)[0] == alpha
     return codes, alpha, packed, a
 
@@ -115,7 +117,7 @@ def test_ffn_7b_sampled():
     M, K, N = wl["M"], wl["K"], wl["N"]
     tg, ag, pg, dag = weights(inp["w_gate"])
     tu, au, pu, dau = weights(inp["w_up"])
-    td, ad, pd, dad = weights(inp["w_down"])
+    td, ad, pd, dad = weights(inp["w_down"], a8=True)
     codes, scale, _ = tw.bitlinear_quantize_act(dev_bf16(inp["x"]), "int4_e3m2", eps=EPS)
     rowmax = torch.empty(M, dtype=torch.float32, device="cuda")
     h = tw.bitlinear_gemm_w158a4("int4_e3m2", codes, scale, K, pg, dag, N, up_packed=pu, up_alpha=dau,
@@ -146,7 +148,7 @@ def test_decode_a8_ffn_full(M):
     K, N = wl["K"], wl["N"]
     tg, ag, pg, dag = weights(inp["w_gate"])
     tu, au, pu, dau = weights(inp["w_up"])
-    td, ad, pd, dad = weights(inp["w_down"])
+    td, ad, pd, dad = weights(inp["w_down"], a8=True)
     xb = inp["x"][:M]
     codes, scale, _ = tw.bitlinear_quantize_act(dev_bf16(xb), "int4", eps=EPS)
     rowmax = torch.zeros(M, dtype=torch.float32, device="cuda")
@@ -166,7 +168,7 @@ def test_attn_out_sampled():
     wl = WORKLOADS["attn_out"]
     inp = workload_inputs("attn_out")
     M, K, N, keep = wl["M"], wl["K"], wl["N"], wl["keep"]
-    t, alpha, packed, a = weights(inp["w"])
+    t, alpha, packed, a = weights(inp["w"], a8=True)
     codes, scale, mask = tw.bitlinear_quantize_act(dev_bf16(inp["x"]), "int8", topk_keep=keep, eps=EPS,
                                                    want_mask=True)
     r = dev_f32(inp["residual"])
@@ -236,7 +238,7 @@ def test_largest_index_space_topk_a8_sampled():
     gen = torch.Generator(device="cuda").manual_seed(4321)
     x = torch.randn((M, K), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     r = torch.randn((M, N), generator=gen, device="cuda", dtype=torch.float32)
-    t, alpha, packed, a = weights(latent_weights(78, N, K))
+    t, alpha, packed, a = weights(latent_weights(78, N, K), a8=True)
     codes, scale, mask = tw.bitlinear_quantize_act(x, "int8", topk_keep=keep, eps=EPS, want_mask=True)
     y = tw.bitlinear_gemm_w158a8_sparse(codes, scale, K, packed, a, N, residual=r)
     torch.cuda.synchronize()
