@@ -97,11 +97,12 @@ def test_quantize_validation(kw, status):
     (dict(eps=0.0), 1), (dict(N=10), 2), (dict(K=300), 2), (dict(N=0), 2),
     (dict(wsb=100), 4), (dict(w=P_MIS), 3), (dict(packed=P_MIS), 3),
 ])
-def test_pack_validation(kw, status):
+@pytest.mark.parametrize("entry", ["bitlinear_pack_ternary", "bitlinear_pack_ternary_a8", "bitlinear_pack_ternary_rows"])
+def test_pack_validation(kw, status, entry):
     a = dict(w=P, N=32, K=256, eps=1e-5, packed=P, alpha=P, ws=P, wsb=4096)
     a.update(kw)
-    st = tw.library().bitlinear_pack_ternary(a["w"], a["N"], a["K"], a["eps"], a["packed"], a["alpha"], a["ws"],
-                                             a["wsb"], None)
+    st = getattr(tw.library(), entry)(a["w"], a["N"], a["K"], a["eps"], a["packed"], a["alpha"], a["ws"],
+                                      a["wsb"], None)
     assert st == status
 
 
