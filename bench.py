@@ -286,7 +286,8 @@ def main():
              "quant_int4_per_tensor_prefill",
              "quant_int4_e3m2_ffn", "gemm_a4_glu_ffn", "quant_int8_h", "gemm_a8_down", "quant_topk_int8_attn",
              "gemm_a8_oproj_residual", "gemm_a8_down_structured", "gemm_a8_oproj_residual_structured",
-             "kv_quant_q4_rope", "kv_quant_k3_rope_bos", "kv_quant_v3_bos", "gemm_a4_qkv_kv_fused"] + \
+             "kv_quant_q4_rope", "kv_quant_k3_rope_bos", "kv_quant_v3_bos", "gemm_a4_qkv_kv_fused",
+             "decode_read_floor_graph"] + \
         [f"decode_m{m}_graph" for m in D["Ms"]] + \
         [f"decode_glu_m{m}_graph" for m in D["Ms"]] + [f"decode_glu_cond_m{m}_graph" for m in D["Ms"]] + \
         ["decode_glu_cond_gate_sparse_m1_graph"] + \
@@ -333,6 +334,7 @@ def main():
         tw.bitlinear_gemm_w158a4_kv("int4_e3m2", pc6, ps6, P["K"], pW, pA, P["N"], kH, bits=(4, 3, 3), eps=EPS,
                                     pos=kpos, cos=kcos, sin=ksin, bos_slot=kslot, n_bos_slots=knslots,
                                     out=kv_fused); mark()
+        read_graph.replay(); mark()                # the read floor where the decode graphs run
         for m in D["Ms"]:
             graphs[m].replay(); mark()
         for m in D["Ms"]:
@@ -376,7 +378,7 @@ def main():
                for m in D["Ms"]}
     peaks = measured_peaks(torch, dev)
 
-    def graph_us(g, reps=20):
+    def graph_us(g, reps=20, launches=ROTATE):
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -385,13 +387,25 @@ def main():
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps / ROTATE
+        return e0.elapsed_time(e1) * 1e3 / reps / launches
     read_us, launch_us = graph_us(read_graph), graph_us(launch_graph)
+    # Inside the step the decode graphs follow the prefill GEMMs and take longer than alone; the read floor
+    # is replayed there too (read_step_us), and every decode graph is timed again here, in the same quiet
+    # phase as the floors, so that each floor fraction compares launches timed under the same conditions.
+    read_step_us = times["decode_read_floor_graph"] / ROTATE
+    q_gemv = {m: graph_us(graphs[m]) for m in D["Ms"]}
+    q_glu = {m: graph_us(glu_graphs[m], launches=ROTATE_GLU) for m in D["Ms"]}
+    q_cond = {m: graph_us(cond_graphs[m], launches=ROTATE_GLU) for m in D["Ms"]}
+    q_cond_sparse = graph_us(cond_sparse_graph, launches=ROTATE_GLU)
+    q_a8 = {m: graph_us(a8_graphs[m]) for m in D["Ms"]}
     peaks["decode_read_floor_us"] = round(read_us, 3)
+    peaks["decode_read_floor_in_step_us"] = round(read_step_us, 3)
     peaks["decode_read_floor_gbs"] = round(D["N"] * D["K"] / 4 / (read_us * 1e-6) / 1e9, 1)
     peaks["launch_floor_us"] = round(launch_us, 3)
     peaks["how_floors"] = ("graph of 24 plain streaming reads of one packed 11008x4096 matrix (11.27 MB, the "
-                           "decode rotation), and of 24 launches reading 16 bytes; microseconds per launch")
+                           "decode rotation), and of 24 launches reading 16 bytes; microseconds per launch, "
+                           "after the timed region; the read graph also runs inside the step, right before "
+                           "the decode graphs (decode_read_floor_in_step_us)")
     # The eager sequence times each call between events on the launch stream, so a short quantizer's
     # figure there also holds the dispatch gap before it (every call is issued from Python). Here each
     # memory-bound quantizer runs back to back from a HIP graph, every launch on its own HBM copy of its
@@ -555,7 +569,8 @@ def main():
                                         what="INT4-on-FP6 QKV GEMM with RoPE and the Q4/K3/V3 (+BOS) KV quantizer "
                                              "in its epilogue, no fp32 output; unfused = GEMM + three KV kernels")
     for m in D["Ms"]:
-        kern[f"decode_m{m}"] = dict(us=gemv_us[m], bound="hbm", gbs=gbs(dec_bytes(m), gemv_us[m]))
+        kern[f"decode_m{m}"] = dict(us=gemv_us[m], bound="hbm", gbs=gbs(dec_bytes(m), gemv_us[m]),
+                                    us_quiet=q_gemv[m], gbs_quiet=gbs(dec_bytes(m), q_gemv[m]))
     for n, us in q_graph_us.items():
         k = kern[n]
         k["us_graph"] = us
@@ -566,7 +581,7 @@ def main():
             k["frac"] = round(k["tops"] / k["peak"], 4)
         else:
             k["frac"] = round(k["gbs"] / HBM_PEAK_GBS, 4)
-        for f in ("us", "tops", "dense_tops", "gbs", "us_graph", "gbs_graph"):
+        for f in ("us", "tops", "dense_tops", "gbs", "us_graph", "gbs_graph", "us_quiet", "gbs_quiet"):
             if f in k:
                 k[f] = round(k[f], 3)
 
@@ -580,9 +595,17 @@ def main():
                           "(prefill_qkv M=4096 K=4096 N=12288)",
                 "avg_kernel_us": round(head_us, 3),
                 "algorithmic": f"2*M*N*K = {ops_prefill:.4g} ops per launch"}
-    decode = {f"m{m}": {"us": round(gemv_us[m], 3), "gbs": round(gbs(dec_bytes(m), gemv_us[m]), 1),
-                        "frac_hbm": round(gbs(dec_bytes(m), gemv_us[m]) / HBM_PEAK_GBS, 4),
-                        "frac_read_floor": round(read_us / gemv_us[m], 4)} for m in D["Ms"]}
+    # us / gbs / frac_hbm: inside the step; *_quiet: the same graph alone, beside the floors
+    def quiet(d, b, us_q):
+        d.update({"us_quiet": round(us_q, 3), "gbs_quiet": round(gbs(b, us_q), 1),
+                  "frac_hbm_quiet": round(gbs(b, us_q) / HBM_PEAK_GBS, 4)})
+        return d
+
+    decode = {f"m{m}": quiet({"us": round(gemv_us[m], 3), "gbs": round(gbs(dec_bytes(m), gemv_us[m]), 1),
+                              "frac_hbm": round(gbs(dec_bytes(m), gemv_us[m]) / HBM_PEAK_GBS, 4),
+                              "frac_read_floor": round(read_us / q_gemv[m], 4),
+                              "frac_read_floor_in_step": round(read_step_us / gemv_us[m], 4)},
+                             dec_bytes(m), q_gemv[m]) for m in D["Ms"]}
     glu_w = F["N"] * F["K"] / 4
 
     def glu_bytes(m, rows_up):
@@ -590,25 +613,29 @@ def main():
 
     for m in D["Ms"]:
         b_full, b_cond = glu_bytes(m, F["N"]), glu_bytes(m, live[m])
-        decode[f"glu_full_m{m}"] = {"us": round(glu_us[m], 3), "gbs": round(gbs(b_full, glu_us[m]), 1),
-                                    "frac_hbm": round(gbs(b_full, glu_us[m]) / HBM_PEAK_GBS, 4)}
-        decode[f"glu_conditional_m{m}"] = {
+        decode[f"glu_full_m{m}"] = quiet({"us": round(glu_us[m], 3), "gbs": round(gbs(b_full, glu_us[m]), 1),
+                                          "frac_hbm": round(gbs(b_full, glu_us[m]) / HBM_PEAK_GBS, 4)},
+                                         b_full, q_glu[m])
+        decode[f"glu_conditional_m{m}"] = quiet({
             "us": round(cond_us[m], 3), "gbs": round(gbs(b_cond, cond_us[m]), 1),
             "frac_hbm": round(gbs(b_cond, cond_us[m]) / HBM_PEAK_GBS, 4),
-            "live_up_rows": round(live[m] / F["N"], 4), "speedup_vs_fused": round(glu_us[m] / cond_us[m], 3)}
+            "live_up_rows": round(live[m] / F["N"], 4), "speedup_vs_fused": round(glu_us[m] / cond_us[m], 3),
+            "speedup_vs_fused_quiet": round(q_glu[m] / q_cond[m], 3)}, b_cond, q_cond[m])
     b_sp = glu_bytes(1, live_sparse)
-    decode["glu_conditional_gate_sparse_m1"] = {
+    decode["glu_conditional_gate_sparse_m1"] = quiet({
         "us": round(cond_sparse_us, 3), "gbs": round(gbs(b_sp, cond_sparse_us), 1),
         "frac_hbm": round(gbs(b_sp, cond_sparse_us) / HBM_PEAK_GBS, 4),
         "live_up_rows": round(live_sparse / F["N"], 4), "speedup_vs_fused": round(glu_us[1] / cond_sparse_us, 3),
+        "speedup_vs_fused_quiet": round(q_glu[1] / q_cond_sparse, 3),
         "input": "gate weights with a seeded share of the token's live channels negated, 32.5% left live "
-                 "(the 67.5% gate sparsity the pages report for 7B); the fused GLU reads every row either way"}
+                 "(the 67.5% gate sparsity the pages report for 7B); the fused GLU reads every row either way"},
+        b_sp, q_cond_sparse)
 
     for m in D["Ms"]:
         b8 = a8_live[m] * 32 * F["K"] / 4 + m * F["N"] + 4 * m + 4 + 4 * m * F["K"]
-        decode[f"a8_m{m}"] = {"us": round(a8_us[m], 3), "gbs": round(gbs(b8, a8_us[m]), 1),
-                              "frac_hbm": round(gbs(b8, a8_us[m]) / HBM_PEAK_GBS, 4),
-                              "live_k_slices": round(a8_live[m] / (F["N"] // 32), 4)}
+        decode[f"a8_m{m}"] = quiet({"us": round(a8_us[m], 3), "gbs": round(gbs(b8, a8_us[m]), 1),
+                                    "frac_hbm": round(gbs(b8, a8_us[m]) / HBM_PEAK_GBS, 4),
+                                    "live_k_slices": round(a8_live[m] / (F["N"] // 32), 4)}, b8, q_a8[m])
 
     # whole BitLinear layers, quantizer and matmul together: consecutive launches on one stream, so the
     # sum of their event intervals is the layer's time on the stream (dispatch gaps included)
