@@ -362,15 +362,14 @@ __device__ __forceinline__ void kv_epilogue_row(const bl_kv_epi& kv, int m, bool
       }
     }
   }
-  uint32_t mx = 0u;
+  // |x| through the float maximum's absolute-value source modifier, one instruction per value (the
+  // values are finite, where this equals the largest magnitude bit pattern, +0 for -0)
+  float mf = 0.f;
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint32_t u = bl_f2u(o[t][v]) & 0x7FFFFFFFu;
-      mx = u > mx ? u : mx;
-    }
-  mx = bl_max_across_rows(mx);
+    for (int v = 0; v < 4; ++v) mf = fmaxf(mf, fabsf(o[t][v]));
+  const uint32_t mx = bl_max_across_rows(bl_f2u(mf));
   const float gamma = bl_u2f(mx);
   const float den = gamma + kv.eps;
   const int r = lane & 15;
